@@ -1,0 +1,241 @@
+"""Benchmark of the mHC layer forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: mhc_pre (RMSNorm, projection, gates, Sinkhorn,
+aggregation) -> the given sublayer output Y -> mhc_post (mixing +
+broadcast-add) -> mhc_amax over the layer's maps.  Default workload: T = 16384
+tokens (batch 4 x seq 4096), n = 4 streams, d = 4096, bf16 state.
+
+Prints ONE JSON line (stdout) with tokens/s, the achieved HBM bandwidth on
+algorithmic bytes, the roofline of the dominant entry point (timed live with
+HIP events on the stream the kernels run on) and the CPU oracle's rate on a
+bounded sample.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor figure
+METRIC = "mHC fwd tokens/sec + achieved HBM GB/s (n=4, d=4096, bf16, 1 GPU)"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(T, n, d, sbytes):
+    """Bytes each entry point must move per call: one pass over its tensors,
+    phi read once.  pre: X in, h and H out, phi; post: X, Y, the 20 mixing /
+    write values per token in, X' out; amax (one layer): H_res in, amax out."""
+    m = n * n + 2 * n
+    pre = T * (n * d * sbytes + d * sbytes + 4 * m) + n * d * m * 4 + 4 * m
+    post = T * (n * d * sbytes + d * sbytes + 4 * (n * n + n) + n * d * sbytes)
+    amax = T * (4 * n * n + 4)
+    return {"mhc_pre": pre, "mhc_post": post, "mhc_amax": amax}
+
+
+def traffic_bytes(path, workload, entry):
+    """HBM bytes per launch of an entry point measured with rocprofv3
+    counters, or None when absent or when the kernel source changed since."""
+    import hashlib
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload, {}).get(entry)
+        if not rec or not rec.get("valid", False):
+            return None
+        h = hashlib.sha256()
+        for p in rec["sources"]:
+            with open(os.path.join(ROOT, p), "rb") as f:
+                h.update(f.read())
+        return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(w, seconds_target=15.0):
+    """The oracle (single-threaded C++, double) on the first tokens of the
+    same workload: mhc_pre + mhc_post per token."""
+    import numpy as np
+
+    import oracle
+    import synth
+    o = oracle.load()
+    phi, bias = synth.make_params(w)
+    probe = 8
+    Xs, Ys = synth.make_state(w, probe), synth.make_sublayer_out(w, probe)
+    t0 = time.perf_counter()
+    r = o.pre(Xs, phi, bias, w.alpha, eps=w.eps, t_max=w.t_max)
+    o.post(Xs, Ys, r["H"].astype(np.float32))
+    per_tok = (time.perf_counter() - t0) / probe
+    ntok = int(max(probe, min(w.T, seconds_target / max(per_tok, 1e-9))))
+    Xs, Ys = synth.make_state(w, ntok), synth.make_sublayer_out(w, ntok)
+    t0 = time.perf_counter()
+    r = o.pre(Xs, phi, bias, w.alpha, eps=w.eps, t_max=w.t_max)
+    o.post(Xs, Ys, r["H"].astype(np.float32))
+    dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {ntok} of {w.T} tokens of {w.name}, mhc_pre + mhc_post, fp64, "
+                      f"{dt:.1f} s on one host thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="layer_bf16_T16384_d4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters (optional)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the forward needs no "
+              f"communication: tokens shard across GPUs with phi replicated).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mhc_hyper_connections_amd as mhc
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mhc.load_library()
+    w = synth.WORKLOADS[args.workload]
+    if w.layers != 1:
+        raise SystemExit("bench.py times single-layer workloads")
+    T, n, d = w.T, w.n, w.d
+    sbytes = 2 if w.dtype == synth.BF16 else 4
+    log(f"workload {w.name}: T={T} n={n} d={d} {'bf16' if sbytes == 2 else 'fp32'}; generating inputs")
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    X = dev(synth.make_state(w))
+    Y = dev(synth.make_sublayer_out(w))
+    phi, bias = (dev(a) for a in synth.make_params(w))
+    m = n * n + 2 * n
+    h = torch.empty((T, d), dtype=X.dtype, device="cuda")
+    H = torch.empty((T, m), dtype=torch.float32, device="cuda")
+    Xo = torch.empty_like(X)
+    amax = torch.empty(T, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, mhc.pre_workspace_size(T, n, d, w.dtype)), dtype=torch.uint8, device="cuda")
+    H1 = H.view(1, T, m)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log("inputs resident; warming up")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mhc.pre(X, phi, bias, alpha=w.alpha, eps=w.eps, t_max=w.t_max, h=h, H=H, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        mhc.post(X, Y, H, out=Xo, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        mhc.amax(H1, n, out_amax=amax, want_all=False, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    # A plain copy of known size (X -> X', one read and one write of the
+    # state): the practical HBM ceiling, and the reference that scales the
+    # rocprofv3 byte counters.
+    copy_bytes = 2 * X.numel() * X.element_size()
+    for _ in range(3):
+        torch.mul(X, 1, out=Xo)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cev[0].record(stream)
+    for _ in range(5):
+        torch.mul(X, 1, out=Xo)
+    cev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_GBps = copy_bytes * 5 / (cev[0].elapsed_time(cev[1]) * 1e-3) / 1e9
+    log(f"plain copy of the state: {copy_GBps:.0f} GB/s")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(K):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = evs[0][0].elapsed_time(evs[K - 1][3])
+    per = {"mhc_pre": [], "mhc_post": [], "mhc_amax": []}
+    for e in evs:
+        per["mhc_pre"].append(e[0].elapsed_time(e[1]))
+        per["mhc_post"].append(e[1].elapsed_time(e[2]))
+        per["mhc_amax"].append(e[2].elapsed_time(e[3]))
+    ms_step = total_ms / K
+    tokens_per_s = T / (ms_step * 1e-3)
+    algo = algorithmic_bytes(T, n, d, sbytes)
+    step_bytes = sum(algo.values())
+    kernels = {}
+    for name, ts in per.items():
+        avg_ms = float(np.mean(ts))
+        kernels[name] = {"avg_us": avg_ms * 1e3, "median_us": float(np.median(ts)) * 1e3,
+                         "algorithmic_bytes": algo[name],
+                         "GBps": algo[name] / (avg_ms * 1e-3) / 1e9,
+                         "frac_of_peak": algo[name] / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    traffic = traffic_bytes(args.traffic_json, w.name, dominant)
+    kd = kernels[dominant]
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": kd["GBps"] / HBM_PEAK_GBPS, "traffic": traffic,
+                "algorithmic_bytes_per_launch": kd["algorithmic_bytes"], "avg_launch_us": kd["avg_us"]}
+    log(f"{ms_step * 1e3:.1f} us/step, {tokens_per_s / 1e6:.2f} M tokens/s; "
+        + ", ".join(f"{k} {v['avg_us']:.1f} us ({v['GBps']:.0f} GB/s)" for k, v in kernels.items()))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w)
+        log(f"oracle: {cpu['value']:.1f} tokens/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sbytes == 2 else "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "n": n, "d": d, "t_max": w.t_max,
+                   "step": "mhc_pre + mhc_post + mhc_amax (one layer), Y given",
+                   "parallelism": "single GPU"},
+        "achieved_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "achieved_frac_of_hbm_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": step_bytes,
+        "copy_GBps": copy_GBps,
+        "wall_s_timed_region": t_wall,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

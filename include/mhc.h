@@ -1,0 +1,161 @@
+/*
+ * libmhc -- the mHC (Manifold-Constrained Hyper-Connections) layer forward on
+ * AMD Instinct MI355X (gfx950), as a plain C ABI.
+ *
+ * The layer widens the residual state of every token to n streams of d
+ * values, X (n x d), and wraps a sublayer F:
+ *     x_hat = RMSNorm(vec(X))                      (over all n*d values)
+ *     logits = alpha_blk * (x_hat . phi) + bias    (phi: n*d x (n*n + 2n))
+ *     H_pre = sigmoid(l_pre), H_post = 2 sigmoid(l_post),
+ *     H_res = Sinkhorn-Knopp(exp(Mat(l_res)))      (t_max passes: columns, then rows)
+ *     h = H_pre . X          -> F -> Y = F(h)
+ *     X' = H_res X + H_post^T Y
+ * Sources: V. Dubrov, "DeepSeek mHC: Manifold-Constrained Hyper-Connections"
+ * (slavadubrov.com), sections "Kernmechanismen" (Eq. 3), "Sinkhorn-Knopp-
+ * projectie", "Details van de parameterisatie"; "mHC" study notes on
+ * DeepSeek-V4 (t6page.pages.dev), equations dsv4-mhc-rmsnorm,
+ * dsv4-mhc-a-tilde/b-tilde/c-tilde, dsv4-mhc-sinkhorn-init, dsv4-mhc-sinkhorn,
+ * dsv4-mhc-gate, dsv4-mhc-hc-update, table tbl-dsv4-mhc-kernels.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers to tensors are DEVICE pointers (hipMalloc / torch CUDA memory);
+ *    the mhc_params pointer is a HOST pointer.  The caller owns every buffer;
+ *    the library never allocates or frees device memory.
+ *  - Layouts are dense row-major:
+ *      X, X_out  [T, n, d]   stream i of token t at X + (t*n + i)*d
+ *      h, Y      [T, d]
+ *      phi       [n*d, m]    fp32, m = n*n + 2n, row k multiplies vec(X)[k]
+ *                            (vec stacks the streams: k = i*d + j); columns
+ *                            pre (n) | res (n*n, row-major, row = output
+ *                            stream) | post (n)
+ *      bias      [m]         fp32, same column order as phi
+ *      H         [T, m]      fp32 maps, same column order: H_pre | H_res | H_post
+ *    The state dtype (X, h, Y, X_out) is MHC_FP32 or MHC_BF16; phi, bias and
+ *    H are always fp32, arithmetic is fp32 on the device.
+ *  - stream is a hipStream_t passed as void*; NULL is the default stream.
+ *    Work is enqueued asynchronously on it; calls return before it runs.
+ *  - Errors: arguments are checked on the host before anything is enqueued
+ *    and a non-zero mhc_status is returned without touching device memory.
+ *    A failed launch returns MHC_ERR_HIP.  Faults during execution surface at
+ *    the caller's next synchronisation.  NaN and Inf propagate; they are not
+ *    checked.  No entry point throws or aborts.
+ *  - Device support: n in {1, 2, 4}; d a multiple of 8; tensor base pointers
+ *    16-byte aligned.  T = 0 is a valid no-op.
+ *  - Results are bitwise reproducible for fixed inputs and shapes: every
+ *    reduction runs in a fixed order and no floating-point atomics are used.
+ *  - The library keeps no mutable state between calls apart from a cache of
+ *    device attributes; calls from several host threads are safe.
+ */
+#ifndef MHC_H
+#define MHC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_ABI_VERSION 1
+
+typedef enum mhc_status {
+  MHC_OK = 0,
+  MHC_ERR_NULL = 1,         /* a required pointer is NULL */
+  MHC_ERR_SHAPE = 2,        /* T, n, d, L, t_max or eps out of range, or sizes overflow */
+  MHC_ERR_DTYPE = 3,        /* unknown state dtype */
+  MHC_ERR_ALIGN = 4,        /* a tensor base pointer is not 16-byte aligned */
+  MHC_ERR_UNSUPPORTED = 5,  /* valid for the method but not built for the device (n = 3, d % 8 != 0) */
+  MHC_ERR_ALIAS = 6,        /* an output overlaps an input other than the permitted exact alias */
+  MHC_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than mhc_pre_workspace_size() */
+  MHC_ERR_HIP = 8           /* a HIP runtime call or a kernel launch failed */
+} mhc_status;
+
+typedef enum mhc_dtype { MHC_FP32 = 0, MHC_BF16 = 1 } mhc_dtype;
+
+/* Shape and hyperparameters of one mHC layer.  t_max = 20 and alpha = 0.01 at
+ * initialisation are the pages' values ("mHC" notes, key hyperparameters);
+ * eps sits under the square root of the RMSNorm (the pages give 1e-20, the
+ * workloads here use 1e-6). */
+typedef struct mhc_params {
+  int64_t T;          /* tokens, >= 0 */
+  int32_t n;          /* streams: 1, 2 or 4 */
+  int32_t d;          /* values per stream, multiple of 8 */
+  int32_t dtype;      /* mhc_dtype of X, h, Y, X_out */
+  int32_t t_max;      /* Sinkhorn-Knopp passes, 0 .. 1000 */
+  float eps;          /* RMSNorm epsilon, finite, >= 0 */
+  float alpha_pre;    /* gate scalars of the three maps */
+  float alpha_res;
+  float alpha_post;
+} mhc_params;
+
+/* ---- mhc_pre: RMSNorm + projection + gates + Sinkhorn + aggregation --------
+ * Computes, per token, the maps H (fp32 [T, m]) and the sublayer input
+ * h = H_pre . X ([T, d], state dtype) from X ([T, n, d]).  Defined by the
+ * "mHC" notes, eqs. dsv4-mhc-rmsnorm, a/b/c-tilde, sinkhorn-init, sinkhorn,
+ * gate; aggregation by Dubrov, "Kernmechanismen", Eq. 3 (the F(H_pre x_l)
+ * term).  The RMS division is applied after the projection,
+ * (x . phi) / r, which is the same value in exact arithmetic (the pages'
+ * "reorder RMSNorm" fusion).
+ *   X         in   [T, n, d] state dtype
+ *   phi       in   [n*d, m] fp32
+ *   bias      in   [m] fp32
+ *   h         out  [T, d] state dtype; must not overlap any input
+ *   H         out  [T, m] fp32; must not overlap any input or h
+ *   workspace in/out scratch of at least mhc_pre_workspace_size(p) bytes,
+ *             16-byte aligned, overlapping nothing else; its contents on entry
+ *             are ignored and on return are unspecified.  May be NULL only if
+ *             the size query returns 0.
+ * Returns MHC_ERR_WORKSPACE when workspace_bytes is too small. */
+mhc_status mhc_pre(const mhc_params* p, const void* X, const float* phi, const float* bias,
+                   void* h, float* H, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device scratch mhc_pre needs for these parameters (0 if p is
+ * invalid).  The amount depends only on T, n and d. */
+size_t mhc_pre_workspace_size(const mhc_params* p);
+
+/* ---- mhc_post: stream mixing + broadcast-add --------------------------------
+ * X_out[t, i, :] = sum_j H_res[t, i, j] X[t, j, :] + H_post[t, i] Y[t, :]
+ * (Dubrov, "Kernmechanismen", Eq. 3; "mHC" notes eq. dsv4-mhc-hc-update and
+ * the fused Post-Res kernel of table tbl-dsv4-mhc-kernels).  One pass over
+ * the state: reads X, Y and the maps once and writes X_out once.
+ *   X      in   [T, n, d] state dtype
+ *   Y      in   [T, d] state dtype (the sublayer output F(h))
+ *   H      in   [T, m] fp32 maps as written by mhc_pre (H_pre is not read)
+ *   X_out  out  [T, n, d] state dtype; may be exactly X (in place); any other
+ *               overlap with X, Y or H is MHC_ERR_ALIAS. */
+mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const float* H,
+                    void* X_out, void* stream);
+
+/* ---- mhc_amax: composite-map Amax Gain Magnitude ---------------------------
+ * For each token, P = H_res,L-1 ... H_res,0 (each layer multiplies the running
+ * product from the left) and
+ *     gain_fwd = max_i sum_j |P_ij|   (largest absolute row sum)
+ *     gain_bwd = max_j sum_i |P_ij|   (largest absolute column sum)
+ *     amax     = max(gain_fwd, gain_bwd)
+ * (Dubrov, "Het probleem van de samengestelde map"; "mHC" notes, section on
+ * HC's composite mapping).  L = 0 gives P = I.
+ *   H_stack    in   [L, T, m] fp32 (each layer's H as written by mhc_pre)
+ *   amax, gain_fwd, gain_bwd   out [T] fp32, each may be NULL
+ *   composite  out  [T, n, n] fp32 row-major, may be NULL
+ * Outputs must not overlap H_stack or one another. */
+mhc_status mhc_amax(int64_t T, int32_t n, int32_t L, const float* H_stack, float* amax,
+                    float* gain_fwd, float* gain_bwd, float* composite, void* stream);
+
+/* ---- mhc_gelu_half: the synthetic sublayer of the layer-stack workload ------
+ * Y = 0.5 * GELU(h) = 0.5 * h * Phi(h) elementwise (exact erf form), in the
+ * state dtype.  Stands in for attention / MLP so that a many-layer stack can
+ * run without a GEMM; it is not part of the mHC method.
+ *   h in [count], Y out [count]; Y may be exactly h, other overlap is an error. */
+mhc_status mhc_gelu_half(int64_t count, int32_t dtype, const void* h, void* Y, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* mhc_status_string(mhc_status status);
+
+/* MHC_ABI_VERSION of the loaded library. */
+int mhc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H */

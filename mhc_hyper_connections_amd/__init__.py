@@ -1,0 +1,18 @@
+"""mhc_hyper_connections_amd: the mHC layer forward on AMD Instinct MI355X (gfx950).
+
+The product is ``libmhc.so``, a C-ABI library of hand-written HIP kernels
+(declared in ``include/mhc.h``).  This package is its thin Python binding:
+
+    h, H = mhc.pre(X, phi, bias, alpha=(a_pre, a_res, a_post), eps=1e-6, t_max=20)
+    Y    = F(h)                                   # the caller's sublayer
+    Xn   = mhc.post(X, Y, H)                      # or out=X for in place
+    a    = mhc.amax(H_stack, n)                   # composite-map Amax over layers
+
+Tensors are torch device tensors: X [T, n, d] and h, Y [T, d] in float32 or
+bfloat16; phi [n*d, n*n+2n], bias [n*n+2n] and H [T, n*n+2n] in float32.
+"""
+from ._binding import (EXPORTS, LIB_PATH, MHC_BF16, MHC_FP32, MhcError, Params, amax, gelu_half,
+                       load_library, make_params, post, pre, pre_workspace_size)
+
+__all__ = ["pre", "post", "amax", "gelu_half", "pre_workspace_size", "load_library", "make_params",
+           "Params", "MhcError", "MHC_FP32", "MHC_BF16", "LIB_PATH", "EXPORTS"]

@@ -1,0 +1,184 @@
+"""ctypes binding of libmhc's C ABI (include/mhc.h): argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI; this module only
+turns torch tensors into device pointers, allocates outputs the caller did not
+pass, and raises on a non-zero status.  There is no CPU fallback: without the
+built ``libmhc.so`` the import of any entry point fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmhc.so")
+
+MHC_FP32, MHC_BF16 = 0, 1
+STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_DTYPE", 4: "MHC_ERR_ALIGN",
+          5: "MHC_ERR_UNSUPPORTED", 6: "MHC_ERR_ALIAS", 7: "MHC_ERR_WORKSPACE", 8: "MHC_ERR_HIP"}
+EXPORTS = ["mhc_pre", "mhc_pre_workspace_size", "mhc_post", "mhc_amax", "mhc_gelu_half",
+           "mhc_status_string", "mhc_abi_version"]
+
+
+class MhcError(RuntimeError):
+    """A libmhc entry point returned a non-zero mhc_status."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    """mirror of struct mhc_params"""
+    _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("t_max", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("alpha_pre", ctypes.c_float), ("alpha_res", ctypes.c_float), ("alpha_post", ctypes.c_float)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmhc.so (cached).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libmhc is not built ({path} missing); run __graft_entry__.build() or "
+                           f"python mhc_hyper_connections_amd/build.py")
+    lib = ctypes.CDLL(path)
+    lib.mhc_pre.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.mhc_pre.restype = ctypes.c_int
+    lib.mhc_pre_workspace_size.argtypes = [ctypes.POINTER(Params)]
+    lib.mhc_pre_workspace_size.restype = ctypes.c_size_t
+    lib.mhc_post.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P]
+    lib.mhc_post.restype = ctypes.c_int
+    lib.mhc_amax.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P]
+    lib.mhc_amax.restype = ctypes.c_int
+    lib.mhc_gelu_half.argtypes = [ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
+    lib.mhc_gelu_half.restype = ctypes.c_int
+    lib.mhc_status_string.argtypes = [ctypes.c_int]
+    lib.mhc_status_string.restype = ctypes.c_char_p
+    lib.mhc_abi_version.argtypes = []
+    lib.mhc_abi_version.restype = ctypes.c_int
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        text = load_library().mhc_status_string(status).decode()
+        raise MhcError(fn, status, text)
+
+
+def make_params(T, n, d, dtype, t_max=20, eps=1e-6, alpha=(0.01, 0.01, 0.01)) -> Params:
+    a = tuple(float(v) for v in alpha)
+    return Params(int(T), int(n), int(d), int(dtype), int(t_max), float(eps), a[0], a[1], a[2])
+
+
+# ---- torch front end ---------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MHC_FP32
+    if t.dtype == torch.bfloat16:
+        return MHC_BF16
+    raise TypeError(f"state tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libmhc works on device tensors only; move the tensors to the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("libmhc expects contiguous tensors")
+
+
+def pre_workspace_size(T, n, d, dtype=MHC_BF16) -> int:
+    p = make_params(T, n, d, dtype)
+    return int(load_library().mhc_pre_workspace_size(ctypes.byref(p)))
+
+
+def pre(X, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, h=None, H=None, workspace=None,
+        stream=None):
+    """mhc_pre: returns (h [T, d] state dtype, H [T, m] fp32)."""
+    torch = _torch()
+    T, n, d = X.shape
+    m = n * n + 2 * n
+    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha)
+    lib = load_library()
+    if h is None:
+        h = torch.empty((T, d), dtype=X.dtype, device=X.device)
+    if H is None:
+        H = torch.empty((T, m), dtype=torch.float32, device=X.device)
+    need = int(lib.mhc_pre_workspace_size(ctypes.byref(p)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _need_device(X, phi, bias, h, H, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mhc_pre", lib.mhc_pre(ctypes.byref(p), _ptr(X), _ptr(phi), _ptr(bias), _ptr(h), _ptr(H),
+                                  _ptr(workspace), ws_bytes, _stream(stream, X.device)))
+    return h, H
+
+
+def post(X, Y, H, out=None, stream=None):
+    """mhc_post: returns X_out [T, n, d] (``out`` may be X itself)."""
+    torch = _torch()
+    T, n, d = X.shape
+    p = make_params(T, n, d, _dtype_code(X))
+    if out is None:
+        out = torch.empty_like(X)
+    _need_device(X, Y, H, out)
+    lib = load_library()
+    _check("mhc_post", lib.mhc_post(ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(H), _ptr(out),
+                                    _stream(stream, X.device)))
+    return out
+
+
+def amax(H_stack, n, out_amax=None, gain_fwd=None, gain_bwd=None, composite=None, want_all=True, stream=None):
+    """mhc_amax over H_stack [L, T, m]: returns dict of the requested outputs."""
+    torch = _torch()
+    L, T, m = H_stack.shape
+    dev = H_stack.device
+    if out_amax is None:
+        out_amax = torch.empty(T, dtype=torch.float32, device=dev)
+    if want_all:
+        gain_fwd = torch.empty(T, dtype=torch.float32, device=dev) if gain_fwd is None else gain_fwd
+        gain_bwd = torch.empty(T, dtype=torch.float32, device=dev) if gain_bwd is None else gain_bwd
+        composite = torch.empty((T, n, n), dtype=torch.float32, device=dev) if composite is None else composite
+    _need_device(H_stack, out_amax, gain_fwd, gain_bwd, composite)
+    lib = load_library()
+    _check("mhc_amax", lib.mhc_amax(T, n, L, _ptr(H_stack), _ptr(out_amax), _ptr(gain_fwd), _ptr(gain_bwd),
+                                    _ptr(composite), _stream(stream, dev)))
+    return {"amax": out_amax, "gain_fwd": gain_fwd, "gain_bwd": gain_bwd, "composite": composite}
+
+
+def gelu_half(h, out=None, stream=None):
+    """The stack workload's sublayer: out = 0.5 GELU(h), state dtype."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(h)
+    _need_device(h, out)
+    lib = load_library()
+    _check("mhc_gelu_half", lib.mhc_gelu_half(h.numel(), _dtype_code(h), _ptr(h), _ptr(out),
+                                              _stream(stream, h.device)))
+    return out

@@ -1,0 +1,172 @@
+// The C ABI of libmhc: host-side argument checks, then dispatch to the HIP
+// kernels on the caller's stream.  Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/mhc.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxT = (int64_t{1} << 31) - 1;
+constexpr int kMaxD = 1 << 20;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+size_t state_bytes(int32_t dtype) { return dtype == MHC_BF16 ? 2 : 4; }
+
+// Common checks of mhc_params; on success fills the element counts.
+mhc_status check_params(const mhc_params* p) {
+  if (!p) return MHC_ERR_NULL;
+  if (p->T < 0 || p->T > kMaxT) return MHC_ERR_SHAPE;
+  if (p->n < 1 || p->n > 16) return MHC_ERR_SHAPE;
+  if (p->d < 1 || p->d > kMaxD) return MHC_ERR_SHAPE;
+  if (p->t_max < 0 || p->t_max > 1000) return MHC_ERR_SHAPE;
+  if (!std::isfinite(p->eps) || p->eps < 0.0f) return MHC_ERR_SHAPE;
+  if (!std::isfinite(p->alpha_pre) || !std::isfinite(p->alpha_res) || !std::isfinite(p->alpha_post))
+    return MHC_ERR_SHAPE;
+  if (p->dtype != MHC_FP32 && p->dtype != MHC_BF16) return MHC_ERR_DTYPE;
+  if (p->n != 1 && p->n != 2 && p->n != 4) return MHC_ERR_UNSUPPORTED;
+  if (p->d % 8 != 0) return MHC_ERR_UNSUPPORTED;
+  // Element counts must fit comfortably in 64-bit byte offsets.
+  const double elems = static_cast<double>(p->T) * p->n * p->d;
+  if (elems * 4.0 > 9.0e18) return MHC_ERR_SHAPE;
+  return MHC_OK;
+}
+
+mhc::DeviceInfo device_info() {
+  // Per-device attribute cache; the only state the library keeps.
+  static std::mutex mu;
+  static int cus[64] = {0};
+  mhc::DeviceInfo info;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  info.device = dev;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && dev < 64) {
+    if (cus[dev] == 0) {
+      int v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+      cus[dev] = v;
+    }
+    info.num_cus = cus[dev];
+  }
+  return info;
+}
+
+mhc_status from_hip(hipError_t e) { return e == hipSuccess ? MHC_OK : MHC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int mhc_abi_version(void) { return MHC_ABI_VERSION; }
+
+const char* mhc_status_string(mhc_status s) {
+  switch (s) {
+    case MHC_OK: return "ok";
+    case MHC_ERR_NULL: return "a required pointer is NULL";
+    case MHC_ERR_SHAPE: return "a size or hyperparameter is out of range";
+    case MHC_ERR_DTYPE: return "unknown state dtype (expected MHC_FP32 or MHC_BF16)";
+    case MHC_ERR_ALIGN: return "a tensor base pointer is not 16-byte aligned";
+    case MHC_ERR_UNSUPPORTED: return "shape not supported on the device (n must be 1, 2 or 4; d a multiple of 8)";
+    case MHC_ERR_ALIAS: return "an output overlaps an input";
+    case MHC_ERR_WORKSPACE: return "workspace missing or too small";
+    case MHC_ERR_HIP: return "a HIP call or kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t mhc_pre_workspace_size(const mhc_params* p) {
+  if (check_params(p) != MHC_OK) return 0;
+  return mhc::pre_workspace_bytes(p->T, p->n, p->d);
+}
+
+mhc_status mhc_pre(const mhc_params* p, const void* X, const float* phi, const float* bias, void* h, float* H,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  mhc_status st = check_params(p);
+  if (st != MHC_OK) return st;
+  if (p->T == 0) return MHC_OK;
+  if (!X || !phi || !bias || !h || !H) return MHC_ERR_NULL;
+  const size_t need = mhc::pre_workspace_bytes(p->T, p->n, p->d);
+  if (need > 0 && !workspace) return MHC_ERR_WORKSPACE;
+  if (workspace_bytes < need) return MHC_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(h) || !aligned16(H) || !aligned16(phi) || !aligned16(bias)) return MHC_ERR_ALIGN;
+  if (need > 0 && !aligned16(workspace)) return MHC_ERR_ALIGN;
+  const int m = p->n * p->n + 2 * p->n;
+  const size_t sb = state_bytes(p->dtype);
+  const Range rX = range_of(X, static_cast<size_t>(p->T) * p->n * p->d * sb);
+  const Range rphi = range_of(phi, static_cast<size_t>(p->n) * p->d * m * 4);
+  const Range rb = range_of(bias, static_cast<size_t>(m) * 4);
+  const Range rh = range_of(h, static_cast<size_t>(p->T) * p->d * sb);
+  const Range rH = range_of(H, static_cast<size_t>(p->T) * m * 4);
+  const Range rw = range_of(workspace, need);
+  if (overlap(rh, rX) || overlap(rh, rphi) || overlap(rh, rb) || overlap(rh, rH)) return MHC_ERR_ALIAS;
+  if (overlap(rH, rX) || overlap(rH, rphi) || overlap(rH, rb)) return MHC_ERR_ALIAS;
+  if (need > 0 && (overlap(rw, rX) || overlap(rw, rphi) || overlap(rw, rb) || overlap(rw, rh) || overlap(rw, rH)))
+    return MHC_ERR_ALIAS;
+  const mhc::DeviceInfo dev = device_info();
+  return from_hip(mhc::launch_pre(*p, X, phi, bias, h, H, workspace, dev, static_cast<hipStream_t>(stream)));
+}
+
+mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out, void* stream) {
+  mhc_status st = check_params(p);
+  if (st != MHC_OK) return st;
+  if (p->T == 0) return MHC_OK;
+  if (!X || !Y || !H || !X_out) return MHC_ERR_NULL;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(H) || !aligned16(X_out)) return MHC_ERR_ALIGN;
+  const int m = p->n * p->n + 2 * p->n;
+  const size_t sb = state_bytes(p->dtype);
+  const size_t xb = static_cast<size_t>(p->T) * p->n * p->d * sb;
+  const Range rX = range_of(X, xb), rY = range_of(Y, static_cast<size_t>(p->T) * p->d * sb);
+  const Range rH = range_of(H, static_cast<size_t>(p->T) * m * 4), rO = range_of(X_out, xb);
+  if (X_out != X && overlap(rO, rX)) return MHC_ERR_ALIAS;
+  if (overlap(rO, rY) || overlap(rO, rH)) return MHC_ERR_ALIAS;
+  return from_hip(mhc::launch_post(*p, X, Y, H, X_out, static_cast<hipStream_t>(stream)));
+}
+
+mhc_status mhc_amax(int64_t T, int32_t n, int32_t L, const float* H_stack, float* amax, float* gain_fwd,
+                    float* gain_bwd, float* composite, void* stream) {
+  if (T < 0 || T > kMaxT || n < 1 || n > 16 || L < 0) return MHC_ERR_SHAPE;
+  if (n != 1 && n != 2 && n != 4) return MHC_ERR_UNSUPPORTED;
+  if (T == 0) return MHC_OK;
+  if (L > 0 && !H_stack) return MHC_ERR_NULL;
+  if (!amax && !gain_fwd && !gain_bwd && !composite) return MHC_ERR_NULL;
+  const int m = n * n + 2 * n;
+  const Range rH = range_of(H_stack, static_cast<size_t>(L) * T * m * 4);
+  const Range outs[4] = {range_of(amax, amax ? T * 4 : 0), range_of(gain_fwd, gain_fwd ? T * 4 : 0),
+                         range_of(gain_bwd, gain_bwd ? T * 4 : 0),
+                         range_of(composite, composite ? static_cast<size_t>(T) * n * n * 4 : 0)};
+  for (int a = 0; a < 4; ++a) {
+    if (L > 0 && overlap(outs[a], rH)) return MHC_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return MHC_ERR_ALIAS;
+  }
+  return from_hip(mhc::launch_amax(T, n, L, H_stack, amax, gain_fwd, gain_bwd, composite,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+mhc_status mhc_gelu_half(int64_t count, int32_t dtype, const void* h, void* Y, void* stream) {
+  if (count < 0) return MHC_ERR_SHAPE;
+  if (dtype != MHC_FP32 && dtype != MHC_BF16) return MHC_ERR_DTYPE;
+  if (count == 0) return MHC_OK;
+  if (!h || !Y) return MHC_ERR_NULL;
+  if (!aligned16(h) || !aligned16(Y)) return MHC_ERR_ALIGN;
+  const size_t b = static_cast<size_t>(count) * state_bytes(dtype);
+  if (Y != h && overlap(range_of(Y, b), range_of(h, b))) return MHC_ERR_ALIAS;
+  return from_hip(mhc::launch_gelu_half(count, dtype, h, Y, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

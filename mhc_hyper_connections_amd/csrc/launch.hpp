@@ -1,0 +1,34 @@
+// Internal launch interface between the C ABI (capi.cpp) and the kernels.
+// Arguments reaching these functions have been validated by the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mhc.h"
+
+namespace mhc {
+
+struct DeviceInfo {
+  int device = 0;
+  int num_cus = 256;       // compute units
+};
+
+// mhc_post: stream mixing + broadcast-add.
+hipError_t launch_post(const mhc_params& p, const void* X, const void* Y, const float* H, void* Xo,
+                       hipStream_t stream);
+
+// mhc_pre: workspace bytes, and the launch (partial projection, then maps + aggregation).
+size_t pre_workspace_bytes(int64_t T, int n, int d);
+hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
+                      float* H, void* workspace, const DeviceInfo& dev, hipStream_t stream);
+
+// mhc_amax: composite-map Amax.
+hipError_t launch_amax(int64_t T, int n, int L, const float* Hs, float* amax, float* gfwd, float* gbwd,
+                       float* comp, hipStream_t stream);
+
+// The stack workload's synthetic sublayer, Y = 0.5 GELU(h).
+hipError_t launch_gelu_half(int64_t count, int dtype, const void* h, void* Y, hipStream_t stream);
+
+}  // namespace mhc

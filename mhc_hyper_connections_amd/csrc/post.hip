@@ -1,0 +1,125 @@
+// mhc_post on gfx950: X'[t, i, :] = sum_j H_res[t, i, j] X[t, j, :] + H_post[t, i] Y[t, :]
+// (Dubrov, "DeepSeek mHC: Manifold-Constrained Hyper-Connections", section
+// "Kernmechanismen", Eq. 3; "mHC" notes on DeepSeek-V4, eq. dsv4-mhc-hc-update
+// and the fused Post-Res kernel of table tbl-dsv4-mhc-kernels, which reads
+// (n+1) C values per token instead of (3n+1) C).
+//
+// Pure streaming, bound by HBM: each thread owns chunks of 8 consecutive
+// values of d and, for each, reads the chunk of all n streams of X plus the
+// chunk of Y (16-byte non-temporal loads), combines them in fp32 registers and
+// writes the n output chunks (16-byte non-temporal stores).  A chunk of X is
+// read before it is written by the same thread, so X' may be X itself.
+// When d/8 is a multiple of 64 every wave stays inside one token, the token
+// index is wave-uniform and the 20 map values come in through scalar loads.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace mhc {
+namespace {
+
+constexpr int POST_THREADS = 256;
+
+template <typename ST, int N, int IPT, bool UNIFORM>
+__global__ __launch_bounds__(POST_THREADS) void post_kernel(int64_t nchunks, int d8,
+                                                            const typename ST::elem* __restrict__ X,
+                                                            const typename ST::elem* __restrict__ Y,
+                                                            const float* __restrict__ H,
+                                                            typename ST::elem* Xo) {
+  constexpr int M = N * N + 2 * N;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t group0 = (static_cast<int64_t>(blockIdx.x) * (POST_THREADS / 64) + wave) * IPT;
+  const int64_t d = static_cast<int64_t>(d8) * 8;
+
+  Raw8<ST> xr[IPT][N];
+  Raw8<ST> yr[IPT];
+  int64_t tok[IPT];
+  int64_t off[IPT];
+  bool ok[IPT];
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    int64_t c = (group0 + k) * 64 + lane;
+    ok[k] = c < nchunks;
+    int64_t t = c / d8;
+    if (UNIFORM) t = __builtin_amdgcn_readfirstlane(static_cast<int>(t));
+    tok[k] = t;
+    off[k] = (c - t * d8) * 8;
+    if (ok[k]) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) xr[k][i] = load_raw8<ST, true>(X + (t * N + i) * d + off[k]);
+      yr[k] = load_raw8<ST, true>(Y + t * d + off[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    if (!ok[k]) continue;
+    const float* Ht = H + tok[k] * M;
+    float res[N][N], post[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) res[i][j] = Ht[N + i * N + j];
+      post[i] = Ht[N + N * N + i];
+    }
+    float x[N][8], y[8];
+#pragma unroll
+    for (int i = 0; i < N; ++i) unpack8(xr[k][i], x[i]);
+    unpack8(yr[k], y);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float acc = res[i][0] * x[0][e];
+#pragma unroll
+        for (int j = 1; j < N; ++j) acc = fmaf(res[i][j], x[j][e], acc);
+        o[e] = fmaf(post[i], y[e], acc);
+      }
+      store8<ST, true>(Xo + (tok[k] * N + i) * d + off[k], o);
+    }
+  }
+}
+
+template <typename ST, int N>
+hipError_t launch_post_t(const mhc_params& p, const void* X, const void* Y, const float* H, void* Xo,
+                         hipStream_t stream) {
+  typedef typename ST::elem E;
+  constexpr int IPT = 2;
+  const int d8 = p.d / 8;
+  const int64_t nchunks = p.T * d8;
+  const int64_t per_block = static_cast<int64_t>(POST_THREADS) * IPT;
+  const int64_t blocks = (nchunks + per_block - 1) / per_block;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (d8 % 64 == 0) {
+    hipLaunchKernelGGL((post_kernel<ST, N, IPT, true>), dim3(static_cast<unsigned>(blocks)), dim3(POST_THREADS), 0,
+                       stream, nchunks, d8, static_cast<const E*>(X), static_cast<const E*>(Y), H,
+                       static_cast<E*>(Xo));
+  } else {
+    hipLaunchKernelGGL((post_kernel<ST, N, IPT, false>), dim3(static_cast<unsigned>(blocks)), dim3(POST_THREADS), 0,
+                       stream, nchunks, d8, static_cast<const E*>(X), static_cast<const E*>(Y), H,
+                       static_cast<E*>(Xo));
+  }
+  return hipGetLastError();
+}
+
+template <typename ST>
+hipError_t launch_post_n(const mhc_params& p, const void* X, const void* Y, const float* H, void* Xo,
+                         hipStream_t stream) {
+  switch (p.n) {
+    case 1: return launch_post_t<ST, 1>(p, X, Y, H, Xo, stream);
+    case 2: return launch_post_t<ST, 2>(p, X, Y, H, Xo, stream);
+    case 4: return launch_post_t<ST, 4>(p, X, Y, H, Xo, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_post(const mhc_params& p, const void* X, const void* Y, const float* H, void* Xo,
+                       hipStream_t stream) {
+  if (p.dtype == MHC_BF16) return launch_post_n<BF16>(p, X, Y, H, Xo, stream);
+  return launch_post_n<F32>(p, X, Y, H, Xo, stream);
+}
+
+}  // namespace mhc

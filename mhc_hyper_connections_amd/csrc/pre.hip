@@ -1,0 +1,356 @@
+// mhc_pre on gfx950: RMSNorm + projection + gates + Sinkhorn-Knopp + aggregation.
+//
+// Method ("mHC" notes on DeepSeek-V4, eqs. dsv4-mhc-rmsnorm, dsv4-mhc-a-tilde /
+// b-tilde / c-tilde, dsv4-mhc-sinkhorn-init, dsv4-mhc-sinkhorn, dsv4-mhc-gate;
+// Dubrov, "DeepSeek mHC: Manifold-Constrained Hyper-Connections", sections
+// "Sinkhorn-Knopp-projectie" and "Kernmechanismen", Eq. 3), per token t:
+//   r = sqrt(sum_k x_k^2 / (n d) + eps)            x = vec(X_t), stream i at [i d, (i+1) d)
+//   z = (x . phi) / r                               RMS division after the projection
+//   l = alpha_blk z + bias
+//   H_pre = sigmoid(l_pre), H_post = 2 sigmoid(l_post)
+//   H_res = t_max x (normalise columns, then rows) of exp(Mat(l_res))
+//   h = sum_i H_pre[i] X_t[i, :]
+//
+// Two launches:
+//  1. pre_partial_kernel -- persistent split-K projection on MFMA.  The
+//     hidden dimension is cut into slices of 256 positions (all n streams of
+//     them: K-slice of 256 n rows of phi).  A workgroup owns one slice for its
+//     whole life and keeps that slice of phi in registers as MFMA B operands
+//     (bf16 state: phi = hi + lo, two bf16 halves, ~16 significant bits, above
+//     the TF32 the pages name in table tbl-dsv4-mhc-mixed-precision; fp32
+//     state: fp32 MFMA).  It then walks token tiles of 16*MB tokens, streaming
+//     the X tile from HBM into registers (16-byte loads; the next tile is
+//     prefetched while the current one is multiplied), and writes, per token,
+//     the slice's 24 partial dot products and partial sum of squares.  No
+//     atomics: every partial has its own slot.
+//  2. pre_finish_kernel -- per token, sums the slices' partials in a fixed
+//     order (sum of squares in fp64 throughout), forms the logits, gates and Sinkhorn (16 lanes per token, one
+//     matrix entry per lane, column and row sums by lane shuffles), writes H
+//     and forms h = H_pre . X from a second read of X.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace mhc {
+namespace {
+
+constexpr int PRE_WAVES = 8;
+constexpr int PRE_THREADS = PRE_WAVES * 64;
+constexpr int PRE_SLICE = PRE_WAVES * 32;   // positions of d per slice (32 per wave)
+
+__host__ __device__ constexpr int num_maps(int n) { return n * n + 2 * n; }
+// Per-token record of one slice in the workspace: m fp32 partial dot
+// products, then the partial sum of squares as an fp64 at an 8-byte aligned
+// float offset.
+__host__ __device__ constexpr int ss_offset(int n) { return (num_maps(n) + 1) & ~1; }
+__host__ __device__ constexpr int part_width(int n) { return ss_offset(n) + 2; }
+
+// MFMA B operand for one (stream, 16-column block): 8 rows of phi per lane.
+template <typename ST> struct PhiOp;
+template <> struct PhiOp<BF16> { bf16x8 hi, lo; };
+template <> struct PhiOp<F32> { float v[8]; };
+
+__device__ __forceinline__ PhiOp<BF16> make_phi_op(const float (&f)[8], BF16) {
+  PhiOp<BF16> o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 hi = static_cast<__bf16>(f[e]);
+    o.hi[e] = hi;
+    o.lo[e] = static_cast<__bf16>(f[e] - static_cast<float>(hi));
+  }
+  return o;
+}
+__device__ __forceinline__ PhiOp<F32> make_phi_op(const float (&f)[8], F32) {
+  PhiOp<F32> o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o.v[e] = f[e];
+  return o;
+}
+
+// acc += A . B for one 16 (tokens) x 32 (positions) x 16 (columns) block.
+// A row = lane % 16 (token), positions 8 (lane / 16) .. +7 held by the lane;
+// B column = lane % 16, same positions.  Output: lane holds rows
+// 4 (lane / 16) .. +3 of column lane % 16.
+__device__ __forceinline__ f32x4 mfma_block(const Raw8<BF16>& a, const PhiOp<BF16>& b, f32x4 acc) {
+  const bf16x8 av = __builtin_bit_cast(bf16x8, a.v);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b.lo, acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ f32x4 mfma_block(const Raw8<F32>& a, const PhiOp<F32>& b, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[e], b.v[e], acc, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[e], b.v[4 + e], acc, 0, 0, 0);
+  return acc;
+}
+
+template <typename ST, int N, int MB>
+__global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int d, int S, int64_t ntiles,
+                                                                  const typename ST::elem* __restrict__ X,
+                                                                  const float* __restrict__ phi,
+                                                                  float* __restrict__ part) {
+  constexpr int M = num_maps(N);
+  constexpr int NB = (M + 15) / 16;
+  constexpr int R = 16 * MB;
+  constexpr int PW = part_width(N);
+  constexpr int SSO = ss_offset(N);
+  __shared__ float red[PRE_WAVES][R][M];
+  __shared__ double red_ss[PRE_WAVES][R];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int s = blockIdx.x % S;
+  const int64_t ntg = gridDim.x / S;
+  const int j0 = s * PRE_SLICE + 32 * w + 8 * g;
+  const bool jv = j0 < d;
+
+  // This lane's rows of phi: rows i*d + j0 .. +7 of column 16 nb + r16.
+  PhiOp<ST> bop[N][NB];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = 16 * nb + r16;
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        f[e] = (jv && col < M) ? phi[static_cast<int64_t>(i * d + j0 + e) * M + col] : 0.0f;
+      bop[i][nb] = make_phi_op(f, ST{});
+    }
+  }
+
+  Raw8<ST> xa[MB][N], xb[MB][N];
+  auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][N]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t t = tile * R + mb * 16 + r16;
+      const bool ok = jv && t < T;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        x[mb][i] = ok ? load_raw8<ST>(X + (t * N + i) * d + j0) : zero_raw8<ST>();
+    }
+  };
+
+  int64_t tile = blockIdx.x / S;
+  if (tile < ntiles) load_tile(tile, xa);
+  for (; tile < ntiles; tile += ntg) {
+    if (tile + ntg < ntiles) load_tile(tile + ntg, xb);
+
+    // Sum of squares in fp64: never overflows for a finite fp32 / bf16 state
+    // (fp32 overflows once the state's RMS passes ~1.8e19 / sqrt(n d)).
+    double ss[MB];
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      double sq = 0.0;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        float x[8];
+        unpack8(xa[mb][i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), sq);
+      }
+      ss[mb] = sq;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < N; ++i) a = mfma_block(xa[mb][i], bop[i][nb], a);
+        acc[mb][nb] = a;
+      }
+    }
+
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = 16 * nb + r16;
+        if (col < M) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) red[w][mb * 16 + 4 * g + v][col] = acc[mb][nb][v];
+        }
+      }
+      double sq = ss[mb];
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+      if (g == 0) red_ss[w][mb * 16 + r16] = sq;
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < R * (M + 1); q += PRE_THREADS) {
+      const int tok = q / (M + 1);
+      const int col = q - tok * (M + 1);
+      const int64_t t = tile * R + tok;
+      if (t < T) {
+        float* row = part + (static_cast<int64_t>(s) * T + t) * PW;
+        if (col < M) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int ww = 0; ww < PRE_WAVES; ++ww) sum += red[ww][tok][col];
+          row[col] = sum;
+        } else {
+          double sum = 0.0;
+#pragma unroll
+          for (int ww = 0; ww < PRE_WAVES; ++ww) sum += red_ss[ww][tok];
+          *reinterpret_cast<double*>(row + SSO) = sum;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < N; ++i) xa[mb][i] = xb[mb][i];
+  }
+}
+
+template <typename ST, int N>
+__global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S,
+                                                         const typename ST::elem* __restrict__ X,
+                                                         const float* __restrict__ part,
+                                                         const float* __restrict__ bias, float a_pre,
+                                                         float a_res, float a_post, float eps, int t_max,
+                                                         typename ST::elem* __restrict__ h,
+                                                         float* __restrict__ H) {
+  constexpr int M = num_maps(N);
+  constexpr int NN = N * N;
+  constexpr int PW = part_width(N);
+  constexpr int SSO = ss_offset(N);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int q = lane >> 4;          // token of this wave's group of 4
+  const int e = lane & 15;          // Sinkhorn entry (i, j) = (e / N, e % N) when e < N*N
+  const int64_t t0 = (static_cast<int64_t>(blockIdx.x) * 4 + w) * 4;
+  const int64_t t = t0 + q;
+  const bool tv = t < T;
+  const int colr = N + e;                                  // residual column of entry e
+  const int colg = (e < N) ? e : (N + NN + (e - N));       // gate column: pre for e < n, post for n <= e < 2n
+
+  // The slices' partials, summed in a fixed order; RMS and logits in fp64
+  // (a handful of values per token), everything after in fp32.
+  double ss = 0.0, zr = 0.0, zg = 0.0;
+  if (tv) {
+    for (int s = 0; s < S; ++s) {
+      const float* P = part + (static_cast<int64_t>(s) * T + t) * PW;
+      ss += *reinterpret_cast<const double*>(P + SSO);
+      if (e < NN) zr += P[colr];
+      if (e < 2 * N) zg += P[colg];
+    }
+  }
+  const double inv_r = 1.0 / sqrt(ss / static_cast<double>(N * d) + static_cast<double>(eps));
+
+  float gv = 0.0f;
+  if (e < 2 * N) {
+    const float l = static_cast<float>(static_cast<double>((e < N) ? a_pre : a_post) * (zg * inv_r) +
+                                       static_cast<double>(bias[colg]));
+    gv = (e < N) ? sigmoidf_(l) : 2.0f * sigmoidf_(l);
+  }
+  float lr = -INFINITY;
+  if (e < NN) lr = static_cast<float>(static_cast<double>(a_res) * (zr * inv_r) + static_cast<double>(bias[colr]));
+  // Subtracting the token's largest residual logit leaves every iterate
+  // unchanged (the first column step divides it out) and keeps exp finite.
+  float mx = lr;
+#pragma unroll
+  for (int off = 1; off < NN; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float mv = (e < NN) ? expf(lr - mx) : 0.0f;
+  for (int it = 0; it < t_max; ++it) {
+    float cs = mv;                                          // column sum: over i (lane bits above log2 n)
+#pragma unroll
+    for (int off = N; off < NN; off <<= 1) cs += __shfl_xor(cs, off);
+    mv = mv / cs;
+    float rs = mv;                                          // row sum: over j (low lane bits)
+#pragma unroll
+    for (int off = 1; off < N; off <<= 1) rs += __shfl_xor(rs, off);
+    mv = mv / rs;
+  }
+  if (tv) {
+    float* Ht = H + t * M;
+    if (e < NN) Ht[colr] = mv;
+    if (e < 2 * N) Ht[colg] = gv;
+  }
+
+  // h = H_pre . X for the wave's 4 tokens, one after another.
+  for (int qq = 0; qq < 4; ++qq) {
+    const int64_t tq = t0 + qq;
+    if (tq >= T) break;
+    float hp[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) hp[i] = __shfl(gv, qq * 16 + i);
+    const typename ST::elem* Xt = X + tq * N * static_cast<int64_t>(d);
+    typename ST::elem* ht = h + tq * static_cast<int64_t>(d);
+    for (int j = lane * 8; j < d; j += 512) {
+      Raw8<ST> xr[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) xr[i] = load_raw8<ST>(Xt + static_cast<int64_t>(i) * d + j);
+      float o[8];
+      {
+        float x[8];
+        unpack8(xr[0], x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = hp[0] * x[k];
+      }
+#pragma unroll
+      for (int i = 1; i < N; ++i) {
+        float x[8];
+        unpack8(xr[i], x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = fmaf(hp[i], x[k], o[k]);
+      }
+      store8<ST>(ht + j, o);
+    }
+  }
+}
+
+int num_slices(int d) { return (d + PRE_SLICE - 1) / PRE_SLICE; }
+
+template <typename ST, int N>
+hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
+                        void* workspace, const DeviceInfo& dev, hipStream_t stream) {
+  typedef typename ST::elem E;
+  constexpr int MB = (sizeof(typename ST::elem) == 2) ? 4 : 2;
+  constexpr int R = 16 * MB;
+  const int S = num_slices(p.d);
+  const int64_t ntiles = (p.T + R - 1) / R;
+  float* part = static_cast<float*>(workspace);
+  int64_t groups = dev.num_cus / S;
+  if (groups < 1) groups = 1;
+  if (groups > ntiles) groups = ntiles;
+  const int64_t grid = groups * S;
+  hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0, stream,
+                     p.T, p.d, S, ntiles, static_cast<const E*>(X), phi, part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t blocks = (p.T + 15) / 16;
+  hipLaunchKernelGGL((pre_finish_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T, p.d, S,
+                     static_cast<const E*>(X), static_cast<const float*>(part), bias, p.alpha_pre, p.alpha_res,
+                     p.alpha_post, p.eps, p.t_max, static_cast<E*>(h), H);
+  return hipGetLastError();
+}
+
+template <typename ST>
+hipError_t launch_pre_n(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
+                        void* ws, const DeviceInfo& dev, hipStream_t stream) {
+  switch (p.n) {
+    case 1: return launch_pre_t<ST, 1>(p, X, phi, bias, h, H, ws, dev, stream);
+    case 2: return launch_pre_t<ST, 2>(p, X, phi, bias, h, H, ws, dev, stream);
+    case 4: return launch_pre_t<ST, 4>(p, X, phi, bias, h, H, ws, dev, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+size_t pre_workspace_bytes(int64_t T, int n, int d) {
+  return static_cast<size_t>(num_slices(d)) * static_cast<size_t>(T) * static_cast<size_t>(part_width(n)) *
+         sizeof(float);
+}
+
+hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
+                      void* workspace, const DeviceInfo& dev, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  if (p.dtype == MHC_BF16) return launch_pre_n<BF16>(p, X, phi, bias, h, H, workspace, dev, stream);
+  return launch_pre_n<F32>(p, X, phi, bias, h, H, workspace, dev, stream);
+}
+
+}  // namespace mhc

@@ -1,0 +1,69 @@
+"""Helpers shared by the GPU parity tests: device transfer, tolerances, comparison."""
+from __future__ import annotations
+
+import numpy as np
+
+import synth
+
+# Tolerances (elementwise |gpu - oracle| <= atol + rtol * |oracle|).
+#  fp32 state: 1e-5 relative, 1e-6 absolute (values near zero) for every output.
+#  bf16 state: h and X' are stored in bf16 -> 2e-2 relative / 1e-2 absolute.
+#  The maps H are fp32 in both cases; with bf16 state they come from exact
+#  bf16 inputs, phi split into two bf16 halves (relative representation error
+#  <= 2^-18) and fp32 accumulation, so 1e-4 / 1e-5 holds with margin even at
+#  alpha = 1.
+TOL = {
+    ("fp32", "state"): (1e-5, 1e-6),
+    ("fp32", "maps"): (1e-5, 1e-6),
+    ("bf16", "state"): (2e-2, 1e-2),
+    ("bf16", "maps"): (1e-4, 1e-5),
+}
+
+
+def dname(dtype: int) -> str:
+    return "bf16" if dtype == synth.BF16 else "fp32"
+
+
+def to_device(a: np.ndarray, device="cuda"):
+    """numpy storage array -> torch device tensor (uint16 arrays become bfloat16)."""
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    """torch tensor -> numpy storage array (bfloat16 becomes uint16 bits)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+def values(a: np.ndarray) -> np.ndarray:
+    """Storage array -> float64 values."""
+    if a.dtype == np.uint16:
+        return synth.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def assert_close(got, ref, rtol, atol, what=""):
+    g = values(got) if isinstance(got, np.ndarray) and got.dtype == np.uint16 else np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    err = np.abs(g - r)
+    bad = err > atol + rtol * np.abs(r)
+    if np.any(bad) or not np.all(np.isfinite(g)):
+        idx = np.unravel_index(np.argmax(np.where(np.isfinite(err), err - rtol * np.abs(r), np.inf)), err.shape)
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} outside tol (rtol={rtol}, atol={atol}); "
+            f"worst at {idx}: gpu={g[idx]!r} oracle={r[idx]!r}; max abs err {np.nanmax(err):.3e}")
+    return float(np.max(err)) if err.size else 0.0
+
+
+def sample_tokens(T: int, count: int, seed: int = 7, tile: int = 64) -> np.ndarray:
+    """First and last tokens, tile edges and random ones, sorted and unique."""
+    rng = np.random.default_rng(seed)
+    pick = {0, T - 1, min(T - 1, tile - 1), min(T - 1, tile), T // 2}
+    pick.update(int(v) for v in rng.integers(0, T, size=max(0, count - len(pick))))
+    return np.array(sorted(p for p in pick if 0 <= p < T), dtype=np.int64)

@@ -1,0 +1,131 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol and
+rejects bad arguments before anything reaches a device.  No GPU needed: all
+calls here return from the host-side checks."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mhc_hyper_connections_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from mhc_hyper_connections_amd import build
+        build.build(force=False)
+    return m.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"mhc_pre", "mhc_post", "mhc_amax", "mhc_pre_workspace_size"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in include/mhc.h but not exported"
+    import mhc_hyper_connections_amd as m
+    assert set(m.EXPORTS) == set(names)
+
+
+def test_abi_version_and_status_strings(lib):
+    ver = int(re.search(r"#define MHC_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.mhc_abi_version() == ver
+    for s in range(9):
+        assert lib.mhc_status_string(s)
+    assert lib.mhc_status_string(12345) == b"unknown status"
+
+
+def _params(**kw):
+    import mhc_hyper_connections_amd as m
+    base = dict(T=64, n=4, d=256, dtype=m.MHC_BF16, t_max=20, eps=1e-6, alpha=(0.01, 0.01, 0.01))
+    base.update(kw)
+    return m.make_params(**base)
+
+
+# Fake, never-dereferenced device addresses, far apart and 16-byte aligned.
+A = [0x10000000 * (k + 1) for k in range(8)]
+
+
+def _pre(lib, p, X=A[0], phi=A[1], bias=A[2], h=A[3], H=A[4], ws=A[5], ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.mhc_pre_workspace_size(ctypes.byref(p))
+    return lib.mhc_pre(ctypes.byref(p), X, phi, bias, h, H, ws, ws_bytes, None)
+
+
+def test_pre_argument_checks(lib):
+    assert lib.mhc_pre(None, A[0], A[1], A[2], A[3], A[4], A[5], 1 << 30, None) == 1      # NULL params
+    assert _pre(lib, _params(n=3)) == 5                                                     # UNSUPPORTED
+    assert _pre(lib, _params(n=0)) == 2                                                     # SHAPE
+    assert _pre(lib, _params(d=12)) == 5                                                    # d % 8
+    assert _pre(lib, _params(dtype=7)) == 3                                                 # DTYPE
+    assert _pre(lib, _params(T=-1)) == 2
+    assert _pre(lib, _params(t_max=-1)) == 2
+    assert _pre(lib, _params(eps=float("nan"))) == 2
+    assert _pre(lib, _params(eps=-1.0)) == 2
+    assert _pre(lib, _params(alpha=(float("inf"), 0, 0))) == 2
+    assert _pre(lib, _params(), X=None) == 1
+    assert _pre(lib, _params(), H=None) == 1
+    assert _pre(lib, _params(), X=A[0] + 8) == 4                                            # ALIGN
+    assert _pre(lib, _params(), ws=None) == 7                                               # WORKSPACE
+    p = _params()
+    need = lib.mhc_pre_workspace_size(ctypes.byref(p))
+    assert _pre(lib, p, ws_bytes=need - 1) == 7
+    assert _pre(lib, _params(), h=A[0] + 16) == 6                                           # h inside X
+    assert _pre(lib, _params(), H=A[3]) == 6                                                # H on h
+    assert _pre(lib, _params(), ws=A[4]) == 6                                               # ws on H
+    assert _pre(lib, _params(T=0), X=None, phi=None) == 0                                   # no-op
+
+
+def test_workspace_size_formula(lib):
+    for (T, n, d) in ((64, 4, 256), (16384, 4, 4096), (5, 2, 264), (1, 1, 8), (4096, 4, 2560)):
+        p = _params(T=T, n=n, d=d)
+        slices = -(-d // 256)
+        width = ((n * n + 2 * n + 1) & ~1) + 2          # m fp32 partials, then an aligned fp64
+        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == slices * T * width * 4
+    assert lib.mhc_pre_workspace_size(None) == 0
+    assert lib.mhc_pre_workspace_size(ctypes.byref(_params(n=3))) == 0
+
+
+def test_post_argument_checks(lib):
+    p = _params()
+    post = lambda p, X=A[0], Y=A[1], H=A[2], O=A[3]: lib.mhc_post(ctypes.byref(p), X, Y, H, O, None)
+    assert lib.mhc_post(None, A[0], A[1], A[2], A[3], None) == 1
+    assert post(_params(n=3)) == 5
+    assert post(p, Y=None) == 1
+    assert post(p, O=A[3] + 4) == 4
+    assert post(p, O=A[0] + 1024) == 6               # partial overlap with X
+    assert post(p, O=A[1]) == 6                      # onto Y
+    assert post(_params(T=0), X=None, Y=None, H=None, O=None) == 0
+
+
+def test_amax_and_gelu_argument_checks(lib):
+    assert lib.mhc_amax(10, 3, 5, A[0], A[1], None, None, None, None) == 5
+    assert lib.mhc_amax(-1, 4, 5, A[0], A[1], None, None, None, None) == 2
+    assert lib.mhc_amax(10, 4, -1, A[0], A[1], None, None, None, None) == 2
+    assert lib.mhc_amax(10, 4, 5, None, A[1], None, None, None, None) == 1
+    assert lib.mhc_amax(10, 4, 5, A[0], None, None, None, None, None) == 1
+    assert lib.mhc_amax(10, 4, 5, A[0], A[0], None, None, None, None) == 6
+    assert lib.mhc_amax(10, 4, 5, A[0], A[1], A[1], None, None, None) == 6
+    assert lib.mhc_amax(0, 4, 5, None, None, None, None, None, None) == 0
+    assert lib.mhc_gelu_half(10, 9, A[0], A[1], None) == 3
+    assert lib.mhc_gelu_half(-1, 1, A[0], A[1], None) == 2
+    assert lib.mhc_gelu_half(10, 1, A[0] + 2, A[1], None) == 4
+    assert lib.mhc_gelu_half(100, 1, A[0], A[0] + 16, None) == 6
+
+
+def test_binding_refuses_host_tensors_and_missing_library(lib):
+    torch = pytest.importorskip("torch")
+    import mhc_hyper_connections_amd as m
+    X = torch.zeros((4, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        m.post(X, torch.zeros((4, 64), dtype=torch.bfloat16), torch.zeros((4, 24)))
+    with pytest.raises(RuntimeError, match="not built"):
+        m.load_library("/nonexistent/libmhc.so")
