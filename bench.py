@@ -93,6 +93,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer_bf16_T16384_d4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pre-algo", type=int, default=0, choices=[0, 1, 2],
+                    help="mhc_pre form: 0 auto, 1 two-pass, 2 one-pass")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
     args = ap.parse_args()
@@ -137,10 +139,13 @@ def main():
     torch.cuda.synchronize()
     log("inputs resident; warming up")
 
+    algo_used = [None]
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        mhc.pre(X, phi, bias, alpha=w.alpha, eps=w.eps, t_max=w.t_max, h=h, H=H, workspace=ws, stream=stream)
+        _, _, algo_used[0] = mhc.pre_ex(X, phi, bias, args.pre_algo, alpha=w.alpha, eps=w.eps, t_max=w.t_max,
+                                        h=h, H=H, workspace=ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         mhc.post(X, Y, H, out=Xo, stream=stream)
@@ -224,6 +229,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": T, "n": n, "d": d, "t_max": w.t_max,
                    "step": "mhc_pre + mhc_post + mhc_amax (one layer), Y given",
+                   "mhc_pre_form": {1: "two-pass", 2: "one-pass"}.get(algo_used[0], str(algo_used[0])),
                    "parallelism": "single GPU"},
         "achieved_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "achieved_frac_of_hbm_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

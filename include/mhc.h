@@ -110,8 +110,38 @@ mhc_status mhc_pre(const mhc_params* p, const void* X, const float* phi, const f
                    void* h, float* H, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device scratch mhc_pre needs for these parameters (0 if p is
- * invalid).  The amount depends only on T, n and d. */
+ * invalid).  The amount depends only on T, n and d and covers both forms of
+ * mhc_pre_ex. */
 size_t mhc_pre_workspace_size(const mhc_params* p);
+
+/* ---- mhc_pre_ex: mhc_pre with a choice of algorithm -------------------------
+ * Same computation, arguments and results as mhc_pre, which is
+ * mhc_pre_ex(..., MHC_PRE_AUTO, NULL, stream).  The two forms differ only in
+ * how many times they read X from HBM:
+ *   MHC_PRE_TWO_PASS  a split-K projection pass, then a maps + aggregation
+ *                     pass that reads X again; any valid shape.
+ *   MHC_PRE_ONE_PASS  bf16 state with 1793 <= d <= 4096 and enough tokens to
+ *                     give every team of workgroups two 32-token tiles: teams
+ *                     of one workgroup per compute unit split d, exchange
+ *                     per-token partial sums through device memory and keep
+ *                     their slice of X in registers until H_pre is known, so
+ *                     X is read once.  Uses a cooperative launch.  Returns
+ *                     MHC_ERR_UNSUPPORTED when it does not apply.
+ *   MHC_PRE_AUTO      the two-pass form, which measures faster on MI355X at
+ *                     every shape the one-pass form covers.
+ * Both sum every partial in a fixed order (results are bitwise reproducible
+ * for a given form); the two forms agree to rounding.
+ * algo_used (nullable, host pointer) receives the form that ran.  After a
+ * one-pass call, the first 4 bytes of the workspace hold 0 unless an
+ * internal wait ran out (then the results are invalid); this cannot happen
+ * when all workgroups of the launch are resident, which the cooperative
+ * launch guarantees. */
+#define MHC_PRE_AUTO 0
+#define MHC_PRE_TWO_PASS 1
+#define MHC_PRE_ONE_PASS 2
+mhc_status mhc_pre_ex(const mhc_params* p, const void* X, const float* phi, const float* bias, void* h,
+                      float* H, void* workspace, size_t workspace_bytes, int32_t algo, int32_t* algo_used,
+                      void* stream);
 
 /* ---- mhc_post: stream mixing + broadcast-add --------------------------------
  * X_out[t, i, :] = sum_j H_res[t, i, j] X[t, j, :] + H_post[t, i] Y[t, :]

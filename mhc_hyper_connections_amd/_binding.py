@@ -16,8 +16,9 @@ LIB_PATH = os.path.join(HERE, "libmhc.so")
 MHC_FP32, MHC_BF16 = 0, 1
 STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_DTYPE", 4: "MHC_ERR_ALIGN",
           5: "MHC_ERR_UNSUPPORTED", 6: "MHC_ERR_ALIAS", 7: "MHC_ERR_WORKSPACE", 8: "MHC_ERR_HIP"}
-EXPORTS = ["mhc_pre", "mhc_pre_workspace_size", "mhc_post", "mhc_amax", "mhc_gelu_half",
+EXPORTS = ["mhc_pre", "mhc_pre_ex", "mhc_pre_workspace_size", "mhc_post", "mhc_amax", "mhc_gelu_half",
            "mhc_status_string", "mhc_abi_version"]
+PRE_AUTO, PRE_TWO_PASS, PRE_ONE_PASS = 0, 1, 2
 
 
 class MhcError(RuntimeError):
@@ -50,6 +51,9 @@ def load_library(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     lib.mhc_pre.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.mhc_pre.restype = ctypes.c_int
+    lib.mhc_pre_ex.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32,
+                               ctypes.POINTER(ctypes.c_int32), _P]
+    lib.mhc_pre_ex.restype = ctypes.c_int
     lib.mhc_pre_workspace_size.argtypes = [ctypes.POINTER(Params)]
     lib.mhc_pre_workspace_size.restype = ctypes.c_size_t
     lib.mhc_post.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P]
@@ -119,8 +123,12 @@ def pre_workspace_size(T, n, d, dtype=MHC_BF16) -> int:
 
 
 def pre(X, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, h=None, H=None, workspace=None,
-        stream=None):
-    """mhc_pre: returns (h [T, d] state dtype, H [T, m] fp32)."""
+        stream=None, algo=None):
+    """mhc_pre: returns (h [T, d] state dtype, H [T, m] fp32).  With ``algo``
+    (PRE_AUTO / PRE_TWO_PASS / PRE_ONE_PASS) it calls mhc_pre_ex instead."""
+    if algo is not None:
+        h, H, _ = pre_ex(X, phi, bias, algo, alpha, eps, t_max, h, H, workspace, stream)
+        return h, H
     torch = _torch()
     T, n, d = X.shape
     m = n * n + 2 * n
@@ -138,6 +146,30 @@ def pre(X, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, h=None, H=No
     _check("mhc_pre", lib.mhc_pre(ctypes.byref(p), _ptr(X), _ptr(phi), _ptr(bias), _ptr(h), _ptr(H),
                                   _ptr(workspace), ws_bytes, _stream(stream, X.device)))
     return h, H
+
+
+def pre_ex(X, phi, bias, algo=PRE_AUTO, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, h=None, H=None,
+           workspace=None, stream=None):
+    """mhc_pre_ex: returns (h, H, algorithm that ran)."""
+    torch = _torch()
+    T, n, d = X.shape
+    m = n * n + 2 * n
+    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha)
+    lib = load_library()
+    if h is None:
+        h = torch.empty((T, d), dtype=X.dtype, device=X.device)
+    if H is None:
+        H = torch.empty((T, m), dtype=torch.float32, device=X.device)
+    need = int(lib.mhc_pre_workspace_size(ctypes.byref(p)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _need_device(X, phi, bias, h, H, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    used = ctypes.c_int32(-1)
+    _check("mhc_pre_ex", lib.mhc_pre_ex(ctypes.byref(p), _ptr(X), _ptr(phi), _ptr(bias), _ptr(h), _ptr(H),
+                                        _ptr(workspace), ws_bytes, int(algo), ctypes.byref(used),
+                                        _stream(stream, X.device)))
+    return h, H, int(used.value)
 
 
 def post(X, Y, H, out=None, stream=None):

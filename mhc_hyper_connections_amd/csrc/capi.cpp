@@ -50,6 +50,7 @@ mhc::DeviceInfo device_info() {
   // Per-device attribute cache; the only state the library keeps.
   static std::mutex mu;
   static int cus[64] = {0};
+  static int coop[64] = {0};
   mhc::DeviceInfo info;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -59,9 +60,13 @@ mhc::DeviceInfo device_info() {
     if (cus[dev] == 0) {
       int v = 0;
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+      int c = 0;
+      if (hipDeviceGetAttribute(&c, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) c = 0;
+      coop[dev] = c ? 1 : -1;
       cus[dev] = v;
     }
     info.num_cus = cus[dev];
+    info.cooperative = coop[dev] > 0;
   }
   return info;
 }
@@ -96,6 +101,13 @@ size_t mhc_pre_workspace_size(const mhc_params* p) {
 
 mhc_status mhc_pre(const mhc_params* p, const void* X, const float* phi, const float* bias, void* h, float* H,
                    void* workspace, size_t workspace_bytes, void* stream) {
+  return mhc_pre_ex(p, X, phi, bias, h, H, workspace, workspace_bytes, MHC_PRE_AUTO, nullptr, stream);
+}
+
+mhc_status mhc_pre_ex(const mhc_params* p, const void* X, const float* phi, const float* bias, void* h, float* H,
+                      void* workspace, size_t workspace_bytes, int32_t algo, int32_t* algo_used, void* stream) {
+  if (algo_used) *algo_used = MHC_PRE_TWO_PASS;
+  if (algo != MHC_PRE_AUTO && algo != MHC_PRE_TWO_PASS && algo != MHC_PRE_ONE_PASS) return MHC_ERR_SHAPE;
   mhc_status st = check_params(p);
   if (st != MHC_OK) return st;
   if (p->T == 0) return MHC_OK;
@@ -118,7 +130,12 @@ mhc_status mhc_pre(const mhc_params* p, const void* X, const float* phi, const f
   if (need > 0 && (overlap(rw, rX) || overlap(rw, rphi) || overlap(rw, rb) || overlap(rw, rh) || overlap(rw, rH)))
     return MHC_ERR_ALIAS;
   const mhc::DeviceInfo dev = device_info();
-  return from_hip(mhc::launch_pre(*p, X, phi, bias, h, H, workspace, dev, static_cast<hipStream_t>(stream)));
+  int used = MHC_PRE_TWO_PASS;
+  const hipError_t e = mhc::launch_pre(*p, X, phi, bias, h, H, workspace, workspace_bytes, algo, &used, dev,
+                                       static_cast<hipStream_t>(stream));
+  if (algo_used) *algo_used = used;
+  if (e == hipErrorNotSupported && algo == MHC_PRE_ONE_PASS) return MHC_ERR_UNSUPPORTED;
+  return from_hip(e);
 }
 
 mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out, void* stream) {

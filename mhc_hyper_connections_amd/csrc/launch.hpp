@@ -13,16 +13,24 @@ namespace mhc {
 struct DeviceInfo {
   int device = 0;
   int num_cus = 256;       // compute units
+  bool cooperative = false;  // cooperative launches (all workgroups co-resident) supported
 };
 
 // mhc_post: stream mixing + broadcast-add.
 hipError_t launch_post(const mhc_params& p, const void* X, const void* Y, const float* H, void* Xo,
                        hipStream_t stream);
 
-// mhc_pre: workspace bytes, and the launch (partial projection, then maps + aggregation).
+// mhc_pre: workspace bytes and the launch.  algo: MHC_PRE_AUTO, MHC_PRE_TWO_PASS
+// or MHC_PRE_ONE_PASS; *used receives the form that ran.
 size_t pre_workspace_bytes(int64_t T, int n, int d);
 hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
-                      float* H, void* workspace, const DeviceInfo& dev, hipStream_t stream);
+                      float* H, void* workspace, size_t ws_bytes, int algo, int* used, const DeviceInfo& dev,
+                      hipStream_t stream);
+
+// The single-pass form (pre_fused.hip): hipErrorNotSupported when it does not apply.
+size_t pre_fused_workspace_bytes(int64_t T, int n, int d);
+hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
+                            float* H, void* workspace, size_t ws_bytes, const DeviceInfo& dev, hipStream_t stream);
 
 // mhc_amax: composite-map Amax.
 hipError_t launch_amax(int64_t T, int n, int L, const float* Hs, float* amax, float* gfwd, float* gbwd,

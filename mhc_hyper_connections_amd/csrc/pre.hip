@@ -27,8 +27,8 @@
 //     order (sum of squares in fp64 throughout), forms the logits, gates and Sinkhorn (16 lanes per token, one
 //     matrix entry per lane, column and row sums by lane shuffles), writes H
 //     and forms h = H_pre . X from a second read of X.
-#include "device.hpp"
 #include "launch.hpp"
+#include "pre_common.hpp"
 
 namespace mhc {
 namespace {
@@ -37,52 +37,11 @@ constexpr int PRE_WAVES = 8;
 constexpr int PRE_THREADS = PRE_WAVES * 64;
 constexpr int PRE_SLICE = PRE_WAVES * 32;   // positions of d per slice (32 per wave)
 
-__host__ __device__ constexpr int num_maps(int n) { return n * n + 2 * n; }
 // Per-token record of one slice in the workspace: m fp32 partial dot
 // products, then the partial sum of squares as an fp64 at an 8-byte aligned
 // float offset.
 __host__ __device__ constexpr int ss_offset(int n) { return (num_maps(n) + 1) & ~1; }
 __host__ __device__ constexpr int part_width(int n) { return ss_offset(n) + 2; }
-
-// MFMA B operand for one (stream, 16-column block): 8 rows of phi per lane.
-template <typename ST> struct PhiOp;
-template <> struct PhiOp<BF16> { bf16x8 hi, lo; };
-template <> struct PhiOp<F32> { float v[8]; };
-
-__device__ __forceinline__ PhiOp<BF16> make_phi_op(const float (&f)[8], BF16) {
-  PhiOp<BF16> o;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 hi = static_cast<__bf16>(f[e]);
-    o.hi[e] = hi;
-    o.lo[e] = static_cast<__bf16>(f[e] - static_cast<float>(hi));
-  }
-  return o;
-}
-__device__ __forceinline__ PhiOp<F32> make_phi_op(const float (&f)[8], F32) {
-  PhiOp<F32> o;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o.v[e] = f[e];
-  return o;
-}
-
-// acc += A . B for one 16 (tokens) x 32 (positions) x 16 (columns) block.
-// A row = lane % 16 (token), positions 8 (lane / 16) .. +7 held by the lane;
-// B column = lane % 16, same positions.  Output: lane holds rows
-// 4 (lane / 16) .. +3 of column lane % 16.
-__device__ __forceinline__ f32x4 mfma_block(const Raw8<BF16>& a, const PhiOp<BF16>& b, f32x4 acc) {
-  const bf16x8 av = __builtin_bit_cast(bf16x8, a.v);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b.hi, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b.lo, acc, 0, 0, 0);
-  return acc;
-}
-__device__ __forceinline__ f32x4 mfma_block(const Raw8<F32>& a, const PhiOp<F32>& b, f32x4 acc) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[e], b.v[e], acc, 0, 0, 0);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[e], b.v[4 + e], acc, 0, 0, 0);
-  return acc;
-}
 
 template <typename ST, int N, int MB>
 __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int d, int S, int64_t ntiles,
@@ -120,23 +79,31 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
       bop[i][nb] = make_phi_op(f, ST{});
     }
   }
+  __builtin_amdgcn_sched_barrier(0);     // finish the phi operands before the first tile's loads
 
   Raw8<ST> xa[MB][N], xb[MB][N];
+  // Every lane loads every chunk from a valid address, with no branch and no
+  // select on the data (either would make the compiler wait for the load on
+  // the spot): tokens past T read token 0 (their rows are never written) and
+  // lanes past d read position 0 (their phi rows are zero and their squares
+  // are dropped below).
+  const int jl = jv ? j0 : 0;
   auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][N]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int64_t t = tile * R + mb * 16 + r16;
-      const bool ok = jv && t < T;
+      const int64_t tt = t < T ? t : 0;
 #pragma unroll
-      for (int i = 0; i < N; ++i)
-        x[mb][i] = ok ? load_raw8<ST>(X + (t * N + i) * d + j0) : zero_raw8<ST>();
+      for (int i = 0; i < N; ++i) x[mb][i] = load_raw8<ST>(X + (tt * N + i) * d + jl);
     }
   };
 
-  int64_t tile = blockIdx.x / S;
-  if (tile < ntiles) load_tile(tile, xa);
-  for (; tile < ntiles; tile += ntg) {
-    if (tile + ntg < ntiles) load_tile(tile + ntg, xb);
+  // One tile: partials of `cur` while the other buffer streams in; once
+  // `cur` is consumed it is refilled with the tile after next.  Two buffers,
+  // prefetch distance two, the loop unrolled by two so the buffers keep
+  // their registers (copying a buffer that is still being loaded would wait
+  // for it and serialise the prefetch).
+  auto step = [&](int64_t tile, Raw8<ST> (&cur)[MB][N]) {
 
     // Sum of squares in fp64: never overflows for a finite fp32 / bf16 state
     // (fp32 overflows once the state's RMS passes ~1.8e19 / sqrt(n d)).
@@ -148,16 +115,16 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         float x[8];
-        unpack8(xa[mb][i], x);
+        unpack8(cur[mb][i], x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) sq = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), sq);
       }
-      ss[mb] = sq;
+      ss[mb] = jv ? sq : 0.0;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < N; ++i) a = mfma_block(xa[mb][i], bop[i][nb], a);
+        for (int i = 0; i < N; ++i) a = mfma_block(cur[mb][i], bop[i][nb], a);
         acc[mb][nb] = a;
       }
     }
@@ -198,10 +165,15 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < N; ++i) xa[mb][i] = xb[mb][i];
+    if (tile + 2 * ntg < ntiles) load_tile(tile + 2 * ntg, cur);
+  };
+
+  int64_t tile = blockIdx.x / S;
+  if (tile < ntiles) load_tile(tile, xa);
+  if (tile + ntg < ntiles) load_tile(tile + ntg, xb);
+  for (; tile < ntiles; tile += 2 * ntg) {
+    step(tile, xa);
+    if (tile + ntg < ntiles) step(tile + ntg, xb);
   }
 }
 
@@ -238,32 +210,16 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
       if (e < 2 * N) zg += P[colg];
     }
   }
-  const double inv_r = 1.0 / sqrt(ss / static_cast<double>(N * d) + static_cast<double>(eps));
+  const double inv_r = inv_rms(ss, N * d, eps);
 
   float gv = 0.0f;
   if (e < 2 * N) {
-    const float l = static_cast<float>(static_cast<double>((e < N) ? a_pre : a_post) * (zg * inv_r) +
-                                       static_cast<double>(bias[colg]));
+    const float l = logit_of(zg, inv_r, (e < N) ? a_pre : a_post, bias[colg]);
     gv = (e < N) ? sigmoidf_(l) : 2.0f * sigmoidf_(l);
   }
   float lr = -INFINITY;
-  if (e < NN) lr = static_cast<float>(static_cast<double>(a_res) * (zr * inv_r) + static_cast<double>(bias[colr]));
-  // Subtracting the token's largest residual logit leaves every iterate
-  // unchanged (the first column step divides it out) and keeps exp finite.
-  float mx = lr;
-#pragma unroll
-  for (int off = 1; off < NN; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  float mv = (e < NN) ? expf(lr - mx) : 0.0f;
-  for (int it = 0; it < t_max; ++it) {
-    float cs = mv;                                          // column sum: over i (lane bits above log2 n)
-#pragma unroll
-    for (int off = N; off < NN; off <<= 1) cs += __shfl_xor(cs, off);
-    mv = mv / cs;
-    float rs = mv;                                          // row sum: over j (low lane bits)
-#pragma unroll
-    for (int off = 1; off < N; off <<= 1) rs += __shfl_xor(rs, off);
-    mv = mv / rs;
-  }
+  if (e < NN) lr = logit_of(zr, inv_r, a_res, bias[colr]);
+  const float mv = sinkhorn16<N>(lr, e, t_max);
   if (tv) {
     float* Ht = H + t * M;
     if (e < NN) Ht[colr] = mv;
@@ -342,13 +298,29 @@ hipError_t launch_pre_n(const mhc_params& p, const void* X, const float* phi, co
 }  // namespace
 
 size_t pre_workspace_bytes(int64_t T, int n, int d) {
-  return static_cast<size_t>(num_slices(d)) * static_cast<size_t>(T) * static_cast<size_t>(part_width(n)) *
-         sizeof(float);
+  const size_t two_pass = static_cast<size_t>(num_slices(d)) * static_cast<size_t>(T) *
+                          static_cast<size_t>(part_width(n)) * sizeof(float);
+  const size_t one_pass = pre_fused_workspace_bytes(T, n, d);
+  return two_pass > one_pass ? two_pass : one_pass;
 }
 
 hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
-                      void* workspace, const DeviceInfo& dev, hipStream_t stream) {
+                      void* workspace, size_t ws_bytes, int algo, int* used, const DeviceInfo& dev,
+                      hipStream_t stream) {
+  if (used) *used = MHC_PRE_TWO_PASS;
   if (p.T == 0) return hipSuccess;
+  // AUTO takes the two-pass form: on MI355X it measures faster at every shape
+  // the one-pass form covers (the cross-team exchange costs more than the
+  // second read of X, which mostly hits the last-level cache).
+  if (algo == MHC_PRE_ONE_PASS) {
+    const hipError_t e = launch_pre_fused(p, X, phi, bias, h, H, workspace, ws_bytes, dev, stream);
+    if (e == hipSuccess) {
+      if (used) *used = MHC_PRE_ONE_PASS;
+      return hipSuccess;
+    }
+    (void)hipGetLastError();                 // clear a refused launch
+    return e;
+  }
   if (p.dtype == MHC_BF16) return launch_pre_n<BF16>(p, X, phi, bias, h, H, workspace, dev, stream);
   return launch_pre_n<F32>(p, X, phi, bias, h, H, workspace, dev, stream);
 }

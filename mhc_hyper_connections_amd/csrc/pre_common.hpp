@@ -1,0 +1,91 @@
+// Device pieces shared by the two forms of mhc_pre: the phi MFMA operands,
+// the projection block, the per-token logits and the Sinkhorn-Knopp
+// iteration on 16 lanes.
+#pragma once
+
+#include "device.hpp"
+
+namespace mhc {
+
+__host__ __device__ constexpr int num_maps(int n) { return n * n + 2 * n; }
+
+// MFMA B operand for one (stream, 16-column block): 8 rows of phi per lane.
+// bf16 state: phi = hi + lo, two bf16 halves (~16 significant bits); fp32
+// state: phi itself for the fp32 MFMA.
+template <typename ST> struct PhiOp;
+template <> struct PhiOp<BF16> { bf16x8 hi, lo; };
+template <> struct PhiOp<F32> { float v[8]; };
+
+__device__ __forceinline__ PhiOp<BF16> make_phi_op(const float (&f)[8], BF16) {
+  PhiOp<BF16> o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 hi = static_cast<__bf16>(f[e]);
+    o.hi[e] = hi;
+    o.lo[e] = static_cast<__bf16>(f[e] - static_cast<float>(hi));
+  }
+  return o;
+}
+__device__ __forceinline__ PhiOp<F32> make_phi_op(const float (&f)[8], F32) {
+  PhiOp<F32> o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o.v[e] = f[e];
+  return o;
+}
+
+// acc += A . B for one 16 (tokens) x 32 (positions) x 16 (columns) block.
+// A row = lane % 16 (token), positions 8 (lane / 16) .. +7 held by the lane;
+// B column = lane % 16, same positions.  Output: lane holds rows
+// 4 (lane / 16) .. +3 of column lane % 16.
+__device__ __forceinline__ f32x4 mfma_block(const Raw8<BF16>& a, const PhiOp<BF16>& b, f32x4 acc) {
+  const bf16x8 av = __builtin_bit_cast(bf16x8, a.v);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b.lo, acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ f32x4 mfma_block(const Raw8<F32>& a, const PhiOp<F32>& b, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[e], b.v[e], acc, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[e], b.v[4 + e], acc, 0, 0, 0);
+  return acc;
+}
+
+// 1 / r with r = sqrt(sum x^2 / K + eps), in fp64.
+__device__ __forceinline__ double inv_rms(double ss, int K, float eps) {
+  return 1.0 / sqrt(ss / static_cast<double>(K) + static_cast<double>(eps));
+}
+
+// logit = alpha * (z / r) + bias, formed in fp64 and rounded once to fp32.
+__device__ __forceinline__ float logit_of(double z, double inv_r, float alpha, float bias) {
+  return static_cast<float>(static_cast<double>(alpha) * (z * inv_r) + static_cast<double>(bias));
+}
+
+// Sinkhorn-Knopp on one token's n x n map held by 16 lanes: lane e (e = lane
+// % 16) owns entry (e / n, e % n) for e < n*n and receives the residual logit
+// `lr` (-inf on lanes e >= n*n).  Returns the entry of H_res after t_max
+// passes of (normalise columns, then rows).  Column and row sums are lane
+// shuffles inside the 16-lane group; every lane of the wave must call it.
+template <int N>
+__device__ __forceinline__ float sinkhorn16(float lr, int e, int t_max) {
+  constexpr int NN = N * N;
+  // Subtracting the token's largest residual logit leaves every iterate
+  // unchanged (the first column step divides it out) and keeps exp finite.
+  float mx = lr;
+#pragma unroll
+  for (int off = 1; off < NN; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float mv = (e < NN) ? expf(lr - mx) : 0.0f;
+  for (int it = 0; it < t_max; ++it) {
+    float cs = mv;                                          // column sum: over i (lane bits above log2 n)
+#pragma unroll
+    for (int off = N; off < NN; off <<= 1) cs += __shfl_xor(cs, off);
+    mv = mv / cs;
+    float rs = mv;                                          // row sum: over j (low lane bits)
+#pragma unroll
+    for (int off = 1; off < N; off <<= 1) rs += __shfl_xor(rs, off);
+    mv = mv / rs;
+  }
+  return mv;
+}
+
+}  // namespace mhc

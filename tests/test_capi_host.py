@@ -84,12 +84,24 @@ def test_pre_argument_checks(lib):
     assert _pre(lib, _params(T=0), X=None, phi=None) == 0                                   # no-op
 
 
+def test_pre_ex_argument_checks(lib):
+    p = _params()
+    need = lib.mhc_pre_workspace_size(ctypes.byref(p))
+    used = ctypes.c_int32(-1)
+    assert lib.mhc_pre_ex(ctypes.byref(p), A[0], A[1], A[2], A[3], A[4], A[5], need, 7, ctypes.byref(used), None) == 2
+    assert used.value == 1                                  # reported even when refused
+    assert lib.mhc_pre_ex(ctypes.byref(_params(n=3)), A[0], A[1], A[2], A[3], A[4], A[5], need, 2, None, None) == 5
+    assert lib.mhc_pre_ex(ctypes.byref(_params(T=0)), None, None, None, None, None, None, 0, 2, None, None) == 0
+
+
 def test_workspace_size_formula(lib):
     for (T, n, d) in ((64, 4, 256), (16384, 4, 4096), (5, 2, 264), (1, 1, 8), (4096, 4, 2560)):
         p = _params(T=T, n=n, d=d)
         slices = -(-d // 256)
         width = ((n * n + 2 * n + 1) & ~1) + 2          # m fp32 partials, then an aligned fp64
-        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == slices * T * width * 4
+        two_pass = slices * T * width * 4
+        one_pass = 256 + 8 * (48 // slices) * 4 * slices * 32 * (n * n + 2 * n + 2) * 8 if 8 <= slices <= 16 else 0
+        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == max(two_pass, one_pass)
     assert lib.mhc_pre_workspace_size(None) == 0
     assert lib.mhc_pre_workspace_size(ctypes.byref(_params(n=3))) == 0
 

@@ -1,0 +1,104 @@
+"""The single-pass form of mhc_pre (MHC_PRE_ONE_PASS) against the oracle.
+
+It applies to bf16 state with ceil(d / 256) in [8, 16] and at least two
+32-token tiles per team of workgroups; teams exchange per-token partial sums
+through device memory.  Each case checks that the one-pass form really ran,
+that no internal wait ran out (the workspace's error word is 0), and that the
+results match the oracle like the two-pass form's do.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import TOL, assert_close, sample_tokens, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def mhc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mhc_hyper_connections_amd as m
+    m.load_library()
+    return m
+
+
+def _run(mhc, w, X, phi, bias, alpha, algo):
+    dX, dphi, dbias = to_device(X), to_device(phi), to_device(bias)
+    ws = torch.zeros(mhc.pre_workspace_size(w.T, w.n, w.d, w.dtype), dtype=torch.uint8, device="cuda")
+    h, H, used = mhc.pre_ex(dX, dphi, dbias, algo, alpha=alpha, eps=w.eps, t_max=w.t_max, workspace=ws)
+    torch.cuda.synchronize()
+    err_word = int(ws[:4].view(torch.int32).item())
+    return to_host(h), to_host(H), used, err_word
+
+
+def _check(mhc, o, w, alpha=None, tokens=None):
+    alpha = w.alpha if alpha is None else alpha
+    X = synth.make_state(w)
+    phi, bias = synth.make_params(w)
+    h, H, used, err = _run(mhc, w, X, phi, bias, alpha, mhc.PRE_ONE_PASS)
+    assert used == mhc.PRE_ONE_PASS
+    assert err == 0, "an exchange wait ran out"
+    tok = np.arange(w.T, dtype=np.int64) if tokens is None else tokens
+    ref = o.pre(X, phi, bias, alpha, eps=w.eps, t_max=w.t_max, tokens=tok)
+    assert_close(H[tok], ref["H"], *TOL[("bf16", "maps")], what=f"{w.name} one-pass H")
+    assert_close(h[tok], ref["h"], *TOL[("bf16", "state")], what=f"{w.name} one-pass h")
+    return X, phi, bias, h, H
+
+
+CASES = [
+    ("layer_bf16_T16384_d4096", {"T": 1024}),            # team of 16, exactly two tiles per team
+    ("layer_bf16_T16384_d4096", {"T": 1100}),            # ragged last tile
+    ("layer_bf16_T4096_d2048", {"T": 2048}),             # team of 8
+    ("stack60_bf16_T4096_d2560", {"T": 1600, "layers": 1, "sublayer": "given"}),   # team of 10, ragged slice
+]
+
+
+@pytest.mark.parametrize("name,changes", CASES, ids=[f"{c[0]}_T{c[1]['T']}" for c in CASES])
+@pytest.mark.parametrize("alpha", [None, (1.0, 1.0, 1.0)], ids=["alpha_cfg", "alpha_1"])
+def test_one_pass_every_token(mhc, oracle_lib, name, changes, alpha):
+    w = synth.scaled(synth.WORKLOADS[name], **changes)
+    _check(mhc, oracle_lib, w, alpha=alpha)
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_one_pass_fewer_streams(mhc, oracle_lib, n):
+    w = synth.Workload(f"one_pass_n{n}", T=1024, n=n, d=4096, dtype=synth.BF16, seed=777 + n)
+    _check(mhc, oracle_lib, w, alpha=(1.0, 0.5, -0.5))
+
+
+@pytest.mark.slow
+def test_one_pass_full_size_sampled(mhc, oracle_lib):
+    w = synth.WORKLOADS["layer_bf16_T16384_d4096"]
+    _check(mhc, oracle_lib, w, tokens=sample_tokens(w.T, 64, tile=32))
+
+
+def test_one_pass_deterministic_and_agrees_with_two_pass(mhc):
+    w = synth.scaled(synth.WORKLOADS["layer_bf16_T16384_d4096"], T=2048)
+    X = synth.make_state(w)
+    phi, bias = synth.make_params(w)
+    a = _run(mhc, w, X, phi, bias, (1.0, 1.0, 1.0), mhc.PRE_ONE_PASS)
+    b = _run(mhc, w, X, phi, bias, (1.0, 1.0, 1.0), mhc.PRE_ONE_PASS)
+    c = _run(mhc, w, X, phi, bias, (1.0, 1.0, 1.0), mhc.PRE_TWO_PASS)
+    assert a[2] == mhc.PRE_ONE_PASS and c[2] == mhc.PRE_TWO_PASS
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.max(np.abs(a[1].astype(np.float64) - c[1])) < 1e-5
+
+
+def test_one_pass_refuses_what_it_does_not_cover(mhc):
+    cases = [
+        synth.Workload("fp32", T=2048, n=4, d=4096, dtype=synth.FP32),          # fp32 state
+        synth.Workload("small_T", T=64, n=4, d=4096, dtype=synth.BF16),         # too few tiles
+        synth.Workload("narrow", T=4096, n=4, d=1024, dtype=synth.BF16),        # team of 4
+    ]
+    for w in cases:
+        X = to_device(synth.make_state(w))
+        phi, bias = (to_device(a) for a in synth.make_params(w))
+        with pytest.raises(mhc.MhcError) as ei:
+            mhc.pre_ex(X, phi, bias, mhc.PRE_ONE_PASS)
+        assert ei.value.status == 5
+        h, H, used = mhc.pre_ex(X, phi, bias, mhc.PRE_AUTO)      # auto falls back
+        assert used == mhc.PRE_TWO_PASS
