@@ -59,6 +59,14 @@ def _bind(lib):
     lib.mhcref_stack.argtypes = [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _D, _I32, _P, _I64,
                                  _P, _P, _P, _P, _P, _P]
     lib.mhcref_stack.restype = _I32
+    lib.mhcref_bwd.argtypes = [_I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _D, _I32, _P, _P, _P, _I64,
+                               _P, _P, _P, _P, _P, _P, _P]
+    lib.mhcref_bwd.restype = _I32
+    lib.mhcref_layer_f64.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P, _D, _I32, _P, _P]
+    lib.mhcref_layer_f64.restype = _I32
+    lib.mhcref_bwd_f64.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P, _D, _I32, _P, _P,
+                                   _P, _P, _P, _P, _P, _P, _P]
+    lib.mhcref_bwd_f64.restype = _I32
     return lib
 
 
@@ -212,4 +220,61 @@ class Oracle:
         out = {"X": Xf, "H": Hs, "amax": a, "gain_fwd": f, "gain_bwd": b}
         if want_sk:
             out["sk_err"] = sk
+        return out
+
+    def bwd(self, X, Y, phi, bias, alpha, G, D, eps=1e-6, t_max=20, tokens=None):
+        """Gradients of sum_t <G_t, X'_t> + <D_t, h_t> for the listed tokens.
+        X, G [T, n, d] and Y, D [T, d] in the storage form.  Returns dict dX
+        [ntok, n, d], dY [ntok, d], dH, dlogit [ntok, m] and dphi [n*d, m],
+        dbias [m], dalpha [3] summed over the listed tokens (all float64)."""
+        X, Y, G, D = (np.ascontiguousarray(a) for a in (X, Y, G, D))
+        T, n, d = X.shape
+        m = n * n + 2 * n
+        assert G.shape == X.shape and Y.shape == (T, d) and D.shape == (T, d)
+        assert X.dtype == Y.dtype == G.dtype == D.dtype
+        phi = np.ascontiguousarray(phi, dtype=np.float32)
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        a3 = np.ascontiguousarray(np.asarray(alpha, dtype=np.float32).reshape(3))
+        tok = _tokens(T, tokens)
+        q = tok.size
+        out = {"dX": np.empty((q, n, d)), "dY": np.empty((q, d)), "dH": np.empty((q, m)),
+               "dlogit": np.empty((q, m)), "dphi": np.empty((n * d, m)), "dbias": np.empty(m),
+               "dalpha": np.empty(3)}
+        rc = self.lib.mhcref_bwd(T, n, d, _dtype_code(X), _ptr(X), _ptr(Y), _ptr(phi), _ptr(bias), _ptr(a3),
+                                 float(eps), int(t_max), _ptr(G), _ptr(D), _ptr(tok), q, _ptr(out["dX"]),
+                                 _ptr(out["dY"]), _ptr(out["dH"]), _ptr(out["dlogit"]), _ptr(out["dphi"]),
+                                 _ptr(out["dbias"]), _ptr(out["dalpha"]))
+        if rc != 0:
+            raise ValueError(f"mhcref_bwd rejected its arguments ({rc})")
+        return out
+
+    @staticmethod
+    def _f64(*arrays):
+        return [np.ascontiguousarray(a, dtype=np.float64) for a in arrays]
+
+    def layer_f64(self, X, Y, phi, bias, alpha, eps=1e-6, t_max=20):
+        """The layer forward with every value in double: returns (h [T, d], X' [T, n, d])."""
+        X, Y, phi, bias, alpha = self._f64(X, Y, phi, bias, np.asarray(alpha).reshape(3))
+        T, n, d = X.shape
+        h, Xo = np.empty((T, d)), np.empty((T, n, d))
+        rc = self.lib.mhcref_layer_f64(T, n, d, _ptr(X), _ptr(Y), _ptr(phi), _ptr(bias), _ptr(alpha), float(eps),
+                                       int(t_max), _ptr(h), _ptr(Xo))
+        if rc != 0:
+            raise ValueError(f"mhcref_layer_f64 rejected its arguments ({rc})")
+        return h, Xo
+
+    def bwd_f64(self, X, Y, phi, bias, alpha, G, D, eps=1e-6, t_max=20):
+        """Backward of layer_f64 over all tokens; same dict as bwd."""
+        X, Y, phi, bias, alpha, G, D = self._f64(X, Y, phi, bias, np.asarray(alpha).reshape(3), G, D)
+        T, n, d = X.shape
+        m = n * n + 2 * n
+        out = {"dX": np.empty((T, n, d)), "dY": np.empty((T, d)), "dH": np.empty((T, m)),
+               "dlogit": np.empty((T, m)), "dphi": np.empty((n * d, m)), "dbias": np.empty(m),
+               "dalpha": np.empty(3)}
+        rc = self.lib.mhcref_bwd_f64(T, n, d, _ptr(X), _ptr(Y), _ptr(phi), _ptr(bias), _ptr(alpha), float(eps),
+                                     int(t_max), _ptr(G), _ptr(D), _ptr(out["dX"]), _ptr(out["dY"]),
+                                     _ptr(out["dH"]), _ptr(out["dlogit"]), _ptr(out["dphi"]), _ptr(out["dbias"]),
+                                     _ptr(out["dalpha"]))
+        if rc != 0:
+            raise ValueError(f"mhcref_bwd_f64 rejected its arguments ({rc})")
         return out

@@ -26,6 +26,13 @@
 // in every one of t_max iterations, with plain division and no early exit;
 // the composite map is H_L ... H_1 (each new layer multiplies from the left).
 //
+// The backward (gradients of <G, X'> + <D, h> for given G and D) is the chain
+// rule of this forward in reverse; the pages state only that training uses a
+// custom backward that recomputes the maps ([P5] mixed-precision table).  It
+// is pinned by central finite differences of the all-double forward and by
+// exact identities (column-shift invariance of Sinkhorn, the alpha = 0 closed
+// form, Euler's theorem for the scale-invariant RMSNorm).
+//
 // Parity pins: Sinkhorn, gates, aggregation, mixing and Amax are pinned by the
 // pages' worked examples and closed forms (see tests/test_oracle_pins.py).
 // RMSNorm and the projection have no printed values on the pages; they are
@@ -135,8 +142,9 @@ struct TokenMaps {
                                     // after the last row step:    max|colsum-1|, max|rowsum-1|
 };
 
-TokenMaps token_maps(int n, int d, const std::vector<double>& x, const float* phi,
-                     const float* bias, const float* alpha3, double eps, int t_max) {
+template <typename P>
+TokenMaps token_maps(int n, int d, const std::vector<double>& x, const P* phi,
+                     const P* bias, const P* alpha3, double eps, int t_max) {
   const int K = n * d;
   const int m = n * n + 2 * n;
   TokenMaps out;
@@ -202,6 +210,162 @@ void mix(int n, int d, const std::vector<double>& x, const std::vector<double>& 
   }
 }
 
+// ---- backward of one token (reading: the pages give no backward formulas, only
+// that the layer is trained with a custom backward that recomputes the maps;
+// this is the chain rule of the forward above, step by step in reverse).
+// The differentiated quantity is L = <G, X'> + <D, h>: G is the gradient
+// arriving at the layer output X' and D the gradient arriving at the sublayer
+// input h, both taken as given (F stays outside the layer, as in the forward).
+
+// Sinkhorn backward: forward again keeping every iterate, then reverse the
+// 2 * t_max normalisations.  dM (n x n) enters as dL/dH_res and leaves as
+// dL/dlogits_res.
+void sinkhorn_backward(int n, const double* logits, int t_max, double* dM) {
+  const int nn = n * n;
+  // iter[s] is the matrix before normalisation s (s = 2t: column step of
+  // iteration t, s = 2t + 1: its row step); sums[s] the divisors it used.
+  std::vector<double> iter(static_cast<size_t>(2 * t_max + 1) * nn), sums(static_cast<size_t>(2 * t_max) * n);
+  double* M0 = iter.data();
+  for (int i = 0; i < nn; ++i) M0[i] = std::exp(logits[i]);
+  for (int st = 0; st < 2 * t_max; ++st) {
+    const double* A = iter.data() + static_cast<size_t>(st) * nn;
+    double* B = iter.data() + static_cast<size_t>(st + 1) * nn;
+    double* sm = sums.data() + static_cast<size_t>(st) * n;
+    const bool col = (st % 2 == 0);
+    for (int a = 0; a < n; ++a) {
+      sm[a] = 0.0;
+      for (int b = 0; b < n; ++b) sm[a] += col ? A[b * n + a] : A[a * n + b];
+    }
+    for (int i = 0; i < n; ++i)
+      for (int j = 0; j < n; ++j) B[i * n + j] = A[i * n + j] / (col ? sm[j] : sm[i]);
+  }
+  // Reverse.  For B = A / s with s the sum of A's line (row or column):
+  // dA = (dB - <dB, B> over that line) / s.
+  std::vector<double> dA(nn);
+  for (int st = 2 * t_max - 1; st >= 0; --st) {
+    const double* B = iter.data() + static_cast<size_t>(st + 1) * nn;
+    const double* sm = sums.data() + static_cast<size_t>(st) * n;
+    const bool col = (st % 2 == 0);
+    for (int a = 0; a < n; ++a) {
+      double dot = 0.0;
+      for (int b = 0; b < n; ++b) {
+        const int e = col ? b * n + a : a * n + b;
+        dot += dM[e] * B[e];
+      }
+      for (int b = 0; b < n; ++b) {
+        const int e = col ? b * n + a : a * n + b;
+        dA[e] = (dM[e] - dot) / sm[a];
+      }
+    }
+    for (int i = 0; i < nn; ++i) dM[i] = dA[i];
+  }
+  // M0 = exp(logits)
+  for (int i = 0; i < nn; ++i) dM[i] *= M0[i];
+}
+
+struct TokenGrads {
+  std::vector<double> dx;       // K
+  std::vector<double> dy;       // d
+  std::vector<double> dH;       // m: dL/dH (pre | res | post)
+  std::vector<double> dlogit;   // m
+  std::vector<double> dz;       // m
+  std::vector<double> xhat;     // K
+  double dalpha[3] = {0, 0, 0};
+};
+
+template <typename P>
+TokenGrads token_backward(int n, int d, const std::vector<double>& x, const std::vector<double>& y,
+                          const P* phi, const P* bias, const P* alpha3, double eps, int t_max,
+                          const std::vector<double>& G, const std::vector<double>& D) {
+  const int K = n * d;
+  const int m = n * n + 2 * n;
+  const TokenMaps tm = token_maps(n, d, x, phi, bias, alpha3, eps, t_max);
+  const double* Hpre = &tm.H[0];
+  const double* Hres = &tm.H[n];
+  const double* Hpost = &tm.H[n + n * n];
+  TokenGrads g;
+  g.dx.assign(K, 0.0);
+  g.dy.assign(d, 0.0);
+  g.dH.assign(m, 0.0);
+  // Mixing + broadcast-add: X'_i = sum_j H_res[i][j] X_j + H_post[i] Y.
+  for (int i = 0; i < n; ++i) {
+    for (int j = 0; j < n; ++j) {
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c) acc += G[i * d + c] * x[j * d + c];
+      g.dH[n + i * n + j] = acc;
+    }
+    double acc = 0.0;
+    for (int c = 0; c < d; ++c) acc += G[i * d + c] * y[c];
+    g.dH[n + n * n + i] = acc;
+  }
+  for (int c = 0; c < d; ++c) {
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i) acc += Hpost[i] * G[i * d + c];
+    g.dy[c] = acc;
+  }
+  for (int j = 0; j < n; ++j)
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int i = 0; i < n; ++i) acc += Hres[i * n + j] * G[i * d + c];
+      g.dx[j * d + c] += acc;
+    }
+  // Aggregation: h = sum_i H_pre[i] X_i.
+  for (int i = 0; i < n; ++i) {
+    double acc = 0.0;
+    for (int c = 0; c < d; ++c) acc += D[c] * x[i * d + c];
+    g.dH[i] = acc;
+    for (int c = 0; c < d; ++c) g.dx[i * d + c] += Hpre[i] * D[c];
+  }
+  // Maps: sigmoid gates, 2 * sigmoid gate, Sinkhorn on exp(logits_res).
+  g.dlogit.assign(m, 0.0);
+  for (int i = 0; i < n; ++i) {
+    const double sp = Hpre[i];
+    g.dlogit[i] = g.dH[i] * sp * (1.0 - sp);
+    const double sq = Hpost[i] / 2.0;
+    g.dlogit[n + n * n + i] = g.dH[n + n * n + i] * 2.0 * sq * (1.0 - sq);
+  }
+  std::vector<double> dM(g.dH.begin() + n, g.dH.begin() + n + n * n);
+  sinkhorn_backward(n, &tm.logit[n], t_max, dM.data());
+  for (int e = 0; e < n * n; ++e) g.dlogit[n + e] = dM[e];
+  // logits = alpha_blk * z + bias.
+  g.dz.assign(m, 0.0);
+  for (int j = 0; j < m; ++j) {
+    const int blk = (j < n) ? 0 : (j < n + n * n) ? 1 : 2;
+    g.dalpha[blk] += g.dlogit[j] * tm.z[j];
+    g.dz[j] = static_cast<double>(alpha3[blk]) * g.dlogit[j];
+  }
+  // z = x_hat . phi with x_hat = x / r, r = sqrt(sum(x^2) / K + eps).
+  g.xhat.assign(K, 0.0);
+  for (int k = 0; k < K; ++k) g.xhat[k] = x[k] / tm.r;
+  std::vector<double> dxh(K, 0.0);
+  for (int k = 0; k < K; ++k) {
+    double acc = 0.0;
+    for (int j = 0; j < m; ++j) acc += static_cast<double>(phi[static_cast<int64_t>(k) * m + j]) * g.dz[j];
+    dxh[k] = acc;
+  }
+  // dL/dr = -sum_k dxh_k x_k / r^2;  dr/dx_k = x_k / (K r).
+  double dr = 0.0;
+  for (int k = 0; k < K; ++k) dr -= dxh[k] * x[k] / (tm.r * tm.r);
+  for (int k = 0; k < K; ++k) g.dx[k] += dxh[k] / tm.r + dr * x[k] / (K * tm.r);
+  return g;
+}
+
+// Parameter gradients are sums over tokens: dphi = sum_t x_hat_t^T dz_t,
+// dbias = sum_t dlogit_t, dalpha = sum_t (per-block <dlogit, z>).
+void clear_param_grads(int K, int m, double* dphi, double* dbias, double* dalpha) {
+  if (dphi) for (int64_t i = 0; i < static_cast<int64_t>(K) * m; ++i) dphi[i] = 0.0;
+  if (dbias) for (int j = 0; j < m; ++j) dbias[j] = 0.0;
+  if (dalpha) for (int j = 0; j < 3; ++j) dalpha[j] = 0.0;
+}
+
+void add_param_grads(const TokenGrads& tg, int K, int m, double* dphi, double* dbias, double* dalpha) {
+  if (dphi)
+    for (int k = 0; k < K; ++k)
+      for (int j = 0; j < m; ++j) dphi[static_cast<int64_t>(k) * m + j] += tg.xhat[k] * tg.dz[j];
+  if (dbias) for (int j = 0; j < m; ++j) dbias[j] += tg.dlogit[j];
+  if (dalpha) for (int j = 0; j < 3; ++j) dalpha[j] += tg.dalpha[j];
+}
+
 // Composite map P = H_L ... H_1 and its Amax Gain Magnitude ([P2] samengestelde
 // map: max absolute row sum (forward) and column sum (backward)).
 template <typename Real>
@@ -243,7 +407,7 @@ bool bad_shape(int64_t T, int n, int d, int dtype) {
 
 extern "C" {
 
-int mhcref_version(void) { return 1; }
+int mhcref_version(void) { return 2; }
 
 // Rounding helpers exposed for the tests: round doubles to bf16 bits (RNE).
 void mhcref_round_bf16(const double* in, uint16_t* out, int64_t count) {
@@ -386,6 +550,82 @@ int mhcref_stack(int64_t T, int n, int d, int dtype, int L, const void* X0, cons
       if (gbwd) gbwd[q] = b;
       if (amax) amax[q] = std::fmax(f, b);
     }
+  }
+  return 0;
+}
+
+// ---- backward ---------------------------------------------------------------
+// Gradients of L = sum_t <G_t, X'_t> + <D_t, h_t> for the listed tokens.
+//   X, G [T, n, d]; Y, D [T, d] in the storage dtype; phi [n*d, m], bias [m],
+//   alpha3 [3] fp32.  Outputs in double: dX [ntok, n, d], dY [ntok, d],
+//   dH [ntok, m] (nullable), dlogit [ntok, m] (nullable); dphi [n*d, m],
+//   dbias [m] and dalpha [3] (nullable) are sums over the listed tokens.
+int mhcref_bwd(int64_t T, int n, int d, int dtype, const void* X, const void* Y, const float* phi,
+               const float* bias, const float* alpha3, double eps, int t_max, const void* G,
+               const void* D, const int64_t* tokens, int64_t ntok, double* dX, double* dY, double* dH,
+               double* dlogit, double* dphi, double* dbias, double* dalpha) {
+  if (bad_shape(T, n, d, dtype) || t_max < 0 || !X || !Y || !phi || !bias || !alpha3 || !G || !D ||
+      !dX || !dY)
+    return -1;
+  const int K = n * d;
+  const int m = n * n + 2 * n;
+  clear_param_grads(K, m, dphi, dbias, dalpha);
+  std::vector<double> x(K), g(K), y(d), dd(d);
+  for (int64_t q = 0; q < ntok; ++q) {
+    const int64_t t = tokens[q];
+    if (t < 0 || t >= T) return -2;
+    for (int k = 0; k < K; ++k) { x[k] = load(dtype, X, t * K + k); g[k] = load(dtype, G, t * K + k); }
+    for (int c = 0; c < d; ++c) { y[c] = load(dtype, Y, t * d + c); dd[c] = load(dtype, D, t * d + c); }
+    const TokenGrads tg = token_backward(n, d, x, y, phi, bias, alpha3, eps, t_max, g, dd);
+    for (int k = 0; k < K; ++k) dX[q * K + k] = tg.dx[k];
+    for (int c = 0; c < d; ++c) dY[q * d + c] = tg.dy[c];
+    if (dH) for (int j = 0; j < m; ++j) dH[q * m + j] = tg.dH[j];
+    if (dlogit) for (int j = 0; j < m; ++j) dlogit[q * m + j] = tg.dlogit[j];
+    add_param_grads(tg, K, m, dphi, dbias, dalpha);
+  }
+  return 0;
+}
+
+// The same layer entirely in double (inputs, parameters, outputs; no storage
+// rounding), for the finite-difference checks of the backward.
+//   X [T, n, d], Y [T, d], phi [n*d, m], bias [m], alpha3 [3]; outputs
+//   h [T, d] and Xo [T, n, d].
+int mhcref_layer_f64(int64_t T, int n, int d, const double* X, const double* Y, const double* phi,
+                     const double* bias, const double* alpha3, double eps, int t_max, double* h,
+                     double* Xo) {
+  if (bad_shape(T, n, d, 0) || t_max < 0 || !X || !Y || !phi || !bias || !alpha3 || !h || !Xo) return -1;
+  const int K = n * d;
+  std::vector<double> x(K), y(d);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int k = 0; k < K; ++k) x[k] = X[t * K + k];
+    for (int c = 0; c < d; ++c) y[c] = Y[t * d + c];
+    const TokenMaps tm = token_maps(n, d, x, phi, bias, alpha3, eps, t_max);
+    aggregate(n, d, x, tm.H.data(), h + t * d);
+    mix(n, d, x, y, &tm.H[n], &tm.H[n + n * n], Xo + t * K);
+  }
+  return 0;
+}
+
+// Backward of mhcref_layer_f64 over all T tokens (same outputs as mhcref_bwd).
+int mhcref_bwd_f64(int64_t T, int n, int d, const double* X, const double* Y, const double* phi,
+                   const double* bias, const double* alpha3, double eps, int t_max, const double* G,
+                   const double* D, double* dX, double* dY, double* dH, double* dlogit, double* dphi,
+                   double* dbias, double* dalpha) {
+  if (bad_shape(T, n, d, 0) || t_max < 0 || !X || !Y || !phi || !bias || !alpha3 || !G || !D || !dX || !dY)
+    return -1;
+  const int K = n * d;
+  const int m = n * n + 2 * n;
+  clear_param_grads(K, m, dphi, dbias, dalpha);
+  std::vector<double> x(K), g(K), y(d), dd(d);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int k = 0; k < K; ++k) { x[k] = X[t * K + k]; g[k] = G[t * K + k]; }
+    for (int c = 0; c < d; ++c) { y[c] = Y[t * d + c]; dd[c] = D[t * d + c]; }
+    const TokenGrads tg = token_backward(n, d, x, y, phi, bias, alpha3, eps, t_max, g, dd);
+    for (int k = 0; k < K; ++k) dX[t * K + k] = tg.dx[k];
+    for (int c = 0; c < d; ++c) dY[t * d + c] = tg.dy[c];
+    if (dH) for (int j = 0; j < m; ++j) dH[t * m + j] = tg.dH[j];
+    if (dlogit) for (int j = 0; j < m; ++j) dlogit[t * m + j] = tg.dlogit[j];
+    add_param_grads(tg, K, m, dphi, dbias, dalpha);
   }
   return 0;
 }

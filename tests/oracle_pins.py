@@ -442,4 +442,159 @@ def pin_stack_matches_layers(o):
     assert np.array_equal(am["amax"], st["amax"])
 
 
+# --------------------------------------------------------------------------
+# Backward.  The pages give no backward formulas, only that the layer trains
+# with a custom backward that recomputes the maps ([P5] mixed-precision table
+# and kernel notes); the oracle's backward is the chain rule of its forward.
+# It is pinned by central finite differences of the all-double forward and by
+# exact identities of the forward.  The differentiated quantity is
+# L = sum_t <G_t, X'_t> + <D_t, h_t> with G and D given.
+
+def _bwd_inputs(rng, T, n, d, alpha):
+    X, phi, bias, al, Y = _layer_inputs(rng, T, n, d, alpha)
+    G = rng.normal(0.0, 1.0, (T, n, d)).astype(np.float32)
+    D = rng.normal(0.0, 1.0, (T, d)).astype(np.float32)
+    return X, Y, phi, bias, al, G, D
+
+
+def _loss(o, X, Y, phi, bias, al, G, D, eps, t_max):
+    h, Xo = o.layer_f64(X, Y, phi, bias, al, eps=eps, t_max=t_max)
+    return float(np.sum(G.astype(np.float64) * Xo) + np.sum(D.astype(np.float64) * h))
+
+
+def _fd_check(o, args, which, idx, analytic, eps, t_max, step, rtol, atol):
+    """Central differences of L in the coordinates ``idx`` of argument ``which``."""
+    base = [np.array(a, dtype=np.float64) for a in args]
+    worst = 0.0
+    for flat in idx:
+        plus = [a.copy() for a in base]
+        minus = [a.copy() for a in base]
+        plus[which].reshape(-1)[flat] += step
+        minus[which].reshape(-1)[flat] -= step
+        fd = (_loss(o, *plus, eps=eps, t_max=t_max) - _loss(o, *minus, eps=eps, t_max=t_max)) / (2.0 * step)
+        an = float(np.asarray(analytic).reshape(-1)[flat])
+        err = abs(fd - an)
+        worst = max(worst, err / (atol + rtol * abs(an)))
+        assert err <= atol + rtol * abs(an), (which, flat, fd, an)
+    return worst
+
+
+def pin_bwd_finite_differences(o):
+    """Every gradient (X, Y, phi, bias, alpha) against central differences of
+    the all-double forward, on a T = 8, n = 4, d = 32 slice of the layer
+    workload's distributions, at the workload's alpha and at a large alpha
+    that makes the projection, gates and Sinkhorn matter."""
+    rng = np.random.default_rng(31)
+    T, n, d = 8, 4, 32
+    m = n * n + 2 * n
+    for alpha in ((0.01, 0.01, 0.01), (1.0, 0.7, -0.4)):
+        X, Y, phi, bias, al, G, D = _bwd_inputs(rng, T, n, d, alpha)
+        g = o.bwd_f64(X, Y, phi, bias, al, G, D, eps=1e-6, t_max=20)
+        args = (X, Y, phi, bias, al, G, D)
+        pick = lambda size, k: rng.choice(size, size=min(k, size), replace=False)
+        # X: 48 coordinates spread over tokens and streams; Y: 16
+        _fd_check(o, args, 0, pick(T * n * d, 48), g["dX"], 1e-6, 20, 1e-5, 1e-6, 1e-8)
+        _fd_check(o, args, 1, pick(T * d, 16), g["dY"], 1e-6, 20, 1e-5, 1e-6, 1e-8)
+        # phi: two entries of every column
+        cols = np.repeat(np.arange(m), 2)
+        rows = rng.integers(0, n * d, cols.size)
+        _fd_check(o, args, 2, rows * m + cols, g["dphi"], 1e-6, 20, 1e-5, 1e-6, 1e-8)
+        _fd_check(o, args, 3, np.arange(m), g["dbias"], 1e-6, 20, 1e-5, 1e-6, 1e-8)
+        _fd_check(o, args, 4, np.arange(3), g["dalpha"], 1e-6, 20, 1e-6, 1e-6, 1e-8)
+
+
+def pin_bwd_single_token_logits(o):
+    """With one token the bias gradient is that token's logit gradient, so
+    central differences in the bias pin dlogit (and through it dH) per token,
+    also after a single Sinkhorn pass and with no pass at all."""
+    rng = np.random.default_rng(32)
+    n, d = 3, 5
+    for t_max in (0, 1, 20):
+        X, Y, phi, bias, al, G, D = _bwd_inputs(rng, 1, n, d, (0.8, 1.3, -0.6))
+        g = o.bwd_f64(X, Y, phi, bias, al, G, D, eps=1e-6, t_max=t_max)
+        assert np.array_equal(g["dlogit"][0], g["dbias"])
+        _fd_check(o, (X, Y, phi, bias, al, G, D), 3, np.arange(n * n + 2 * n), g["dbias"], 1e-6, t_max,
+                  1e-5, 1e-6, 1e-8)
+
+
+def pin_bwd_column_shift_invariance(o):
+    """Adding a constant to one column of the residual logits scales that
+    column of exp(.) and is undone exactly by the first column normalisation,
+    so each column of dL/dlogits_res sums to zero (row shifts are not exact)."""
+    rng = np.random.default_rng(33)
+    T, n, d = 4, 4, 16
+    X, Y, phi, bias, al, G, D = _bwd_inputs(rng, T, n, d, (1.0, 1.0, 1.0))
+    for t_max in (1, 20):
+        g = o.bwd_f64(X, Y, phi, bias, al, G, D, t_max=t_max)
+        dres = g["dlogit"][:, n:n + n * n].reshape(T, n, n)
+        scale = np.max(np.abs(dres))
+        assert scale > 1e-3
+        assert np.max(np.abs(dres.sum(axis=1))) <= 1e-13 * scale, dres.sum(axis=1)
+        if t_max == 1:      # one pass is far from converged: row shifts do change the result
+            assert np.max(np.abs(dres.sum(axis=2))) > 1e-3 * scale
+
+
+def pin_bwd_alpha0_closed_form(o):
+    """alpha = 0: the maps do not depend on X, so dX_j = sum_i H_res[i][j] G_i
+    + sigmoid(b_pre,j) D and dY = sum_i 2 sigmoid(b_post,i) G_i with
+    H_res = SK(exp(b_res)); dphi = 0; dH_res[i][j] = <G_i, X_j>,
+    dH_post[i] = <G_i, Y>, dH_pre[i] = <D, X_i>."""
+    rng = np.random.default_rng(34)
+    T, n, d = 3, 4, 8
+    X, Y, phi, bias, _, G, D = _bwd_inputs(rng, T, n, d, (0.0, 0.0, 0.0))
+    g = o.bwd_f64(X, Y, phi, bias, (0.0, 0.0, 0.0), G, D)
+    b = bias.astype(np.float64)
+    Hres = o.sinkhorn(b[n:n + n * n].reshape(n, n), 20)
+    spre = 1.0 / (1.0 + np.exp(-b[:n]))
+    wpost = 2.0 / (1.0 + np.exp(-b[n + n * n:]))
+    Xd, Gd, Yd, Dd = (a.astype(np.float64) for a in (X, G, Y, D))
+    for t in range(T):
+        assert np.allclose(g["dX"][t], Hres.T @ Gd[t] + spre[:, None] * Dd[t][None, :], rtol=1e-13, atol=1e-14)
+        assert np.allclose(g["dY"][t], wpost @ Gd[t], rtol=1e-13, atol=1e-14)
+        assert np.allclose(g["dH"][t, n:n + n * n].reshape(n, n), Gd[t] @ Xd[t].T, rtol=1e-13, atol=1e-13)
+        assert np.allclose(g["dH"][t, n + n * n:], Gd[t] @ Yd[t], rtol=1e-13, atol=1e-13)
+        assert np.allclose(g["dH"][t, :n], Xd[t] @ Dd[t], rtol=1e-13, atol=1e-13)
+    assert np.all(g["dphi"] == 0.0)
+
+
+def pin_bwd_euler_homogeneity(o):
+    """With eps = 0 the maps are invariant to scaling X, so h and X' - H_post Y
+    are homogeneous of degree 1 in X (Euler): sum x . dx equals
+    sum_t <G_t, H_res X_t> + <D_t, h_t>, i.e. the RMSNorm path's share of dx
+    is orthogonal to x."""
+    rng = np.random.default_rng(35)
+    T, n, d = 3, 4, 8
+    X, Y, phi, bias, _, G, D = _bwd_inputs(rng, T, n, d, (1.0, 1.0, 1.0))
+    al = (1.5, 0.8, -1.1)
+    g = o.bwd_f64(X, Y, phi, bias, al, G, D, eps=0.0)
+    h, Xo = o.layer_f64(X, np.zeros_like(Y), phi, bias, al, eps=0.0)
+    lhs = float(np.sum(X.astype(np.float64) * g["dX"]))
+    rhs = float(np.sum(G.astype(np.float64) * Xo) + np.sum(D.astype(np.float64) * h))
+    assert abs(lhs - rhs) <= 1e-11 * (abs(rhs) + 1.0), (lhs, rhs)
+
+
+def pin_bwd_storage_forms_agree(o):
+    """The storage-typed backward (fp32 and bf16 state, any token list) gives
+    the all-double backward's values on the same numbers; parameter gradients
+    add over disjoint token lists."""
+    rng = np.random.default_rng(36)
+    T, n, d = 5, 4, 8
+    X, Y, phi, bias, al, G, D = _bwd_inputs(rng, T, n, d, (0.5, 0.5, 0.5))
+    ref = o.bwd_f64(X, Y, phi, bias, al, G, D)
+    got = o.bwd(X, Y, phi, bias, al, G, D)
+    for k in ref:
+        assert np.allclose(got[k], ref[k], rtol=1e-14, atol=1e-15), k
+    bits = [o.round_bf16(a.astype(np.float64)) for a in (X, Y, G, D)]
+    vals = [(b.astype(np.uint32) << 16).view(np.float32) for b in bits]
+    refb = o.bwd_f64(vals[0], vals[1], phi, bias, al, vals[2], vals[3])
+    gotb = o.bwd(bits[0], bits[1], phi, bias, al, bits[2], bits[3])
+    for k in refb:
+        assert np.allclose(gotb[k], refb[k], rtol=1e-14, atol=1e-15), k
+    a = o.bwd(X, Y, phi, bias, al, G, D, tokens=[4, 1])
+    b = o.bwd(X, Y, phi, bias, al, G, D, tokens=[0, 2, 3])
+    assert np.allclose(a["dX"], ref["dX"][[4, 1]], rtol=1e-15, atol=0)
+    for k in ("dphi", "dbias", "dalpha"):
+        assert np.allclose(a[k] + b[k], ref[k], rtol=1e-12, atol=1e-15), k
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -23,7 +23,8 @@ MUTANTS = {
     "rms_eps_outside_sqrt": ("std::sqrt(ss / K + eps)", "std::sqrt(ss / K) + eps"),
     "rms_mean_over_d": ("std::sqrt(ss / K + eps)", "std::sqrt(ss / d + eps)"),
     "rms_not_applied": ("acc += xh[k] *", "acc += x[k] *"),
-    "phi_transposed": ("phi[static_cast<int64_t>(k) * m + j]", "phi[static_cast<int64_t>(j) * K + k]"),
+    "phi_transposed": ("acc += xh[k] * static_cast<double>(phi[static_cast<int64_t>(k) * m + j]);",
+                       "acc += xh[k] * static_cast<double>(phi[static_cast<int64_t>(j) * K + k]);"),
     "alpha_blocks_swapped": ("(j < n) ? alpha3[0] : (j < n + n * n) ? alpha3[1] : alpha3[2]",
                              "(j < n) ? alpha3[2] : (j < n + n * n) ? alpha3[1] : alpha3[0]"),
     "bias_dropped": ("out.logit[j] = a * out.z[j] + static_cast<double>(bias[j]);", "out.logit[j] = a * out.z[j];"),
@@ -49,6 +50,22 @@ MUTANTS = {
                     "rs += P[i * n + j]; cs += P[j * n + i];"),
     "bf16_truncates": ("std::nearbyint(a / q) * q", "std::trunc(a / q) * q"),
     "gelu_wrong_cdf": ("std::erf(h / std::sqrt(2.0))", "std::tanh(h / std::sqrt(2.0))"),
+    "bwd_rms_drops_radius_term": ("g.dx[k] += dxh[k] / tm.r + dr * x[k] / (K * tm.r);", "g.dx[k] += dxh[k] / tm.r;"),
+    "bwd_sinkhorn_sign": ("dA[e] = (dM[e] - dot) / sm[a];", "dA[e] = (dM[e] + dot) / sm[a];"),
+    "bwd_sinkhorn_forward_order": ("for (int st = 2 * t_max - 1; st >= 0; --st) {",
+                                   "for (int st = 0; st < 2 * t_max; ++st) {"),
+    "bwd_sinkhorn_no_exp_factor": ("for (int i = 0; i < nn; ++i) dM[i] *= M0[i];", ""),
+    "bwd_write_gate_not_doubled": ("g.dH[n + n * n + i] * 2.0 * sq * (1.0 - sq);",
+                                   "g.dH[n + n * n + i] * sq * (1.0 - sq);"),
+    "bwd_mix_not_transposed": ("acc += Hres[i * n + j] * G[i * d + c];", "acc += Hres[j * n + i] * G[i * d + c];"),
+    "bwd_alpha_from_logits": ("g.dalpha[blk] += g.dlogit[j] * tm.z[j];", "g.dalpha[blk] += g.dlogit[j] * tm.logit[j];"),
+    "bwd_dz_without_alpha": ("g.dz[j] = static_cast<double>(alpha3[blk]) * g.dlogit[j];", "g.dz[j] = g.dlogit[j];"),
+    "bwd_dphi_unnormalised": ("g.xhat[k] = x[k] / tm.r;", "g.xhat[k] = x[k];"),
+    "bwd_dy_uses_read_map": ("acc += Hpost[i] * G[i * d + c];", "acc += Hpre[i] * G[i * d + c];"),
+    "bwd_drops_aggregation": ("for (int c = 0; c < d; ++c) g.dx[i * d + c] += Hpre[i] * D[c];", ""),
+    "bwd_dHres_transposed": ("acc += G[i * d + c] * x[j * d + c];", "acc += G[j * d + c] * x[i * d + c];"),
+    "bwd_dHpre_uses_output_grad": ("for (int c = 0; c < d; ++c) acc += D[c] * x[i * d + c];",
+                                   "for (int c = 0; c < d; ++c) acc += G[i * d + c] * x[i * d + c];"),
     "stack_skips_rounding": ("for (int k = 0; k < K; ++k) x[k] = store_round(dtype, xo[k]);",
                              "for (int k = 0; k < K; ++k) x[k] = xo[k];"),
 }
