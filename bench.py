@@ -42,6 +42,72 @@ def algorithmic_bytes(T, n, d, sbytes):
     return {"mhc_pre": pre, "mhc_post": post, "mhc_amax": amax}
 
 
+def backward_bytes(T, n, d, sbytes):
+    """Bytes the backward entry points must move.  post_bwd: X, G, Y and the
+    mixing / write maps in; dX, dY and their dH columns out.  pre_bwd
+    recomputes the maps, so it reads X and D twice (the token's dlogits are
+    known only after a full pass), dX once to update it and dH's columns;
+    it writes dX, and reads phi and writes dphi once."""
+    m = n * n + 2 * n
+    K = n * d
+    post = T * (3 * K * sbytes + 2 * d * sbytes + 8 * (n * n + n))
+    pre = T * (3 * K * sbytes + 2 * d * sbytes + 4 * (n * n + n) + K * sbytes) + 2 * K * m * 4 + 4 * (m + 3)
+    return {"mhc_post_bwd": post, "mhc_pre_bwd": pre}
+
+
+def time_backward(mhc, torch, w, X, Y, phi, bias, H, steps, warmup, stream):
+    """Average time of mhc_post_bwd and mhc_pre_bwd on the layer forward +
+    backward workload's gradients (same shapes as the forward workload)."""
+    import numpy as np
+
+    import synth
+    wb = synth.WORKLOADS["layer_fwdbwd_bf16_T16384_d4096"]
+    if (wb.T, wb.n, wb.d, wb.dtype) != (w.T, w.n, w.d, w.dtype):
+        return None
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+
+    G, D = (dev(a) for a in synth.make_grads(wb))
+    T, n, d = w.T, w.n, w.d
+    m = n * n + 2 * n
+    dX = torch.empty_like(X)
+    dY = torch.empty_like(Y)
+    dH = torch.zeros((T, m), dtype=torch.float32, device="cuda")
+    dphi = torch.empty((n * d, m), dtype=torch.float32, device="cuda")
+    dbias = torch.empty(m, dtype=torch.float32, device="cuda")
+    dalpha = torch.empty(3, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mhc.pre_bwd_workspace_size(T, n, d, w.dtype), dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mhc.post_bwd(X, Y, H, G, dX=dX, dY=dY, dH=dH, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        mhc.pre_bwd(X, phi, bias, D, dH, dX, alpha=w.alpha, eps=w.eps, t_max=w.t_max, dphi=dphi, dbias=dbias,
+                    dalpha=dalpha, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    sb = 2 if w.dtype == synth.BF16 else 4
+    algo = backward_bytes(T, n, d, sb)
+    out = {"workload": wb.name, "steps": steps}
+    for name, (a, b) in (("mhc_post_bwd", (0, 1)), ("mhc_pre_bwd", (1, 2))):
+        avg_ms = float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+        out[name] = {"avg_us": avg_ms * 1e3, "algorithmic_bytes": algo[name],
+                     "GBps": algo[name] / (avg_ms * 1e-3) / 1e9}
+    out["fwd_bwd_tokens_per_s"] = None
+    return out
+
+
 def traffic_bytes(path, workload, entry):
     """HBM bytes per launch of an entry point measured with rocprofv3
     counters, or None when absent or when the kernel source changed since."""
@@ -93,6 +159,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer_bf16_T16384_d4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--pre-algo", type=int, default=0, choices=[0, 1, 2],
                     help="mhc_pre form: 0 auto, 1 two-pass, 2 one-pass")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
@@ -208,6 +275,17 @@ def main():
     log(f"{ms_step * 1e3:.1f} us/step, {tokens_per_s / 1e6:.2f} M tokens/s; "
         + ", ".join(f"{k} {v['avg_us']:.1f} us ({v['GBps']:.0f} GB/s)" for k, v in kernels.items()))
 
+    backward = None
+    if not args.no_backward:
+        log("timing the backward (mhc_post_bwd + mhc_pre_bwd)")
+        backward = time_backward(mhc, torch, w, X, Y, phi, bias, H, max(5, K // 2), 3, stream)
+        if backward is not None:
+            bwd_us = backward["mhc_post_bwd"]["avg_us"] + backward["mhc_pre_bwd"]["avg_us"]
+            backward["fwd_bwd_tokens_per_s"] = T / ((ms_step * 1e3 + bwd_us) * 1e-6)
+            log(f"backward: post_bwd {backward['mhc_post_bwd']['avg_us']:.1f} us "
+                f"({backward['mhc_post_bwd']['GBps']:.0f} GB/s), pre_bwd {backward['mhc_pre_bwd']['avg_us']:.1f} us "
+                f"({backward['mhc_pre_bwd']['GBps']:.0f} GB/s)")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -238,6 +316,7 @@ def main():
         "wall_s_timed_region": t_wall,
         "roofline": roofline,
         "kernels": kernels,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 1
+#define MHC_ABI_VERSION 2
 
 typedef enum mhc_status {
   MHC_OK = 0,
@@ -66,7 +66,7 @@ typedef enum mhc_status {
   MHC_ERR_ALIGN = 4,        /* a tensor base pointer is not 16-byte aligned */
   MHC_ERR_UNSUPPORTED = 5,  /* valid for the method but not built for the device (n = 3, d % 8 != 0) */
   MHC_ERR_ALIAS = 6,        /* an output overlaps an input other than the permitted exact alias */
-  MHC_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than mhc_pre_workspace_size() */
+  MHC_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than the entry point's size query */
   MHC_ERR_HIP = 8           /* a HIP runtime call or a kernel launch failed */
 } mhc_status;
 
@@ -155,6 +155,47 @@ mhc_status mhc_pre_ex(const mhc_params* p, const void* X, const float* phi, cons
  *               overlap with X, Y or H is MHC_ERR_ALIAS. */
 mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const float* H,
                     void* X_out, void* stream);
+
+/* ---- backward ----------------------------------------------------------------
+ * The pages give no backward formulas; they state that the layer is trained
+ * with a custom backward that recomputes the maps rather than storing them
+ * ("mHC" notes, table tbl-dsv4-mhc-mixed-precision and the kernel notes).  The
+ * two entry points below are the chain rule of mhc_post and mhc_pre, split
+ * where the sublayer sits: a training step calls mhc_post_bwd, then the
+ * sublayer's own backward (dY -> dh), then mhc_pre_bwd.  G = dL/dX_out and
+ * D = dL/dh arrive in the state dtype; parameter gradients are fp32.
+ *
+ * mhc_post_bwd: for X_out = H_res X + H_post^T Y,
+ *   dX[t, j, :] = sum_i H_res[t, i, j] G[t, i, :]   written, state dtype
+ *   dY[t, :]    = sum_i H_post[t, i]   G[t, i, :]   written, state dtype
+ *   dH[t, n + i*n + j] = <G[t, i, :], X[t, j, :]>   written, fp32
+ *   dH[t, n + n*n + i] = <G[t, i, :], Y[t, :]>      written, fp32
+ * dH[t, 0 .. n-1] (the read map's part) is left untouched.
+ *   X, G in [T, n, d]; Y in [T, d]; H in [T, m] (as written by mhc_pre)
+ *   dX out [T, n, d]; dY out [T, d]; dH out [T, m]
+ * No output may overlap an input or another output. */
+mhc_status mhc_post_bwd(const mhc_params* p, const void* X, const void* Y, const float* H, const void* G,
+                        void* dX, void* dY, float* dH, void* stream);
+
+/* mhc_pre_bwd: for h = H_pre X and the maps of mhc_pre, recomputed from X:
+ *   dX    += H_pre D + the RMSNorm / projection path      read-modify-write,
+ *            (dX as left by mhc_post_bwd)                 state dtype
+ *   dphi   = sum_t x_hat_t dz_t^T     [n*d, m] fp32, written
+ *   dbias  = sum_t dlogits_t          [m] fp32, written
+ *   dalpha = per block (pre, res, post) sum_t <dlogits_t, z_t>   [3] fp32, written
+ * with dlogits from dH[:, n:] (res and post parts, as written by
+ * mhc_post_bwd) and dH_pre = <D, X_i> (computed here), through the gates and
+ * Sinkhorn's 2 t_max normalisations in reverse.  Sums over tokens run in a
+ * fixed order.  t_max must be <= 128 (else MHC_ERR_UNSUPPORTED).
+ *   X in [T, n, d]; phi, bias as for mhc_pre; D in [T, d]; dH in [T, m]
+ *   workspace: at least mhc_pre_bwd_workspace_size(p) bytes, 16-byte aligned;
+ *   contents on entry ignored, on return unspecified.
+ * No output may overlap an input or another output.  T = 0 writes zero
+ * parameter gradients. */
+size_t mhc_pre_bwd_workspace_size(const mhc_params* p);
+mhc_status mhc_pre_bwd(const mhc_params* p, const void* X, const float* phi, const float* bias, const void* D,
+                       const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* ---- mhc_amax: composite-map Amax Gain Magnitude ---------------------------
  * For each token, P = H_res,L-1 ... H_res,0 (each layer multiplies the running

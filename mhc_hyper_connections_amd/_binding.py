@@ -17,7 +17,7 @@ MHC_FP32, MHC_BF16 = 0, 1
 STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_DTYPE", 4: "MHC_ERR_ALIGN",
           5: "MHC_ERR_UNSUPPORTED", 6: "MHC_ERR_ALIAS", 7: "MHC_ERR_WORKSPACE", 8: "MHC_ERR_HIP"}
 EXPORTS = ["mhc_pre", "mhc_pre_ex", "mhc_pre_workspace_size", "mhc_post", "mhc_amax", "mhc_gelu_half",
-           "mhc_status_string", "mhc_abi_version"]
+           "mhc_post_bwd", "mhc_pre_bwd", "mhc_pre_bwd_workspace_size", "mhc_status_string", "mhc_abi_version"]
 PRE_AUTO, PRE_TWO_PASS, PRE_ONE_PASS = 0, 1, 2
 
 
@@ -62,6 +62,12 @@ def load_library(path: str = LIB_PATH):
     lib.mhc_amax.restype = ctypes.c_int
     lib.mhc_gelu_half.argtypes = [ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
     lib.mhc_gelu_half.restype = ctypes.c_int
+    lib.mhc_post_bwd.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.mhc_post_bwd.restype = ctypes.c_int
+    lib.mhc_pre_bwd_workspace_size.argtypes = [ctypes.POINTER(Params)]
+    lib.mhc_pre_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.mhc_pre_bwd.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.mhc_pre_bwd.restype = ctypes.c_int
     lib.mhc_status_string.argtypes = [ctypes.c_int]
     lib.mhc_status_string.restype = ctypes.c_char_p
     lib.mhc_abi_version.argtypes = []
@@ -214,3 +220,49 @@ def gelu_half(h, out=None, stream=None):
     _check("mhc_gelu_half", lib.mhc_gelu_half(h.numel(), _dtype_code(h), _ptr(h), _ptr(out),
                                               _stream(stream, h.device)))
     return out
+
+
+def post_bwd(X, Y, H, G, dX=None, dY=None, dH=None, stream=None):
+    """mhc_post_bwd: returns (dX [T, n, d], dY [T, d], dH [T, m]); dH's first
+    n columns (the read map's) are left as they were."""
+    torch = _torch()
+    T, n, d = X.shape
+    m = n * n + 2 * n
+    p = make_params(T, n, d, _dtype_code(X))
+    dX = torch.empty_like(X) if dX is None else dX
+    dY = torch.empty_like(Y) if dY is None else dY
+    dH = torch.zeros((T, m), dtype=torch.float32, device=X.device) if dH is None else dH
+    _need_device(X, Y, H, G, dX, dY, dH)
+    lib = load_library()
+    _check("mhc_post_bwd", lib.mhc_post_bwd(ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(H), _ptr(G), _ptr(dX), _ptr(dY),
+                                            _ptr(dH), _stream(stream, X.device)))
+    return dX, dY, dH
+
+
+def pre_bwd_workspace_size(T, n, d, dtype=MHC_BF16) -> int:
+    p = make_params(T, n, d, dtype)
+    return int(load_library().mhc_pre_bwd_workspace_size(ctypes.byref(p)))
+
+
+def pre_bwd(X, phi, bias, D, dH, dX, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, dphi=None, dbias=None,
+            dalpha=None, workspace=None, stream=None):
+    """mhc_pre_bwd: adds the read map's and the maps' share to dX (in place)
+    and returns (dphi [n*d, m], dbias [m], dalpha [3]), all fp32."""
+    torch = _torch()
+    T, n, d = X.shape
+    m = n * n + 2 * n
+    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha)
+    lib = load_library()
+    dev = X.device
+    dphi = torch.empty((n * d, m), dtype=torch.float32, device=dev) if dphi is None else dphi
+    dbias = torch.empty(m, dtype=torch.float32, device=dev) if dbias is None else dbias
+    dalpha = torch.empty(3, dtype=torch.float32, device=dev) if dalpha is None else dalpha
+    need = int(lib.mhc_pre_bwd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need_device(X, phi, bias, D, dH, dX, dphi, dbias, dalpha, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("mhc_pre_bwd", lib.mhc_pre_bwd(ctypes.byref(p), _ptr(X), _ptr(phi), _ptr(bias), _ptr(D), _ptr(dH),
+                                          _ptr(dX), _ptr(dphi), _ptr(dbias), _ptr(dalpha), _ptr(workspace), ws_bytes,
+                                          _stream(stream, dev)))
+    return dphi, dbias, dalpha

@@ -1,0 +1,786 @@
+// Backward of the mHC layer on gfx950: mhc_post_bwd and mhc_pre_bwd.
+//
+// The pages state only that the layer is trained with a custom backward that
+// recomputes the maps instead of storing them ("mHC" notes on DeepSeek-V4,
+// table tbl-dsv4-mhc-mixed-precision and the kernel notes; Dubrov, "DeepSeek
+// mHC: Manifold-Constrained Hyper-Connections", on the training cost).  The
+// formulas below are the chain rule of the forward (post.hip, pre.hip):
+//
+//   post:  X'_i = sum_j H_res[i][j] X_j + H_post[i] Y
+//          dX_j = sum_i H_res[i][j] G_i      dY = sum_i H_post[i] G_i
+//          dH_res[i][j] = <G_i, X_j>         dH_post[i] = <G_i, Y>
+//   pre:   h = sum_i H_pre[i] X_i
+//          dX_i += H_pre[i] D               dH_pre[i] = <D, X_i>
+//          maps: sigmoid / 2 sigmoid gates, Sinkhorn reversed over its 2 t_max
+//          normalisations (for B = A / s over one line: dA = (dB - <dB, B>) / s),
+//          exp -> dl = dlogits;  dz = alpha_blk dl
+//          dphi += x_hat dz^T, dbias += dl, dalpha_blk += <dl_blk, z_blk>
+//          dx += phi dz / r - (z . dz) x / (K r^2)       (RMSNorm, K = n d)
+//
+// mhc_pre_bwd runs four launches:
+//   A. the forward's split-K partial kernel, extended with <D, X_i>
+//      (pre.hip): per slice and token, x . phi, <D, X_i> and sum x^2;
+//   B. per token (16 lanes): sums the partials in a fixed order, recomputes
+//      r, the logits, gates and Sinkhorn (iterates kept in LDS) and runs the
+//      maps' backward; writes g = dz / r, H_pre and (z . dz) / (K r^2) for C,
+//      and the token's dlogits and alpha terms for D;
+//   C. streams X, D and dX once more: dX += H_pre D + phi g - coef x, and
+//      accumulates this chunk of tokens' share of dphi = sum_t x_t g_t^T;
+//   D. fixed-order reductions of the dphi chunks and of dbias, dalpha over T.
+#include <type_traits>
+
+#include "launch.hpp"
+#include "pre_common.hpp"
+
+namespace mhc {
+namespace {
+
+// Per-token record written by B for C: g (m) | H_pre (n) | coef | zeros, 32
+// floats (one MFMA K-block of g for n <= 4).
+__host__ __device__ constexpr int tok_width(int) { return 32; }
+// Per-token record written by B for D: dlogits (m) | alpha terms pre, res, post.
+__host__ __device__ constexpr int pg_width(int n) { return num_maps(n) + 3; }
+
+constexpr int kBwdMaxTmax = 128;          // Sinkhorn iterates kept in LDS: 2 t_max floats per lane
+constexpr int APPLY_THREADS = 256;
+constexpr int APPLY_CH = 64;              // token records staged per batch in kernel C
+
+// ---- mhc_post_bwd -------------------------------------------------------------
+// One wave per token: lanes walk the token's chunks of 8 values, write dX and
+// dY, and accumulate the n*n + n dot products, reduced across the wave at the
+// end.  H is read with wave-uniform (scalar) loads.
+template <typename ST, int N>
+__global__ __launch_bounds__(256) void post_bwd_kernel(int64_t T, int d, const typename ST::elem* __restrict__ X,
+                                                       const typename ST::elem* __restrict__ Y,
+                                                       const float* __restrict__ H,
+                                                       const typename ST::elem* __restrict__ G,
+                                                       typename ST::elem* __restrict__ dX,
+                                                       typename ST::elem* __restrict__ dY, float* __restrict__ dH) {
+  constexpr int M = num_maps(N);
+  constexpr int NN = N * N;
+  constexpr int NA = NN + N;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                       // wave-uniform
+  const float* Ht = H + t * M;
+  float res[N][N], post[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) res[i][j] = Ht[N + i * N + j];
+    post[i] = Ht[N + NN + i];
+  }
+  float acc[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) acc[a] = 0.0f;
+  const int d8 = d / 8;
+  const int64_t xrow = t * N * static_cast<int64_t>(d);
+  const int64_t yrow = t * static_cast<int64_t>(d);
+  for (int c = lane; c < d8; c += 64) {
+    const int64_t off = static_cast<int64_t>(c) * 8;
+    Raw8<ST> xr[N], gr[N], yr;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      xr[i] = load_raw8<ST, true>(X + xrow + static_cast<int64_t>(i) * d + off);
+      gr[i] = load_raw8<ST, true>(G + xrow + static_cast<int64_t>(i) * d + off);
+    }
+    yr = load_raw8<ST, true>(Y + yrow + off);
+    float x[N][8], g[N][8], y[8];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      unpack8(xr[i], x[i]);
+      unpack8(gr[i], g[i]);
+    }
+    unpack8(yr, y);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        float a = acc[i * N + j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaf(g[i][e], x[j][e], a);
+        acc[i * N + j] = a;
+      }
+      float a = acc[NN + i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = fmaf(g[i][e], y[e], a);
+      acc[NN + i] = a;
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float s = res[0][j] * g[0][e];
+#pragma unroll
+        for (int i = 1; i < N; ++i) s = fmaf(res[i][j], g[i][e], s);
+        o[e] = s;
+      }
+      store8<ST, true>(dX + xrow + static_cast<int64_t>(j) * d + off, o);
+    }
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float s = post[0] * g[0][e];
+#pragma unroll
+      for (int i = 1; i < N; ++i) s = fmaf(post[i], g[i][e], s);
+      o[e] = s;
+    }
+    store8<ST, true>(dY + yrow + off, o);
+  }
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    float v = acc[a];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    acc[a] = v;
+  }
+  if (lane < NA) {
+    float v = acc[0];
+#pragma unroll
+    for (int a = 1; a < NA; ++a) v = (lane == a) ? acc[a] : v;
+    dH[t * M + N + lane] = v;               // res (row-major) then post: columns N .. M-1
+  }
+}
+
+template <typename ST, int N>
+hipError_t launch_post_bwd_t(const mhc_params& p, const void* X, const void* Y, const float* H, const void* G,
+                             void* dX, void* dY, float* dH, hipStream_t stream) {
+  typedef typename ST::elem E;
+  const int64_t blocks = (p.T + 3) / 4;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((post_bwd_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T, p.d,
+                     static_cast<const E*>(X), static_cast<const E*>(Y), H, static_cast<const E*>(G),
+                     static_cast<E*>(dX), static_cast<E*>(dY), dH);
+  return hipGetLastError();
+}
+
+// ---- mhc_pre_bwd, launch B: the maps' backward, 16 lanes per token ------------
+// Also writes g transposed in blocks of 32 tokens, gT[t / 32][j][t % 32]
+// (j < 32, zero for j >= m and for the padding tokens T <= t < Tpad), the
+// operand layout of the dphi contraction over tokens in launch C.
+template <int N>
+__global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tpad, int d, int S, int PW, int SSO,
+                                                           const float* __restrict__ part,
+                                                           const float* __restrict__ bias, float a_pre,
+                                                           float a_res, float a_post, float eps, int t_max,
+                                                           const float* __restrict__ dH, float* __restrict__ tok,
+                                                           float* __restrict__ gT, float* __restrict__ pg) {
+  extern __shared__ float iters[];          // [2 t_max][64]: Sinkhorn matrix before each normalisation
+  constexpr int M = num_maps(N);
+  constexpr int NN = N * N;
+  constexpr int TW = tok_width(N);
+  constexpr int PGW = pg_width(N);
+  const int lane = threadIdx.x;
+  const int q = lane >> 4;
+  const int e = lane & 15;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + q;
+  const bool tv = t < T;
+  const int colr = N + e;
+  const int colg = (e < N) ? e : (N + NN + (e - N));
+  const bool is_res = e < NN;
+  const bool is_gate = e < 2 * N;
+
+  double ss = 0.0, zr = 0.0, zg = 0.0, dp = 0.0;
+  if (tv) {
+    for (int s = 0; s < S; ++s) {
+      const float* P = part + (static_cast<int64_t>(s) * T + t) * PW;
+      ss += *reinterpret_cast<const double*>(P + SSO);
+      if (is_res) zr += P[colr];
+      if (is_gate) zg += P[colg];
+      if (e < N) dp += P[M + e];
+    }
+  }
+  const double inv_r = inv_rms(ss, N * d, eps);
+
+  // Forward maps, as in the forward kernel.
+  const float a_gate = (e < N) ? a_pre : a_post;
+  float sg = 0.0f;
+  if (is_gate) sg = sigmoidf_(logit_of(zg, inv_r, a_gate, bias[colg]));
+  float lr = -INFINITY;
+  if (is_res) lr = logit_of(zr, inv_r, a_res, bias[colr]);
+  float mx = lr;
+#pragma unroll
+  for (int off = 1; off < NN; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (t_max == 0) mx = 0.0f;
+  const float m0 = is_res ? expf(lr - mx) : 0.0f;
+  float mv = m0;
+  for (int it = 0; it < t_max; ++it) {
+    iters[(2 * it) * 64 + lane] = mv;
+    float cs = mv;
+#pragma unroll
+    for (int off = N; off < NN; off <<= 1) cs += __shfl_xor(cs, off);
+    mv = mv / cs;
+    iters[(2 * it + 1) * 64 + lane] = mv;
+    float rs = mv;
+#pragma unroll
+    for (int off = 1; off < N; off <<= 1) rs += __shfl_xor(rs, off);
+    mv = mv / rs;
+  }
+
+  // Gradients arriving at the maps: res and post from mhc_post_bwd, pre from <D, X_i>.
+  float dm = (is_res && tv) ? dH[t * M + colr] : 0.0f;
+  float dgate = 0.0f;
+  if (e < N) dgate = static_cast<float>(dp);
+  else if (is_gate && tv) dgate = dH[t * M + colg];
+
+  // Sinkhorn in reverse.  Step 2 it normalised columns, step 2 it + 1 rows.
+  for (int st = 2 * t_max - 1; st >= 0; --st) {
+    const float A = iters[st * 64 + lane];
+    const bool col = (st & 1) == 0;
+    float sum = A, dot;
+    if (col) {
+#pragma unroll
+      for (int off = N; off < NN; off <<= 1) sum += __shfl_xor(sum, off);
+    } else {
+#pragma unroll
+      for (int off = 1; off < N; off <<= 1) sum += __shfl_xor(sum, off);
+    }
+    const float B = A / sum;
+    dot = dm * B;
+    if (col) {
+#pragma unroll
+      for (int off = N; off < NN; off <<= 1) dot += __shfl_xor(dot, off);
+    } else {
+#pragma unroll
+      for (int off = 1; off < N; off <<= 1) dot += __shfl_xor(dot, off);
+    }
+    dm = (dm - dot) / sum;
+  }
+  // exp: the per-token max shift cancels (it scales M0 and dM0 inversely).
+  const float dl_res = is_res ? dm * m0 : 0.0f;
+  const float dsg = (e < N) ? sg * (1.0f - sg) : 2.0f * sg * (1.0f - sg);
+  const float dl_gate = is_gate ? dgate * dsg : 0.0f;
+
+  const float z_res = static_cast<float>(zr * inv_r);
+  const float z_gate = static_cast<float>(zg * inv_r);
+  const float dz_res = a_res * dl_res;
+  const float dz_gate = a_gate * dl_gate;
+  float zdz = (is_res ? z_res * dz_res : 0.0f) + (is_gate ? z_gate * dz_gate : 0.0f);
+  float tpre = (e < N) ? dl_gate * z_gate : 0.0f;
+  float tres = is_res ? dl_res * z_res : 0.0f;
+  float tpost = (is_gate && e >= N) ? dl_gate * z_gate : 0.0f;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    zdz += __shfl_xor(zdz, off);
+    tpre += __shfl_xor(tpre, off);
+    tres += __shfl_xor(tres, off);
+    tpost += __shfl_xor(tpost, off);
+  }
+  if (t >= Tpad) return;
+  float* gblk = gT + (t >> 5) * 32 * 32 + (t & 31);
+  if (!tv) {                                   // padding token: zero operand column
+    gblk[e * 32] = 0.0f;
+    gblk[(e + 16) * 32] = 0.0f;
+    return;
+  }
+  const float ir = static_cast<float>(inv_r);
+  float* rec = tok + t * TW;
+  float* prow = pg + t * PGW;
+  if (is_res) {
+    const float gv = dz_res * ir;
+    rec[colr] = gv;
+    gblk[colr * 32] = gv;
+    prow[colr] = dl_res;
+  }
+  if (is_gate) {
+    const float gv = dz_gate * ir;
+    rec[colg] = gv;
+    gblk[colg * 32] = gv;
+    prow[colg] = dl_gate;
+  }
+  if (M + e < 32) gblk[(M + e) * 32] = 0.0f;
+  if (M + 16 + e < 32) gblk[(M + 16 + e) * 32] = 0.0f;
+  if (e < N) rec[M + e] = sg;                 // H_pre
+  if (e == 0) {
+    rec[M + N] = static_cast<float>(static_cast<double>(zdz) * inv_r * inv_r / static_cast<double>(N * d));
+    prow[M + 0] = tpre;
+    prow[M + 1] = tres;
+    prow[M + 2] = tpost;
+  }
+  if (M + N + 1 + e < TW) rec[M + N + 1 + e] = 0.0f;
+  if (M + N + 17 + e < TW) rec[M + N + 17 + e] = 0.0f;
+}
+
+// ---- launch C: dX update and chunked dphi, one position per thread ------------
+// Block (x, y): positions k = x * 256 + thread of vec(X) (k = i d + c), tokens
+// of chunk y.  Each thread keeps its row of phi and its 24 dphi sums.
+template <typename ST, int N>
+__global__ __launch_bounds__(APPLY_THREADS) void pre_bwd_apply_kernel(int64_t T, int d, int64_t tchunk,
+                                                                      const typename ST::elem* __restrict__ X,
+                                                                      const typename ST::elem* __restrict__ D,
+                                                                      const float* __restrict__ phi,
+                                                                      const float* __restrict__ tok,
+                                                                      typename ST::elem* __restrict__ dX,
+                                                                      float* __restrict__ dphi_part) {
+  constexpr int M = num_maps(N);
+  constexpr int TW = tok_width(N);
+  __shared__ float rec[APPLY_CH][TW];
+  const int K = N * d;
+  const int k = blockIdx.x * APPLY_THREADS + threadIdx.x;
+  const bool kv = k < K;
+  const int kk = kv ? k : 0;
+  const int i = kk / d;
+  const int c = kk - i * d;
+  float ph[M], acc[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    ph[j] = phi[static_cast<int64_t>(kk) * M + j];
+    acc[j] = 0.0f;
+  }
+  const int64_t t_begin = static_cast<int64_t>(blockIdx.y) * tchunk;
+  const int64_t t_end = (t_begin + tchunk < T) ? t_begin + tchunk : T;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += APPLY_CH) {
+    const int nt = static_cast<int>((t_end - t0 < APPLY_CH) ? t_end - t0 : APPLY_CH);
+    __syncthreads();
+    for (int q = threadIdx.x; q < nt * TW; q += APPLY_THREADS) rec[q / TW][q % TW] = tok[t0 * TW + q];
+    __syncthreads();
+    if (!kv) continue;
+    for (int tt = 0; tt < nt; ++tt) {
+      const int64_t t = t0 + tt;
+      const float x = static_cast<float>(load_elem<ST>(X, t * K + k));
+      const float dd = static_cast<float>(load_elem<ST>(D, t * d + c));
+      float v = static_cast<float>(load_elem<ST>(dX, t * K + k));
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        const float g = rec[tt][j];
+        s = fmaf(ph[j], g, s);
+        acc[j] = fmaf(x, g, acc[j]);
+      }
+      v += fmaf(rec[tt][M + i], dd, s - rec[tt][M + N] * x);
+      store_elem<ST>(dX, t * K + k, v);
+    }
+  }
+  if (!kv) return;
+  float* out = dphi_part + (static_cast<int64_t>(blockIdx.y) * K + k) * M;
+#pragma unroll
+  for (int j = 0; j < M; ++j) out[j] = acc[j];
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(int64_t count, float* __restrict__ out) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (q < count) out[q] = 0.0f;
+}
+
+// ---- launch C on MFMA (bf16 state) -----------------------------------------------
+// Workgroup (slice s, token chunk y): the 256 positions s*256 .. +255 of every
+// stream (32 per wave, 8 per lane as in the forward's partial kernel) for the
+// chunk's tokens, 16 per tile.
+//  * dX update: the lane's 8 positions of one token need (phi g)[k] =
+//    sum_j phi[k][j] g[t][j].  One 16x16x32 MFMA block computes 16 phi rows x
+//    16 tokens with j as the contraction; the phi rows are loaded in the
+//    order that puts output rows 4 (lane/16) + v of block b at positions
+//    8 (lane/16) + 4 b + v, i.e. exactly the lane's load-layout positions, so
+//    the result is added to x, D and dX in registers.  phi and g enter as two
+//    bf16 halves each (hi + lo; the lo x lo product is dropped): ~2^-16
+//    relative, so the term stays accurate where it cancels against the others.
+//  * dphi += x^T g: a contraction over tokens, so x goes through a wave-local
+//    LDS tile of 16 tokens (written in load layout, read as 4 tokens of one
+//    position per lane for a 16x16x16 MFMA); g comes from the transposed copy
+//    gT.  x is exact in bf16, g = hi + lo, fp32 accumulation.
+//  The phi operands live in LDS (the registers hold two tiles in flight and
+//  the dphi accumulators); lanes whose 8 columns are all past m hold zeros
+//  and are not stored.
+constexpr int AM_WAVES = 8;
+constexpr int AM_THREADS = AM_WAVES * 64;
+constexpr int AM_SLICE = AM_WAVES * 32;
+constexpr int XS_PITCH = 36;      // halfwords per token row of the LDS tile: the column reads hit distinct banks
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split_bf16(const float (&f)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = static_cast<__bf16>(f[e]);
+    hi[e] = h;
+    lo[e] = static_cast<__bf16>(f[e] - static_cast<float>(h));
+  }
+}
+
+__device__ __forceinline__ void split_bf16x4(const f32x4& f, s16x4& hi, s16x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 h = static_cast<__bf16>(f[e]);
+    hi[e] = __builtin_bit_cast(short, h);
+    lo[e] = __builtin_bit_cast(short, static_cast<__bf16>(f[e] - static_cast<float>(h)));
+  }
+}
+
+template <int N>
+struct ApplyTile {
+  Raw8<BF16> x[N], dv;
+  f32x4 ga, gb;          // g[t][8 (lane/16) .. +7]
+  float hp[N];           // H_pre[t][i]
+  float coef;            // (z . dz) / (K r^2)
+};
+
+template <int N>
+__global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t T, int d, int64_t tchunk,
+                                                                        const uint16_t* __restrict__ X,
+                                                                        const uint16_t* __restrict__ D,
+                                                                        const float* __restrict__ phi,
+                                                                        const float* __restrict__ tok,
+                                                                        const float* __restrict__ gT,
+                                                                        uint16_t* __restrict__ dX,
+                                                                        float* __restrict__ dphi_part) {
+  constexpr int M = num_maps(N);
+  constexpr int TW = tok_width(N);
+  constexpr int NJB = (M + 15) / 16;
+  constexpr int NGQ = (M + 7) / 8;                 // lane groups with any column j < m
+  __shared__ uint16_t xs[AM_WAVES][N][16][XS_PITCH];
+  __shared__ bf16x8 phl[AM_WAVES][N][2][NGQ * 16][2];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int c0w = blockIdx.x * AM_SLICE + 32 * w;
+  const int j0 = c0w + 8 * g;
+  const bool jv = j0 < d;
+  const int jl = jv ? j0 : 0;
+  const bool gq = g < NGQ;
+  const int lq = gq ? lane : 0;
+
+  if (gq) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int pos = c0w + 8 * (r16 >> 2) + 4 * b + (r16 & 3);
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int col = 8 * g + e;
+          f[e] = (pos < d && col < M) ? phi[static_cast<int64_t>(i * d + pos) * M + col] : 0.0f;
+        }
+        bf16x8 hi, lo;
+        split_bf16(f, hi, lo);
+        phl[w][i][b][lane][0] = hi;
+        phl[w][i][b][lane][1] = lo;
+      }
+    }
+  }
+  f32x4 acc[2 * N][NJB];
+#pragma unroll
+  for (int a = 0; a < 2 * N; ++a) {
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) acc[a][jb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  __syncthreads();
+
+  const int64_t t_begin = static_cast<int64_t>(blockIdx.y) * tchunk;
+  const int64_t t_end = (t_begin + tchunk < T) ? t_begin + tchunk : T;
+  const int64_t ntile = (t_end - t_begin + 15) / 16;
+
+  auto load = [&](int64_t q, ApplyTile<N>& b) {
+    const int64_t t = t_begin + q * 16 + r16;
+    const int64_t tt = t < T ? t : 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) b.x[i] = load_raw8<BF16>(X + (tt * N + i) * d + jl);
+    b.dv = load_raw8<BF16>(D + tt * d + jl);
+    const float* rec = tok + tt * TW;
+    b.ga = *reinterpret_cast<const f32x4*>(rec + 8 * g);
+    b.gb = *reinterpret_cast<const f32x4*>(rec + 8 * g + 4);
+#pragma unroll
+    for (int i = 0; i < N; ++i) b.hp[i] = rec[M + i];
+    b.coef = rec[M + N];
+  };
+
+  // dX of the tile in flight: one buffer, loaded one tile ahead (two
+  // buffers of everything would not fit the registers).
+  Raw8<BF16> dxo[N];
+  auto load_dx = [&](int64_t q) {
+    const int64_t t = t_begin + q * 16 + r16;
+    const int64_t tt = t < T ? t : 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) dxo[i] = load_raw8<BF16>(dX + (tt * N + i) * d + jl);
+  };
+
+  auto step = [&](int64_t q, ApplyTile<N>& b) {
+    const int64_t t = t_begin + q * 16 + r16;
+    const bool ok = t < t_end && jv;
+    float gf[8] = {b.ga[0], b.ga[1], b.ga[2], b.ga[3], b.gb[0], b.gb[1], b.gb[2], b.gb[3]};
+    bf16x8 ghi, glo;
+    split_bf16(gf, ghi, glo);
+    float dv[8];
+    unpack8(b.dv, dv);
+    const bf16x8 zero8 = {};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      f32x4 o[2];
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const bf16x8 ahi = gq ? phl[w][i][bb][lq][0] : zero8;
+        const bf16x8 alo = gq ? phl[w][i][bb][lq][1] : zero8;
+        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, ghi, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, glo, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, ghi, c, 0, 0, 0);
+        o[bb] = c;
+      }
+      float x[8], xo[8], r[8];
+      unpack8(b.x[i], x);
+      unpack8(dxo[i], xo);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r[e] = xo[e] + fmaf(b.hp[i], dv[e], o[0][e] - b.coef * x[e]);
+        r[4 + e] = xo[4 + e] + fmaf(b.hp[i], dv[4 + e], o[1][e] - b.coef * x[4 + e]);
+      }
+      if (ok) store8<BF16>(dX + (t * N + i) * d + j0, r);
+      const u32x4 xv = ok ? b.x[i].v : u32x4{0u, 0u, 0u, 0u};
+      uint32_t* row = reinterpret_cast<uint32_t*>(&xs[w][i][r16][8 * g]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) row[k] = xv[k];
+    }
+    if (q + 1 < ntile) load_dx(q + 1);
+  };
+
+  auto dphi_tile = [&](int64_t q) {
+    __syncthreads();
+    const int64_t t0 = t_begin + q * 16;                 // multiple of 16
+    const float* gblk = gT + (t0 >> 5) * 32 * 32 + (t0 & 31) + 4 * g;
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gblk + (16 * jb + r16) * 32);
+      s16x4 bhi, blo;
+      split_bf16x4(gv, bhi, blo);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          s16x4 a;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) a[u] = static_cast<short>(xs[w][i][4 * g + u][16 * bb + r16]);
+          f32x4 c = acc[2 * i + bb][jb];
+          c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, blo, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bhi, c, 0, 0, 0);
+          acc[2 * i + bb][jb] = c;
+        }
+      }
+    }
+    __syncthreads();
+  };
+
+  ApplyTile<N> ta, tb;
+  if (ntile > 0) {
+    load(0, ta);
+    load_dx(0);
+  }
+  if (ntile > 1) load(1, tb);
+  for (int64_t q = 0; q < ntile; q += 2) {
+    step(q, ta);
+    if (q + 2 < ntile) load(q + 2, ta);
+    dphi_tile(q);
+    if (q + 1 < ntile) {
+      step(q + 1, tb);
+      if (q + 3 < ntile) load(q + 3, tb);
+      dphi_tile(q + 1);
+    }
+  }
+
+  float* out = dphi_part + static_cast<int64_t>(blockIdx.y) * N * static_cast<int64_t>(d) * M;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const int col = 16 * jb + r16;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int pos = c0w + 16 * bb + 4 * g + v;
+          if (pos < d && col < M) out[static_cast<int64_t>(i * d + pos) * M + col] = acc[2 * i + bb][jb][v];
+        }
+      }
+    }
+  }
+}
+
+// ---- launch D: fixed-order reductions ------------------------------------------
+// dphi[k][j] = sum over chunks in order.
+__global__ __launch_bounds__(256) void reduce_chunks_kernel(int64_t count, int nch, const float* __restrict__ part,
+                                                            float* __restrict__ out) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (q >= count) return;
+  float s = 0.0f;
+  for (int ch = 0; ch < nch; ++ch) s += part[static_cast<int64_t>(ch) * count + q];
+  out[q] = s;
+}
+
+// Column sums of pg [T][W] over T: one block per column, strided partial sums
+// then a fixed tree.  Columns 0 .. m-1 go to dbias, m .. m+2 to dalpha.
+__global__ __launch_bounds__(256) void reduce_columns_kernel(int64_t T, int W, int m, const float* __restrict__ pg,
+                                                             float* __restrict__ dbias, float* __restrict__ dalpha) {
+  __shared__ float red[256];
+  const int col = blockIdx.x;
+  float s = 0.0f;
+  for (int64_t t = threadIdx.x; t < T; t += 256) s += pg[t * W + col];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (col < m) dbias[col] = red[0];
+    else dalpha[col - m] = red[0];
+  }
+}
+
+int64_t kblocks_of(int64_t K) { return (K + APPLY_THREADS - 1) / APPLY_THREADS; }
+
+// Workspace layout of mhc_pre_bwd (each part 256-byte aligned).
+struct BwdLayout {
+  size_t part, tok, gT, pg, dphi, total;
+  int S, PW, SSO, nch;
+  int64_t tchunk, Tpad;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+BwdLayout bwd_layout(int64_t T, int n, int d, int dtype) {
+  BwdLayout L{};
+  const int m = num_maps(n);
+  const int64_t K = static_cast<int64_t>(n) * d;
+  L.S = pre_num_slices(d);
+  L.PW = pre_part_width(n, true);
+  L.SSO = pre_part_ss_offset(n, true);
+  L.Tpad = (T + 31) / 32 * 32;
+  // Token chunks of launch C.  bf16 (MFMA form): one workgroup per slice and
+  // chunk, ~512 workgroups, chunks a multiple of 32 tokens.  fp32: blocks of
+  // 256 positions, ~2048 blocks, chunks of at least 64 tokens.
+  int64_t nch, unit;
+  if (dtype == MHC_BF16) {
+    nch = (512 + L.S - 1) / L.S;
+    unit = 32;
+  } else {
+    const int64_t kblocks = kblocks_of(K);
+    nch = (2048 + kblocks - 1) / kblocks;
+    unit = APPLY_CH;
+  }
+  const int64_t max_ch = (T + unit - 1) / unit;
+  if (nch > max_ch) nch = max_ch;
+  if (nch < 1) nch = 1;
+  L.tchunk = (T + nch - 1) / nch;
+  L.tchunk = (L.tchunk + unit - 1) / unit * unit;
+  if (L.tchunk < unit) L.tchunk = unit;
+  L.nch = static_cast<int>((T + L.tchunk - 1) / L.tchunk);
+  if (L.nch < 1) L.nch = 1;
+  size_t off = 0;
+  L.part = off;
+  off = align256(off + static_cast<size_t>(L.S) * T * L.PW * sizeof(float));
+  L.tok = off;
+  off = align256(off + static_cast<size_t>(T) * tok_width(n) * sizeof(float));
+  L.gT = off;
+  off = align256(off + static_cast<size_t>(L.Tpad) * 32 * sizeof(float));
+  L.pg = off;
+  off = align256(off + static_cast<size_t>(T) * pg_width(n) * sizeof(float));
+  L.dphi = off;
+  off = align256(off + static_cast<size_t>(L.nch) * K * m * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+template <typename ST, int N>
+hipError_t launch_pre_bwd_t(const mhc_params& p, const void* X, const float* phi, const float* bias, const void* D,
+                            const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* workspace,
+                            const DeviceInfo& dev, hipStream_t stream) {
+  typedef typename ST::elem E;
+  constexpr int M = num_maps(N);
+  const BwdLayout L = bwd_layout(p.T, N, p.d, p.dtype);
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  float* tok = reinterpret_cast<float*>(ws + L.tok);
+  float* gT = reinterpret_cast<float*>(ws + L.gT);
+  float* pg = reinterpret_cast<float*>(ws + L.pg);
+  float* dphi_part = reinterpret_cast<float*>(ws + L.dphi);
+  const int64_t K = static_cast<int64_t>(N) * p.d;
+  if (p.T == 0) {                            // sums over no tokens
+    const int64_t count = K * M;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, stream,
+                       count, dphi);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(256), 0, stream, static_cast<int64_t>(M), dbias);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(256), 0, stream, static_cast<int64_t>(3), dalpha);
+    return hipGetLastError();
+  }
+
+  hipError_t err = launch_pre_partial_with_d(p, X, D, phi, part, dev, stream);
+  if (err != hipSuccess) return err;
+
+  const int64_t tblocks = (L.Tpad + 3) / 4;
+  if (tblocks > 0x7FFFFFFF || kblocks_of(K) > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const size_t lds = static_cast<size_t>(2 * (p.t_max > 0 ? p.t_max : 1)) * 64 * sizeof(float);
+  if (tblocks > 0) {
+    hipLaunchKernelGGL((pre_bwd_token_kernel<N>), dim3(static_cast<unsigned>(tblocks)), dim3(64), lds, stream, p.T,
+                       L.Tpad, p.d, L.S, L.PW, L.SSO, static_cast<const float*>(part), bias, p.alpha_pre, p.alpha_res,
+                       p.alpha_post, p.eps, p.t_max, dH, tok, gT, pg);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+
+  if (std::is_same<ST, BF16>::value) {
+    hipLaunchKernelGGL((pre_bwd_apply_mfma_kernel<N>), dim3(static_cast<unsigned>(L.S), static_cast<unsigned>(L.nch)),
+                       dim3(AM_THREADS), 0, stream, p.T, p.d, L.tchunk, static_cast<const uint16_t*>(X),
+                       static_cast<const uint16_t*>(D), phi, static_cast<const float*>(tok),
+                       static_cast<const float*>(gT), static_cast<uint16_t*>(dX), dphi_part);
+  } else {
+    const int64_t kblocks = kblocks_of(K);
+    hipLaunchKernelGGL((pre_bwd_apply_kernel<ST, N>), dim3(static_cast<unsigned>(kblocks), static_cast<unsigned>(L.nch)),
+                       dim3(APPLY_THREADS), 0, stream, p.T, p.d, L.tchunk, static_cast<const E*>(X),
+                       static_cast<const E*>(D), phi, static_cast<const float*>(tok), static_cast<E*>(dX), dphi_part);
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  const int64_t count = K * M;
+  hipLaunchKernelGGL(reduce_chunks_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, stream,
+                     count, L.nch, static_cast<const float*>(dphi_part), dphi);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(reduce_columns_kernel, dim3(pg_width(N)), dim3(256), 0, stream, p.T, pg_width(N), M,
+                     static_cast<const float*>(pg), dbias, dalpha);
+  return hipGetLastError();
+}
+
+template <typename ST>
+hipError_t launch_pre_bwd_n(const mhc_params& p, const void* X, const float* phi, const float* bias, const void* D,
+                            const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* ws,
+                            const DeviceInfo& dev, hipStream_t stream) {
+  switch (p.n) {
+    case 1: return launch_pre_bwd_t<ST, 1>(p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, ws, dev, stream);
+    case 2: return launch_pre_bwd_t<ST, 2>(p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, ws, dev, stream);
+    case 4: return launch_pre_bwd_t<ST, 4>(p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, ws, dev, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_post_bwd(const mhc_params& p, const void* X, const void* Y, const float* H, const void* G, void* dX,
+                           void* dY, float* dH, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  const bool bf = p.dtype == MHC_BF16;
+  switch (p.n) {
+    case 1: return bf ? launch_post_bwd_t<BF16, 1>(p, X, Y, H, G, dX, dY, dH, stream)
+                      : launch_post_bwd_t<F32, 1>(p, X, Y, H, G, dX, dY, dH, stream);
+    case 2: return bf ? launch_post_bwd_t<BF16, 2>(p, X, Y, H, G, dX, dY, dH, stream)
+                      : launch_post_bwd_t<F32, 2>(p, X, Y, H, G, dX, dY, dH, stream);
+    case 4: return bf ? launch_post_bwd_t<BF16, 4>(p, X, Y, H, G, dX, dY, dH, stream)
+                      : launch_post_bwd_t<F32, 4>(p, X, Y, H, G, dX, dY, dH, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int pre_bwd_max_tmax() { return kBwdMaxTmax; }
+
+size_t pre_bwd_workspace_bytes(int64_t T, int n, int d, int dtype) { return bwd_layout(T, n, d, dtype).total; }
+
+hipError_t launch_pre_bwd(const mhc_params& p, const void* X, const float* phi, const float* bias, const void* D,
+                          const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* workspace,
+                          const DeviceInfo& dev, hipStream_t stream) {
+  if (p.dtype == MHC_BF16)
+    return launch_pre_bwd_n<BF16>(p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, workspace, dev, stream);
+  return launch_pre_bwd_n<F32>(p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, workspace, dev, stream);
+}
+
+}  // namespace mhc

@@ -154,6 +154,71 @@ mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const flo
   return from_hip(mhc::launch_post(*p, X, Y, H, X_out, static_cast<hipStream_t>(stream)));
 }
 
+mhc_status mhc_post_bwd(const mhc_params* p, const void* X, const void* Y, const float* H, const void* G, void* dX,
+                        void* dY, float* dH, void* stream) {
+  mhc_status st = check_params(p);
+  if (st != MHC_OK) return st;
+  if (p->T == 0) return MHC_OK;
+  if (!X || !Y || !H || !G || !dX || !dY || !dH) return MHC_ERR_NULL;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(H) || !aligned16(G) || !aligned16(dX) || !aligned16(dY) ||
+      !aligned16(dH))
+    return MHC_ERR_ALIGN;
+  const int m = p->n * p->n + 2 * p->n;
+  const size_t sb = state_bytes(p->dtype);
+  const size_t xb = static_cast<size_t>(p->T) * p->n * p->d * sb;
+  const size_t yb = static_cast<size_t>(p->T) * p->d * sb;
+  const Range ins[4] = {range_of(X, xb), range_of(Y, yb), range_of(H, static_cast<size_t>(p->T) * m * 4),
+                        range_of(G, xb)};
+  const Range outs[3] = {range_of(dX, xb), range_of(dY, yb), range_of(dH, static_cast<size_t>(p->T) * m * 4)};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 4; ++b)
+      if (overlap(outs[a], ins[b])) return MHC_ERR_ALIAS;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(outs[a], outs[b])) return MHC_ERR_ALIAS;
+  }
+  return from_hip(mhc::launch_post_bwd(*p, X, Y, H, G, dX, dY, dH, static_cast<hipStream_t>(stream)));
+}
+
+size_t mhc_pre_bwd_workspace_size(const mhc_params* p) {
+  if (check_params(p) != MHC_OK) return 0;
+  return mhc::pre_bwd_workspace_bytes(p->T, p->n, p->d, p->dtype);
+}
+
+mhc_status mhc_pre_bwd(const mhc_params* p, const void* X, const float* phi, const float* bias, const void* D,
+                       const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  mhc_status st = check_params(p);
+  if (st != MHC_OK) return st;
+  if (p->t_max > mhc::pre_bwd_max_tmax()) return MHC_ERR_UNSUPPORTED;
+  if (!dphi || !dbias || !dalpha) return MHC_ERR_NULL;
+  if (p->T > 0 && (!X || !phi || !bias || !D || !dH || !dX)) return MHC_ERR_NULL;
+  const size_t need = mhc::pre_bwd_workspace_bytes(p->T, p->n, p->d, p->dtype);
+  if (!workspace || workspace_bytes < need) return MHC_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(phi) || !aligned16(bias) || !aligned16(D) || !aligned16(dH) || !aligned16(dX) ||
+      !aligned16(dphi) || !aligned16(dbias) || !aligned16(dalpha) || !aligned16(workspace))
+    return MHC_ERR_ALIGN;
+  const bool empty = p->T == 0;
+  const int m = p->n * p->n + 2 * p->n;
+  const size_t sb = state_bytes(p->dtype);
+  const size_t xb = static_cast<size_t>(p->T) * p->n * p->d * sb;
+  const Range ins[5] = {range_of(X, xb), range_of(phi, empty ? 0 : static_cast<size_t>(p->n) * p->d * m * 4),
+                        range_of(bias, empty ? 0 : static_cast<size_t>(m) * 4),
+                        range_of(D, static_cast<size_t>(p->T) * p->d * sb),
+                        range_of(dH, static_cast<size_t>(p->T) * m * 4)};
+  const Range outs[5] = {range_of(dX, xb), range_of(dphi, static_cast<size_t>(p->n) * p->d * m * 4),
+                         range_of(dbias, static_cast<size_t>(m) * 4), range_of(dalpha, 3 * 4),
+                         range_of(workspace, need)};
+  for (int a = 0; a < 5; ++a) {
+    for (int b = 0; b < 5; ++b)
+      if (overlap(outs[a], ins[b])) return MHC_ERR_ALIAS;
+    for (int b = a + 1; b < 5; ++b)
+      if (overlap(outs[a], outs[b])) return MHC_ERR_ALIAS;
+  }
+  const mhc::DeviceInfo dev = device_info();
+  return from_hip(mhc::launch_pre_bwd(*p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, workspace, dev,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 mhc_status mhc_amax(int64_t T, int32_t n, int32_t L, const float* H_stack, float* amax, float* gain_fwd,
                     float* gain_bwd, float* composite, void* stream) {
   if (T < 0 || T > kMaxT || n < 1 || n > 16 || L < 0) return MHC_ERR_SHAPE;

@@ -103,6 +103,18 @@ __device__ __forceinline__ void store8<F32, true>(float* p, const float (&x)[8])
   __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, q + 1);
 }
 
+// Single state values (slow paths only).
+template <typename ST> __device__ __forceinline__ float load_elem(const typename ST::elem* p, int64_t i);
+template <> __device__ __forceinline__ float load_elem<F32>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_elem<BF16>(const uint16_t* p, int64_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+template <typename ST> __device__ __forceinline__ void store_elem(typename ST::elem* p, int64_t i, float v);
+template <> __device__ __forceinline__ void store_elem<F32>(float* p, int64_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void store_elem<BF16>(uint16_t* p, int64_t i, float v) {
+  p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
 __device__ __forceinline__ float sigmoidf_(float u) { return 1.0f / (1.0f + expf(-u)); }
 
 }  // namespace mhc

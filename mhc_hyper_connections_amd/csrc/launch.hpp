@@ -32,6 +32,26 @@ size_t pre_fused_workspace_bytes(int64_t T, int n, int d);
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
                             float* H, void* workspace, size_t ws_bytes, const DeviceInfo& dev, hipStream_t stream);
 
+// Split-K partials of mhc_pre's projection plus, per stream i, <D, X_i> over
+// the slice (pre.hip).  part: [S][T][pre_part_width(n, true)] floats with
+// S = pre_num_slices(d); per token: m partial dot products x . phi, n partial
+// <D, X_i>, and the partial sum of squares as an fp64 at float offset
+// pre_part_ss_offset(n, true).
+int pre_num_slices(int d);
+int pre_part_width(int n, bool with_d);
+int pre_part_ss_offset(int n, bool with_d);
+hipError_t launch_pre_partial_with_d(const mhc_params& p, const void* X, const void* D, const float* phi, float* part,
+                                     const DeviceInfo& dev, hipStream_t stream);
+
+// Backward (bwd.hip).
+hipError_t launch_post_bwd(const mhc_params& p, const void* X, const void* Y, const float* H, const void* G, void* dX,
+                           void* dY, float* dH, hipStream_t stream);
+size_t pre_bwd_workspace_bytes(int64_t T, int n, int d, int dtype);
+int pre_bwd_max_tmax();
+hipError_t launch_pre_bwd(const mhc_params& p, const void* X, const float* phi, const float* bias, const void* D,
+                          const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* workspace,
+                          const DeviceInfo& dev, hipStream_t stream);
+
 // mhc_amax: composite-map Amax.
 hipError_t launch_amax(int64_t T, int n, int L, const float* Hs, float* amax, float* gfwd, float* gbwd,
                        float* comp, hipStream_t stream);

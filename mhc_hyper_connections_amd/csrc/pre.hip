@@ -38,22 +38,26 @@ constexpr int PRE_THREADS = PRE_WAVES * 64;
 constexpr int PRE_SLICE = PRE_WAVES * 32;   // positions of d per slice (32 per wave)
 
 // Per-token record of one slice in the workspace: m fp32 partial dot
-// products, then the partial sum of squares as an fp64 at an 8-byte aligned
-// float offset.
-__host__ __device__ constexpr int ss_offset(int n) { return (num_maps(n) + 1) & ~1; }
-__host__ __device__ constexpr int part_width(int n) { return ss_offset(n) + 2; }
+// products (then, for the backward, n more: <D, X_i> over the slice), then
+// the partial sum of squares as an fp64 at an 8-byte aligned float offset.
+__host__ __device__ constexpr int ss_offset(int n, bool with_d = false) {
+  return (num_maps(n) + (with_d ? n : 0) + 1) & ~1;
+}
+__host__ __device__ constexpr int part_width(int n, bool with_d = false) { return ss_offset(n, with_d) + 2; }
 
-template <typename ST, int N, int MB>
+template <typename ST, int N, int MB, bool WITH_D>
 __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int d, int S, int64_t ntiles,
                                                                   const typename ST::elem* __restrict__ X,
+                                                                  const typename ST::elem* __restrict__ Dg,
                                                                   const float* __restrict__ phi,
                                                                   float* __restrict__ part) {
   constexpr int M = num_maps(N);
   constexpr int NB = (M + 15) / 16;
   constexpr int R = 16 * MB;
-  constexpr int PW = part_width(N);
-  constexpr int SSO = ss_offset(N);
-  __shared__ float red[PRE_WAVES][R][M];
+  constexpr int ND = WITH_D ? N : 0;
+  constexpr int PW = part_width(N, WITH_D);
+  constexpr int SSO = ss_offset(N, WITH_D);
+  __shared__ float red[PRE_WAVES][R][M + ND];
   __shared__ double red_ss[PRE_WAVES][R];
 
   const int lane = threadIdx.x & 63;
@@ -81,20 +85,21 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
   }
   __builtin_amdgcn_sched_barrier(0);     // finish the phi operands before the first tile's loads
 
-  Raw8<ST> xa[MB][N], xb[MB][N];
+  Raw8<ST> xa[MB][N + ND], xb[MB][N + ND];     // chunk N: D (backward only)
   // Every lane loads every chunk from a valid address, with no branch and no
   // select on the data (either would make the compiler wait for the load on
   // the spot): tokens past T read token 0 (their rows are never written) and
   // lanes past d read position 0 (their phi rows are zero and their squares
   // are dropped below).
   const int jl = jv ? j0 : 0;
-  auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][N]) {
+  auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][N + ND]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int64_t t = tile * R + mb * 16 + r16;
       const int64_t tt = t < T ? t : 0;
 #pragma unroll
       for (int i = 0; i < N; ++i) x[mb][i] = load_raw8<ST>(X + (tt * N + i) * d + jl);
+      if (WITH_D) x[mb][N] = load_raw8<ST>(Dg + tt * d + jl);
     }
   };
 
@@ -103,21 +108,30 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
   // prefetch distance two, the loop unrolled by two so the buffers keep
   // their registers (copying a buffer that is still being loaded would wait
   // for it and serialise the prefetch).
-  auto step = [&](int64_t tile, Raw8<ST> (&cur)[MB][N]) {
+  auto step = [&](int64_t tile, Raw8<ST> (&cur)[MB][N + ND]) {
 
     // Sum of squares in fp64: never overflows for a finite fp32 / bf16 state
     // (fp32 overflows once the state's RMS passes ~1.8e19 / sqrt(n d)).
     double ss[MB];
+    float dd[MB][ND > 0 ? ND : 1];
     f32x4 acc[MB][NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       double sq = 0.0;
+      float dv[8];
+      if (WITH_D) unpack8(cur[mb][N], dv);
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         float x[8];
         unpack8(cur[mb][i], x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) sq = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), sq);
+        if (WITH_D) {
+          float a = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a = fmaf(dv[e], x[e], a);
+          dd[mb][i] = jv ? a : 0.0f;
+        }
       }
       ss[mb] = jv ? sq : 0.0;
 #pragma unroll
@@ -143,15 +157,24 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
       sq += __shfl_xor(sq, 16);
       sq += __shfl_xor(sq, 32);
       if (g == 0) red_ss[w][mb * 16 + r16] = sq;
+      if (WITH_D) {
+#pragma unroll
+        for (int i = 0; i < ND; ++i) {
+          float a = dd[mb][i];
+          a += __shfl_xor(a, 16);
+          a += __shfl_xor(a, 32);
+          if (g == 0) red[w][mb * 16 + r16][M + i] = a;
+        }
+      }
     }
     __syncthreads();
-    for (int q = threadIdx.x; q < R * (M + 1); q += PRE_THREADS) {
-      const int tok = q / (M + 1);
-      const int col = q - tok * (M + 1);
+    for (int q = threadIdx.x; q < R * (M + ND + 1); q += PRE_THREADS) {
+      const int tok = q / (M + ND + 1);
+      const int col = q - tok * (M + ND + 1);
       const int64_t t = tile * R + tok;
       if (t < T) {
         float* row = part + (static_cast<int64_t>(s) * T + t) * PW;
-        if (col < M) {
+        if (col < M + ND) {
           float sum = 0.0f;
 #pragma unroll
           for (int ww = 0; ww < PRE_WAVES; ++ww) sum += red[ww][tok][col];
@@ -273,8 +296,8 @@ hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, co
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
   const int64_t grid = groups * S;
-  hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0, stream,
-                     p.T, p.d, S, ntiles, static_cast<const E*>(X), phi, part);
+  hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, false>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
+                     stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(nullptr), phi, part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t blocks = (p.T + 15) / 16;
@@ -295,7 +318,43 @@ hipError_t launch_pre_n(const mhc_params& p, const void* X, const float* phi, co
   }
 }
 
+template <typename ST, int N>
+hipError_t launch_partial_d_t(const mhc_params& p, const void* X, const void* D, const float* phi, float* part,
+                              const DeviceInfo& dev, hipStream_t stream) {
+  typedef typename ST::elem E;
+  constexpr int MB = (sizeof(typename ST::elem) == 2) ? 2 : 1;     // fits the registers without spilling
+  constexpr int R = 16 * MB;
+  const int S = num_slices(p.d);
+  const int64_t ntiles = (p.T + R - 1) / R;
+  int64_t groups = dev.num_cus / S;
+  if (groups < 1) groups = 1;
+  if (groups > ntiles) groups = ntiles;
+  const int64_t grid = groups * S;
+  hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, true>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
+                     stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(D), phi, part);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int pre_num_slices(int d) { return num_slices(d); }
+int pre_part_width(int n, bool with_d) { return part_width(n, with_d); }
+int pre_part_ss_offset(int n, bool with_d) { return ss_offset(n, with_d); }
+
+hipError_t launch_pre_partial_with_d(const mhc_params& p, const void* X, const void* D, const float* phi, float* part,
+                                     const DeviceInfo& dev, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  const bool bf = p.dtype == MHC_BF16;
+  switch (p.n) {
+    case 1: return bf ? launch_partial_d_t<BF16, 1>(p, X, D, phi, part, dev, stream)
+                      : launch_partial_d_t<F32, 1>(p, X, D, phi, part, dev, stream);
+    case 2: return bf ? launch_partial_d_t<BF16, 2>(p, X, D, phi, part, dev, stream)
+                      : launch_partial_d_t<F32, 2>(p, X, D, phi, part, dev, stream);
+    case 4: return bf ? launch_partial_d_t<BF16, 4>(p, X, D, phi, part, dev, stream)
+                      : launch_partial_d_t<F32, 4>(p, X, D, phi, part, dev, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 size_t pre_workspace_bytes(int64_t T, int n, int d) {
   const size_t two_pass = static_cast<size_t>(num_slices(d)) * static_cast<size_t>(T) *

@@ -70,10 +70,12 @@ template <int N>
 __device__ __forceinline__ float sinkhorn16(float lr, int e, int t_max) {
   constexpr int NN = N * N;
   // Subtracting the token's largest residual logit leaves every iterate
-  // unchanged (the first column step divides it out) and keeps exp finite.
+  // unchanged (the first column step divides it out) and keeps exp finite;
+  // with no pass at all the map is exp(logits) itself.
   float mx = lr;
 #pragma unroll
   for (int off = 1; off < NN; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (t_max == 0) mx = 0.0f;
   float mv = (e < NN) ? expf(lr - mx) : 0.0f;
   for (int it = 0; it < t_max; ++it) {
     float cs = mv;                                          // column sum: over i (lane bits above log2 n)

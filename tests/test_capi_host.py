@@ -141,3 +141,39 @@ def test_binding_refuses_host_tensors_and_missing_library(lib):
         m.post(X, torch.zeros((4, 64), dtype=torch.bfloat16), torch.zeros((4, 24)))
     with pytest.raises(RuntimeError, match="not built"):
         m.load_library("/nonexistent/libmhc.so")
+
+
+def test_post_bwd_argument_checks(lib):
+    p = _params()
+    f = lambda p, X=A[0], Y=A[1], H=A[2], G=A[3], dX=A[4], dY=A[5], dH=A[6]: \
+        lib.mhc_post_bwd(ctypes.byref(p), X, Y, H, G, dX, dY, dH, None)
+    assert lib.mhc_post_bwd(None, *A[:7], None) == 1
+    assert f(_params(n=3)) == 5
+    assert f(p, G=None) == 1
+    assert f(p, dH=A[6] + 4) == 4
+    assert f(p, dX=A[3]) == 6                         # dX onto G
+    assert f(p, dY=A[4] + 64) == 6                    # dY inside dX
+    assert f(p, dH=A[0]) == 6                         # dH onto X
+    assert f(_params(T=0), X=None, Y=None, H=None, G=None, dX=None, dY=None, dH=None) == 0
+
+
+def test_pre_bwd_argument_checks(lib):
+    p = _params()
+    need = lib.mhc_pre_bwd_workspace_size(ctypes.byref(p))
+    assert need > 0
+
+    def f(p, X=A[0], phi=A[1], bias=A[2], D=A[3], dH=A[4], dX=A[5], dphi=A[6], dbias=A[7],
+          dalpha=A[7] + 4096, ws=A[7] + 8192, ws_bytes=None):
+        nb = lib.mhc_pre_bwd_workspace_size(ctypes.byref(p)) if ws_bytes is None else ws_bytes
+        return lib.mhc_pre_bwd(ctypes.byref(p), X, phi, bias, D, dH, dX, dphi, dbias, dalpha, ws, nb, None)
+    assert f(_params(n=3)) == 5
+    assert f(_params(t_max=129)) == 5                  # Sinkhorn iterates beyond the backward's LDS budget
+    assert f(p, D=None) == 1
+    assert f(p, ws=None) == 7
+    assert f(p, ws_bytes=need - 1) == 7
+    assert f(p, dphi=A[6] + 8) == 4
+    assert f(p, dX=A[0]) == 6                          # dX onto X
+    assert f(p, dbias=A[6]) == 6                       # dbias onto dphi
+    assert f(p, ws=A[4]) == 6                          # workspace onto dH
+    assert lib.mhc_pre_bwd_workspace_size(None) == 0
+    assert lib.mhc_pre_bwd_workspace_size(ctypes.byref(_params(n=3))) == 0

@@ -1,0 +1,194 @@
+"""mhc_post_bwd + mhc_pre_bwd against the oracle's backward.
+
+The checked quantity is the gradient of sum_t <G_t, X'_t> + <D_t, h_t> with
+G = dX' and D = dh drawn as inputs (the sublayer stays outside the layer).
+The chain is the one a training step runs: mhc_post_bwd writes dX (residual
+part), dY and dH's res / post columns; mhc_pre_bwd adds the read map's and the
+maps' share to dX and writes dphi, dbias, dalpha.
+
+Tolerances: dX and dY as the forward's state outputs (fp32: 1e-5 / 1e-6;
+bf16: 2e-2 / 1e-2).  dH and the parameter gradients are fp32 sums over d or
+over tokens: elementwise 1e-4 (dH) or 1e-3 (parameter gradients) relative
+plus 1e-5 (dH) or 1e-4 (parameters) of the array's largest magnitude.  The
+bound covers fp32 accumulation over up to 16384 terms and the fp32 Sinkhorn
+backward (2 t_max steps of a division each, ~1e-6 relative); it is ~20x
+tighter than a bf16 tolerance.
+"""
+import concurrent.futures as cf
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import TOL, assert_close, dname, sample_tokens, to_device, to_host, values
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def mhc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mhc_hyper_connections_amd as m
+    m.load_library()
+    return m
+
+
+def assert_scaled(got, ref, rtol, atol_frac, what):
+    ref = np.asarray(ref, np.float64)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    return assert_close(np.asarray(got, np.float64), ref, rtol, atol_frac * scale + 1e-30, what)
+
+
+def _inputs(w, T=None):
+    T = w.T if T is None else T
+    X = synth.make_state(w, T)
+    Y = synth.make_sublayer_out(w, T)
+    G, D = synth.make_grads(w, T)
+    phi, bias = synth.make_params(w)
+    return X, Y, G, D, phi, bias
+
+
+def _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha, t_max=None):
+    """Forward maps, then the backward chain.  Returns host arrays."""
+    t_max = w.t_max if t_max is None else t_max
+    dX_, dY_, dG, dD = to_device(X), to_device(Y), to_device(G), to_device(D)
+    dphi_, dbias_ = to_device(phi), to_device(bias)
+    _, H = mhc.pre(dX_, dphi_, dbias_, alpha=alpha, eps=w.eps, t_max=t_max)
+    m = w.m
+    dH = torch.full((X.shape[0], m), 7.0, dtype=torch.float32, device="cuda")
+    gX, gY, dH = mhc.post_bwd(dX_, dY_, H, dG, dH=dH)
+    torch.cuda.synchronize()
+    dX_post = to_host(gX).copy()
+    dH_host = to_host(dH).copy()
+    gphi, gbias, galpha = mhc.pre_bwd(dX_, dphi_, dbias_, dD, dH, gX, alpha=alpha, eps=w.eps, t_max=t_max)
+    torch.cuda.synchronize()
+    return {"dX": to_host(gX), "dY": to_host(gY), "dH": dH_host, "dX_post": dX_post,
+            "dphi": to_host(gphi), "dbias": to_host(gbias), "dalpha": to_host(galpha)}
+
+
+def _check(o, w, got, X, Y, G, D, phi, bias, alpha, t_max=None, tokens=None, params=True):
+    t_max = w.t_max if t_max is None else t_max
+    n = w.n
+    tok = np.arange(X.shape[0]) if tokens is None else tokens
+    ref = o.bwd(X, Y, phi, bias, alpha, G, D, eps=w.eps, t_max=t_max, tokens=tok)
+    dn = dname(w.dtype)
+    assert np.all(got["dH"][:, :n] == 7.0), "mhc_post_bwd wrote the read map's columns of dH"
+    assert_scaled(got["dH"][tok][:, n:], ref["dH"][:, n:], 1e-4, 1e-5, f"{w.name} dH")
+    assert_close(got["dY"][tok], ref["dY"], *TOL[(dn, "state")], what=f"{w.name} dY")
+    assert_close(got["dX"][tok], ref["dX"], *TOL[(dn, "state")], what=f"{w.name} dX")
+    if params:
+        assert_scaled(got["dbias"], ref["dbias"], 1e-3, 1e-4, f"{w.name} dbias")
+        assert_scaled(got["dalpha"], ref["dalpha"], 1e-3, 1e-4, f"{w.name} dalpha")
+        assert_scaled(got["dphi"], ref["dphi"], 1e-3, 1e-4, f"{w.name} dphi")
+    return ref
+
+
+CASES = [
+    # (workload, changes, alpha)
+    ("layer_fp32_T64_d256", {}, None),
+    ("layer_fp32_T64_d256", {}, (1.0, 0.7, -0.4)),
+    ("layer_fwdbwd_bf16_T16384_d4096", {"T": 1100}, None),          # ragged token tiles and chunks
+    ("layer_fwdbwd_bf16_T16384_d4096", {"T": 257}, (1.0, 0.7, -0.4)),
+    ("layer_bf16_T4096_d2048", {"T": 700}, None),
+    ("stack60_bf16_T4096_d2560", {"T": 300, "layers": 1, "sublayer": "given"}, None),   # ragged slice of d
+]
+
+
+@pytest.mark.parametrize("name,changes,alpha", CASES,
+                         ids=[f"{c[0]}_T{c[1].get('T', 'all')}_{'acfg' if c[2] is None else 'a1'}" for c in CASES])
+def test_backward_every_token(mhc, oracle_lib, name, changes, alpha):
+    w = synth.scaled(synth.WORKLOADS[name], **changes)
+    alpha = w.alpha if alpha is None else alpha
+    X, Y, G, D, phi, bias = _inputs(w)
+    print(f"[bwd] {w.name} T={w.T} n={w.n} d={w.d} alpha={alpha}", flush=True)
+    got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha)
+    _check(oracle_lib, w, got, X, Y, G, D, phi, bias, alpha)
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_backward_fewer_streams(mhc, oracle_lib, n):
+    for dtype in (synth.FP32, synth.BF16):
+        w = synth.Workload(f"bwd_n{n}_{dname(dtype)}", T=97, n=n, d=264, dtype=dtype, seed=900 + n)
+        alpha = (0.9, 1.2, -0.7)
+        X, Y, G, D, phi, bias = _inputs(w)
+        got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha)
+        _check(oracle_lib, w, got, X, Y, G, D, phi, bias, alpha)
+
+
+@pytest.mark.parametrize("t_max", [0, 1, 3])
+def test_backward_few_sinkhorn_passes(mhc, oracle_lib, t_max):
+    """Few Sinkhorn passes.  With none, H_res = exp(logits) is not normalised
+    (entries near e^4 at a large alpha_res) and dX is a difference of terms
+    ~100x larger than itself, beyond fp32's 1e-5; that case runs at the
+    workload's alpha."""
+    w = synth.Workload(f"bwd_tmax{t_max}", T=80, n=4, d=128, dtype=synth.FP32, seed=950 + t_max)
+    alpha = (0.5, 1.5, 0.5) if t_max > 0 else w.alpha
+    X, Y, G, D, phi, bias = _inputs(w)
+    got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha, t_max=t_max)
+    _check(oracle_lib, w, got, X, Y, G, D, phi, bias, alpha, t_max=t_max)
+
+
+def test_backward_empty_and_deterministic(mhc):
+    w = synth.scaled(synth.WORKLOADS["layer_fwdbwd_bf16_T16384_d4096"], T=512)
+    X, Y, G, D, phi, bias = _inputs(w)
+    a = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, w.alpha)
+    b = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, w.alpha)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    # T = 0: parameter gradients are written as zeros.
+    e = synth.scaled(w, T=0)
+    X0 = to_device(np.zeros((0, w.n, w.d), np.uint16))
+    D0 = to_device(np.zeros((0, w.d), np.uint16))
+    dH0 = torch.zeros((0, w.m), dtype=torch.float32, device="cuda")
+    dphi = torch.full((w.K, w.m), 3.0, device="cuda")
+    dbias = torch.full((w.m,), 3.0, device="cuda")
+    dalpha = torch.full((3,), 3.0, device="cuda")
+    mhc.pre_bwd(X0, to_device(phi), to_device(bias), D0, dH0, X0.clone(), alpha=e.alpha, dphi=dphi, dbias=dbias,
+                dalpha=dalpha)
+    torch.cuda.synchronize()
+    assert float(dphi.abs().max()) == 0.0 and float(dbias.abs().max()) == 0.0 and float(dalpha.abs().max()) == 0.0
+
+
+def _oracle_param_grads_threaded(o, w, X, Y, G, D, phi, bias, alpha, chunk=256):
+    """The oracle's parameter gradients over all tokens, token chunks on
+    worker threads (the oracle call releases the GIL), summed in chunk order."""
+    T = X.shape[0]
+    starts = list(range(0, T, chunk))
+
+    def run(s):
+        tok = np.arange(s, min(T, s + chunk), dtype=np.int64)
+        r = o.bwd(X, Y, phi, bias, alpha, G, D, eps=w.eps, t_max=w.t_max, tokens=tok)
+        return r["dphi"], r["dbias"], r["dalpha"]
+
+    workers = min(16, os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(run, starts))
+    dphi = np.zeros_like(parts[0][0])
+    dbias = np.zeros_like(parts[0][1])
+    dalpha = np.zeros_like(parts[0][2])
+    for p in parts:
+        dphi += p[0]
+        dbias += p[1]
+        dalpha += p[2]
+    return dphi, dbias, dalpha
+
+
+@pytest.mark.slow
+def test_backward_full_size(mhc, oracle_lib):
+    """T = 16384, n = 4, d = 4096 bf16 in the launch configuration the
+    benchmark times: per-token gradients on sampled tokens, parameter
+    gradients over all tokens."""
+    w = synth.WORKLOADS["layer_fwdbwd_bf16_T16384_d4096"]
+    X, Y, G, D, phi, bias = _inputs(w)
+    print(f"[bwd] full size {w.name}", flush=True)
+    got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, w.alpha)
+    tok = sample_tokens(w.T, 48, tile=32)
+    _check(oracle_lib, w, got, X, Y, G, D, phi, bias, w.alpha, tokens=tok, params=False)
+    dphi, dbias, dalpha = _oracle_param_grads_threaded(oracle_lib, w, X, Y, G, D, phi, bias, w.alpha)
+    assert_scaled(got["dbias"], dbias, 1e-3, 1e-4, "full dbias")
+    assert_scaled(got["dalpha"], dalpha, 1e-3, 1e-4, "full dalpha")
+    assert_scaled(got["dphi"], dphi, 1e-3, 1e-4, "full dphi")
