@@ -38,7 +38,8 @@ namespace {
 // Per-token record written by B for C: g (m) | H_pre (n) | coef | zeros, 32
 // floats (one MFMA K-block of g for n <= 4).
 __host__ __device__ constexpr int tok_width(int) { return 32; }
-// Per-token record written by B for D: dlogits (m) | alpha terms pre, res, post.
+// Per-token values written by B for D, column-major [pg_width][Tpad]:
+// dlogits (m columns), then the alpha terms pre, res, post.
 __host__ __device__ constexpr int pg_width(int n) { return num_maps(n) + 3; }
 
 constexpr int kBwdMaxTmax = 128;          // Sinkhorn iterates kept in LDS: 2 t_max floats per lane
@@ -170,7 +171,6 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
   constexpr int M = num_maps(N);
   constexpr int NN = N * N;
   constexpr int TW = tok_width(N);
-  constexpr int PGW = pg_width(N);
   const int lane = threadIdx.x;
   const int q = lane >> 4;
   const int e = lane & 15;
@@ -269,34 +269,36 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
   }
   if (t >= Tpad) return;
   float* gblk = gT + (t >> 5) * 32 * 32 + (t & 31);
-  if (!tv) {                                   // padding token: zero operand column
+  if (!tv) {                                   // padding token: zero operand column and sums
     gblk[e * 32] = 0.0f;
     gblk[(e + 16) * 32] = 0.0f;
+    if (e < pg_width(N)) pg[e * Tpad + t] = 0.0f;
+    if (e + 16 < pg_width(N)) pg[(e + 16) * Tpad + t] = 0.0f;
     return;
   }
   const float ir = static_cast<float>(inv_r);
   float* rec = tok + t * TW;
-  float* prow = pg + t * PGW;
+  float* pcol = pg + t;                       // column-major: column c at pg + c * Tpad
   if (is_res) {
     const float gv = dz_res * ir;
     rec[colr] = gv;
     gblk[colr * 32] = gv;
-    prow[colr] = dl_res;
+    pcol[colr * Tpad] = dl_res;
   }
   if (is_gate) {
     const float gv = dz_gate * ir;
     rec[colg] = gv;
     gblk[colg * 32] = gv;
-    prow[colg] = dl_gate;
+    pcol[colg * Tpad] = dl_gate;
   }
   if (M + e < 32) gblk[(M + e) * 32] = 0.0f;
   if (M + 16 + e < 32) gblk[(M + 16 + e) * 32] = 0.0f;
   if (e < N) rec[M + e] = sg;                 // H_pre
   if (e == 0) {
     rec[M + N] = static_cast<float>(static_cast<double>(zdz) * inv_r * inv_r / static_cast<double>(N * d));
-    prow[M + 0] = tpre;
-    prow[M + 1] = tres;
-    prow[M + 2] = tpost;
+    pcol[(M + 0) * Tpad] = tpre;
+    pcol[(M + 1) * Tpad] = tres;
+    pcol[(M + 2) * Tpad] = tpost;
   }
   if (M + N + 1 + e < TW) rec[M + N + 1 + e] = 0.0f;
   if (M + N + 17 + e < TW) rec[M + N + 17 + e] = 0.0f;
@@ -413,6 +415,7 @@ struct ApplyTile {
   f32x4 ga, gb;          // g[t][8 (lane/16) .. +7]
   float hp[N];           // H_pre[t][i]
   float coef;            // (z . dz) / (K r^2)
+  f32x4 gt[(num_maps(N) + 15) / 16];   // gT operand of the tile's dphi block
 };
 
 template <int N>
@@ -474,7 +477,7 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
 
   auto load = [&](int64_t q, ApplyTile<N>& b) {
     const int64_t t = t_begin + q * 16 + r16;
-    const int64_t tt = t < T ? t : 0;
+    const int64_t tt = t < t_end ? t : 0;
 #pragma unroll
     for (int i = 0; i < N; ++i) b.x[i] = load_raw8<BF16>(X + (tt * N + i) * d + jl);
     b.dv = load_raw8<BF16>(D + tt * d + jl);
@@ -484,6 +487,13 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
 #pragma unroll
     for (int i = 0; i < N; ++i) b.hp[i] = rec[M + i];
     b.coef = rec[M + N];
+    // With the tile, not later: load completions are counted in order, so a
+    // load issued after the next prefetch would make its wait drain that too.
+    int64_t t0 = t_begin + q * 16;
+    if (t0 >= t_end) t0 = t_begin;                       // padding tile of an odd count: x is zero
+    const float* gblk = gT + (t0 >> 5) * 32 * 32 + (t0 & 31) + 4 * g;
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) b.gt[jb] = *reinterpret_cast<const f32x4*>(gblk + (16 * jb + r16) * 32);
   };
 
   // dX of the tile in flight: one buffer, loaded one tile ahead (two
@@ -491,7 +501,7 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
   Raw8<BF16> dxo[N];
   auto load_dx = [&](int64_t q) {
     const int64_t t = t_begin + q * 16 + r16;
-    const int64_t tt = t < T ? t : 0;
+    const int64_t tt = t < t_end ? t : 0;
 #pragma unroll
     for (int i = 0; i < N; ++i) dxo[i] = load_raw8<BF16>(dX + (tt * N + i) * d + jl);
   };
@@ -526,24 +536,22 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
         r[e] = xo[e] + fmaf(b.hp[i], dv[e], o[0][e] - b.coef * x[e]);
         r[4 + e] = xo[4 + e] + fmaf(b.hp[i], dv[4 + e], o[1][e] - b.coef * x[4 + e]);
       }
-      if (ok) store8<BF16>(dX + (t * N + i) * d + j0, r);
+      if (ok) store8<BF16>(dX + (t * N + i) * d + j0, r);     // the one branch around memory: a store
       const u32x4 xv = ok ? b.x[i].v : u32x4{0u, 0u, 0u, 0u};
       uint32_t* row = reinterpret_cast<uint32_t*>(&xs[w][i][r16][8 * g]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) row[k] = xv[k];
     }
-    if (q + 1 < ntile) load_dx(q + 1);
+    load_dx(q + 1);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  auto dphi_tile = [&](int64_t q) {
+  auto dphi_tile = [&](const ApplyTile<N>& b) {
     __syncthreads();
-    const int64_t t0 = t_begin + q * 16;                 // multiple of 16
-    const float* gblk = gT + (t0 >> 5) * 32 * 32 + (t0 & 31) + 4 * g;
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(gblk + (16 * jb + r16) * 32);
       s16x4 bhi, blo;
-      split_bf16x4(gv, bhi, blo);
+      split_bf16x4(b.gt[jb], bhi, blo);
 #pragma unroll
       for (int i = 0; i < N; ++i) {
 #pragma unroll
@@ -561,21 +569,23 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
     __syncthreads();
   };
 
+  // Tiles in pairs, every prefetch unconditional (tiles past the chunk read
+  // token 0 and store nothing): no load behind a branch, so the compiler's
+  // waits drain only the buffer about to be used.
   ApplyTile<N> ta, tb;
-  if (ntile > 0) {
-    load(0, ta);
-    load_dx(0);
-  }
-  if (ntile > 1) load(1, tb);
+  load(0, ta);
+  load_dx(0);
+  load(1, tb);
+  __builtin_amdgcn_sched_barrier(0);
   for (int64_t q = 0; q < ntile; q += 2) {
     step(q, ta);
-    if (q + 2 < ntile) load(q + 2, ta);
-    dphi_tile(q);
-    if (q + 1 < ntile) {
-      step(q + 1, tb);
-      if (q + 3 < ntile) load(q + 3, tb);
-      dphi_tile(q + 1);
-    }
+    dphi_tile(ta);
+    load(q + 2, ta);
+    __builtin_amdgcn_sched_barrier(0);
+    step(q + 1, tb);
+    dphi_tile(tb);
+    load(q + 3, tb);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   float* out = dphi_part + static_cast<int64_t>(blockIdx.y) * N * static_cast<int64_t>(d) * M;
@@ -607,15 +617,24 @@ __global__ __launch_bounds__(256) void reduce_chunks_kernel(int64_t count, int n
   out[q] = s;
 }
 
-// Column sums of pg [T][W] over T: one block per column, strided partial sums
-// then a fixed tree.  Columns 0 .. m-1 go to dbias, m .. m+2 to dalpha.
-__global__ __launch_bounds__(256) void reduce_columns_kernel(int64_t T, int W, int m, const float* __restrict__ pg,
+// Column sums of pg [W][Tpad] over tokens: one block per column, thread k
+// adds tokens k, k + 256, ... (coalesced), then a fixed tree.  Columns
+// 0 .. m-1 go to dbias, m .. m+2 to dalpha.
+__global__ __launch_bounds__(256) void reduce_columns_kernel(int64_t Tpad, int m, const float* __restrict__ pg,
                                                              float* __restrict__ dbias, float* __restrict__ dalpha) {
   __shared__ float red[256];
   const int col = blockIdx.x;
-  float s = 0.0f;
-  for (int64_t t = threadIdx.x; t < T; t += 256) s += pg[t * W + col];
-  red[threadIdx.x] = s;
+  const float* c = pg + static_cast<int64_t>(col) * Tpad;
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  int64_t t = threadIdx.x;
+  for (; t + 768 < Tpad; t += 1024) {
+    s0 += c[t];
+    s1 += c[t + 256];
+    s2 += c[t + 512];
+    s3 += c[t + 768];
+  }
+  for (; t < Tpad; t += 256) s0 += c[t];
+  red[threadIdx.x] = (s0 + s1) + (s2 + s3);
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
@@ -668,13 +687,13 @@ BwdLayout bwd_layout(int64_t T, int n, int d, int dtype) {
   if (L.nch < 1) L.nch = 1;
   size_t off = 0;
   L.part = off;
-  off = align256(off + static_cast<size_t>(L.S) * T * L.PW * sizeof(float));
+  off = align256(off + pre_partial_bytes(T, n, d, true));
   L.tok = off;
   off = align256(off + static_cast<size_t>(T) * tok_width(n) * sizeof(float));
   L.gT = off;
   off = align256(off + static_cast<size_t>(L.Tpad) * 32 * sizeof(float));
   L.pg = off;
-  off = align256(off + static_cast<size_t>(T) * pg_width(n) * sizeof(float));
+  off = align256(off + static_cast<size_t>(L.Tpad) * pg_width(n) * sizeof(float));
   L.dphi = off;
   off = align256(off + static_cast<size_t>(L.nch) * K * m * sizeof(float));
   L.total = off;
@@ -737,7 +756,7 @@ hipError_t launch_pre_bwd_t(const mhc_params& p, const void* X, const float* phi
                      count, L.nch, static_cast<const float*>(dphi_part), dphi);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(reduce_columns_kernel, dim3(pg_width(N)), dim3(256), 0, stream, p.T, pg_width(N), M,
+  hipLaunchKernelGGL(reduce_columns_kernel, dim3(pg_width(N)), dim3(256), 0, stream, L.Tpad, M,
                      static_cast<const float*>(pg), dbias, dalpha);
   return hipGetLastError();
 }

@@ -40,6 +40,7 @@ hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi
 int pre_num_slices(int d);
 int pre_part_width(int n, bool with_d);
 int pre_part_ss_offset(int n, bool with_d);
+size_t pre_partial_bytes(int64_t T, int n, int d, bool with_d);   // records + trash slots
 hipError_t launch_pre_partial_with_d(const mhc_params& p, const void* X, const void* D, const float* phi, float* part,
                                      const DeviceInfo& dev, hipStream_t stream);
 

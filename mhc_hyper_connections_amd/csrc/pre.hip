@@ -37,6 +37,10 @@ constexpr int PRE_WAVES = 8;
 constexpr int PRE_THREADS = PRE_WAVES * 64;
 constexpr int PRE_SLICE = PRE_WAVES * 32;   // positions of d per slice (32 per wave)
 
+// Write-only slots after the partial records that absorb the stores of
+// items past the end (one double per thread).
+constexpr size_t kPartTrashBytes = PRE_THREADS * sizeof(double);
+
 // Per-token record of one slice in the workspace: m fp32 partial dot
 // products (then, for the backward, n more: <D, X_i> over the slice), then
 // the partial sum of squares as an fp64 at an 8-byte aligned float offset.
@@ -66,6 +70,7 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
   const int g = lane >> 4;
   const int s = blockIdx.x % S;
   const int64_t ntg = gridDim.x / S;
+  float* const trash = part + static_cast<int64_t>(S) * T * PW;     // kPartTrashBytes of write-only slots
   const int j0 = s * PRE_SLICE + 32 * w + 8 * g;
   const bool jv = j0 < d;
 
@@ -168,38 +173,65 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
       }
     }
     __syncthreads();
-    for (int q = threadIdx.x; q < R * (M + ND + 1); q += PRE_THREADS) {
-      const int tok = q / (M + ND + 1);
-      const int col = q - tok * (M + ND + 1);
+    // Partial records out: a fixed number of stores per thread and no branch
+    // (stores share the load counter; an unknown count would make the next
+    // tile's wait drain the prefetch).  Items past the tile or past T go to
+    // the trash slots after the records.
+    constexpr int NF = R * (M + ND);
+    constexpr int FPT = (NF + PRE_THREADS - 1) / PRE_THREADS;
+#pragma unroll
+    for (int k = 0; k < FPT; ++k) {
+      const int q = threadIdx.x + k * PRE_THREADS;
+      const int qq = q < NF ? q : 0;
+      const int tok = qq / (M + ND);
+      const int col = qq - tok * (M + ND);
+      float sum = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < PRE_WAVES; ++ww) sum += red[ww][tok][col];
       const int64_t t = tile * R + tok;
-      if (t < T) {
-        float* row = part + (static_cast<int64_t>(s) * T + t) * PW;
-        if (col < M + ND) {
-          float sum = 0.0f;
+      float* dst = (q < NF && t < T) ? part + (static_cast<int64_t>(s) * T + t) * PW + col : trash + threadIdx.x;
+      *dst = sum;
+    }
+    {
+      const int tok = static_cast<int>(threadIdx.x) < R ? static_cast<int>(threadIdx.x) : 0;
+      double sum = 0.0;
 #pragma unroll
-          for (int ww = 0; ww < PRE_WAVES; ++ww) sum += red[ww][tok][col];
-          row[col] = sum;
-        } else {
-          double sum = 0.0;
-#pragma unroll
-          for (int ww = 0; ww < PRE_WAVES; ++ww) sum += red_ss[ww][tok];
-          *reinterpret_cast<double*>(row + SSO) = sum;
-        }
-      }
+      for (int ww = 0; ww < PRE_WAVES; ++ww) sum += red_ss[ww][tok];
+      const int64_t t = tile * R + tok;
+      double* dst = (static_cast<int>(threadIdx.x) < R && t < T)
+                        ? reinterpret_cast<double*>(part + (static_cast<int64_t>(s) * T + t) * PW + SSO)
+                        : reinterpret_cast<double*>(trash) + threadIdx.x;
+      *dst = sum;
     }
     __syncthreads();
-    if (tile + 2 * ntg < ntiles) load_tile(tile + 2 * ntg, cur);
+    load_tile(tile + 2 * ntg, cur);
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch here: the scheduler would sink it to its use
   };
 
-  int64_t tile = blockIdx.x / S;
-  if (tile < ntiles) load_tile(tile, xa);
-  if (tile + ntg < ntiles) load_tile(tile + ntg, xb);
-  for (; tile < ntiles; tile += 2 * ntg) {
-    step(tile, xa);
-    if (tile + ntg < ntiles) step(tile + ntg, xb);
+  // Every workgroup walks the same number of tiles, an even number, and
+  // every prefetch is issued unconditionally (tiles past the end read token
+  // 0, which stays in cache, and write nothing).  With no branch around a
+  // load, the compiler counts the loads in flight exactly and waits only for
+  // the buffer it is about to use; a conditional prefetch made it wait for
+  // both buffers, which halved the loads in flight.
+  const int64_t tile0 = blockIdx.x / S;
+  const int64_t per_wg = (ntiles + ntg - 1) / ntg;
+  load_tile(tile0, xa);
+  load_tile(tile0 + ntg, xb);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int64_t k = 0; k < per_wg; k += 2) {
+    step(tile0 + k * ntg, xa);
+    step(tile0 + (k + 1) * ntg, xb);
   }
 }
 
+// One token per wave.  The token's X streams in passes of 64 lanes x 8
+// positions, two passes in flight; the first two are issued before the
+// partials are summed (they do not depend on the maps).  All four 16-lane
+// groups compute the same maps (Sinkhorn is a few hundred instructions);
+// group 0 writes H.  Lanes past d work on the last chunk again and store
+// the same values to the same place, so no load or store sits behind a
+// branch and the compiler keeps both passes in flight.
 template <typename ST, int N>
 __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S,
                                                          const typename ST::elem* __restrict__ X,
@@ -213,71 +245,114 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
   constexpr int PW = part_width(N);
   constexpr int SSO = ss_offset(N);
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int q = lane >> 4;          // token of this wave's group of 4
   const int e = lane & 15;          // Sinkhorn entry (i, j) = (e / N, e % N) when e < N*N
-  const int64_t t0 = (static_cast<int64_t>(blockIdx.x) * 4 + w) * 4;
-  const int64_t t = t0 + q;
-  const bool tv = t < T;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;               // wave-uniform
   const int colr = N + e;                                  // residual column of entry e
   const int colg = (e < N) ? e : (N + NN + (e - N));       // gate column: pre for e < n, post for n <= e < 2n
 
-  // The slices' partials, summed in a fixed order; RMS and logits in fp64
-  // (a handful of values per token), everything after in fp32.
-  double ss = 0.0, zr = 0.0, zg = 0.0;
-  if (tv) {
-    for (int s = 0; s < S; ++s) {
-      const float* P = part + (static_cast<int64_t>(s) * T + t) * PW;
-      ss += *reinterpret_cast<const double*>(P + SSO);
-      if (e < NN) zr += P[colr];
-      if (e < 2 * N) zg += P[colg];
-    }
+  const typename ST::elem* Xt = X + t * N * static_cast<int64_t>(d);
+  typename ST::elem* ht = h + t * static_cast<int64_t>(d);
+  const int npass = (d + 511) / 512;
+  auto pos = [&](int p) {
+    const int j = p * 512 + lane * 8;
+    return j < d ? j : d - 8;
+  };
+  Raw8<ST> xa[N], xb[N];
+  auto load_pass = [&](int p, Raw8<ST> (&x)[N]) {
+    const int j = pos(p < npass ? p : npass - 1);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = load_raw8<ST, true>(Xt + static_cast<int64_t>(i) * d + j);
+  };
+
+  // The slices' partials, summed in a fixed order (16-lane group q takes
+  // slices q, q+4, ..., then the four groups are added); RMS and logits in
+  // fp64 (a handful of values per token), everything after in fp32.  The
+  // first slices' loads are issued before the X prefetch (load completions
+  // are counted in order, so waiting for them must not wait for X).
+  const int q = lane >> 4;
+  const bool er = e < NN, eg = e < 2 * N;
+  const int cr = er ? colr : 0, cg = eg ? colg : 0;
+  constexpr int SPG = 4;                      // slices per group in registers: S <= 16
+  double pss[SPG];
+  float pzr[SPG], pzg[SPG];
+#pragma unroll
+  for (int k = 0; k < SPG; ++k) {
+    const int s = q + 4 * k;
+    const float* P = part + (static_cast<int64_t>(s < S ? s : 0) * T + t) * PW;
+    pss[k] = *reinterpret_cast<const double*>(P + SSO);
+    pzr[k] = P[cr];
+    pzg[k] = P[cg];
   }
+  const float bias_r = bias[cr], bias_g = bias[cg];
+  load_pass(0, xa);
+  load_pass(1, xb);
+  __builtin_amdgcn_sched_barrier(0);
+  double ss = 0.0, zr = 0.0, zg = 0.0;
+#pragma unroll
+  for (int k = 0; k < SPG; ++k) {
+    const bool sv = q + 4 * k < S;
+    ss += sv ? pss[k] : 0.0;
+    zr += sv ? static_cast<double>(pzr[k]) : 0.0;
+    zg += sv ? static_cast<double>(pzg[k]) : 0.0;
+  }
+  for (int s = q + 4 * SPG; s < S; s += 4) {     // d > 4096 only
+    const float* P = part + (static_cast<int64_t>(s) * T + t) * PW;
+    ss += *reinterpret_cast<const double*>(P + SSO);
+    zr += P[cr];
+    zg += P[cg];
+  }
+  ss += __shfl_xor(ss, 16);
+  zr += __shfl_xor(zr, 16);
+  zg += __shfl_xor(zg, 16);
+  ss += __shfl_xor(ss, 32);
+  zr += __shfl_xor(zr, 32);
+  zg += __shfl_xor(zg, 32);
+  if (!er) zr = 0.0;
+  if (!eg) zg = 0.0;
   const double inv_r = inv_rms(ss, N * d, eps);
 
   float gv = 0.0f;
   if (e < 2 * N) {
-    const float l = logit_of(zg, inv_r, (e < N) ? a_pre : a_post, bias[colg]);
+    const float l = logit_of(zg, inv_r, (e < N) ? a_pre : a_post, bias_g);
     gv = (e < N) ? sigmoidf_(l) : 2.0f * sigmoidf_(l);
   }
   float lr = -INFINITY;
-  if (e < NN) lr = logit_of(zr, inv_r, a_res, bias[colr]);
+  if (e < NN) lr = logit_of(zr, inv_r, a_res, bias_r);
   const float mv = sinkhorn16<N>(lr, e, t_max);
-  if (tv) {
+  if (lane < 16) {
     float* Ht = H + t * M;
     if (e < NN) Ht[colr] = mv;
     if (e < 2 * N) Ht[colg] = gv;
   }
+  float hp[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) hp[i] = __shfl(gv, i);
 
-  // h = H_pre . X for the wave's 4 tokens, one after another.
-  for (int qq = 0; qq < 4; ++qq) {
-    const int64_t tq = t0 + qq;
-    if (tq >= T) break;
-    float hp[N];
+  auto emit = [&](int p, Raw8<ST> (&x)[N]) {
+    float o[8];
+    {
+      float v[8];
+      unpack8(x[0], v);
 #pragma unroll
-    for (int i = 0; i < N; ++i) hp[i] = __shfl(gv, qq * 16 + i);
-    const typename ST::elem* Xt = X + tq * N * static_cast<int64_t>(d);
-    typename ST::elem* ht = h + tq * static_cast<int64_t>(d);
-    for (int j = lane * 8; j < d; j += 512) {
-      Raw8<ST> xr[N];
-#pragma unroll
-      for (int i = 0; i < N; ++i) xr[i] = load_raw8<ST>(Xt + static_cast<int64_t>(i) * d + j);
-      float o[8];
-      {
-        float x[8];
-        unpack8(xr[0], x);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = hp[0] * x[k];
-      }
-#pragma unroll
-      for (int i = 1; i < N; ++i) {
-        float x[8];
-        unpack8(xr[i], x);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = fmaf(hp[i], x[k], o[k]);
-      }
-      store8<ST>(ht + j, o);
+      for (int k = 0; k < 8; ++k) o[k] = hp[0] * v[k];
     }
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+      float v[8];
+      unpack8(x[i], v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = fmaf(hp[i], v[k], o[k]);
+    }
+    store8<ST, true>(ht + pos(p < npass ? p : npass - 1), o);
+  };
+  for (int p = 0; p < npass; p += 2) {
+    emit(p, xa);
+    load_pass(p + 2, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    emit(p + 1, xb);
+    load_pass(p + 3, xb);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -287,7 +362,7 @@ template <typename ST, int N>
 hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
                         void* workspace, const DeviceInfo& dev, hipStream_t stream) {
   typedef typename ST::elem E;
-  constexpr int MB = (sizeof(typename ST::elem) == 2) ? 4 : 2;
+  constexpr int MB = 2;                  // 32-token tiles: two in flight fit the registers
   constexpr int R = 16 * MB;
   const int S = num_slices(p.d);
   const int64_t ntiles = (p.T + R - 1) / R;
@@ -300,7 +375,7 @@ hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, co
                      stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(nullptr), phi, part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t blocks = (p.T + 15) / 16;
+  const int64_t blocks = (p.T + 3) / 4;
   hipLaunchKernelGGL((pre_finish_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T, p.d, S,
                      static_cast<const E*>(X), static_cast<const float*>(part), bias, p.alpha_pre, p.alpha_res,
                      p.alpha_post, p.eps, p.t_max, static_cast<E*>(h), H);
@@ -356,9 +431,13 @@ hipError_t launch_pre_partial_with_d(const mhc_params& p, const void* X, const v
   }
 }
 
+size_t pre_partial_bytes(int64_t T, int n, int d, bool with_d) {
+  return static_cast<size_t>(num_slices(d)) * static_cast<size_t>(T) * static_cast<size_t>(part_width(n, with_d)) *
+             sizeof(float) + kPartTrashBytes;
+}
+
 size_t pre_workspace_bytes(int64_t T, int n, int d) {
-  const size_t two_pass = static_cast<size_t>(num_slices(d)) * static_cast<size_t>(T) *
-                          static_cast<size_t>(part_width(n)) * sizeof(float);
+  const size_t two_pass = pre_partial_bytes(T, n, d, false);
   const size_t one_pass = pre_fused_workspace_bytes(T, n, d);
   return two_pass > one_pass ? two_pass : one_pass;
 }
