@@ -152,7 +152,111 @@ def cpu_baseline(w, seconds_target=15.0):
                       f"{dt:.1f} s on one host thread"}
 
 
+# ---- rocprofv3 results -> profiles/ ------------------------------------------
+# Which kernels make up each entry point (substrings of the demangled names).
+ENTRY_KERNELS = {
+    "mhc_pre": ["pre_partial_kernel<mhc::BF16, 4, 2, false>", "pre_finish_kernel<mhc::BF16, 4>"],
+    "mhc_post": ["post_kernel<mhc::BF16, 4"],
+    "mhc_amax": ["amax_kernel<4>"],
+    "mhc_post_bwd": ["post_bwd_kernel<mhc::BF16, 4>"],
+    "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 2, true>", "pre_bwd_token_kernel<4>",
+                    "pre_bwd_apply_mfma_kernel<4>", "reduce_chunks_kernel", "reduce_columns_kernel"],
+}
+ENTRY_SOURCES = {
+    "mhc_pre": ["pre.hip", "pre_common.hpp", "device.hpp"],
+    "mhc_post": ["post.hip", "device.hpp"],
+    "mhc_amax": ["amax.hip", "device.hpp"],
+    "mhc_post_bwd": ["bwd.hip", "device.hpp"],
+    "mhc_pre_bwd": ["bwd.hip", "pre.hip", "pre_common.hpp", "device.hpp"],
+}
+COPY_KERNEL = "MulFunctor"          # torch.mul(X, 1, out=X'): reads and writes the 512 MiB state once
+
+
+def _db_rows(path, query):
+    import sqlite3
+    with sqlite3.connect(path) as con:
+        return list(con.execute(query))
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def _counter_per_kernel(path, counter):
+    per = {}
+    for name, cname, val in _db_rows(path, "select kernel_name, counter_name, value from counters_collection"):
+        if cname == counter:
+            per.setdefault(name, []).append(float(val))
+    return per
+
+
+def write_traffic(fetch_db, write_db, out_path, workload="layer_bf16_T16384_d4096"):
+    """HBM bytes per launch of each entry point from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the plain copy of the state (known: 512 MiB read and
+    512 MiB written).  Records the sources' hash so a changed kernel voids it."""
+    import hashlib
+    fetch = _counter_per_kernel(fetch_db, "FETCH_SIZE")
+    write = _counter_per_kernel(write_db, "WRITE_SIZE")
+    copy_bytes = 512 * 1024 * 1024
+    cf = [k for k in fetch if COPY_KERNEL in k]
+    cw = [k for k in write if COPY_KERNEL in k]
+    if not cf or not cw:
+        raise SystemExit("the plain-copy kernel is missing from the counter runs")
+    fetch_scale = copy_bytes / (_median(fetch[cf[0]]) * 1024)
+    write_scale = copy_bytes / (_median(write[cw[0]]) * 1024)
+    entries = {}
+    for entry, pats in ENTRY_KERNELS.items():
+        rb = wb = 0.0
+        found = 0
+        for pat in pats:
+            kf = [k for k in fetch if pat in k]
+            kw = [k for k in write if pat in k]
+            if kf and kw:
+                found += 1
+                rb += _median(fetch[kf[0]]) * 1024 * fetch_scale
+                wb += _median(write[kw[0]]) * 1024 * write_scale
+        if found != len(pats):
+            continue
+        h = hashlib.sha256()
+        srcs = [os.path.join("mhc_hyper_connections_amd", "csrc", f) for f in ENTRY_SOURCES[entry]]
+        for p in srcs:
+            with open(os.path.join(ROOT, p), "rb") as f:
+                h.update(f.read())
+        entries[entry] = {"bytes_per_launch": int(rb + wb), "read_bytes": int(rb), "write_bytes": int(wb),
+                          "kernels": pats, "source_sha256_16": h.hexdigest()[:16], "sources": srcs, "valid": True}
+    doc = {"_note": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median), "
+                    "each scaled by what the same counter reads for a plain copy of the 512 MiB state "
+                    f"(FETCH_SIZE x {fetch_scale:.5f}, WRITE_SIZE x {write_scale:.5f}). Valid while the "
+                    "sources' hash matches.",
+           "fetch_scale": fetch_scale, "write_scale": write_scale, workload: entries}
+    with open(out_path, "w") as f:
+        json.dump(doc, f, indent=1)
+    return doc
+
+
+def summarize_trace(stats_db):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (per-kernel average durations)."""
+    rows = _db_rows(stats_db, "select name, total_calls, average, percentage from top_kernels")
+    lines = ["| kernel | calls | average us | share of GPU time |", "|---|---|---|---|"]
+    for name, calls, avg, pct in rows:          # average is in microseconds
+        short = name.replace("void ", "").replace("mhc::(anonymous namespace)::", "").split("(")[0]
+        if "MulFunctor" in name:
+            short = "torch mul (plain copy of the state, 1 read + 1 write of 512 MiB)"
+        lines.append(f"| `{short[:90]}` | {calls} | {avg:.1f} | {pct:.1f}% |")
+    return "\n".join(lines)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--write-traffic":
+        doc = write_traffic(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) > 4 else
+                            os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+        print(json.dumps(doc, indent=1))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        print(summarize_trace(sys.argv[2]))
+        return
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)

@@ -346,7 +346,11 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
     }
     store8<ST, true>(ht + pos(p < npass ? p : npass - 1), o);
   };
-  for (int p = 0; p < npass; p += 2) {
+  // Prefetch two passes ahead while passes remain; the last one or two
+  // passes are emitted after the loop (a prefetch past the end would read
+  // the state again, and these loads bypass the caches).
+  int p = 0;
+  for (; p + 2 < npass; p += 2) {
     emit(p, xa);
     load_pass(p + 2, xa);
     __builtin_amdgcn_sched_barrier(0);
@@ -354,6 +358,8 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
     load_pass(p + 3, xb);
     __builtin_amdgcn_sched_barrier(0);
   }
+  emit(p, xa);
+  if (p + 1 < npass) emit(p + 1, xb);
 }
 
 int num_slices(int d) { return (d + PRE_SLICE - 1) / PRE_SLICE; }
