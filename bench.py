@@ -108,6 +108,68 @@ def time_backward(mhc, torch, w, X, Y, phi, bias, H, steps, warmup, stream):
     return out
 
 
+def time_stack(mhc, torch, reps=5, warmup=2):
+    """The 60-layer stack workload (T=4096, n=4, d=2560, F = 0.5 GELU): the
+    whole stack timed with the separate entry points per layer (pre, F,
+    post) and with mhc_post_pre chaining each layer's post into the next
+    layer's pre; plus the per-token composite Amax over its maps."""
+    import numpy as np
+
+    import synth
+    w = synth.WORKLOADS["stack60_bf16_T4096_d2560"]
+    T, n, d, L, m = w.T, w.n, w.d, w.layers, w.m
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    X0 = dev(synth.make_state(w))
+    params = [tuple(dev(a) for a in synth.make_params(w, layer=l)) for l in range(L)]
+    X = torch.empty_like(X0)
+    h = torch.empty((T, d), dtype=X0.dtype, device="cuda")
+    Y = torch.empty_like(h)
+    Hs = torch.empty((L, T, m), dtype=torch.float32, device="cuda")
+    ws = torch.empty(mhc.pre_workspace_size(T, n, d, w.dtype), dtype=torch.uint8, device="cuda")
+    amax = torch.empty(T, dtype=torch.float32, device="cuda")
+    kw = dict(alpha=w.alpha, eps=w.eps, t_max=w.t_max)
+
+    def separate():
+        X.copy_(X0)
+        for l in range(L):
+            mhc.pre(X, params[l][0], params[l][1], h=h, H=Hs[l], workspace=ws, **kw)
+            mhc.gelu_half(h, out=Y)
+            mhc.post(X, Y, Hs[l], out=X)
+
+    def fused():
+        X.copy_(X0)
+        mhc.pre(X, params[0][0], params[0][1], h=h, H=Hs[0], workspace=ws, **kw)
+        for l in range(L - 1):
+            mhc.gelu_half(h, out=Y)
+            mhc.post_pre(X, Y, Hs[l], params[l + 1][0], params[l + 1][1], out=X, h=h, H_next=Hs[l + 1],
+                         workspace=ws, **kw)
+        mhc.gelu_half(h, out=Y)
+        mhc.post(X, Y, Hs[L - 1], out=X)
+
+    out = {"workload": w.name, "layers": L}
+    for name, fn in (("separate", separate), ("fused_post_pre", fused)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        out[name] = {"total_ms": ms, "per_layer_us": ms * 1e3 / L}
+    mhc.amax(Hs, n, out_amax=amax, want_all=False)
+    a = amax.cpu().numpy()
+    out["amax"] = {"max": float(a.max()), "mean": float(a.mean()), "min": float(a.min())}
+    return out
+
+
 def traffic_bytes(path, workload, entry):
     """HBM bytes per launch of an entry point measured with rocprofv3
     counters, or None when absent or when the kernel source changed since."""
@@ -264,6 +326,7 @@ def main():
     ap.add_argument("--workload", default="layer_bf16_T16384_d4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 60-layer stack timing")
     ap.add_argument("--pre-algo", type=int, default=0, choices=[0, 1, 2],
                     help="mhc_pre form: 0 auto, 1 two-pass, 2 one-pass")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
@@ -390,6 +453,14 @@ def main():
                 f"({backward['mhc_post_bwd']['GBps']:.0f} GB/s), pre_bwd {backward['mhc_pre_bwd']['avg_us']:.1f} us "
                 f"({backward['mhc_pre_bwd']['GBps']:.0f} GB/s)")
 
+    stack = None
+    if not args.no_stack:
+        log("timing the 60-layer stack (separate entry points, then mhc_post_pre)")
+        stack = time_stack(mhc, torch)
+        log(f"stack: separate {stack['separate']['total_ms']:.2f} ms "
+            f"({stack['separate']['per_layer_us']:.1f} us/layer), fused {stack['fused_post_pre']['total_ms']:.2f} ms "
+            f"({stack['fused_post_pre']['per_layer_us']:.1f} us/layer); amax max {stack['amax']['max']:.6f}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -421,6 +492,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "backward": backward,
+        "stack": stack,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 2
+#define MHC_ABI_VERSION 3
 
 typedef enum mhc_status {
   MHC_OK = 0,
@@ -155,6 +155,28 @@ mhc_status mhc_pre_ex(const mhc_params* p, const void* X, const float* phi, cons
  *               overlap with X, Y or H is MHC_ERR_ALIAS. */
 mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const float* H,
                     void* X_out, void* stream);
+
+/* ---- mhc_post_pre: mhc_post of layer l, then mhc_pre of layer l+1 -------------
+ * In a stack the state a layer writes is the state the next layer reads.
+ * This entry point does both in one pass over the new state: it forms
+ *   X_out = H_res X + H_post^T Y            (layer l's maps H, as mhc_post)
+ * and, from the stored X_out, layer l+1's maps H_next and its sublayer input
+ * h (as mhc_pre with phi, bias and p's alphas / eps / t_max).  The results
+ * are bitwise those of mhc_post followed by mhc_pre; the second read of X_out
+ * that the separate calls make for the projection is saved (the pages fuse
+ * the layer's kernels for the same reason: [t6] tbl-dsv4-mhc-kernels).
+ *   X       in   [T, n, d] layer l's input state
+ *   Y       in   [T, d] layer l's sublayer output
+ *   H       in   [T, m] layer l's maps
+ *   X_out   out  [T, n, d] X_{l+1}; may be exactly X, other overlap refused
+ *   phi, bias    layer l+1's parameters
+ *   h       out  [T, d] layer l+1's sublayer input
+ *   H_next  out  [T, m] layer l+1's maps
+ *   workspace    at least mhc_pre_workspace_size(p) bytes
+ * n = 1 runs the two entry points one after the other. */
+mhc_status mhc_post_pre(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out,
+                        const float* phi, const float* bias, void* h, float* H_next, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* ---- backward ----------------------------------------------------------------
  * The pages give no backward formulas; they state that the layer is trained

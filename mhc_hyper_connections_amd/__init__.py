@@ -6,6 +6,7 @@ The product is ``libmhc.so``, a C-ABI library of hand-written HIP kernels
     h, H = mhc.pre(X, phi, bias, alpha=(a_pre, a_res, a_post), eps=1e-6, t_max=20)
     Y    = F(h)                                   # the caller's sublayer
     Xn   = mhc.post(X, Y, H)                      # or out=X for in place
+    Xn, h2, H2 = mhc.post_pre(X, Y, H, phi2, bias2)   # this layer's post + the next layer's pre
     a    = mhc.amax(H_stack, n)                   # composite-map Amax over layers
 
     dX, dY, dH = mhc.post_bwd(X, Y, H, G)         # backward: G = dL/dXn
@@ -16,10 +17,10 @@ Tensors are torch device tensors: X [T, n, d] and h, Y [T, d] in float32 or
 bfloat16; phi [n*d, n*n+2n], bias [n*n+2n] and H [T, n*n+2n] in float32.
 """
 from ._binding import (EXPORTS, LIB_PATH, MHC_BF16, MHC_FP32, PRE_AUTO, PRE_ONE_PASS, PRE_TWO_PASS, MhcError,
-                       Params, amax, gelu_half, load_library, make_params, post, post_bwd, pre, pre_bwd,
+                       Params, amax, gelu_half, load_library, make_params, post, post_bwd, post_pre, pre, pre_bwd,
                        pre_bwd_workspace_size, pre_ex, pre_workspace_size)
 
-__all__ = ["pre", "pre_ex", "post", "amax", "gelu_half", "pre_workspace_size", "post_bwd", "pre_bwd",
+__all__ = ["pre", "pre_ex", "post", "post_pre", "amax", "gelu_half", "pre_workspace_size", "post_bwd", "pre_bwd",
            "pre_bwd_workspace_size", "load_library", "make_params",
            "Params", "MhcError", "MHC_FP32", "MHC_BF16", "PRE_AUTO", "PRE_TWO_PASS", "PRE_ONE_PASS", "LIB_PATH",
            "EXPORTS"]

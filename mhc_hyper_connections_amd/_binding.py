@@ -17,7 +17,8 @@ MHC_FP32, MHC_BF16 = 0, 1
 STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_DTYPE", 4: "MHC_ERR_ALIGN",
           5: "MHC_ERR_UNSUPPORTED", 6: "MHC_ERR_ALIAS", 7: "MHC_ERR_WORKSPACE", 8: "MHC_ERR_HIP"}
 EXPORTS = ["mhc_pre", "mhc_pre_ex", "mhc_pre_workspace_size", "mhc_post", "mhc_amax", "mhc_gelu_half",
-           "mhc_post_bwd", "mhc_pre_bwd", "mhc_pre_bwd_workspace_size", "mhc_status_string", "mhc_abi_version"]
+           "mhc_post_pre", "mhc_post_bwd", "mhc_pre_bwd", "mhc_pre_bwd_workspace_size", "mhc_status_string",
+           "mhc_abi_version"]
 PRE_AUTO, PRE_TWO_PASS, PRE_ONE_PASS = 0, 1, 2
 
 
@@ -62,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     lib.mhc_amax.restype = ctypes.c_int
     lib.mhc_gelu_half.argtypes = [ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
     lib.mhc_gelu_half.restype = ctypes.c_int
+    lib.mhc_post_pre.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.mhc_post_pre.restype = ctypes.c_int
     lib.mhc_post_bwd.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P]
     lib.mhc_post_bwd.restype = ctypes.c_int
     lib.mhc_pre_bwd_workspace_size.argtypes = [ctypes.POINTER(Params)]
@@ -266,3 +269,27 @@ def pre_bwd(X, phi, bias, D, dH, dX, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=2
                                           _ptr(dX), _ptr(dphi), _ptr(dbias), _ptr(dalpha), _ptr(workspace), ws_bytes,
                                           _stream(stream, dev)))
     return dphi, dbias, dalpha
+
+
+def post_pre(X, Y, H, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, out=None, h=None, H_next=None,
+             workspace=None, stream=None):
+    """mhc_post_pre: layer l's mixing, then layer l+1's maps and sublayer
+    input.  Returns (X_next [T, n, d], h [T, d], H_next [T, m]); ``out`` may
+    be X itself."""
+    torch = _torch()
+    T, n, d = X.shape
+    m = n * n + 2 * n
+    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha)
+    lib = load_library()
+    out = torch.empty_like(X) if out is None else out
+    h = torch.empty((T, d), dtype=X.dtype, device=X.device) if h is None else h
+    H_next = torch.empty((T, m), dtype=torch.float32, device=X.device) if H_next is None else H_next
+    need = int(lib.mhc_pre_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=X.device)
+    _need_device(X, Y, H, phi, bias, out, h, H_next, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("mhc_post_pre", lib.mhc_post_pre(ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(H), _ptr(out), _ptr(phi),
+                                            _ptr(bias), _ptr(h), _ptr(H_next), _ptr(workspace), ws_bytes,
+                                            _stream(stream, X.device)))
+    return out, h, H_next

@@ -154,6 +154,40 @@ mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const flo
   return from_hip(mhc::launch_post(*p, X, Y, H, X_out, static_cast<hipStream_t>(stream)));
 }
 
+mhc_status mhc_post_pre(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out,
+                        const float* phi, const float* bias, void* h, float* H_next, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  mhc_status st = check_params(p);
+  if (st != MHC_OK) return st;
+  if (p->T == 0) return MHC_OK;
+  if (!X || !Y || !H || !X_out || !phi || !bias || !h || !H_next) return MHC_ERR_NULL;
+  const size_t need = mhc::pre_workspace_bytes(p->T, p->n, p->d);
+  if (!workspace || workspace_bytes < need) return MHC_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(H) || !aligned16(X_out) || !aligned16(phi) || !aligned16(bias) ||
+      !aligned16(h) || !aligned16(H_next) || !aligned16(workspace))
+    return MHC_ERR_ALIGN;
+  const int m = p->n * p->n + 2 * p->n;
+  const size_t sb = state_bytes(p->dtype);
+  const size_t xb = static_cast<size_t>(p->T) * p->n * p->d * sb;
+  const size_t hb = static_cast<size_t>(p->T) * p->d * sb;
+  const size_t mb = static_cast<size_t>(p->T) * m * 4;
+  const Range rX = range_of(X, xb), rO = range_of(X_out, xb);
+  if (X_out != X && overlap(rO, rX)) return MHC_ERR_ALIAS;
+  const Range ins[4] = {range_of(Y, hb), range_of(H, mb), range_of(phi, static_cast<size_t>(p->n) * p->d * m * 4),
+                        range_of(bias, static_cast<size_t>(m) * 4)};
+  const Range outs[4] = {rO, range_of(h, hb), range_of(H_next, mb), range_of(workspace, need)};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 4; ++b)
+      if (overlap(outs[a], ins[b])) return MHC_ERR_ALIAS;
+    if (a > 0 && overlap(outs[a], rX)) return MHC_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return MHC_ERR_ALIAS;
+  }
+  const mhc::DeviceInfo dev = device_info();
+  return from_hip(mhc::launch_post_pre(*p, X, Y, H, X_out, phi, bias, h, H_next, workspace, dev,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 mhc_status mhc_post_bwd(const mhc_params* p, const void* X, const void* Y, const float* H, const void* G, void* dX,
                         void* dY, float* dH, void* stream) {
   mhc_status st = check_params(p);

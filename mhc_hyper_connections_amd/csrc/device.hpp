@@ -77,6 +77,30 @@ __device__ __forceinline__ void unpack8(const Raw8<F32>& r, float (&x)[8]) {
   }
 }
 
+// Round 8 values to the storage form (bf16: nearest, ties to even) and store it.
+__device__ __forceinline__ Raw8<BF16> pack8(const float (&x)[8], BF16) {
+  return Raw8<BF16>{u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])}};
+}
+__device__ __forceinline__ Raw8<F32> pack8(const float (&x)[8], F32) {
+  return Raw8<F32>{f32x4{x[0], x[1], x[2], x[3]}, f32x4{x[4], x[5], x[6], x[7]}};
+}
+template <bool NT>
+__device__ __forceinline__ void store_raw8(uint16_t* p, const Raw8<BF16>& r) {
+  if (NT) __builtin_nontemporal_store(r.v, reinterpret_cast<u32x4*>(p));
+  else *reinterpret_cast<u32x4*>(p) = r.v;
+}
+template <bool NT>
+__device__ __forceinline__ void store_raw8(float* p, const Raw8<F32>& r) {
+  f32x4* q = reinterpret_cast<f32x4*>(p);
+  if (NT) {
+    __builtin_nontemporal_store(r.a, q);
+    __builtin_nontemporal_store(r.b, q + 1);
+  } else {
+    q[0] = r.a;
+    q[1] = r.b;
+  }
+}
+
 template <typename ST, bool NT = false>
 __device__ __forceinline__ void store8(typename ST::elem* p, const float (&x)[8]);
 

@@ -27,6 +27,11 @@ hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, cons
                       float* H, void* workspace, size_t ws_bytes, int algo, int* used, const DeviceInfo& dev,
                       hipStream_t stream);
 
+// mhc_post of layer l fused with mhc_pre of layer l+1 (pre.hip); workspace as mhc_pre's.
+hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, const float* Hprev, void* Xout,
+                           const float* phi, const float* bias, void* h, float* H, void* workspace, const DeviceInfo& dev,
+                           hipStream_t stream);
+
 // The single-pass form (pre_fused.hip): hipErrorNotSupported when it does not apply.
 size_t pre_fused_workspace_bytes(int64_t T, int n, int d);
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,

@@ -38,8 +38,8 @@ constexpr int PRE_THREADS = PRE_WAVES * 64;
 constexpr int PRE_SLICE = PRE_WAVES * 32;   // positions of d per slice (32 per wave)
 
 // Write-only slots after the partial records that absorb the stores of
-// items past the end (one double per thread).
-constexpr size_t kPartTrashBytes = PRE_THREADS * sizeof(double);
+// items past the end (16 bytes per thread).
+constexpr size_t kPartTrashBytes = PRE_THREADS * 16;
 
 // Per-token record of one slice in the workspace: m fp32 partial dot
 // products (then, for the backward, n more: <D, X_i> over the slice), then
@@ -49,16 +49,29 @@ __host__ __device__ constexpr int ss_offset(int n, bool with_d = false) {
 }
 __host__ __device__ constexpr int part_width(int n, bool with_d = false) { return ss_offset(n, with_d) + 2; }
 
-template <typename ST, int N, int MB, bool WITH_D>
+// MODE 0: the forward's projection partials of X.
+// MODE 1: the backward's: also <D, X_i> per stream (Dg = D).
+// MODE 2: the previous layer's mhc_post fused in front: X is X_l, Dg is
+//         Y_l, Hin its maps; the tile's X_{l+1} = H_res X_l + H_post Y_l is
+//         formed with mhc_post's arithmetic, stored to Xout, and its
+//         projection partials (for the next layer) computed from the stored
+//         values.
+template <typename ST, int N, int MB, int MODE>
 __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int d, int S, int64_t ntiles,
-                                                                  const typename ST::elem* __restrict__ X,
+                                                                  const typename ST::elem* X,
                                                                   const typename ST::elem* __restrict__ Dg,
                                                                   const float* __restrict__ phi,
-                                                                  float* __restrict__ part) {
+                                                                  float* __restrict__ part,
+                                                                  const float* __restrict__ Hin,
+                                                                  typename ST::elem* Xout) {
+  constexpr bool WITH_D = MODE == 1;
+  constexpr bool FUSE_POST = MODE == 2;
   constexpr int M = num_maps(N);
   constexpr int NB = (M + 15) / 16;
   constexpr int R = 16 * MB;
   constexpr int ND = WITH_D ? N : 0;
+  constexpr int NX = N + ((WITH_D || FUSE_POST) ? 1 : 0);   // chunks per token row: streams, then D or Y
+  constexpr int HV = FUSE_POST ? M / 4 : 1;                 // the maps row of the previous layer, as f32x4
   constexpr int PW = part_width(N, WITH_D);
   constexpr int SSO = ss_offset(N, WITH_D);
   __shared__ float red[PRE_WAVES][R][M + ND];
@@ -90,21 +103,26 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
   }
   __builtin_amdgcn_sched_barrier(0);     // finish the phi operands before the first tile's loads
 
-  Raw8<ST> xa[MB][N + ND], xb[MB][N + ND];     // chunk N: D (backward only)
+  Raw8<ST> xa[MB][NX], xb[MB][NX];             // chunk N: D (backward) or Y (fused post)
+  f32x4 ha[MB][HV], hb[MB][HV];                // the previous layer's maps (fused post only)
   // Every lane loads every chunk from a valid address, with no branch and no
   // select on the data (either would make the compiler wait for the load on
   // the spot): tokens past T read token 0 (their rows are never written) and
   // lanes past d read position 0 (their phi rows are zero and their squares
   // are dropped below).
   const int jl = jv ? j0 : 0;
-  auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][N + ND]) {
+  auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][NX], f32x4 (&hv)[MB][HV]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int64_t t = tile * R + mb * 16 + r16;
       const int64_t tt = t < T ? t : 0;
 #pragma unroll
       for (int i = 0; i < N; ++i) x[mb][i] = load_raw8<ST>(X + (tt * N + i) * d + jl);
-      if (WITH_D) x[mb][N] = load_raw8<ST>(Dg + tt * d + jl);
+      if constexpr (WITH_D || FUSE_POST) x[mb][N] = load_raw8<ST>(Dg + tt * d + jl);
+      if constexpr (FUSE_POST) {
+#pragma unroll
+        for (int v = 0; v < HV; ++v) hv[mb][v] = *reinterpret_cast<const f32x4*>(Hin + tt * M + 4 * v);
+      }
     }
   };
 
@@ -113,7 +131,42 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
   // prefetch distance two, the loop unrolled by two so the buffers keep
   // their registers (copying a buffer that is still being loaded would wait
   // for it and serialise the prefetch).
-  auto step = [&](int64_t tile, Raw8<ST> (&cur)[MB][N + ND]) {
+  auto step = [&](int64_t tile, Raw8<ST> (&cur)[MB][NX], f32x4 (&hv)[MB][HV]) {
+    if constexpr (FUSE_POST) {
+      // X_{l+1} = H_res X_l + H_post Y_l, term order as in mhc_post; the
+      // stored (rounded) values replace X_l for the projection below.
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        float mix[N * N + N];
+#pragma unroll
+        for (int q = 0; q < N * N + N; ++q) mix[q] = hv[mb][(N + q) >> 2][(N + q) & 3];
+        float x[N][8], y[8];
+#pragma unroll
+        for (int i = 0; i < N; ++i) unpack8(cur[mb][i], x[i]);
+        unpack8(cur[mb][N], y);
+        const int64_t t = tile * R + mb * 16 + r16;
+        Raw8<ST> nx[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float a = mix[i * N] * x[0][e];
+#pragma unroll
+            for (int j = 1; j < N; ++j) a = fmaf(mix[i * N + j], x[j][e], a);
+            o[e] = fmaf(mix[N * N + i], y[e], a);
+          }
+          nx[i] = pack8(o, ST{});
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          typename ST::elem* dst = (t < T && jv) ? Xout + (t * N + i) * d + j0
+                                                 : reinterpret_cast<typename ST::elem*>(trash) + threadIdx.x * 8;
+          store_raw8<true>(dst, nx[i]);
+          cur[mb][i] = nx[i];
+        }
+      }
+    }
 
     // Sum of squares in fp64: never overflows for a finite fp32 / bf16 state
     // (fp32 overflows once the state's RMS passes ~1.8e19 / sqrt(n d)).
@@ -204,7 +257,7 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
       *dst = sum;
     }
     __syncthreads();
-    load_tile(tile + 2 * ntg, cur);
+    load_tile(tile + 2 * ntg, cur, hv);
     __builtin_amdgcn_sched_barrier(0);   // keep the prefetch here: the scheduler would sink it to its use
   };
 
@@ -216,13 +269,18 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
   // both buffers, which halved the loads in flight.
   const int64_t tile0 = blockIdx.x / S;
   const int64_t per_wg = (ntiles + ntg - 1) / ntg;
-  load_tile(tile0, xa);
-  load_tile(tile0 + ntg, xb);
+  load_tile(tile0, xa, ha);
+  __builtin_amdgcn_sched_barrier(0);     // all of the first buffer's loads before the second's
+  load_tile(tile0 + ntg, xb, hb);
   __builtin_amdgcn_sched_barrier(0);
-  for (int64_t k = 0; k < per_wg; k += 2) {
-    step(tile0 + k * ntg, xa);
-    step(tile0 + (k + 1) * ntg, xb);
-  }
+  // do-while: at least one pair runs (T >= 1), and without the zero-trip
+  // guard the compiler cannot sink the prologue's loads below a branch.
+  int64_t k = 0;
+  do {
+    step(tile0 + k * ntg, xa, ha);
+    step(tile0 + (k + 1) * ntg, xb, hb);
+    k += 2;
+  } while (k < per_wg);
 }
 
 // One token per wave.  The token's X streams in passes of 64 lanes x 8
@@ -377,13 +435,43 @@ hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, co
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
   const int64_t grid = groups * S;
-  hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, false>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
-                     stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(nullptr), phi, part);
+  hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 0>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
+                     stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(nullptr), phi, part,
+                     static_cast<const float*>(nullptr), static_cast<E*>(nullptr));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t blocks = (p.T + 3) / 4;
   hipLaunchKernelGGL((pre_finish_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T, p.d, S,
                      static_cast<const E*>(X), static_cast<const float*>(part), bias, p.alpha_pre, p.alpha_res,
+                     p.alpha_post, p.eps, p.t_max, static_cast<E*>(h), H);
+  return hipGetLastError();
+}
+
+// mhc_post of the previous layer fused into the partial pass (MODE 2), then
+// the finishing pass on the new state.  16-token tiles: a tile buffer also
+// holds Y and the previous layer's maps.
+template <typename ST, int N>
+hipError_t launch_post_pre_t(const mhc_params& p, const void* X, const void* Y, const float* Hprev, void* Xout,
+                             const float* phi, const float* bias, void* h, float* H, void* workspace,
+                             const DeviceInfo& dev, hipStream_t stream) {
+  typedef typename ST::elem E;
+  constexpr int MB = 1;
+  constexpr int R = 16 * MB;
+  const int S = num_slices(p.d);
+  const int64_t ntiles = (p.T + R - 1) / R;
+  float* part = static_cast<float*>(workspace);
+  int64_t groups = dev.num_cus / S;
+  if (groups < 1) groups = 1;
+  if (groups > ntiles) groups = ntiles;
+  const int64_t grid = groups * S;
+  hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 2>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
+                     stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(Y), phi, part,
+                     Hprev, static_cast<E*>(Xout));
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t blocks = (p.T + 3) / 4;
+  hipLaunchKernelGGL((pre_finish_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T, p.d, S,
+                     static_cast<const E*>(Xout), static_cast<const float*>(part), bias, p.alpha_pre, p.alpha_res,
                      p.alpha_post, p.eps, p.t_max, static_cast<E*>(h), H);
   return hipGetLastError();
 }
@@ -411,8 +499,9 @@ hipError_t launch_partial_d_t(const mhc_params& p, const void* X, const void* D,
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
   const int64_t grid = groups * S;
-  hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, true>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
-                     stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(D), phi, part);
+  hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 1>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
+                     stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(D), phi, part,
+                     static_cast<const float*>(nullptr), static_cast<E*>(nullptr));
   return hipGetLastError();
 }
 
@@ -440,6 +529,26 @@ hipError_t launch_pre_partial_with_d(const mhc_params& p, const void* X, const v
 size_t pre_partial_bytes(int64_t T, int n, int d, bool with_d) {
   return static_cast<size_t>(num_slices(d)) * static_cast<size_t>(T) * static_cast<size_t>(part_width(n, with_d)) *
              sizeof(float) + kPartTrashBytes;
+}
+
+hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, const float* Hprev, void* Xout,
+                           const float* phi, const float* bias, void* h, float* H, void* workspace, const DeviceInfo& dev,
+                           hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  const bool bf = p.dtype == MHC_BF16;
+  switch (p.n) {
+    case 2: return bf ? launch_post_pre_t<BF16, 2>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream)
+                      : launch_post_pre_t<F32, 2>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream);
+    case 4: return bf ? launch_post_pre_t<BF16, 4>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream)
+                      : launch_post_pre_t<F32, 4>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream);
+    default: {   // n = 1: m = 3 maps per token; the two entry points one after the other
+      hipError_t e = launch_post(p, X, Y, Hprev, Xout, stream);
+      if (e != hipSuccess) return e;
+      int used = 0;
+      return launch_pre(p, Xout, phi, bias, h, H, workspace, pre_workspace_bytes(p.T, p.n, p.d), MHC_PRE_TWO_PASS,
+                        &used, dev, stream);
+    }
+  }
 }
 
 size_t pre_workspace_bytes(int64_t T, int n, int d) {

@@ -67,3 +67,20 @@ def sample_tokens(T: int, count: int, seed: int = 7, tile: int = 64) -> np.ndarr
     pick = {0, T - 1, min(T - 1, tile - 1), min(T - 1, tile), T // 2}
     pick.update(int(v) for v in rng.integers(0, T, size=max(0, count - len(pick))))
     return np.array(sorted(p for p in pick if 0 <= p < T), dtype=np.int64)
+
+
+def check_stack_state(got, ref):
+    """Final state of the 60-layer stack.  The bf16 stack amplifies a single
+    storage rounding: the oracle itself moves outputs by up to ~5% when one
+    input value changes by one bf16 ulp (tests/test_stack_conditioning.py).
+    So: 99.9% of values within the bf16 tolerance, every value within 10%;
+    the absolute part scales with the token's RMS, which grows ~2^57 over the
+    60 layers."""
+    g, r = values(got), values(ref)
+    scale = np.sqrt(np.mean(r * r, axis=(1, 2), keepdims=True))
+    err = np.abs(g - r)
+    inside = err <= 2e-2 * np.abs(r) + 1e-2 * scale
+    assert np.all(np.isfinite(g))
+    assert inside.mean() >= 0.999, f"{(~inside).sum()} of {inside.size} outside the bf16 tolerance"
+    worst = float(np.max((err - 1e-2 * scale) / np.maximum(np.abs(r), 1e-30)))
+    assert np.all(err <= 0.1 * np.abs(r) + 1e-2 * scale), f"worst relative error {worst:.3f}"

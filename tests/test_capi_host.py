@@ -99,7 +99,7 @@ def test_workspace_size_formula(lib):
         p = _params(T=T, n=n, d=d)
         slices = -(-d // 256)
         width = ((n * n + 2 * n + 1) & ~1) + 2          # m fp32 partials, then an aligned fp64
-        two_pass = slices * T * width * 4 + 512 * 8     # records + write-only trash slots
+        two_pass = slices * T * width * 4 + 512 * 16    # records + write-only trash slots (16 B per thread)
         one_pass = 256 + 8 * (48 // slices) * 4 * slices * 32 * (n * n + 2 * n + 2) * 8 if 8 <= slices <= 16 else 0
         assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == max(two_pass, one_pass)
     assert lib.mhc_pre_workspace_size(None) == 0
@@ -177,3 +177,22 @@ def test_pre_bwd_argument_checks(lib):
     assert f(p, ws=A[4]) == 6                          # workspace onto dH
     assert lib.mhc_pre_bwd_workspace_size(None) == 0
     assert lib.mhc_pre_bwd_workspace_size(ctypes.byref(_params(n=3))) == 0
+
+
+def test_post_pre_argument_checks(lib):
+    p = _params()
+    need = lib.mhc_pre_workspace_size(ctypes.byref(p))
+
+    def f(p, X=A[0], Y=A[1], H=A[2], O=A[3], phi=A[4], bias=A[5], h=A[6], Hn=A[7], ws=A[7] + (1 << 24), nb=None):
+        nb = need if nb is None else nb
+        return lib.mhc_post_pre(ctypes.byref(p), X, Y, H, O, phi, bias, h, Hn, ws, nb, None)
+    assert f(_params(n=3)) == 5
+    assert f(p, phi=None) == 1
+    assert f(p, ws=None) == 7
+    assert f(p, nb=need - 1) == 7
+    assert f(p, O=A[0] + 512) == 6                     # partial overlap with X
+    assert f(p, h=A[1]) == 6                           # h onto Y
+    assert f(p, Hn=A[6]) == 6                          # H_next onto h
+    assert f(p, ws=A[2]) == 6                          # workspace onto the previous maps
+    assert f(p, X=A[0] + 4) == 4
+    assert f(_params(T=0), X=None) == 0

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import TOL, assert_close, dname, sample_tokens, to_device, to_host, values
+from gpu_helpers import check_stack_state, TOL, assert_close, dname, sample_tokens, to_device, to_host, values
 
 pytestmark = pytest.mark.gpu
 
@@ -162,23 +162,6 @@ def test_gelu_half(mhc, oracle_lib):
         y = to_host(mhc.gelu_half(to_device(h)))
         tol = (1e-5, 1e-6) if dt == synth.FP32 else (8e-3, 1e-6)
         assert_close(y, oracle_lib.gelu_half(h), *tol, what="gelu_half")
-
-
-def check_stack_state(got, ref):
-    """Final state of the 60-layer stack.  The bf16 stack amplifies a single
-    storage rounding: the oracle itself moves outputs by up to ~5% when one
-    input value changes by one bf16 ulp (tests/test_stack_conditioning.py).
-    So: 99.9% of values within the bf16 tolerance, every value within 10%;
-    the absolute part scales with the token's RMS, which grows ~2^57 over the
-    60 layers."""
-    g, r = values(got), values(ref)
-    scale = np.sqrt(np.mean(r * r, axis=(1, 2), keepdims=True))
-    err = np.abs(g - r)
-    inside = err <= 2e-2 * np.abs(r) + 1e-2 * scale
-    assert np.all(np.isfinite(g))
-    assert inside.mean() >= 0.999, f"{(~inside).sum()} of {inside.size} outside the bf16 tolerance"
-    worst = float(np.max((err - 1e-2 * scale) / np.maximum(np.abs(r), 1e-30)))
-    assert np.all(err <= 0.1 * np.abs(r) + 1e-2 * scale), f"worst relative error {worst:.3f}"
 
 
 def _stack(mhc, w, T, L):
