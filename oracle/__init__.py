@@ -59,6 +59,11 @@ def _bind(lib):
     lib.mhcref_stack.argtypes = [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _D, _I32, _P, _I64,
                                  _P, _P, _P, _P, _P, _P]
     lib.mhcref_stack.restype = _I32
+    lib.mhcref_pre_hc.argtypes = [_I64, _I32, _I32, _I32, _P, _P, _P, _P, _D, _P, _I64, _P, _P]
+    lib.mhcref_pre_hc.restype = _I32
+    lib.mhcref_stack_hc.argtypes = [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _D, _P, _I64,
+                                    _P, _P, _P, _P, _P]
+    lib.mhcref_stack_hc.restype = _I32
     lib.mhcref_bwd.argtypes = [_I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _D, _I32, _P, _P, _P, _I64,
                                _P, _P, _P, _P, _P, _P, _P]
     lib.mhcref_bwd.restype = _I32
@@ -278,3 +283,40 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"mhcref_bwd_f64 rejected its arguments ({rc})")
         return out
+
+    def pre_hc(self, X, phi, bias, alpha, eps=1e-6, tokens=None):
+        """HC-form maps (bias + alpha * tanh(z)) and aggregation: dict H, h."""
+        X = np.ascontiguousarray(X)
+        T, n, d = X.shape
+        m = n * n + 2 * n
+        phi = np.ascontiguousarray(phi, dtype=np.float32)
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        a3 = np.ascontiguousarray(np.asarray(alpha, dtype=np.float32).reshape(3))
+        tok = _tokens(T, tokens)
+        q = tok.size
+        H, h = np.empty((q, m)), np.empty((q, d))
+        rc = self.lib.mhcref_pre_hc(T, n, d, _dtype_code(X), _ptr(X), _ptr(phi), _ptr(bias), _ptr(a3), float(eps),
+                                    _ptr(tok), q, _ptr(h), _ptr(H))
+        if rc != 0:
+            raise ValueError(f"mhcref_pre_hc rejected its arguments ({rc})")
+        return {"H": H, "h": h}
+
+    def stack_hc(self, X0, phis, biases, alphas, eps=1e-6, tokens=None):
+        """The L-layer stack with HC-form maps; same outputs as stack()."""
+        X0 = np.ascontiguousarray(X0)
+        T, n, d = X0.shape
+        m = n * n + 2 * n
+        phis = np.ascontiguousarray(phis, dtype=np.float32)
+        L = phis.shape[0]
+        biases = np.ascontiguousarray(biases, dtype=np.float32)
+        alphas = np.ascontiguousarray(alphas, dtype=np.float32)
+        tok = _tokens(T, tokens)
+        q = tok.size
+        Xf = np.empty((q, n, d), dtype=X0.dtype)
+        Hs = np.empty((L, q, m), dtype=np.float32)
+        a, f, b = np.empty(q), np.empty(q), np.empty(q)
+        rc = self.lib.mhcref_stack_hc(T, n, d, _dtype_code(X0), L, _ptr(X0), _ptr(phis), _ptr(biases), _ptr(alphas),
+                                      float(eps), _ptr(tok), q, _ptr(Xf), _ptr(Hs), _ptr(a), _ptr(f), _ptr(b))
+        if rc != 0:
+            raise ValueError(f"mhcref_stack_hc rejected its arguments ({rc})")
+        return {"X": Xf, "H": Hs, "amax": a, "gain_fwd": f, "gain_bwd": b}

@@ -189,6 +189,34 @@ TokenMaps token_maps(int n, int d, const std::vector<double>& x, const P* phi,
   return out;
 }
 
+// ---- the HC form of the maps, for contrast ([P2] Kernmechanismen: in HC every
+// map is a learned static part, a bias, plus an input-dependent term passed
+// through tanh, so its values can take either sign; Details van de
+// parameterisatie: mHC replaces that tanh by the sigmoid gates).  Reading:
+// H = bias + alpha_blk * tanh(z) for all three maps, with z = x_hat . phi as
+// in mHC and no Sinkhorn.
+std::vector<double> hc_maps(int n, int d, const std::vector<double>& x, const float* phi, const float* bias,
+                            const float* alpha3, double eps) {
+  const int m = n * n + 2 * n;
+  const TokenMaps tm = token_maps(n, d, x, phi, bias, alpha3, eps, 0);   // r and z only
+  std::vector<double> H(m);
+  for (int j = 0; j < m; ++j) {
+    const int blk = (j < n) ? 0 : (j < n + n * n) ? 1 : 2;     // pre | res | post
+    const double a = static_cast<double>(alpha3[blk]);
+    H[j] = static_cast<double>(bias[j]) + a * std::tanh(tm.z[j]);
+  }
+  return H;
+}
+
+// The maps of one layer for one token: kind 0 = mHC, kind 1 = HC.
+std::vector<double> layer_maps(int kind, int n, int d, const std::vector<double>& x, const float* phi,
+                               const float* bias, const float* alpha3, double eps, int t_max, double* sk_err) {
+  if (kind == 1) return hc_maps(n, d, x, phi, bias, alpha3, eps);
+  TokenMaps tm = token_maps(n, d, x, phi, bias, alpha3, eps, t_max);
+  if (sk_err) for (int j = 0; j < 4; ++j) sk_err[j] = tm.sk_err[j];
+  return tm.H;
+}
+
 // Aggregation h = H_pre . X   ([P2] Kernmechanismen, Eq. 3: F(H_pre x_l)).
 void aggregate(int n, int d, const std::vector<double>& x, const double* Hpre, double* h) {
   for (int c = 0; c < d; ++c) {
@@ -407,7 +435,7 @@ bool bad_shape(int64_t T, int n, int d, int dtype) {
 
 extern "C" {
 
-int mhcref_version(void) { return 2; }
+int mhcref_version(void) { return 3; }
 
 // Rounding helpers exposed for the tests: round doubles to bf16 bits (RNE).
 void mhcref_round_bf16(const double* in, uint16_t* out, int64_t count) {
@@ -512,10 +540,10 @@ int mhcref_gelu_half(int64_t count, int dtype, const void* h, double* y) {
 //   X0 [T, n, d] storage; phis [L, n*d, m]; biases [L, m]; alphas [L, 3].
 //   Outputs: Xf [ntok, n, d] storage dtype; Hs [L, ntok, m] fp32 (nullable);
 //   amax / gfwd / gbwd [ntok] (nullable); sk_err [L, ntok, 4] (nullable).
-int mhcref_stack(int64_t T, int n, int d, int dtype, int L, const void* X0, const float* phis,
-                 const float* biases, const float* alphas, double eps, int t_max,
-                 const int64_t* tokens, int64_t ntok, void* Xf, float* Hs, double* amax,
-                 double* gfwd, double* gbwd, double* sk_err) {
+static int stack_impl(int kind, int64_t T, int n, int d, int dtype, int L, const void* X0, const float* phis,
+                      const float* biases, const float* alphas, double eps, int t_max,
+                      const int64_t* tokens, int64_t ntok, void* Xf, float* Hs, double* amax,
+                      double* gfwd, double* gbwd, double* sk_err) {
   if (bad_shape(T, n, d, dtype) || L < 0 || t_max < 0 || !X0 || !phis || !biases || !alphas || !Xf)
     return -1;
   const int K = n * d;
@@ -528,13 +556,14 @@ int mhcref_stack(int64_t T, int n, int d, int dtype, int L, const void* X0, cons
     for (int k = 0; k < K; ++k) x[k] = load(dtype, X0, t * K + k);
     for (int l = 0; l < L; ++l) {
       const float* phi = phis + static_cast<int64_t>(l) * K * m;
-      TokenMaps tm = token_maps(n, d, x, phi, biases + l * m, alphas + 3 * l, eps, t_max);
-      if (sk_err) for (int j = 0; j < 4; ++j) sk_err[(static_cast<int64_t>(l) * ntok + q) * 4 + j] = tm.sk_err[j];
+      double skl[4] = {0, 0, 0, 0};
+      const std::vector<double> Hd = layer_maps(kind, n, d, x, phi, biases + l * m, alphas + 3 * l, eps, t_max, skl);
+      if (sk_err) for (int j = 0; j < 4; ++j) sk_err[(static_cast<int64_t>(l) * ntok + q) * 4 + j] = skl[j];
       for (int j = 0; j < m; ++j) {
-        Hl[l * m + j] = static_cast<float>(tm.H[j]);
+        Hl[l * m + j] = static_cast<float>(Hd[j]);
         Hr[j] = static_cast<double>(Hl[l * m + j]);
       }
-      aggregate(n, d, x, tm.H.data(), h.data());
+      aggregate(n, d, x, Hd.data(), h.data());
       for (int c = 0; c < d; ++c) h[c] = store_round(dtype, h[c]);
       for (int c = 0; c < d; ++c) y[c] = store_round(dtype, gelu_half(h[c]));
       mix(n, d, x, y, &Hr[n], &Hr[n + n * n], xo.data());
@@ -550,6 +579,40 @@ int mhcref_stack(int64_t T, int n, int d, int dtype, int L, const void* X0, cons
       if (gbwd) gbwd[q] = b;
       if (amax) amax[q] = std::fmax(f, b);
     }
+  }
+  return 0;
+}
+
+int mhcref_stack(int64_t T, int n, int d, int dtype, int L, const void* X0, const float* phis,
+                 const float* biases, const float* alphas, double eps, int t_max,
+                 const int64_t* tokens, int64_t ntok, void* Xf, float* Hs, double* amax,
+                 double* gfwd, double* gbwd, double* sk_err) {
+  return stack_impl(0, T, n, d, dtype, L, X0, phis, biases, alphas, eps, t_max, tokens, ntok, Xf, Hs, amax, gfwd,
+                    gbwd, sk_err);
+}
+
+// The same stack with the HC form of the maps (no Sinkhorn, no gates).
+int mhcref_stack_hc(int64_t T, int n, int d, int dtype, int L, const void* X0, const float* phis,
+                    const float* biases, const float* alphas, double eps, const int64_t* tokens, int64_t ntok,
+                    void* Xf, float* Hs, double* amax, double* gfwd, double* gbwd) {
+  return stack_impl(1, T, n, d, dtype, L, X0, phis, biases, alphas, eps, 0, tokens, ntok, Xf, Hs, amax, gfwd, gbwd,
+                    nullptr);
+}
+
+// HC-form maps and aggregation for the listed tokens (outputs as mhcref_pre's H and h).
+int mhcref_pre_hc(int64_t T, int n, int d, int dtype, const void* X, const float* phi, const float* bias,
+                  const float* alpha3, double eps, const int64_t* tokens, int64_t ntok, double* h, double* H) {
+  if (bad_shape(T, n, d, dtype) || !X || !phi || !bias || !alpha3 || !H) return -1;
+  const int K = n * d;
+  const int m = n * n + 2 * n;
+  std::vector<double> x(K);
+  for (int64_t q = 0; q < ntok; ++q) {
+    const int64_t t = tokens[q];
+    if (t < 0 || t >= T) return -2;
+    for (int k = 0; k < K; ++k) x[k] = load(dtype, X, t * K + k);
+    const std::vector<double> Hd = hc_maps(n, d, x, phi, bias, alpha3, eps);
+    for (int j = 0; j < m; ++j) H[q * m + j] = Hd[j];
+    if (h) aggregate(n, d, x, Hd.data(), h + q * d);
   }
   return 0;
 }

@@ -597,4 +597,73 @@ def pin_bwd_storage_forms_agree(o):
         assert np.allclose(a[k] + b[k], ref[k], rtol=1e-12, atol=1e-15), k
 
 
+# --------------------------------------------------------------------------
+# The HC form of the maps, for contrast ([P2] Kernmechanismen: a static bias
+# plus an input-dependent term through tanh, either sign; reading
+# H = bias + alpha_blk * tanh(z), no Sinkhorn).
+
+def pin_hc_maps_closed_form(o):
+    """One-hot phi columns give z exactly (as for mHC), so every map is
+    bias + alpha_blk * tanh(c / r); alpha = 0 leaves the bias itself, which
+    for HC is the map (no exp, no normalisation, no gate)."""
+    n, d, m = 4, 8, 24
+    rng = np.random.default_rng(40)
+    X = rng.normal(0, 1, (1, n, d)).astype(np.float32)
+    x = X.reshape(-1).astype(np.float64)
+    r = math.sqrt(float(np.mean(x * x)) + 1e-6)
+    phi = np.zeros((n * d, m), dtype=np.float32)
+    for j in range(m):
+        phi[(5 * j) % (n * d), j] = 1.0
+    bias = rng.normal(0, 0.5, m).astype(np.float32)
+    alpha = (0.7, -1.3, 2.1)
+    H = o.pre_hc(X, phi, bias, alpha)["H"][0]
+    for j in range(m):
+        a = float(np.float32(alpha[0] if j < n else alpha[1] if j < n + n * n else alpha[2]))
+        expect = float(bias[j]) + a * math.tanh(x[(5 * j) % (n * d)] / r)
+        assert abs(H[j] - expect) <= 1e-12, (j, H[j], expect)
+    H0 = o.pre_hc(X, phi, bias, (0.0, 0.0, 0.0))
+    assert np.array_equal(H0["H"][0], bias.astype(np.float64))
+    assert np.allclose(H0["h"][0], bias[:n].astype(np.float64) @ X[0].astype(np.float64), rtol=1e-14, atol=1e-14)
+
+
+def pin_hc_odd_and_bounded(o):
+    """tanh is odd and bounded: H(phi) + H(-phi) = 2 bias, |H - bias| < |alpha|,
+    and the residual map is not normalised (its rows do not sum to one)."""
+    rng = np.random.default_rng(41)
+    X, phi, bias, _, _ = _layer_inputs(rng, 5, 4, 16, (1.0, 1.0, 1.0), bres=1.0)
+    phi = (phi * 50).astype(np.float32)                 # large z: tanh saturates
+    alpha = (0.5, 0.8, -0.6)
+    a = o.pre_hc(X, phi, bias, alpha)["H"]
+    b = o.pre_hc(X, (-phi).astype(np.float32), bias, alpha)["H"]
+    assert np.allclose(a + b, 2.0 * bias.astype(np.float64)[None, :], rtol=0, atol=1e-14)
+    lim = np.concatenate([np.full(4, 0.5), np.full(16, 0.8), np.full(4, 0.6)]).astype(np.float32)
+    assert np.all(np.abs(a - bias.astype(np.float64)[None, :]) <= lim.astype(np.float64)[None, :])
+    rows = a[:, 4:20].reshape(5, 4, 4).sum(axis=2)
+    assert np.max(np.abs(rows - 1.0)) > 0.1
+
+
+def pin_hc_stack_compounds(o):
+    """The pages' point about the composite map: with every residual map
+    1.1 I (alpha = 0, bias only) the product over 60 layers is 1.1^60 I, an
+    Amax of 1.1^60 ~ 304 (the pages' ~300), and with zero read and write
+    maps the state itself is scaled by 1.1^60.  The mHC form of the same
+    bias is doubly stochastic: Amax 1 (to Sinkhorn's 20-pass accuracy)."""
+    n, d, T, L = 4, 8, 3, 60
+    rng = np.random.default_rng(42)
+    X0 = rng.normal(0, 1, (T, n, d)).astype(np.float32)
+    phis = rng.normal(0, 0.02, (L, n * d, 24)).astype(np.float32)
+    biases = np.zeros((L, 24), np.float32)
+    biases[:, 4:20] = (1.1 * np.eye(n)).reshape(-1)
+    biases[:, :4] = 0.0                                  # HC read map 0: h = 0, F(0) = 0
+    biases[:, 20:] = 0.0                                 # HC write map 0
+    alphas = np.zeros((L, 3), np.float32)
+    g = float(np.float32(1.1)) ** 60                     # the bias is stored in fp32
+    hc = o.stack_hc(X0, phis, biases, alphas)
+    assert np.allclose(hc["amax"], g, rtol=1e-12), hc["amax"]
+    assert abs(g - 304.48) < 0.01
+    assert np.allclose(hc["X"].astype(np.float64), g * X0.astype(np.float64), rtol=1e-5, atol=0)
+    mhc = o.stack(X0, phis, biases, alphas)              # doubly stochastic to Sinkhorn's 20-pass accuracy
+    assert np.all(np.abs(mhc["amax"] - 1.0) < 1e-5), mhc["amax"]
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

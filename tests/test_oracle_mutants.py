@@ -66,6 +66,12 @@ MUTANTS = {
     "bwd_dHres_transposed": ("acc += G[i * d + c] * x[j * d + c];", "acc += G[j * d + c] * x[i * d + c];"),
     "bwd_dHpre_uses_output_grad": ("for (int c = 0; c < d; ++c) acc += D[c] * x[i * d + c];",
                                    "for (int c = 0; c < d; ++c) acc += G[i * d + c] * x[i * d + c];"),
+    "hc_no_tanh": ("H[j] = static_cast<double>(bias[j]) + a * std::tanh(tm.z[j]);",
+                   "H[j] = static_cast<double>(bias[j]) + a * tm.z[j];"),
+    "hc_alpha_inside_tanh": ("H[j] = static_cast<double>(bias[j]) + a * std::tanh(tm.z[j]);",
+                             "H[j] = static_cast<double>(bias[j]) + std::tanh(a * tm.z[j]) * 1.5;"),
+    "hc_drops_bias": ("H[j] = static_cast<double>(bias[j]) + a * std::tanh(tm.z[j]);", "H[j] = a * std::tanh(tm.z[j]);"),
+    "stack_hc_uses_mhc_maps": ("if (kind == 1) return hc_maps(n, d, x, phi, bias, alpha3, eps);", ""),
     "stack_skips_rounding": ("for (int k = 0; k < K; ++k) x[k] = store_round(dtype, xo[k]);",
                              "for (int k = 0; k < K; ++k) x[k] = xo[k];"),
 }
