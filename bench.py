@@ -167,6 +167,26 @@ def time_stack(mhc, torch, reps=5, warmup=2):
     mhc.amax(Hs, n, out_amax=amax, want_all=False)
     a = amax.cpu().numpy()
     out["amax"] = {"max": float(a.max()), "mean": float(a.mean()), "min": float(a.min())}
+
+    # Contrast: the HC form of the maps on the HC stack workload (b_res =
+    # I + N(0, 0.3) per layer, as in the pages' NumPy demo), and the mHC maps
+    # on the same biases; per-token composite Amax of each.
+    wc = synth.WORKLOADS["hc_stack60_bf16_T4096_d2560"]
+    cparams = [tuple(dev(a) for a in synth.make_params(wc, layer=l)) for l in range(L)]
+    X0c = dev(synth.make_state(wc))
+    contrast = {"workload": wc.name}
+    for name, maps in (("hc", mhc.MAPS_HC), ("mhc_same_biases", mhc.MAPS_MHC)):
+        kc = dict(alpha=wc.alpha, eps=wc.eps, t_max=wc.t_max, maps=maps)
+        X.copy_(X0c)
+        mhc.pre(X, cparams[0][0], cparams[0][1], h=h, H=Hs[0], workspace=ws, **kc)
+        for l in range(L - 1):
+            mhc.gelu_half(h, out=Y)
+            mhc.post_pre(X, Y, Hs[l], cparams[l + 1][0], cparams[l + 1][1], out=X, h=h, H_next=Hs[l + 1],
+                         workspace=ws, **kc)
+        mhc.amax(Hs, n, out_amax=amax, want_all=False)
+        a = amax.cpu().numpy()
+        contrast[name] = {"amax_max": float(a.max()), "amax_median": float(np.median(a)), "amax_min": float(a.min())}
+    out["contrast"] = contrast
     return out
 
 
@@ -459,7 +479,9 @@ def main():
         stack = time_stack(mhc, torch)
         log(f"stack: separate {stack['separate']['total_ms']:.2f} ms "
             f"({stack['separate']['per_layer_us']:.1f} us/layer), fused {stack['fused_post_pre']['total_ms']:.2f} ms "
-            f"({stack['fused_post_pre']['per_layer_us']:.1f} us/layer); amax max {stack['amax']['max']:.6f}")
+            f"({stack['fused_post_pre']['per_layer_us']:.1f} us/layer); amax max {stack['amax']['max']:.6f}; "
+            f"contrast: HC amax median {stack['contrast']['hc']['amax_median']:.1f}, mHC on the same biases "
+            f"{stack['contrast']['mhc_same_biases']['amax_median']:.4f}")
 
     cpu = None
     if not args.no_cpu_baseline:

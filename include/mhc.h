@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 3
+#define MHC_ABI_VERSION 4
 
 typedef enum mhc_status {
   MHC_OK = 0,
@@ -86,7 +86,20 @@ typedef struct mhc_params {
   float alpha_pre;    /* gate scalars of the three maps */
   float alpha_res;
   float alpha_post;
+  int32_t maps;       /* MHC_MAPS_MHC (0): the mHC maps; MHC_MAPS_HC (1): the
+                         unconstrained HC form, for contrast (see below) */
 } mhc_params;
+
+/* The form of the maps.  MHC_MAPS_MHC is the method: H_pre = sigmoid(l_pre),
+ * H_post = 2 sigmoid(l_post), H_res = Sinkhorn(exp(Mat(l_res))) with
+ * l = alpha_blk z + bias.  MHC_MAPS_HC is the form mHC constrains (Dubrov,
+ * "Kernmechanismen": a static bias plus an input-dependent term through
+ * tanh, any sign), read as H = bias + alpha_blk * tanh(z) for all three maps,
+ * no Sinkhorn.  The same z = x_hat . phi feeds both.  mhc_pre, mhc_pre_ex
+ * (two-pass form only) and mhc_post_pre accept both; mhc_pre_bwd takes the
+ * mHC form only (MHC_ERR_UNSUPPORTED otherwise). */
+#define MHC_MAPS_MHC 0
+#define MHC_MAPS_HC 1
 
 /* ---- mhc_pre: RMSNorm + projection + gates + Sinkhorn + aggregation --------
  * Computes, per token, the maps H (fp32 [T, m]) and the sublayer input

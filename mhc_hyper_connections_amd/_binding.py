@@ -34,7 +34,8 @@ class Params(ctypes.Structure):
     """mirror of struct mhc_params"""
     _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("t_max", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("alpha_pre", ctypes.c_float), ("alpha_res", ctypes.c_float), ("alpha_post", ctypes.c_float)]
+                ("alpha_pre", ctypes.c_float), ("alpha_res", ctypes.c_float), ("alpha_post", ctypes.c_float),
+                ("maps", ctypes.c_int32)]
 
 
 _lib = None
@@ -86,9 +87,12 @@ def _check(fn: str, status: int):
         raise MhcError(fn, status, text)
 
 
-def make_params(T, n, d, dtype, t_max=20, eps=1e-6, alpha=(0.01, 0.01, 0.01)) -> Params:
+MAPS_MHC, MAPS_HC = 0, 1
+
+
+def make_params(T, n, d, dtype, t_max=20, eps=1e-6, alpha=(0.01, 0.01, 0.01), maps=MAPS_MHC) -> Params:
     a = tuple(float(v) for v in alpha)
-    return Params(int(T), int(n), int(d), int(dtype), int(t_max), float(eps), a[0], a[1], a[2])
+    return Params(int(T), int(n), int(d), int(dtype), int(t_max), float(eps), a[0], a[1], a[2], int(maps))
 
 
 # ---- torch front end ---------------------------------------------------------
@@ -132,16 +136,17 @@ def pre_workspace_size(T, n, d, dtype=MHC_BF16) -> int:
 
 
 def pre(X, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, h=None, H=None, workspace=None,
-        stream=None, algo=None):
+        stream=None, algo=None, maps=MAPS_MHC):
     """mhc_pre: returns (h [T, d] state dtype, H [T, m] fp32).  With ``algo``
-    (PRE_AUTO / PRE_TWO_PASS / PRE_ONE_PASS) it calls mhc_pre_ex instead."""
+    (PRE_AUTO / PRE_TWO_PASS / PRE_ONE_PASS) it calls mhc_pre_ex instead.
+    ``maps``: MAPS_MHC (the method) or MAPS_HC (the unconstrained contrast)."""
     if algo is not None:
-        h, H, _ = pre_ex(X, phi, bias, algo, alpha, eps, t_max, h, H, workspace, stream)
+        h, H, _ = pre_ex(X, phi, bias, algo, alpha, eps, t_max, h, H, workspace, stream, maps=maps)
         return h, H
     torch = _torch()
     T, n, d = X.shape
     m = n * n + 2 * n
-    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha)
+    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha, maps)
     lib = load_library()
     if h is None:
         h = torch.empty((T, d), dtype=X.dtype, device=X.device)
@@ -158,12 +163,12 @@ def pre(X, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, h=None, H=No
 
 
 def pre_ex(X, phi, bias, algo=PRE_AUTO, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, h=None, H=None,
-           workspace=None, stream=None):
+           workspace=None, stream=None, maps=MAPS_MHC):
     """mhc_pre_ex: returns (h, H, algorithm that ran)."""
     torch = _torch()
     T, n, d = X.shape
     m = n * n + 2 * n
-    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha)
+    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha, maps)
     lib = load_library()
     if h is None:
         h = torch.empty((T, d), dtype=X.dtype, device=X.device)
@@ -272,14 +277,14 @@ def pre_bwd(X, phi, bias, D, dH, dX, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=2
 
 
 def post_pre(X, Y, H, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, out=None, h=None, H_next=None,
-             workspace=None, stream=None):
+             workspace=None, stream=None, maps=MAPS_MHC):
     """mhc_post_pre: layer l's mixing, then layer l+1's maps and sublayer
     input.  Returns (X_next [T, n, d], h [T, d], H_next [T, m]); ``out`` may
     be X itself."""
     torch = _torch()
     T, n, d = X.shape
     m = n * n + 2 * n
-    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha)
+    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha, maps)
     lib = load_library()
     out = torch.empty_like(X) if out is None else out
     h = torch.empty((T, d), dtype=X.dtype, device=X.device) if h is None else h

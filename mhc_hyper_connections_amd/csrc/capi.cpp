@@ -38,6 +38,7 @@ mhc_status check_params(const mhc_params* p) {
   if (!std::isfinite(p->alpha_pre) || !std::isfinite(p->alpha_res) || !std::isfinite(p->alpha_post))
     return MHC_ERR_SHAPE;
   if (p->dtype != MHC_FP32 && p->dtype != MHC_BF16) return MHC_ERR_DTYPE;
+  if (p->maps != MHC_MAPS_MHC && p->maps != MHC_MAPS_HC) return MHC_ERR_SHAPE;
   if (p->n != 1 && p->n != 2 && p->n != 4) return MHC_ERR_UNSUPPORTED;
   if (p->d % 8 != 0) return MHC_ERR_UNSUPPORTED;
   // Element counts must fit comfortably in 64-bit byte offsets.
@@ -223,7 +224,7 @@ mhc_status mhc_pre_bwd(const mhc_params* p, const void* X, const float* phi, con
                        size_t workspace_bytes, void* stream) {
   mhc_status st = check_params(p);
   if (st != MHC_OK) return st;
-  if (p->t_max > mhc::pre_bwd_max_tmax()) return MHC_ERR_UNSUPPORTED;
+  if (p->t_max > mhc::pre_bwd_max_tmax() || p->maps != MHC_MAPS_MHC) return MHC_ERR_UNSUPPORTED;
   if (!dphi || !dbias || !dalpha) return MHC_ERR_NULL;
   if (p->T > 0 && (!X || !phi || !bias || !D || !dH || !dX)) return MHC_ERR_NULL;
   const size_t need = mhc::pre_bwd_workspace_bytes(p->T, p->n, p->d, p->dtype);

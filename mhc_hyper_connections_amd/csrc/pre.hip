@@ -290,7 +290,7 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
 // group 0 writes H.  Lanes past d work on the last chunk again and store
 // the same values to the same place, so no load or store sits behind a
 // branch and the compiler keeps both passes in flight.
-template <typename ST, int N>
+template <typename ST, int N, bool HC>
 __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S,
                                                          const typename ST::elem* __restrict__ X,
                                                          const float* __restrict__ part,
@@ -371,13 +371,21 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
   const double inv_r = inv_rms(ss, N * d, eps);
 
   float gv = 0.0f;
-  if (e < 2 * N) {
-    const float l = logit_of(zg, inv_r, (e < N) ? a_pre : a_post, bias_g);
-    gv = (e < N) ? sigmoidf_(l) : 2.0f * sigmoidf_(l);
+  float mv = 0.0f;
+  if constexpr (HC) {
+    // The unconstrained HC form: bias + alpha_blk * tanh(z), in fp64 per value.
+    if (e < 2 * N) gv = static_cast<float>(static_cast<double>(bias_g) +
+                                           static_cast<double>((e < N) ? a_pre : a_post) * tanh(zg * inv_r));
+    if (e < NN) mv = static_cast<float>(static_cast<double>(bias_r) + static_cast<double>(a_res) * tanh(zr * inv_r));
+  } else {
+    if (e < 2 * N) {
+      const float l = logit_of(zg, inv_r, (e < N) ? a_pre : a_post, bias_g);
+      gv = (e < N) ? sigmoidf_(l) : 2.0f * sigmoidf_(l);
+    }
+    float lr = -INFINITY;
+    if (e < NN) lr = logit_of(zr, inv_r, a_res, bias_r);
+    mv = sinkhorn16<N>(lr, e, t_max);
   }
-  float lr = -INFINITY;
-  if (e < NN) lr = logit_of(zr, inv_r, a_res, bias_r);
-  const float mv = sinkhorn16<N>(lr, e, t_max);
   if (lane < 16) {
     float* Ht = H + t * M;
     if (e < NN) Ht[colr] = mv;
@@ -422,6 +430,24 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
 
 int num_slices(int d) { return (d + PRE_SLICE - 1) / PRE_SLICE; }
 
+// The finishing pass, in the form of the maps p asks for.
+template <typename ST, int N>
+hipError_t launch_finish(const mhc_params& p, const void* X, const float* part, const float* bias, void* h, float* H,
+                         hipStream_t stream) {
+  typedef typename ST::elem E;
+  const int S = num_slices(p.d);
+  const int64_t blocks = (p.T + 3) / 4;
+  if (p.maps == MHC_MAPS_HC)
+    hipLaunchKernelGGL((pre_finish_kernel<ST, N, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       p.T, p.d, S, static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post,
+                       p.eps, p.t_max, static_cast<E*>(h), H);
+  else
+    hipLaunchKernelGGL((pre_finish_kernel<ST, N, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       p.T, p.d, S, static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post,
+                       p.eps, p.t_max, static_cast<E*>(h), H);
+  return hipGetLastError();
+}
+
 template <typename ST, int N>
 hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
                         void* workspace, const DeviceInfo& dev, hipStream_t stream) {
@@ -440,11 +466,7 @@ hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, co
                      static_cast<const float*>(nullptr), static_cast<E*>(nullptr));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t blocks = (p.T + 3) / 4;
-  hipLaunchKernelGGL((pre_finish_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T, p.d, S,
-                     static_cast<const E*>(X), static_cast<const float*>(part), bias, p.alpha_pre, p.alpha_res,
-                     p.alpha_post, p.eps, p.t_max, static_cast<E*>(h), H);
-  return hipGetLastError();
+  return launch_finish<ST, N>(p, X, part, bias, h, H, stream);
 }
 
 // mhc_post of the previous layer fused into the partial pass (MODE 2), then
@@ -469,11 +491,7 @@ hipError_t launch_post_pre_t(const mhc_params& p, const void* X, const void* Y, 
                      Hprev, static_cast<E*>(Xout));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t blocks = (p.T + 3) / 4;
-  hipLaunchKernelGGL((pre_finish_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T, p.d, S,
-                     static_cast<const E*>(Xout), static_cast<const float*>(part), bias, p.alpha_pre, p.alpha_res,
-                     p.alpha_post, p.eps, p.t_max, static_cast<E*>(h), H);
-  return hipGetLastError();
+  return launch_finish<ST, N>(p, Xout, part, bias, h, H, stream);
 }
 
 template <typename ST>

@@ -409,7 +409,8 @@ size_t pre_fused_workspace_bytes(int64_t /*T*/, int n, int d) {
 // (without launching anything) when it does not, so the caller can fall back.
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
                             float* H, void* workspace, size_t ws_bytes, const DeviceInfo& dev, hipStream_t stream) {
-  if (p.dtype != MHC_BF16 || (p.n != 4 && p.n != 2 && p.n != 1)) return hipErrorNotSupported;
+  if (p.dtype != MHC_BF16 || (p.n != 4 && p.n != 2 && p.n != 1) || p.maps != MHC_MAPS_MHC)
+    return hipErrorNotSupported;
   const int S = fused_slices(p.d);
   if (S < FS_MIN || S > FS_MAX || !dev.cooperative || dev.num_cus % 8 != 0) return hipErrorNotSupported;
   const int per_xcd = dev.num_cus / 8;

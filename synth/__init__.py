@@ -96,6 +96,7 @@ class Workload:
     eps: float = 1e-6
     t_max: int = 20
     sublayer: str = "given"     # "given": Y drawn N(0,1); "gelu_half": Y = 0.5 GELU(h)
+    maps: str = "mhc"           # "mhc": the method's maps; "hc": the unconstrained HC form (contrast)
     backward: bool = False
     seed: int = 1000
     note: str = ""
@@ -122,6 +123,10 @@ WORKLOADS = {
     "layer_fwdbwd_bf16_T16384_d4096": Workload("layer_fwdbwd_bf16_T16384_d4096", T=16384, n=4, d=4096, dtype=BF16,
                                                backward=True, seed=1004,
                                                note="single layer forward + backward"),
+    "hc_stack60_bf16_T4096_d2560": Workload("hc_stack60_bf16_T4096_d2560", T=4096, n=4, d=2560, dtype=BF16, layers=60,
+                                            bres_diag=1.0, bres_std=0.3, sublayer="gelu_half", maps="hc", seed=1005,
+                                            note="contrast: the 60-layer stack with HC's unconstrained maps, "
+                                                 "b_res = I + N(0, 0.3) as in the pages' NumPy demo"),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

@@ -45,7 +45,7 @@ def test_abi_version_and_status_strings(lib):
 
 def _params(**kw):
     import mhc_hyper_connections_amd as m
-    base = dict(T=64, n=4, d=256, dtype=m.MHC_BF16, t_max=20, eps=1e-6, alpha=(0.01, 0.01, 0.01))
+    base = dict(T=64, n=4, d=256, dtype=m.MHC_BF16, t_max=20, eps=1e-6, alpha=(0.01, 0.01, 0.01), maps=m.MAPS_MHC)
     base.update(kw)
     return m.make_params(**base)
 
@@ -196,3 +196,12 @@ def test_post_pre_argument_checks(lib):
     assert f(p, ws=A[2]) == 6                          # workspace onto the previous maps
     assert f(p, X=A[0] + 4) == 4
     assert f(_params(T=0), X=None) == 0
+
+
+def test_maps_field(lib):
+    import mhc_hyper_connections_amd as m
+    assert _pre(lib, _params(maps=7)) == 2                          # unknown form of the maps
+    p = _params(maps=m.MAPS_HC)
+    assert lib.mhc_pre_bwd(ctypes.byref(p), *A[:8], A[7] + 4096, A[7] + 8192,
+                           lib.mhc_pre_bwd_workspace_size(ctypes.byref(p)), None) == 5   # no HC backward
+    assert ctypes.sizeof(m.Params) == 48

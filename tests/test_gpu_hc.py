@@ -1,0 +1,111 @@
+"""The HC contrast form of the maps (bias + alpha * tanh(z), no Sinkhorn) on
+the GPU against the oracle's HC form, and the 60-layer HC stack whose
+composite residual map grows where mHC's stays at 1."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import TOL, assert_close, dname, sample_tokens, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def mhc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mhc_hyper_connections_amd as m
+    m.load_library()
+    return m
+
+
+CASES = [
+    ("layer_bf16_T16384_d4096", {"T": 1100}),
+    ("layer_fp32_T64_d256", {}),
+    ("hc_stack60_bf16_T4096_d2560", {"T": 300, "layers": 1, "sublayer": "given"}),
+]
+
+
+@pytest.mark.parametrize("name,changes", CASES, ids=[f"{c[0]}_T{c[1].get('T', 'all')}" for c in CASES])
+@pytest.mark.parametrize("alpha", [None, (0.8, 1.2, -0.5)], ids=["alpha_cfg", "alpha_large"])
+def test_hc_maps_every_token(mhc, oracle_lib, name, changes, alpha):
+    w = synth.scaled(synth.WORKLOADS[name], **changes)
+    alpha = w.alpha if alpha is None else alpha
+    X = synth.make_state(w)
+    phi, bias = synth.make_params(w)
+    h, H = mhc.pre(to_device(X), to_device(phi), to_device(bias), alpha=alpha, eps=w.eps, maps=mhc.MAPS_HC)
+    torch.cuda.synchronize()
+    ref = oracle_lib.pre_hc(X, phi, bias, alpha, eps=w.eps)
+    dn = dname(w.dtype)
+    # HC passes an error in z straight through: dH = alpha (1 - tanh^2) dz,
+    # with dz ~ 2e-5 from fp32 accumulation over n*d terms; mHC's gates and
+    # normalisation damp it.  So the absolute part scales with |alpha|.
+    rtol, atol = TOL[(dn, "maps")]
+    atol = atol * max(1.0, 4.0 * max(abs(a) for a in alpha))
+    assert_close(to_host(H), ref["H"], rtol, atol, what=f"{w.name} HC maps")
+    assert_close(to_host(h), ref["h"], *TOL[(dn, "state")], what=f"{w.name} HC h")
+
+
+def test_hc_forms_and_refusals(mhc):
+    """HC runs in the two-pass form only (AUTO picks it; ONE_PASS refuses),
+    and the maps differ from mHC's on the same inputs."""
+    w = synth.scaled(synth.WORKLOADS["layer_bf16_T16384_d4096"], T=2048)
+    X = to_device(synth.make_state(w))
+    phi, bias = (to_device(a) for a in synth.make_params(w))
+    with pytest.raises(mhc.MhcError) as ei:
+        mhc.pre_ex(X, phi, bias, mhc.PRE_ONE_PASS, maps=mhc.MAPS_HC)
+    assert ei.value.status == 5
+    h, H, used = mhc.pre_ex(X, phi, bias, mhc.PRE_AUTO, maps=mhc.MAPS_HC)
+    assert used == mhc.PRE_TWO_PASS
+    _, Hm = mhc.pre(X, phi, bias)
+    assert float((H - Hm).abs().max()) > 0.1
+
+
+def _hc_stack(mhc, w, T, L, maps):
+    X0 = synth.make_state(w, T)
+    phis, biases = zip(*(synth.make_params(w, layer=l) for l in range(L)))
+    X = to_device(X0)
+    Hs = torch.empty((L, T, w.m), dtype=torch.float32, device="cuda")
+    kw = dict(alpha=w.alpha, eps=w.eps, t_max=w.t_max, maps=maps)
+    h, _ = mhc.pre(X, to_device(phis[0]), to_device(biases[0]), H=Hs[0], **kw)
+    for l in range(L - 1):
+        X, h, _ = mhc.post_pre(X, mhc.gelu_half(h), Hs[l], to_device(phis[l + 1]), to_device(biases[l + 1]), out=X,
+                               H_next=Hs[l + 1], **kw)
+    X = mhc.post(X, mhc.gelu_half(h), Hs[L - 1], out=X)
+    am = mhc.amax(Hs, w.n)
+    torch.cuda.synchronize()
+    return X0, np.stack(phis), np.stack(biases), to_host(X), to_host(Hs), {k: to_host(v) for k, v in am.items()}
+
+
+@pytest.mark.parametrize("T,sampled", [(40, False), (4096, True)], ids=["T40", "T4096_sampled"])
+def test_hc_stack60(mhc, oracle_lib, T, sampled):
+    """The 60-layer stack with HC maps against the oracle: final state, every
+    layer's maps, per-token composite Amax; and the contrast: on the same
+    biases the mHC maps keep the composite at Amax ~1 while HC's grows by
+    orders of magnitude."""
+    w = synth.WORKLOADS["hc_stack60_bf16_T4096_d2560"]
+    L = w.layers
+    X0, phis, biases, Xg, Hg, am = _hc_stack(mhc, w, T, L, mhc.MAPS_HC)
+    tok = sample_tokens(T, 12) if sampled else np.arange(T, dtype=np.int64)
+    alphas = np.tile(np.array(w.alpha, np.float32), (L, 1))
+    ref = oracle_lib.stack_hc(X0, phis, biases, alphas, eps=w.eps, tokens=tok)
+    # The HC stack is ill-conditioned: one ulp on one input value moves the
+    # oracle's own results this much (tests/test_stack_conditioning.py), so
+    # the comparison sits above that: >= 95% of final values within the bf16
+    # tolerance, every error within 0.5 of the token RMS, maps within 3e-3,
+    # composite Amax within 5e-3.
+    g = synth.bf16_bits_to_f32(Xg[tok]).astype(np.float64)
+    r = synth.bf16_bits_to_f32(ref["X"]).astype(np.float64)
+    scale = np.sqrt(np.mean(r * r, axis=(1, 2), keepdims=True))
+    err = np.abs(g - r)
+    assert np.all(np.isfinite(g))
+    assert np.mean(err <= 2e-2 * np.abs(r) + 1e-2 * scale) >= 0.95
+    assert float(np.max(err / scale)) <= 0.5
+    assert_close(Hg[:, tok], ref["H"], 0.0, 3e-3, what="HC stack maps")
+    rel = np.abs(am["amax"][tok] - ref["amax"]) / ref["amax"]
+    assert np.all(rel <= 5e-3), rel.max()
+    assert np.median(am["amax"]) > 50.0
+    _, _, _, _, _, am_m = _hc_stack(mhc, w, T, L, mhc.MAPS_MHC)
+    assert np.max(am_m["amax"]) < 1.01
