@@ -61,31 +61,74 @@ __device__ __forceinline__ float logit_of(double z, double inv_r, float alpha, f
   return static_cast<float>(static_cast<double>(alpha) * (z * inv_r) + static_cast<double>(bias));
 }
 
+// Lane exchanges inside 16-lane rows without the LDS unit (DPP): quad
+// permutes for partners e^1 and e^2, row rotations for partners at +-4 and 8
+// (lanes e and e^8 are 8 apart either way).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor1(float v) { return dpp<0xB1>(v); }    // quad_perm [1,0,3,2]
+__device__ __forceinline__ float lane_xor2(float v) { return dpp<0x4E>(v); }    // quad_perm [2,3,0,1]
+__device__ __forceinline__ float lane_rot8(float v) { return dpp<0x128>(v); }   // row_ror:8 = partner e^8
+__device__ __forceinline__ float lane_rot4(float v) { return dpp<0x124>(v); }   // row_ror:4
+
+// Sum over the lanes of a Sinkhorn line, the same value on every lane of
+// the line.  Rows (fixed i, j varies: the low lane bits): (v + v^1) + its ^2
+// partner.  Columns (fixed j, i varies: the lane bits above log2 n): for
+// n = 4, p = v + v^8 pairs rows i and i+2, then p + rot4(p) adds the other
+// pair; every lane of the column adds the same two addends, so all hold the
+// same bits whichever way the rotation runs.  For n = 2 a column is lanes
+// {e, e^2}.
+template <int N>
+__device__ __forceinline__ float row_sum(float v) {
+  if constexpr (N == 1) {
+    return v;
+  } else if constexpr (N == 2) {
+    return v + lane_xor1(v);
+  } else {
+    const float q = v + lane_xor1(v);
+    return q + lane_xor2(q);
+  }
+}
+template <int N>
+__device__ __forceinline__ float col_sum(float v) {
+  if constexpr (N == 1) {
+    return v;
+  } else if constexpr (N == 2) {
+    return v + lane_xor2(v);
+  } else {
+    const float p = v + lane_rot8(v);
+    return p + lane_rot4(p);
+  }
+}
+
 // Sinkhorn-Knopp on one token's n x n map held by 16 lanes: lane e (e = lane
 // % 16) owns entry (e / n, e % n) for e < n*n and receives the residual logit
 // `lr` (-inf on lanes e >= n*n).  Returns the entry of H_res after t_max
-// passes of (normalise columns, then rows).  Column and row sums are lane
-// shuffles inside the 16-lane group; every lane of the wave must call it.
+// passes of (normalise columns, then rows).  Every lane of the wave must
+// call it (n = 1, 2, 4).
 template <int N>
 __device__ __forceinline__ float sinkhorn16(float lr, int e, int t_max) {
+  static_assert(N == 1 || N == 2 || N == 4, "16-lane Sinkhorn covers n <= 4");
   constexpr int NN = N * N;
   // Subtracting the token's largest residual logit leaves every iterate
   // unchanged (the first column step divides it out) and keeps exp finite;
   // with no pass at all the map is exp(logits) itself.
   float mx = lr;
-#pragma unroll
-  for (int off = 1; off < NN; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if constexpr (NN >= 4) {
+    mx = fmaxf(mx, lane_xor1(mx));
+    mx = fmaxf(mx, lane_xor2(mx));
+  }
+  if constexpr (NN >= 16) {
+    mx = fmaxf(mx, lane_rot8(mx));
+    mx = fmaxf(mx, lane_rot4(mx));
+  }
   if (t_max == 0) mx = 0.0f;
   float mv = (e < NN) ? expf(lr - mx) : 0.0f;
   for (int it = 0; it < t_max; ++it) {
-    float cs = mv;                                          // column sum: over i (lane bits above log2 n)
-#pragma unroll
-    for (int off = N; off < NN; off <<= 1) cs += __shfl_xor(cs, off);
-    mv = mv / cs;
-    float rs = mv;                                          // row sum: over j (low lane bits)
-#pragma unroll
-    for (int off = 1; off < N; off <<= 1) rs += __shfl_xor(rs, off);
-    mv = mv / rs;
+    mv = mv / col_sum<N>(mv);
+    mv = mv / row_sum<N>(mv);
   }
   return mv;
 }

@@ -1,52 +1,93 @@
-// mhc_pre in ONE pass over the state (bf16), for 8 <= ceil(d / 256) <= 16.
+// mhc_pre in ONE pass over the state (bf16): X travels from HBM once.
 //
 // Same method as pre.hip ("mHC" notes on DeepSeek-V4, eqs. dsv4-mhc-rmsnorm,
 // a/b/c-tilde, sinkhorn-init, sinkhorn, gate; Dubrov, "DeepSeek mHC:
-// Manifold-Constrained Hyper-Connections", Eq. 3 for h = H_pre . X).
+// Manifold-Constrained Hyper-Connections", Eq. 3 for h = H_pre . X, and the
+// section "Kernmechanismen" for the unconstrained HC maps).
 //
 // Why one pass is hard: H_pre needs the reduction over all n*d values of a
 // token before h = H_pre . X can be formed, and phi (n*d x 24, 1.5 MiB at
-// d = 4096) is too large for one CU.  Here teams of S workgroups (one per CU)
-// split d: member s keeps its 256-position slice of phi in LDS and, for every
-// 32-token tile, streams its slice of X from HBM into registers once.
-//   1. MFMA partial dot products + fp64 partial sum of squares of the tile,
-//      reduced over the 8 waves in LDS, then posted to the team as tagged
-//      64-bit words (value | tile tag << 32, device-scope stores: no fence,
-//      no wait on the writer's side).
-//   2. One tile later, every member reads the posted pre-columns and sums of
-//      squares of all S members (device-scope loads, issued BEFORE the next
-//      prefetch so the in-order wait covers only data that is due anyway),
-//      forms H_pre of the 32 tokens and h for its slice from the X tile it
-//      still holds in registers.  The tile never travels from HBM twice.
-//   3. Member s also reads all 24 columns of its ceil(32 / S) tokens and runs
-//      the gates + Sinkhorn for them (16 lanes per token), writing H.  No one
-//      in the kernel waits for these rows, so Sinkhorn is off the critical path.
-// The team's tiles are pipelined: X of tile k+1 streams in while tile k's
-// partials are posted and tile k-1's h is formed.  Slots in the exchange
-// area form a ring of 4 (a member can be at most about one tile ahead of the
-// slowest, see the slot-reuse note in the launcher).  Every sum runs in a
-// fixed order: results are bitwise reproducible.  All waits are bounded; a
-// wait that runs out records an error word in the workspace header instead
-// of hanging.  The launch is cooperative (all workgroups co-resident).
+// d = 4096) is too large for one CU.  So the hidden dimension is split over a
+// team of S = ceil(d / 256) workgroups (8 <= S <= 16), one per CU, all on one
+// XCD: they exchange per-token sums through that XCD's L2.  Member s owns
+// positions [256 s, 256 s + 256) of every stream; the team walks 16-token
+// tiles.  A workgroup runs ten waves with fixed roles:
+//  * waves 0-7 stream.  Wave w holds positions 32 w .. 32 w + 31 of the
+//    member's slice for the tile's 16 tokens in registers (lane = token row
+//    and 8 positions, the MFMA A layout; one 16-byte load per stream).  Per
+//    tile it forms the slice's m partial dot products with phi on MFMA (phi
+//    as bf16 hi + lo halves, kept in LDS) and the fp64 partial sum of
+//    squares, and hands them to the exchange wave through LDS.  D tiles
+//    later, once that tile's H_pre has come back, it forms h = H_pre . X for
+//    its positions from the registers that still hold the tile, and stores
+//    it.  These waves issue no memory operation but their X loads and h
+//    stores, a fixed number per tile (masked lanes use out-of-range buffer
+//    offsets, which move no data), so the in-order completion count only
+//    ever makes them wait for their oldest tile.
+//  * wave 8 exchanges, in round i:
+//      A  tile i: sums the 8 waves' partials per token in a fixed order and
+//         posts the member's record: 16 tokens x (m partials, fp64 sum of
+//         squares as two halves), each a tagged 64-bit word (value | tag << 32).
+//      B  tile i-1, reduce-scatter: member s owns tokens s and s + S of the
+//         tile.  It reads every member's record of them, sums in member
+//         order (fp64), forms r, the logits and the gates, posts H_pre and
+//         hands the residual logits to wave 9.
+//      C  tile i-2, broadcast: reads H_pre of all 16 tokens and hands it to
+//         the streaming waves.
+//  * wave 9 runs Sinkhorn-Knopp for the member's own tokens and writes H.
+// Exchange words are written with plain stores (through the CU's L1 into the
+// XCD's L2) and read with agent-scope loads (which skip the L1); a word whose
+// tag is not yet the tile's is read again.  A member clears its own slots at
+// the start and the team meets on words stamped with the call's sequence
+// number, so words of earlier calls never match.  Every sum runs in a fixed
+// order: results are bitwise reproducible.  All waits are bounded; one that
+// runs out marks the workgroup broken (no further waits; results invalid)
+// and the call's sequence number is stored into the workspace's error word.
+// The launch is cooperative (all workgroups co-resident).
+#include <atomic>
+
 #include "launch.hpp"
 #include "pre_common.hpp"
 
 namespace mhc {
 namespace {
 
-constexpr int FW = 8;                  // waves per workgroup
-constexpr int FT = FW * 64;            // threads per workgroup
-constexpr int FSLICE = FW * 32;        // positions of d per team member
-constexpr int FMB = 2;                 // 16-token blocks per tile
-constexpr int FR = 16 * FMB;           // tokens per tile
-constexpr int FSLOTS = 4;              // exchange ring depth
-constexpr int FS_MIN = 8;              // team size range (ceil(d / FSLICE))
-constexpr int FS_MAX = 16;
-constexpr int FTPR_MAX = (FR + FS_MIN - 1) / FS_MIN;   // tokens whose maps one member forms
-constexpr size_t FHDR = 256;           // workspace header: error word
-constexpr unsigned kSpinLimit = 1u << 14;   // ~tens of ms per word; far beyond any legitimate wait
+typedef unsigned long long u64;
 
-struct FusedArgs {
+constexpr int OW = 8;                   // streaming waves
+constexpr int OX = 2;                   // exchange waves (tiles alternate between them)
+constexpr int OT = (OW + OX + 1) * 64;  // + the exchange waves + the Sinkhorn wave
+constexpr int OSLICE = OW * 32;         // positions of d per member
+constexpr int OR = 16;                  // tokens per tile
+constexpr int OS_MIN = 8;               // team size range (ceil(d / OSLICE))
+constexpr int OS_MAX = 16;
+constexpr int OTPR = (OR + OS_MIN - 1) / OS_MIN;   // most tokens a member owns per tile
+constexpr int OSLOTS = 4;               // exchange ring depth (tiles); >= 4 is safe, see below
+constexpr int ORR = 3;                  // LDS ring of partials (tiles)
+constexpr int OMR = 4;                  // LDS ring of H_pre (tiles; a slot is rewritten once its tile's h is out)
+constexpr int OKR = 4;                  // LDS ring of Sinkhorn inputs (tiles; taken two at a time)
+constexpr int OD = 3;                   // tiles between a tile's partials and its h (>= 2, see below)
+constexpr int OP = 4;                   // X tiles in flight ahead of the one being multiplied
+constexpr int ONB = OD + OP;            // X tile buffers per lane
+constexpr size_t OHDR = 256;            // workspace header: the error word
+constexpr int OXCD = 8;                 // XCDs of the device (MI355X)
+constexpr unsigned kLdsSpin = 1u << 20; // bounded waits: far beyond any legitimate one
+constexpr unsigned kMemSpin = 1u << 16;
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: loads read 0, stores drop
+
+// Deadlock freedom and slot reuse.  Streaming waves post tile k's partials
+// before waiting for tile k-D's H_pre, which the exchange wave produces in
+// round k-D+2 <= k; a round waits only for partials the waves have posted.
+// A round first reads the records of tile i-1 and the H_pre words of tile
+// i-2, posted in the previous round.  A member rewrites tile k's record slot
+// in round k+OSLOTS, after its round k+OSLOTS-1 has read every owner's H_pre
+// of tile k+OSLOTS-3, which the owners posted after their reads of tile
+// k+OSLOTS-3's records: with OSLOTS >= 4 all reads of tile k's records are
+// done; an owner rewrites tile k's H_pre words in round k+OSLOTS+1, after
+// reading every member's record of tile k+OSLOTS, which they posted after
+// their round k+OSLOTS-1 and so after reading tile k's H_pre words.
+
+struct OneArgs {
   int64_t T;
   int d, S, tpx, teams, tpr;
   int64_t ntiles;
@@ -57,411 +98,656 @@ struct FusedArgs {
   int t_max;
   uint16_t* h;
   float* H;
-  unsigned long long* xch;
-  unsigned* err;
+  u64* hdr;        // [0] error word
+  u64* start;      // [team][OS_MAX] start words
+  u64* ring;       // [team][OSLOTS][slot words]
+  int64_t slotw;   // words per slot: S * OR * record words, then OR * n H_pre words
+  u64 epoch;       // sequence number of the call (never 0)
+  int xbytes, hbytes;
 };
 
-__device__ __forceinline__ unsigned long long xword(float v, unsigned tag) {
-  return (static_cast<unsigned long long>(tag) << 32) | static_cast<unsigned long long>(__float_as_uint(v));
+__device__ __forceinline__ u64 xword(uint32_t v, uint32_t tag) {
+  return (static_cast<u64>(tag) << 32) | static_cast<u64>(v);
 }
-__device__ __forceinline__ void xstore(unsigned long long* p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ u64 agent_load(const u64* p) {
+  return __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned long long xload(const unsigned long long* p) {
-  return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Flags in LDS, shared by the workgroup's waves.  Atomic accesses (never
+// cached in registers, never merged) on the variables themselves, so the
+// compiler keeps them LDS operations: a generic (flat) access would also
+// count as a vector memory operation, and waiting for it would wait for
+// every X load in flight.
+__device__ __forceinline__ int flag_get(int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void flag_set(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// LDS writes issued so far have completed: a wave that then sees a flag
+// written after this point also sees them.
+__device__ __forceinline__ void lds_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Wait (wave-uniform) until *flag >= want.  false when the workgroup is or
+// becomes broken.
+__device__ __forceinline__ bool wait_ge(int* flag, int want, int* broken) {
+  unsigned n = 0;
+  while (flag_get(flag) < want) {
+    if (flag_get(broken)) return false;
+    if (++n > kLdsSpin) {
+      flag_set(broken, 1);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
 }
 
-template <int N>
-__global__ __launch_bounds__(FT) void pre_fused_kernel(FusedArgs a) {
+// Wait (wave-uniform) until flags[w] >= want for every w < OW; lane w
+// reads flag w.
+__device__ __forceinline__ bool wait_all_ge(int* flags, int want, int* broken, int lane) {
+  unsigned n = 0;
+  while (true) {
+    const int v = (lane < OW) ? flag_get(&flags[lane < OW ? lane : 0]) : 0x7fffffff;
+    if (__all(v >= want)) return true;
+    if (flag_get(broken)) return false;
+    if (++n > kLdsSpin) {
+      flag_set(broken, 1);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Sum over the 16 lanes of a row in fp64, the same bits on every lane: quad
+// butterfly (partners e^1, e^2), then partners e^8 (rotation by 8), then the
+// other pair of quads (rotation by 4: either direction reaches a lane of the
+// same pair, so every lane adds the same two values).
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+  const u64 b = __builtin_bit_cast(u64, v);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, 0xF, 0xF, false));
+  const uint32_t hi =
+      static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(double, (static_cast<u64>(hi) << 32) | lo);
+}
+__device__ __forceinline__ double row16_sum(double v) {
+  v = v + dpp64<0xB1>(v);
+  v = v + dpp64<0x4E>(v);
+  v = v + dpp64<0x128>(v);
+  v = v + dpp64<0x124>(v);
+  return v;
+}
+
+template <int N, bool HC>
+__global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
   constexpr int M = num_maps(N);
   constexpr int NB = (M + 15) / 16;
   constexpr int NN = N * N;
-  constexpr int W = M + 2;             // words per token record: m partials, sum of squares (hi, lo)
-  constexpr int WA = N + 2;            // pre columns + sum of squares, read for every token
-  constexpr int WB = M - N;            // residual + post columns, read for the member's own tokens
-  constexpr int KMAX = (FS_MAX * FR * WA + FS_MAX * FTPR_MAX * WB + FT - 1) / FT;   // words per thread
+  constexpr int SSO = (M + 1) & ~1;     // word of the sum of squares in a token record (even)
+  constexpr int W = SSO + 2;            // words per token record (even: records are 16-byte pairs)
+  constexpr int NP = W / 2;             // word pairs per token record
+  constexpr int NRB = (NP + 3) / 4;     // reduce-scatter loads per owned token (a pair per 16-lane row)
+  constexpr int PHE = 4 * M;            // phi operand entries per (wave, stream, half)
+  constexpr int MP = (M + 3) / 4;       // 4-column groups per token in the partials ring
+  constexpr int SHARE = (OR * NP + OW - 1) / OW;   // record pairs each streaming wave posts per tile
+  static_assert(SHARE <= 64, "one pair per lane");
 
-  __shared__ u32x4 phi_l[FW][N][2][4][M];    // MFMA B operands: [wave][stream][hi/lo][lane group][column]
-  __shared__ float red[FW][FR][M];
-  __shared__ double red_ss[FW][FR];
-  __shared__ float xin[FS_MAX * FR * WA + FS_MAX * FTPR_MAX * WB];   // part a: [member][tok][WA], then part b
-  float (*xin_a)[FR][WA] = reinterpret_cast<float (*)[FR][WA]>(xin);
-  float (*xin_b)[FTPR_MAX][WB] = reinterpret_cast<float (*)[FTPR_MAX][WB]>(xin + FS_MAX * FR * WA);
-  __shared__ float hp[FR][N];
+  __shared__ u32x4 phi_l[OW][N][2][PHE];   // MFMA B operands, entry nb*64 + g*cn + r (cn = columns of block nb)
+  __shared__ f32x4 red[ORR][OW][OR][MP];   // per wave and token: m partials (padded to 4s)
+  __shared__ double red_ss[ORR][OW][OR];
+  __shared__ double xs[OX][OTPR][W];       // an owned token's column sums over the team, per exchange wave
+  __shared__ float maps[OMR][OR][N];
+  __shared__ float2 skin[OKR][OTPR][16];   // (residual logit or HC value, gate value) per entry
+  __shared__ int64_t sktok[OKR][OTPR];     // global token, or -1
+  __shared__ int part_ready[OW];           // wave w has written the partials of tiles < part_ready[w]
+  __shared__ int posted[OW];               // wave w has posted its record share of tiles < posted[w]
+  __shared__ int maps_tag[OMR];            // H_pre of tile t is in slot t % OMR once maps_tag[slot] > t
+  __shared__ int sk_tag[OKR];              // likewise for the Sinkhorn inputs
+  __shared__ int sk_free, broken;
+  __shared__ int misplaced;
 
-  const int wg = blockIdx.x;
-  const int xcd = wg & 7;
-  const int idx = wg >> 3;
-  if (idx >= a.tpx * a.S) return;            // not part of a team (cooperative grid of one workgroup per CU)
-  const int S = a.S;
-  const int team = xcd * a.tpx + idx / S;    // teams live inside one XCD (workgroup w runs on XCD w % 8)
-  const int s = idx - (idx / S) * S;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
-  const int d = a.d;
-  const int j0 = s * FSLICE + 32 * wave + 8 * g;
-  const bool jv = j0 < d;
-  const int64_t T = a.T;
-  const int64_t J = (a.ntiles > team) ? (a.ntiles - team + a.teams - 1) / a.teams : 0;
+  int* const vbroken = &broken;
 
-  // This member's slice of phi into LDS as bf16 hi / lo operand halves.
-  for (int q = tid; q < FW * N * 4 * M; q += FT) {
-    const int col = q % M;
-    const int gg = (q / M) & 3;
-    const int i = (q / (4 * M)) % N;
-    const int ww = q / (4 * M * N);
-    const int jj = s * FSLICE + 32 * ww + 8 * gg;
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (jj < d) ? a.phi[static_cast<int64_t>(i * d + jj + e) * M + col] : 0.0f;
-    const PhiOp<BF16> op = make_phi_op(f, BF16{});
-    phi_l[ww][i][0][gg][col] = __builtin_bit_cast(u32x4, op.hi);
-    phi_l[ww][i][1][gg][col] = __builtin_bit_cast(u32x4, op.lo);
+  // Team membership.  Workgroups are dispatched to the XCDs round-robin
+  // (workgroup b runs on XCD b % 8), so teams follow from the index; the
+  // hardware's XCD id is checked, and a workgroup placed otherwise marks the
+  // call broken (its team's waits then run out and report, never hang).
+  if (tid == 0) {
+    const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;   // HW_REG_XCC_ID
+    misplaced = (xcc == (blockIdx.x & (OXCD - 1))) ? 0 : 1;
+    for (int q = 0; q < OMR; ++q) maps_tag[q] = 0;
+    for (int q = 0; q < OKR; ++q) sk_tag[q] = 0;
+    sk_free = 0;
+    broken = misplaced;
+  }
+  if (tid < OW) {
+    part_ready[tid] = 0;
+    posted[tid] = 0;
   }
   __syncthreads();
+  const int S = a.S;
+  const int idx = static_cast<int>(blockIdx.x) / OXCD;
+  if (idx >= a.tpx * S) return;   // not part of a team (whole workgroup)
+  if (misplaced != 0 && tid == 0) __hip_atomic_store(a.hdr, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int team = static_cast<int>(blockIdx.x & (OXCD - 1)) * a.tpx + idx / S;
+  const int s = idx % S;
+  const int d = a.d;
+  const int64_t T = a.T;
+  const int teams = a.teams;
+  const int J = (a.ntiles > team) ? static_cast<int>((a.ntiles - team + teams - 1) / teams) : 0;
 
-  auto tile_of = [&](int64_t jt) -> int64_t { return team + jt * a.teams; };
-  // Unconditional loads from always-valid addresses (no branch, no select on
-  // the data, either of which would make the compiler wait for the load on
-  // the spot): tokens past T read token 0 (never written back), lanes past d
-  // read position 0 (zero phi rows; squares dropped; h not stored).
-  const int jl = jv ? j0 : 0;
-  auto load_tile = [&](int64_t jt, Raw8<BF16> (&x)[FMB][N]) {
-    const int64_t t0 = tile_of(jt) * FR;
+  // Streaming lanes: lane = (token row r16, position group g) of wave w.
+  const int w = wave;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int j0 = s * OSLICE + 32 * w + 8 * g;
+  const bool jv = wave < OW && j0 < d;
+  const __amdgpu_buffer_rsrc_t xrx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X), 0, a.xbytes, 0x00020000);
+  auto load_tile = [&](int jt, u32x4 (&x)[N]) {
+    const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + r16;
+    const bool ok = jt < J && t < T && jv;
+    const uint32_t o0 = ok ? static_cast<uint32_t>((t * N * d + j0) * 2) : kOob;
+    const uint32_t st = ok ? static_cast<uint32_t>(d * 2) : 0u;
 #pragma unroll
-    for (int mb = 0; mb < FMB; ++mb) {
-      const int64_t t = t0 + mb * 16 + r16;
-      const int64_t tt = t < T ? t : 0;
+    for (int i = 0; i < N; ++i)
+      x[i] = __builtin_amdgcn_raw_buffer_load_b128(xrx, static_cast<int>(o0 + i * st), 0, 2);
+  };
+  // The first X tiles go out before the set-up below, which they overlap.
+  u32x4 xb[ONB][N];
+  if (wave < OW) {
 #pragma unroll
-      for (int i = 0; i < N; ++i) x[mb][i] = load_raw8<BF16, true>(a.X + (tt * N + i) * d + jl);
+    for (int p = 0; p < OP; ++p) {
+      load_tile(p, xb[p]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  auto xrec = [&](int64_t jt, int member, int tok) -> unsigned long long* {
-    return a.xch + ((static_cast<int64_t>(team) * FSLOTS + (jt % FSLOTS)) * S + member) * (FR * W) + tok * W;
-  };
+  }
 
-  Raw8<BF16> b0[FMB][N], b1[FMB][N], b2[FMB][N];
-  if (J > 0) load_tile(0, b0);
-  if (J > 1) load_tile(1, b1);
-  const int tpr = a.tpr;
-  bool broken = false;                 // a wait ran out: stop waiting (results are invalid, the error word is set)
-  // Word q of a tile's reads, laid out for the largest team so that the
-  // decomposition uses constants only: part a = [member < FS_MAX][token][WA],
-  // part b = [member < FS_MAX][own token < FTPR_MAX][WB].  Returns the word's
-  // offset in the tile's slot, or -1 when the word does not exist; lds is
-  // its index in xin.
-  constexpr int QA = FS_MAX * FR * WA;
-  constexpr int QTOT = QA + FS_MAX * FTPR_MAX * WB;
-  auto word_of = [&](int q, int& lds) -> int {
-    lds = q;
-    if (q < QA) {
-      const int member = q / (FR * WA);
-      const int rem = q - member * (FR * WA);
-      const int tok = rem / WA;
-      const int c = rem - tok * WA;
-      if (member >= S) return -1;
-      return member * (FR * W) + tok * W + ((c < N) ? c : M + (c - N));
-    }
-    const int qb = q - QA;
-    const int member = qb / (FTPR_MAX * WB);
-    const int rem = qb - member * (FTPR_MAX * WB);
-    const int qq = rem / WB;
-    const int cb = rem - qq * WB;
-    const int tok = s * tpr + qq;
-    if (member >= S || qq >= tpr || tok >= FR) return -1;
-    return member * (FR * W) + tok * W + N + cb;
-  };
-
-  unsigned long long wv[KMAX];           // the team's words of the previous tile, in flight between rounds
-
-  // One round, for tile jt: its partials from `xc` are posted; then tile
-  // jt - 1's exchange words (read at the end of the previous round) are
-  // checked, its H_pre and h (from `xh`) formed and its maps written; then
-  // the reads of tile jt's words are issued and tile jt + 2 starts streaming
-  // into `xh`, free by now.  Every wait therefore covers only operations
-  // older than the prefetch in flight.  The rounds are unrolled by three so
-  // the buffers rotate roles without register copies.
-  auto round = [&](int64_t jt, Raw8<BF16> (&xh)[FMB][N], Raw8<BF16> (&xc)[FMB][N]) {
-    const int64_t p = jt - 1;
-    if (jt < J) {
-      // 1. Partials of tile jt over this member's slice.
-      double ssq[FMB];
-      f32x4 acc[FMB][NB];
+  // This member's slice of phi into LDS as bf16 hi / lo operand halves: the
+  // slice's rows of each stream are contiguous in phi, read in 16-byte
+  // pieces (all issued before any is used), and each value goes to element
+  // e of operand entry (wave, stream, column) for its position 32 w + 8 g + e.
+  {
+    constexpr int G = (M % 4 == 0) ? 4 : 1;            // floats per load
+    constexpr int PER = OSLICE * M / G;                  // loads per stream
+    constexpr int KPHI = (N * PER + OT - 1) / OT;
+    float pv[KPHI][G];
 #pragma unroll
-      for (int mb = 0; mb < FMB; ++mb) {
-        double sq = 0.0;
+    for (int k = 0; k < KPHI; ++k) {
+      const int q = tid + k * OT;
+      const int i = q / PER;
+      const int f = (q - i * PER) * G;
+      const int row = f / M;
+      const int j = s * OSLICE + row;
+      const bool ok = q < N * PER && j < d;
+      const float* src = a.phi + (static_cast<int64_t>(i) * d + j) * M + (f - row * M);
+      if constexpr (G == 4) {
+        const f32x4 v = ok ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-          float x[8];
-          unpack8(xc[mb][i], x);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sq = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), sq);
-        }
-        ssq[mb] = jv ? sq : 0.0;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = 0; c < 4; ++c) pv[k][c] = v[c];
+      } else {
+        pv[k][0] = ok ? *src : 0.0f;
       }
+    }
+#pragma unroll
+    for (int k = 0; k < KPHI; ++k) {
+      const int q = tid + k * OT;
+      if (q < N * PER) {
+        const int i = q / PER;
+        const int f = (q - i * PER) * G;
+        const int row = f / M;
+        const int ww = row >> 5, gg = (row >> 3) & 3, e = row & 7;
+#pragma unroll
+        for (int c = 0; c < G; ++c) {
+          const int col = f - row * M + c;
+          const int nb = col >> 4;
+          const int cn = (M - 16 * nb < 16) ? M - 16 * nb : 16;
+          const int ent = 64 * nb + gg * cn + (col & 15);
+          const __bf16 hi = static_cast<__bf16>(pv[k][c]);
+          const __bf16 lo = static_cast<__bf16>(pv[k][c] - static_cast<float>(hi));
+          reinterpret_cast<__bf16*>(&phi_l[ww][i][0][ent])[e] = hi;
+          reinterpret_cast<__bf16*>(&phi_l[ww][i][1][ent])[e] = lo;
+        }
+      }
+    }
+  }
+
+  // Clear this member's words of every ring slot (its records, the H_pre
+  // words of the tokens it owns) before any wave posts into them; the team
+  // then meets on the start words, so no member reads a slot before its
+  // writer has cleared it.
+  u64* const tring = a.ring + static_cast<int64_t>(team) * OSLOTS * a.slotw;
+  const int64_t recw = static_cast<int64_t>(S) * OR * W;   // record words per slot
+  for (int q = tid; q < OSLOTS * OR * W; q += OT)
+    tring[(q / (OR * W)) * a.slotw + static_cast<int64_t>(s) * OR * W + q % (OR * W)] = 0ull;
+  for (int q = tid; q < OSLOTS * OTPR * N; q += OT) {
+    const int sl = q / (OTPR * N);
+    const int r = q - sl * (OTPR * N);
+    const int tok = s + (r / N) * S;
+    if (r / N < a.tpr && tok < OR) tring[sl * a.slotw + recw + tok * N + r % N] = 0ull;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int ring_bytes = static_cast<int>(OSLOTS * a.slotw * 8);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(tring, 0, ring_bytes, 0x00020000);
+  constexpr int kOff = 0x7FFFFFF0;       // past the ring
+  auto rec_off = [&](int jt, int m, int tok, int word) -> int {
+    return static_cast<int>(((jt % OSLOTS) * a.slotw + (m * OR + tok) * W + word) * 8);
+  };
+
+  if (wave < OW) {
+    // ---------------------------------------------------------------- streaming
+    const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(a.h, 0, a.hbytes, 0x00020000);
+
+    // Tile jt's partials over this wave's 32 positions into the LDS ring.
+    auto partials = [&](int jt, const u32x4 (&x)[N]) {
+      double sq = 0.0;
+      f32x4 acc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < N; ++i) {
+        float v[8];
+        unpack8(Raw8<BF16>{x[i]}, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq = fma(static_cast<double>(v[e]), static_cast<double>(v[e]), sq);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const int col = 16 * nb + r16;
-          PhiOp<BF16> b;
+          const int cn = (M - 16 * nb < 16) ? M - 16 * nb : 16;
+          const bool cv = r16 < cn;
+          const int ent = 64 * nb + g * cn + (cv ? r16 : 0);
           const u32x4 zero = {0u, 0u, 0u, 0u};
-          b.hi = __builtin_bit_cast(bf16x8, col < M ? phi_l[wave][i][0][g][col] : zero);
-          b.lo = __builtin_bit_cast(bf16x8, col < M ? phi_l[wave][i][1][g][col] : zero);
-#pragma unroll
-          for (int mb = 0; mb < FMB; ++mb) acc[mb][nb] = mfma_block(xc[mb][i], b, acc[mb][nb]);
+          const u32x4 hi = phi_l[w][i][0][ent], lo = phi_l[w][i][1][ent];
+          PhiOp<BF16> b;
+          b.hi = __builtin_bit_cast(bf16x8, cv ? hi : zero);
+          b.lo = __builtin_bit_cast(bf16x8, cv ? lo : zero);
+          acc[nb] = mfma_block(Raw8<BF16>{x[i]}, b, acc[nb]);
         }
+        __builtin_amdgcn_sched_barrier(0);   // read phi per stream, next to its MFMAs (registers)
       }
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+      const int slot = jt % ORR;
+      wait_all_ge(posted, jt - ORR + 1, vbroken, lane);   // every wave has posted the slot's last tile
 #pragma unroll
-      for (int mb = 0; mb < FMB; ++mb) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int col = 16 * nb + r16;
-          if (col < M) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) red[wave][mb * 16 + 4 * g + v][col] = acc[mb][nb][v];
-          }
-        }
-        double sq = ssq[mb];
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
-        if (g == 0) red_ss[wave][mb * 16 + r16] = sq;
-      }
-      __syncthreads();
-      // 2. Post the tile's record: m partial dot products, sum of squares as hi + lo.
-      const unsigned tag = static_cast<unsigned>(jt + 1);
-      unsigned long long* mine = xrec(jt, s, 0);
-      for (int q = tid; q < FR * W; q += FT) {
-        const int tok = q / W;
-        const int col = q - tok * W;
-        float v;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = 16 * nb + r16;
         if (col < M) {
-          v = 0.0f;
 #pragma unroll
-          for (int ww = 0; ww < FW; ++ww) v += red[ww][tok][col];
-        } else {
-          double sd = 0.0;
-#pragma unroll
-          for (int ww = 0; ww < FW; ++ww) sd += red_ss[ww][tok];
-          const float hi = static_cast<float>(sd);
-          v = (col == M) ? hi : static_cast<float>(sd - static_cast<double>(hi));
+          for (int v = 0; v < 4; ++v) red[slot][w][4 * g + v][col >> 2][col & 3] = acc[nb][v];
         }
-        xstore(mine + q, xword(v, tag));
       }
-      __syncthreads();
+      if (g == 0) red_ss[slot][w][r16] = sq;
+      lds_done();
+      if (lane == 0) flag_set(&part_ready[w], jt + 1);
+    };
+
+    // This wave's share of tile jp's record: pairs SHARE w .. SHARE w + SHARE-1
+    // of the 16 tokens x NP pairs, each the 8 waves' partials added in wave
+    // order, posted with one 16-byte store (lanes without a pair store out of
+    // range, which moves no data).
+    auto post_share = [&](int jp) {
+      const bool have = jp >= 0 && jp < J;
+      if (have) wait_all_ge(part_ready, jp + 1, vbroken, lane);
+      const int q = SHARE * w + lane;
+      const bool qv = have && lane < SHARE && q < OR * NP;
+      const int qq = qv ? q : 0;
+      const int tok = qq / NP;
+      const int p = qq - tok * NP;
+      const int rs = (have ? jp : 0) % ORR;
+      uint32_t v0 = 0u, v1 = 0u;
+      if (qv) {
+        if (2 * p == SSO) {
+          double sd = red_ss[rs][0][tok];
+#pragma unroll
+          for (int ww = 1; ww < OW; ++ww) sd += red_ss[rs][ww][tok];
+          const u64 b = __builtin_bit_cast(u64, sd);
+          v0 = static_cast<uint32_t>(b);
+          v1 = static_cast<uint32_t>(b >> 32);
+        } else {
+          // columns 2p and 2p + 1: one 8-byte read per wave
+          const float2* r2 = reinterpret_cast<const float2*>(&red[rs][0][tok][0]) + p;
+          constexpr int WS = OR * MP * 2;                 // float2 stride between waves
+          float2 x = r2[0];
+#pragma unroll
+          for (int ww = 1; ww < OW; ++ww) {
+            const float2 y = r2[ww * WS];
+            x.x += y.x;
+            x.y += y.y;
+          }
+          v0 = __float_as_uint(x.x);
+          v1 = __float_as_uint(x.y);
+        }
+      }
+      const uint32_t tag = static_cast<uint32_t>(jp + 1);
+      const int off = qv ? rec_off(jp, s, tok, 2 * p) : kOff;
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{v0, tag, v1, tag}, xr, off, 0, 0);
+      lds_done();
+      if (have && lane == 0) flag_set(&posted[w], jp + 1);
+    };
+
+    auto emit = [&](int jt, const u32x4 (&x)[N]) {
+      const bool have = jt >= 0 && jt < J;
+      float hp[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) hp[i] = 0.0f;
+      if (have) {
+        wait_ge(&maps_tag[jt % OMR], jt + 1, vbroken);
+#pragma unroll
+        for (int i = 0; i < N; ++i) hp[i] = maps[jt % OMR][r16][i];
+      }
+      // Unpack the held tile afresh: reusing the values unpacked D steps
+      // earlier for the sum of squares would keep 32 floats per held tile
+      // live instead of 16 packed registers.
+      u32x4 y[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        y[i] = x[i];
+        asm volatile("" : "+v"(y[i]));
+      }
+      float o[8];
+      {
+        float v[8];
+        unpack8(Raw8<BF16>{y[0]}, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = hp[0] * v[e];
+      }
+#pragma unroll
+      for (int i = 1; i < N; ++i) {
+        float v[8];
+        unpack8(Raw8<BF16>{y[i]}, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(hp[i], v[e], o[e]);
+      }
+      const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + r16;
+      const bool ok = have && t < T && jv;
+      const uint32_t ho = ok ? static_cast<uint32_t>((t * d + j0) * 2) : kOob;
+      __builtin_amdgcn_raw_buffer_store_b128(pack8(o, BF16{}).v, hr, static_cast<int>(ho), 0, 2);
+    };
+
+    // Tile k lives in buffer k % ONB; the buffer of tile k - OD, emitted in
+    // step k, then receives tile k + OP.  Every step issues N loads and two
+    // stores, with no branch around any of them.
+    const int kend = ((J + OD + ONB - 1) / ONB) * ONB;
+    for (int k0 = 0; k0 < kend; k0 += ONB) {
+#pragma unroll
+      for (int u = 0; u < ONB; ++u) {
+        const int k = k0 + u;
+        if (k < J) partials(k, xb[u]);
+        post_share(k - 1);
+        emit(k - OD, xb[(u + OP) % ONB]);
+        load_tile(k + OP, xb[(u + OP) % ONB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else if (wave < OW + OX) {
+    // ---------------------------------------------------------------- exchange
+    // Exchange wave x takes the tiles t with t % OX == x.  Meet the team
+    // first: every member's slots are clear once its start word holds this
+    // call's sequence number.
+    const int xw = wave - OW;
+    u64* st = a.start + static_cast<int64_t>(team) * OS_MAX;
+    if (lane == 0 && xw == 0) st[s] = a.epoch;
+    if (lane < S) {
+      unsigned n = 0;
+      while (agent_load(st + lane) != a.epoch) {
+        if (flag_get(vbroken)) break;
+        if (++n > kMemSpin) {
+          flag_set(vbroken, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
     }
 
-    if (jt >= 1) {
-      // In the last round no barrier has passed since the previous round's
-      // step 6 (wave FW-1 may still read xin): wait for it before overwriting.
-      if (jt == J) __syncthreads();
-      // 3. Check the tags of tile jt - 1's words (re-reading any not yet posted).
-      const unsigned want = static_cast<unsigned>(p + 1);
-      const unsigned long long* slot = xrec(p, 0, 0);
+    const int tpr = a.tpr;
+    // Loads carry sc1: they skip the CU's L1 and read the XCD's L2.  Few,
+    // wide memory instructions: this wave shares the CU's memory pipeline
+    // with the streaming waves and would otherwise queue behind their loads.
+    auto ld2 = [&](int off) -> u32x4 { return __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 16); };
+    // Reduce-scatter reads: load r of owned token o covers word pairs 4 r ..
+    // 4 r + 3, one per 16-lane row; lane m of a row reads member m's pair.
+    const int rq = lane >> 4;
+    const int rm = lane & 15;
+    auto rs_off = [&](int jt, int o, int r) -> int {
+      const int p = 4 * r + rq;
+      const int tok = s + o * S;
+      if (o >= tpr || tok >= OR || p >= NP || rm >= S) return kOff;
+      return rec_off(jt, rm, tok, 2 * p);
+    };
+    auto bc_off = [&](int jt) -> int {
+      return (2 * lane < OR * N) ? static_cast<int>(((jt % OSLOTS) * a.slotw + recw + 2 * lane) * 8) : kOff;
+    };
+    // Wait until both words of a pair carry `tag` (reading it again as needed).
+    auto settle = [&](u32x4 v, int off, uint32_t tag) -> u32x4 {
+      unsigned n = 0;
+      while (off != kOff && (v.y != tag || v.w != tag)) {
+        if (flag_get(vbroken)) break;
+        if (++n > kMemSpin) {
+          flag_set(vbroken, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        asm volatile("" ::: "memory");
+        v = ld2(off);
+      }
+      return v;
+    };
+    u32x4 rsv[OTPR][NRB];
+    // Tile jb: once this member's waves have posted their record of it (the
+    // other members post theirs at about the same time), the reduce-scatter
+    // (B) and then the broadcast of the owners' H_pre (C).
+    for (int jb = xw; jb < J; jb += OX) {
+      wait_all_ge(posted, jb + 1, vbroken, lane);
 #pragma unroll
-      for (int k = 0; k < KMAX; ++k) {
-        const int q = tid + k * FT;
-        int lds = 0;
-        const int off = (q < QTOT) ? word_of(q, lds) : -1;
-        if (off >= 0) {
-          unsigned long long v = wv[k];
-          unsigned spins = 0;
-          while (!broken && static_cast<unsigned>(v >> 32) != want) {
-            if (++spins > kSpinLimit) {
-              atomicOr(a.err, 1u);
-              broken = true;
-              break;
+      for (int o = 0; o < OTPR; ++o) {
+        if (o < tpr) {
+#pragma unroll
+          for (int r = 0; r < NRB; ++r) rsv[o][r] = ld2(rs_off(jb, o, r));
+        }
+      }
+      const uint32_t tag = static_cast<uint32_t>(jb + 1);
+      // B: the team's sums for the tokens this member owns: a fixed tree over
+      // the members across each 16-lane row, in fp64.
+#pragma unroll
+      for (int o = 0; o < OTPR; ++o) {
+        if (o < tpr) {
+#pragma unroll
+          for (int r = 0; r < NRB; ++r) {
+            const int off = rs_off(jb, o, r);
+            const u32x4 v = settle(rsv[o][r], off, tag);
+            const int p = 4 * r + rq;
+            double d0 = 0.0, d1 = 0.0;
+            if (off != kOff) {
+              if (2 * p == SSO) {
+                d0 = __builtin_bit_cast(double, (static_cast<u64>(v.z) << 32) | v.x);
+              } else {
+                d0 = static_cast<double>(__uint_as_float(v.x));
+                d1 = static_cast<double>(__uint_as_float(v.z));
+              }
             }
-            __builtin_amdgcn_s_sleep(2);
-            v = xload(slot + off);
+            d0 = row16_sum(d0);
+            d1 = row16_sum(d1);
+            if (rm == 0 && p < NP) {
+              xs[xw][o][2 * p] = d0;
+              xs[xw][o][2 * p + 1] = d1;
+            }
           }
-          xin[lds] = __uint_as_float(static_cast<unsigned>(v));
         }
       }
-      __syncthreads();
-      // 4. H_pre of the tile's tokens (every member, identical arithmetic).
-      if (tid < FR * N) {
-        const int tok = tid / N;
-        const int i = tid - tok * N;
-        double z = 0.0, ss = 0.0;
-        for (int m2 = 0; m2 < S; ++m2) {
-          z += static_cast<double>(xin_a[m2][tok][i]);
-          ss += static_cast<double>(xin_a[m2][tok][N]) + static_cast<double>(xin_a[m2][tok][N + 1]);
-        }
-        const double inv_r = inv_rms(ss, N * d, a.eps);
-        hp[tok][i] = sigmoidf_(logit_of(z, inv_r, a.a_pre, a.bias[i]));
-      }
-      __syncthreads();
-      // 5. h = H_pre . X for this member's slice, from the tile still in registers.
-      const int64_t t0 = tile_of(p) * FR;
-#pragma unroll
-      for (int mb = 0; mb < FMB; ++mb) {
-        const int tok = mb * 16 + r16;
-        const int64_t t = t0 + tok;
-        if (jv && t < T) {
-          float o[8];
-          {
-            float x[8];
-            unpack8(xh[mb][0], x);
-            const float w0 = hp[tok][0];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = w0 * x[e];
-          }
-#pragma unroll
-          for (int i = 1; i < N; ++i) {
-            float x[8];
-            unpack8(xh[mb][i], x);
-            const float wi = hp[tok][i];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = fmaf(wi, x[e], o[e]);
-          }
-          store8<BF16, true>(a.h + t * d + j0, o);
-        }
-      }
-      // 6. Gates + Sinkhorn for this member's tokens; nothing here waits for them.
-      if (wave == FW - 1) {
-        const int qq = lane >> 4;
-        const int e = lane & 15;
-        const int tok = s * tpr + qq;
-        const bool tv = qq < tpr && tok < FR && t0 + tok < T;
-        const int tk = tok < FR ? tok : 0;
-        const int qc = qq < FTPR_MAX ? qq : 0;
-        double ss = 0.0, zr = 0.0, zg = 0.0;
-        for (int m2 = 0; m2 < S; ++m2) {
-          ss += static_cast<double>(xin_a[m2][tk][N]) + static_cast<double>(xin_a[m2][tk][N + 1]);
-          if (e < NN) zr += static_cast<double>(xin_b[m2][qc][e]);
-          if (e < N) zg += static_cast<double>(xin_a[m2][tk][e]);
-          else if (e < 2 * N) zg += static_cast<double>(xin_b[m2][qc][NN + (e - N)]);
-        }
-        const double inv_r = inv_rms(ss, N * d, a.eps);
-        const int colg = (e < N) ? e : (N + NN + (e - N));
-        float gv = 0.0f;
+      lds_done();
+      // Lane (o, e) of the maps: entry e of owned token o.
+      const int o = lane >> 4;
+      const int e = lane & 15;
+      const int tok = s + o * S;
+      const bool own = o < tpr && tok < OR;
+      const int oo = o < OTPR ? o : 0;
+      const int colr = N + e;
+      const int colg = (e < N) ? e : (N + NN + (e - N));
+      const int cr = e < NN ? colr : 0, cg = e < 2 * N ? colg : 0;
+      const double ss = xs[xw][oo][SSO];
+      const double zr = xs[xw][oo][cr];
+      const double zg = xs[xw][oo][cg];
+      const double inv_r = inv_rms(ss, N * d, a.eps);
+      float gv = 0.0f, rv = -INFINITY;
+      if constexpr (HC) {
+        if (e < 2 * N)
+          gv = static_cast<float>(static_cast<double>(a.bias[cg]) +
+                                  static_cast<double>((e < N) ? a.a_pre : a.a_post) * tanh(zg * inv_r));
+        rv = (e < NN) ? static_cast<float>(static_cast<double>(a.bias[cr]) +
+                                           static_cast<double>(a.a_res) * tanh(zr * inv_r))
+                      : 0.0f;
+      } else {
         if (e < 2 * N) {
-          const float l = logit_of(zg, inv_r, (e < N) ? a.a_pre : a.a_post, a.bias[colg]);
+          const float l = logit_of(zg, inv_r, (e < N) ? a.a_pre : a.a_post, a.bias[cg]);
           gv = (e < N) ? sigmoidf_(l) : 2.0f * sigmoidf_(l);
         }
-        float lr = -INFINITY;
-        if (e < NN) lr = logit_of(zr, inv_r, a.a_res, a.bias[N + e]);
-        const float mv = sinkhorn16<N>(lr, e, a.t_max);
-        if (tv) {
-          float* Ht = a.H + (t0 + tok) * M;
-          if (e < NN) Ht[N + e] = mv;
-          if (e < 2 * N) Ht[colg] = gv;
-        }
+        if (e < NN) rv = logit_of(zr, inv_r, a.a_res, a.bias[cr]);
+      }
+      u64* slot = tring + (jb % OSLOTS) * a.slotw;
+      if (own && e < N) slot[recw + tok * N + e] = xword(__float_as_uint(gv), tag);
+      // C's read goes out now; the other owners post at about the same time.
+      const int boff = bc_off(jb);
+      u32x4 bcv = ld2(boff);
+      // Hand the token's values to the Sinkhorn wave.
+      wait_ge(&sk_free, jb - OKR + 1, vbroken);
+      const int ks = jb % OKR;
+      if (o < OTPR) {
+        skin[ks][o][e] = make_float2(rv, gv);
+        const int64_t t = (team + static_cast<int64_t>(jb) * teams) * OR + tok;
+        if (e == 0) sktok[ks][o] = (own && t < T) ? t : -1;
+      }
+      lds_done();
+      if (lane == 0) flag_set(&sk_tag[ks], jb + 1);
+      // C: H_pre of the tile's 16 tokens, for the streaming waves.
+      bcv = settle(bcv, boff, tag);
+      if (boff != kOff) {
+        const int w0 = 2 * lane;
+        maps[jb % OMR][w0 / N][w0 % N] = __uint_as_float(bcv.x);
+        maps[jb % OMR][(w0 + 1) / N][(w0 + 1) % N] = __uint_as_float(bcv.z);
+      }
+      lds_done();
+      if (lane == 0) flag_set(&maps_tag[jb % OMR], jb + 1);
+    }
+    if (flag_get(vbroken) && lane == 0) __hip_atomic_store(a.hdr, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    // ----------------------------------------------------------------- Sinkhorn
+    // Two tiles per pass: lanes 32 q .. 32 q + 31 take tile jt + q, 16 lanes
+    // per owned token.
+    const int q = lane >> 5;
+    const int o = (lane >> 4) & 1;
+    const int e = lane & 15;
+    const int colg = (e < N) ? e : (N + NN + (e - N));
+    for (int jt = 0; jt < J; jt += 2) {
+      const int jn = (jt + 2 < J) ? jt + 2 : J;
+      wait_ge(&sk_tag[jt % OKR], jt + 1, vbroken);
+      if (jt + 1 < J) wait_ge(&sk_tag[(jt + 1) % OKR], jt + 2, vbroken);
+      const int tj = jt + q;
+      const bool tv = tj < J;
+      const int ks = (tv ? tj : jt) % OKR;
+      const float2 in = skin[ks][o][e];
+      const int64_t t = tv ? sktok[ks][o] : -1;
+      lds_done();
+      if (lane == 0) flag_set(&sk_free, jn);
+      float mv = in.x;
+      if constexpr (!HC) mv = sinkhorn16<N>(e < NN ? in.x : -INFINITY, e, a.t_max);
+      if (t >= 0) {
+        float* Ht = a.H + t * M;
+        if (e < NN) Ht[N + e] = mv;
+        if (e < 2 * N) Ht[colg] = in.y;
       }
     }
-    // 7. Issue the reads of tile jt's words, then stream tile jt + 2 into xh.
-    if (jt < J) {
-      const unsigned long long* slot = xrec(jt, 0, 0);
-#pragma unroll
-      for (int k = 0; k < KMAX; ++k) {
-        const int q = tid + k * FT;
-        int lds;
-        const int off = (q < QTOT) ? word_of(q, lds) : -1;
-        wv[k] = (off >= 0) ? xload(slot + off) : 0ull;
-      }
-    }
-    asm volatile("" ::: "memory");
-    if (jt + 2 < J) load_tile(jt + 2, xh);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  for (int64_t jt = 0; jt <= J; jt += 3) {
-    round(jt, b2, b0);
-    if (jt + 1 <= J) round(jt + 1, b0, b1);
-    if (jt + 2 <= J) round(jt + 2, b1, b2);
   }
 }
 
-__global__ __launch_bounds__(256) void clear_words_kernel(unsigned long long* p, int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
-    p[i] = 0ull;
+int one_pass_slices(int d) { return (d + OSLICE - 1) / OSLICE; }
+
+// Token record: m partials, padding to an even word, the fp64 sum of squares.
+int record_words(int n) { return ((num_maps(n) + 1) & ~1) + 2; }
+int64_t slot_words(int S, int n) { return static_cast<int64_t>(S) * OR * record_words(n) + OR * n; }
+
+int max_teams(int S) { return OXCD * (48 / S); }   // devices with up to 48 CUs per XCD
+
+template <int N, bool HC>
+const void* one_pass_kernel_ptr() {
+  return reinterpret_cast<const void*>(&pre_one_pass_kernel<N, HC>);
 }
 
-int fused_slices(int d) { return (d + FSLICE - 1) / FSLICE; }
-
-size_t fused_exchange_words(int teams, int S, int n) {
-  return static_cast<size_t>(teams) * FSLOTS * S * FR * (num_maps(n) + 2);
-}
-
-template <int N>
-const void* fused_kernel_ptr() {
-  return reinterpret_cast<const void*>(&pre_fused_kernel<N>);
-}
+std::atomic<u64> g_epoch{0};
 
 }  // namespace
 
-// Bytes the fused form may need: header + exchange ring, for devices with up
-// to 48 CUs per XCD.
+// Bytes the single-pass form needs: header, start words and the exchange
+// ring, for devices with up to 48 CUs per XCD.
 size_t pre_fused_workspace_bytes(int64_t /*T*/, int n, int d) {
-  const int S = fused_slices(d);
-  if (S < FS_MIN || S > FS_MAX) return 0;
-  const int teams = 8 * (48 / S);
-  return FHDR + fused_exchange_words(teams, S, n) * sizeof(unsigned long long);
+  const int S = one_pass_slices(d);
+  if (S < OS_MIN || S > OS_MAX) return 0;
+  const int teams = max_teams(S);
+  return OHDR + static_cast<size_t>(teams) * OS_MAX * sizeof(u64) +
+         static_cast<size_t>(teams) * OSLOTS * static_cast<size_t>(slot_words(S, n)) * sizeof(u64);
 }
 
 // Launch the single-pass form when it applies; returns hipErrorNotSupported
 // (without launching anything) when it does not, so the caller can fall back.
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
                             float* H, void* workspace, size_t ws_bytes, const DeviceInfo& dev, hipStream_t stream) {
-  if (p.dtype != MHC_BF16 || (p.n != 4 && p.n != 2 && p.n != 1) || p.maps != MHC_MAPS_MHC)
-    return hipErrorNotSupported;
-  const int S = fused_slices(p.d);
-  if (S < FS_MIN || S > FS_MAX || !dev.cooperative || dev.num_cus % 8 != 0) return hipErrorNotSupported;
-  const int per_xcd = dev.num_cus / 8;
+  if (p.dtype != MHC_BF16 || (p.n != 4 && p.n != 2 && p.n != 1)) return hipErrorNotSupported;
+  const int S = one_pass_slices(p.d);
+  if (S < OS_MIN || S > OS_MAX || !dev.cooperative || dev.num_cus % OXCD != 0) return hipErrorNotSupported;
+  const int per_xcd = dev.num_cus / OXCD;
   const int tpx = per_xcd / S;
   if (tpx < 1) return hipErrorNotSupported;
-  const int teams = 8 * tpx;
-  const int64_t ntiles = (p.T + FR - 1) / FR;
-  if (ntiles < 2 * static_cast<int64_t>(teams)) return hipErrorNotSupported;   // too little work to fill the teams
-  const size_t words = fused_exchange_words(teams, S, p.n);
-  if (FHDR + words * sizeof(unsigned long long) > ws_bytes) return hipErrorNotSupported;
+  const int teams = OXCD * tpx;
+  if (teams > max_teams(S)) return hipErrorNotSupported;
+  const int64_t ntiles = (p.T + OR - 1) / OR;
+  if (ntiles < teams) return hipErrorNotSupported;   // too little work to give every team a tile
+  // Buffer ranges are 31-bit byte counts.
+  const int64_t xbytes = p.T * p.n * static_cast<int64_t>(p.d) * 2;
+  const int64_t hbytes = p.T * static_cast<int64_t>(p.d) * 2;
+  if (xbytes >= (int64_t{1} << 31) || p.T < 1) return hipErrorNotSupported;
+  if (pre_fused_workspace_bytes(p.T, p.n, p.d) > ws_bytes) return hipErrorNotSupported;
+  const bool hc = p.maps == MHC_MAPS_HC;
   const void* fn = nullptr;
   switch (p.n) {
-    case 1: fn = fused_kernel_ptr<1>(); break;
-    case 2: fn = fused_kernel_ptr<2>(); break;
-    default: fn = fused_kernel_ptr<4>(); break;
+    case 1: fn = hc ? one_pass_kernel_ptr<1, true>() : one_pass_kernel_ptr<1, false>(); break;
+    case 2: fn = hc ? one_pass_kernel_ptr<2, true>() : one_pass_kernel_ptr<2, false>(); break;
+    default: fn = hc ? one_pass_kernel_ptr<4, true>() : one_pass_kernel_ptr<4, false>(); break;
   }
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, FT, 0) != hipSuccess || occ < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, OT, 0) != hipSuccess || occ < 1)
     return hipErrorNotSupported;
 
   char* base = static_cast<char*>(workspace);
-  unsigned long long* xch = reinterpret_cast<unsigned long long*>(base + FHDR);
-  // Clear the header and the ring: tags of an earlier call must never match.
-  const int64_t nclear = static_cast<int64_t>(words + FHDR / sizeof(unsigned long long));
-  hipLaunchKernelGGL(clear_words_kernel, dim3(1024), dim3(256), 0, stream, reinterpret_cast<unsigned long long*>(base),
-                     nclear);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  FusedArgs fa;
-  fa.T = p.T;
-  fa.d = p.d;
-  fa.S = S;
-  fa.tpx = tpx;
-  fa.teams = teams;
-  fa.tpr = (FR + S - 1) / S;
-  fa.ntiles = ntiles;
-  fa.X = static_cast<const uint16_t*>(X);
-  fa.phi = phi;
-  fa.bias = bias;
-  fa.a_pre = p.alpha_pre;
-  fa.a_res = p.alpha_res;
-  fa.a_post = p.alpha_post;
-  fa.eps = p.eps;
-  fa.t_max = p.t_max;
-  fa.h = static_cast<uint16_t*>(h);
-  fa.H = H;
-  fa.xch = xch;
-  fa.err = reinterpret_cast<unsigned*>(base);
-  void* args[] = {&fa};
-  return hipLaunchCooperativeKernel(fn, dim3(dev.num_cus), dim3(FT), args, 0, stream);
+  OneArgs a;
+  a.T = p.T;
+  a.d = p.d;
+  a.S = S;
+  a.tpx = tpx;
+  a.teams = teams;
+  a.tpr = (OR + S - 1) / S;
+  a.ntiles = ntiles;
+  a.X = static_cast<const uint16_t*>(X);
+  a.phi = phi;
+  a.bias = bias;
+  a.a_pre = p.alpha_pre;
+  a.a_res = p.alpha_res;
+  a.a_post = p.alpha_post;
+  a.eps = p.eps;
+  a.t_max = p.t_max;
+  a.h = static_cast<uint16_t*>(h);
+  a.H = H;
+  a.hdr = reinterpret_cast<u64*>(base);
+  a.start = reinterpret_cast<u64*>(base + OHDR);
+  a.ring = a.start + static_cast<size_t>(max_teams(S)) * OS_MAX;
+  a.slotw = slot_words(S, p.n);
+  a.epoch = ++g_epoch;
+  a.xbytes = static_cast<int>(xbytes);
+  a.hbytes = static_cast<int>(hbytes);
+  void* args[] = {&a};
+  return hipLaunchCooperativeKernel(fn, dim3(dev.num_cus), dim3(OT), args, 0, stream);
 }
 
 }  // namespace mhc

@@ -100,7 +100,13 @@ def test_workspace_size_formula(lib):
         slices = -(-d // 256)
         width = ((n * n + 2 * n + 1) & ~1) + 2          # m fp32 partials, then an aligned fp64
         two_pass = slices * T * width * 4 + 512 * 16    # records + write-only trash slots (16 B per thread)
-        one_pass = 256 + 8 * (48 // slices) * 4 * slices * 32 * (n * n + 2 * n + 2) * 8 if 8 <= slices <= 16 else 0
+        # one pass: header, 16 start words per team, then per team 4 ring slots of 16-token
+        # records (m + 2 words per member and token) and n H_pre words per token, 8 B a word;
+        # room for 8 XCDs x floor(48 / slices) teams
+        teams = 8 * (48 // slices)
+        record = ((n * n + 2 * n + 1) & ~1) + 2            # m partials, even padding, fp64 sum of squares
+        slot = slices * 16 * record + 16 * n
+        one_pass = 256 + teams * 16 * 8 + teams * 4 * slot * 8 if 8 <= slices <= 16 else 0
         assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == max(two_pass, one_pass)
     assert lib.mhc_pre_workspace_size(None) == 0
     assert lib.mhc_pre_workspace_size(ctypes.byref(_params(n=3))) == 0

@@ -1,10 +1,10 @@
 """The single-pass form of mhc_pre (MHC_PRE_ONE_PASS) against the oracle.
 
-It applies to bf16 state with ceil(d / 256) in [8, 16] and at least two
-32-token tiles per team of workgroups; teams exchange per-token partial sums
-through device memory.  Each case checks that the one-pass form really ran,
-that no internal wait ran out (the workspace's error word is 0), and that the
-results match the oracle like the two-pass form's do.
+It applies to bf16 state with ceil(d / 256) in [8, 16] and at least one
+16-token tile per team of workgroups; a team's members split d and exchange
+per-token sums through their XCD's L2.  Each case checks that the one-pass
+form really ran, that no internal wait ran out (the workspace's error word is
+0), and that the results match the oracle like the two-pass form's do.
 """
 import numpy as np
 import pytest
@@ -26,10 +26,10 @@ def mhc():
     return m
 
 
-def _run(mhc, w, X, phi, bias, alpha, algo):
+def _run(mhc, w, X, phi, bias, alpha, algo, maps=0):
     dX, dphi, dbias = to_device(X), to_device(phi), to_device(bias)
     ws = torch.zeros(mhc.pre_workspace_size(w.T, w.n, w.d, w.dtype), dtype=torch.uint8, device="cuda")
-    h, H, used = mhc.pre_ex(dX, dphi, dbias, algo, alpha=alpha, eps=w.eps, t_max=w.t_max, workspace=ws)
+    h, H, used = mhc.pre_ex(dX, dphi, dbias, algo, alpha=alpha, eps=w.eps, t_max=w.t_max, workspace=ws, maps=maps)
     torch.cuda.synchronize()
     err_word = int(ws[:4].view(torch.int32).item())
     return to_host(h), to_host(H), used, err_word
@@ -102,3 +102,38 @@ def test_one_pass_refuses_what_it_does_not_cover(mhc):
         assert ei.value.status == 5
         h, H, used = mhc.pre_ex(X, phi, bias, mhc.PRE_AUTO)      # auto falls back
         assert used == mhc.PRE_TWO_PASS
+
+
+@pytest.mark.parametrize("T", [1100, 16384])
+def test_one_pass_hc_maps(mhc, oracle_lib, T):
+    """The unconstrained HC maps through the single pass: same tolerance rule
+    as the two-pass HC test (the absolute part scales with |alpha|)."""
+    w = synth.scaled(synth.WORKLOADS["layer_bf16_T16384_d4096"], T=T)
+    X = synth.make_state(w)
+    phi, bias = synth.make_params(w)
+    alpha = (0.8, 0.6, 1.2)
+    h, H, used, err = _run(mhc, w, X, phi, bias, alpha, mhc.PRE_ONE_PASS, maps=mhc.MAPS_HC)
+    assert used == mhc.PRE_ONE_PASS and err == 0
+    tok = np.arange(T, dtype=np.int64) if T < 2000 else sample_tokens(T, 48, tile=16)
+    ref = oracle_lib.pre_hc(X, phi, bias, alpha, eps=w.eps, tokens=tok)
+    rtol, atol = TOL[("bf16", "maps")]
+    assert_close(H[tok], ref["H"], rtol, atol * 4.0 * max(alpha), what="one-pass HC H")
+    assert_close(h[tok], ref["h"], *TOL[("bf16", "state")], what="one-pass HC h")
+
+
+def test_one_pass_repeated_calls_same_workspace(mhc):
+    """Back-to-back calls on one workspace (the exchange ring keeps the last
+    call's words): every call must produce the same bits and a clear error word."""
+    w = synth.scaled(synth.WORKLOADS["layer_bf16_T16384_d4096"], T=4096)
+    X = to_device(synth.make_state(w))
+    phi, bias = (to_device(a) for a in synth.make_params(w))
+    ws = torch.zeros(mhc.pre_workspace_size(w.T, w.n, w.d, w.dtype), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(6):
+        h, H, used = mhc.pre_ex(X, phi, bias, mhc.PRE_ONE_PASS, alpha=w.alpha, workspace=ws)
+        assert used == mhc.PRE_ONE_PASS
+        outs.append((to_host(h).copy(), to_host(H).copy()))
+    torch.cuda.synchronize()
+    assert int(ws[:8].view(torch.int64).item()) == 0
+    for o in outs[1:]:
+        assert np.array_equal(o[0], outs[0][0]) and np.array_equal(o[1], outs[0][1])
