@@ -237,15 +237,17 @@ def cpu_baseline(w, seconds_target=15.0):
 # ---- rocprofv3 results -> profiles/ ------------------------------------------
 # Which kernels make up each entry point (substrings of the demangled names).
 ENTRY_KERNELS = {
-    "mhc_pre": ["pre_partial_kernel<mhc::BF16, 4, 2, false>", "pre_finish_kernel<mhc::BF16, 4>"],
+    "mhc_pre": ["pre_one_pass_kernel<4, false>"],                      # the form MHC_PRE_AUTO takes here
+    "mhc_pre_two_pass": ["pre_partial_kernel<mhc::BF16, 4, 2, 0>", "pre_finish_kernel<mhc::BF16, 4, false>"],
     "mhc_post": ["post_kernel<mhc::BF16, 4"],
     "mhc_amax": ["amax_kernel<4>"],
     "mhc_post_bwd": ["post_bwd_kernel<mhc::BF16, 4>"],
-    "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 2, true>", "pre_bwd_token_kernel<4>",
+    "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 2, 1>", "pre_bwd_token_kernel<4>",
                     "pre_bwd_apply_mfma_kernel<4>", "reduce_chunks_kernel", "reduce_columns_kernel"],
 }
 ENTRY_SOURCES = {
-    "mhc_pre": ["pre.hip", "pre_common.hpp", "device.hpp"],
+    "mhc_pre": ["pre_fused.hip", "pre_common.hpp", "device.hpp"],
+    "mhc_pre_two_pass": ["pre.hip", "pre_common.hpp", "device.hpp"],
     "mhc_post": ["post.hip", "device.hpp"],
     "mhc_amax": ["amax.hip", "device.hpp"],
     "mhc_post_bwd": ["bwd.hip", "device.hpp"],
@@ -454,13 +456,34 @@ def main():
                          "GBps": algo[name] / (avg_ms * 1e-3) / 1e9,
                          "frac_of_peak": algo[name] / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    traffic = traffic_bytes(args.traffic_json, w.name, dominant)
+    form_key = {"mhc_pre": "mhc_pre" if algo_used[0] == 2 else "mhc_pre_two_pass"}
+    traffic = traffic_bytes(args.traffic_json, w.name, form_key.get(dominant, dominant))
     kd = kernels[dominant]
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": kd["GBps"] / HBM_PEAK_GBPS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": kd["algorithmic_bytes"], "avg_launch_us": kd["avg_us"]}
     log(f"{ms_step * 1e3:.1f} us/step, {tokens_per_s / 1e6:.2f} M tokens/s; "
         + ", ".join(f"{k} {v['avg_us']:.1f} us ({v['GBps']:.0f} GB/s)" for k, v in kernels.items()))
+
+    # The other form of mhc_pre on the same inputs, for reference.
+    forms = {}
+    for form_algo, name in ((2, "one-pass"), (1, "two-pass")):
+        try:
+            for _ in range(3):
+                mhc.pre_ex(X, phi, bias, form_algo, alpha=w.alpha, eps=w.eps, t_max=w.t_max, h=h, H=H, workspace=ws,
+                           stream=stream)
+            fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            fev[0].record(stream)
+            for _ in range(max(5, K // 2)):
+                mhc.pre_ex(X, phi, bias, form_algo, alpha=w.alpha, eps=w.eps, t_max=w.t_max, h=h, H=H, workspace=ws,
+                           stream=stream)
+            fev[1].record(stream)
+            torch.cuda.synchronize()
+            us = fev[0].elapsed_time(fev[1]) / max(5, K // 2) * 1e3
+            forms[name] = {"avg_us": us, "GBps": algorithmic_bytes(T, n, d, sbytes)["mhc_pre"] / (us * 1e-6) / 1e9}
+        except mhc.MhcError:
+            forms[name] = None
+    log("mhc_pre forms: " + ", ".join(f"{k} {v['avg_us']:.1f} us" for k, v in forms.items() if v))
 
     backward = None
     if not args.no_backward:
@@ -513,6 +536,7 @@ def main():
         "wall_s_timed_region": t_wall,
         "roofline": roofline,
         "kernels": kernels,
+        "mhc_pre_forms": forms,
         "backward": backward,
         "stack": stack,
         "cpu_baseline": cpu,

@@ -133,22 +133,24 @@ size_t mhc_pre_workspace_size(const mhc_params* p);
  * how many times they read X from HBM:
  *   MHC_PRE_TWO_PASS  a split-K projection pass, then a maps + aggregation
  *                     pass that reads X again; any valid shape.
- *   MHC_PRE_ONE_PASS  bf16 state with 1793 <= d <= 4096 and enough tokens to
- *                     give every team of workgroups two 32-token tiles: teams
- *                     of one workgroup per compute unit split d, exchange
- *                     per-token partial sums through device memory and keep
- *                     their slice of X in registers until H_pre is known, so
- *                     X is read once.  Uses a cooperative launch.  Returns
- *                     MHC_ERR_UNSUPPORTED when it does not apply.
- *   MHC_PRE_AUTO      the two-pass form, which measures faster on MI355X at
- *                     every shape the one-pass form covers.
+ *   MHC_PRE_ONE_PASS  bf16 state with 1793 <= d <= 4096 and at least one
+ *                     16-token tile per team: teams of S = ceil(d / 256)
+ *                     workgroups (one per compute unit, all on one XCD)
+ *                     split d, exchange per-token sums through the XCD's L2
+ *                     and keep their slice of X in registers until H_pre is
+ *                     known, so X is read once.  Uses a cooperative launch.
+ *                     Returns MHC_ERR_UNSUPPORTED when it does not apply.
+ *   MHC_PRE_AUTO      the one-pass form where it measures faster on MI355X
+ *                     (n = 4, teams that fill whole XCDs, at least 40 tiles
+ *                     per team: T >= 10240 at d = 4096), else the two-pass.
  * Both sum every partial in a fixed order (results are bitwise reproducible
  * for a given form); the two forms agree to rounding.
  * algo_used (nullable, host pointer) receives the form that ran.  After a
- * one-pass call, the first 4 bytes of the workspace hold 0 unless an
- * internal wait ran out (then the results are invalid); this cannot happen
- * when all workgroups of the launch are resident, which the cooperative
- * launch guarantees. */
+ * one-pass call, the first 8 bytes of the workspace hold 0, or the
+ * sequence number of a one-pass call whose internal wait ran out (its
+ * results are invalid); the library never clears it.  A wait can only run
+ * out if the workgroups of the launch are not all resident or not placed on
+ * the XCDs round-robin, which the cooperative launch on MI355X rules out. */
 #define MHC_PRE_AUTO 0
 #define MHC_PRE_TWO_PASS 1
 #define MHC_PRE_ONE_PASS 2

@@ -34,6 +34,7 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
 
 // The single-pass form (pre_fused.hip): hipErrorNotSupported when it does not apply.
 size_t pre_fused_workspace_bytes(int64_t T, int n, int d);
+bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev);   // what MHC_PRE_AUTO picks
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
                             float* H, void* workspace, size_t ws_bytes, const DeviceInfo& dev, hipStream_t stream);
 

@@ -580,9 +580,13 @@ hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, cons
                       hipStream_t stream) {
   if (used) *used = MHC_PRE_TWO_PASS;
   if (p.T == 0) return hipSuccess;
-  // AUTO takes the two-pass form: on MI355X it measures faster at every shape
-  // the one-pass form covers (the cross-team exchange costs more than the
-  // second read of X, which mostly hits the last-level cache).
+  if (algo == MHC_PRE_AUTO && pre_fused_preferred(p, dev)) {
+    if (launch_pre_fused(p, X, phi, bias, h, H, workspace, ws_bytes, dev, stream) == hipSuccess) {
+      if (used) *used = MHC_PRE_ONE_PASS;
+      return hipSuccess;
+    }
+    (void)hipGetLastError();                 // refused: the two-pass form below
+  }
   if (algo == MHC_PRE_ONE_PASS) {
     const hipError_t e = launch_pre_fused(p, X, phi, bias, h, H, workspace, ws_bytes, dev, stream);
     if (e == hipSuccess) {

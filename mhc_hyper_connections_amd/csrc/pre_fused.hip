@@ -62,12 +62,12 @@ constexpr int OR = 16;                  // tokens per tile
 constexpr int OS_MIN = 8;               // team size range (ceil(d / OSLICE))
 constexpr int OS_MAX = 16;
 constexpr int OTPR = (OR + OS_MIN - 1) / OS_MIN;   // most tokens a member owns per tile
-constexpr int OSLOTS = 4;               // exchange ring depth (tiles); >= 4 is safe, see below
+constexpr int OSLOTS = 4;               // exchange ring depth (tiles); see below
 constexpr int ORR = 3;                  // LDS ring of partials (tiles)
 constexpr int OMR = 4;                  // LDS ring of H_pre (tiles; a slot is rewritten once its tile's h is out)
 constexpr int OKR = 4;                  // LDS ring of Sinkhorn inputs (tiles; taken two at a time)
-constexpr int OD = 3;                   // tiles between a tile's partials and its h (>= 2, see below)
-constexpr int OP = 4;                   // X tiles in flight ahead of the one being multiplied
+constexpr int OD = 4;                   // tiles between a tile's partials and its h; see below
+constexpr int OP = 3;                   // X tiles in flight ahead of the one being multiplied
 constexpr int ONB = OD + OP;            // X tile buffers per lane
 constexpr size_t OHDR = 256;            // workspace header: the error word
 constexpr int OXCD = 8;                 // XCDs of the device (MI355X)
@@ -75,17 +75,21 @@ constexpr unsigned kLdsSpin = 1u << 20; // bounded waits: far beyond any legitim
 constexpr unsigned kMemSpin = 1u << 16;
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: loads read 0, stores drop
 
-// Deadlock freedom and slot reuse.  Streaming waves post tile k's partials
-// before waiting for tile k-D's H_pre, which the exchange wave produces in
-// round k-D+2 <= k; a round waits only for partials the waves have posted.
-// A round first reads the records of tile i-1 and the H_pre words of tile
-// i-2, posted in the previous round.  A member rewrites tile k's record slot
-// in round k+OSLOTS, after its round k+OSLOTS-1 has read every owner's H_pre
-// of tile k+OSLOTS-3, which the owners posted after their reads of tile
-// k+OSLOTS-3's records: with OSLOTS >= 4 all reads of tile k's records are
-// done; an owner rewrites tile k's H_pre words in round k+OSLOTS+1, after
-// reading every member's record of tile k+OSLOTS, which they posted after
-// their round k+OSLOTS-1 and so after reading tile k's H_pre words.
+// Progress and slot reuse.  In step k a streaming wave writes tile k's
+// partials, posts its share of tile k-1's record, then emits tile k-OD,
+// which waits for that tile's H_pre.  An exchange wave handles tile j once
+// every streaming wave of its member has posted tile j's record: B (read the
+// members' records of the owned tokens, post H_pre) and C (read all owners'
+// H_pre).  Nothing waits for a later step, so every wait ends.
+// A member posts tile k's record after finishing step k, hence after
+// emitting tile k-OD, hence after its C of every tile <= k-OD, which came
+// after every owner's B of those tiles.  Tile k's record and H_pre words
+// overwrite those of tile k-OSLOTS, which is therefore read by then when
+// OSLOTS >= OD; tile k's H_pre goes into LDS slot k % OMR, whose previous
+// tile, k-OMR, has been emitted when OMR >= OD.
+static_assert(OSLOTS >= OD, "exchange words of a tile are rewritten only after every member has read them");
+static_assert(OMR >= OD, "an H_pre slot in LDS is rewritten only after its tile has been emitted");
+static_assert(OD >= 2, "a tile's H_pre needs the next step's record post");
 
 struct OneArgs {
   int64_t T;
@@ -688,6 +692,19 @@ size_t pre_fused_workspace_bytes(int64_t /*T*/, int n, int d) {
   const int teams = max_teams(S);
   return OHDR + static_cast<size_t>(teams) * OS_MAX * sizeof(u64) +
          static_cast<size_t>(teams) * OSLOTS * static_cast<size_t>(slot_words(S, n)) * sizeof(u64);
+}
+
+// Whether MHC_PRE_AUTO takes the single pass: measured faster on MI355X for
+// n = 4 when the teams fill whole XCDs and each gets at least 40 tiles (at
+// T = 16384, d = 4096: 194 us against 227 us); for n <= 2 a tile carries too
+// little data to hide the exchange.
+bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev) {
+  if (p.dtype != MHC_BF16 || p.n != 4 || !dev.cooperative || dev.num_cus % OXCD != 0) return false;
+  const int S = one_pass_slices(p.d);
+  const int per_xcd = dev.num_cus / OXCD;
+  if (S < OS_MIN || S > OS_MAX || per_xcd % S != 0) return false;
+  const int64_t teams = static_cast<int64_t>(OXCD) * (per_xcd / S);
+  return (p.T + OR - 1) / OR >= 40 * teams;
 }
 
 // Launch the single-pass form when it applies; returns hipErrorNotSupported
