@@ -11,39 +11,42 @@
 // team of S = ceil(d / 256) workgroups (8 <= S <= 16), one per CU, all on one
 // XCD: they exchange per-token sums through that XCD's L2.  Member s owns
 // positions [256 s, 256 s + 256) of every stream; the team walks 16-token
-// tiles.  A workgroup runs ten waves with fixed roles:
+// tiles.  Workgroups are dispatched to the XCDs round-robin, so team and
+// member follow from the workgroup index (checked against the hardware XCD
+// id).  A workgroup runs eleven waves with fixed roles:
 //  * waves 0-7 stream.  Wave w holds positions 32 w .. 32 w + 31 of the
-//    member's slice for the tile's 16 tokens in registers (lane = token row
-//    and 8 positions, the MFMA A layout; one 16-byte load per stream).  Per
-//    tile it forms the slice's m partial dot products with phi on MFMA (phi
+//    member's slice for a tile's 16 tokens in registers (lane = token row
+//    and 8 positions, the MFMA A layout; one 16-byte load per stream).  In
+//    step k it forms tile k's m partial dot products with phi on MFMA (phi
 //    as bf16 hi + lo halves, kept in LDS) and the fp64 partial sum of
-//    squares, and hands them to the exchange wave through LDS.  D tiles
-//    later, once that tile's H_pre has come back, it forms h = H_pre . X for
-//    its positions from the registers that still hold the tile, and stores
-//    it.  These waves issue no memory operation but their X loads and h
-//    stores, a fixed number per tile (masked lanes use out-of-range buffer
-//    offsets, which move no data), so the in-order completion count only
-//    ever makes them wait for their oldest tile.
-//  * wave 8 exchanges, in round i:
-//      A  tile i: sums the 8 waves' partials per token in a fixed order and
-//         posts the member's record: 16 tokens x (m partials, fp64 sum of
-//         squares as two halves), each a tagged 64-bit word (value | tag << 32).
-//      B  tile i-1, reduce-scatter: member s owns tokens s and s + S of the
-//         tile.  It reads every member's record of them, sums in member
-//         order (fp64), forms r, the logits and the gates, posts H_pre and
-//         hands the residual logits to wave 9.
-//      C  tile i-2, broadcast: reads H_pre of all 16 tokens and hands it to
-//         the streaming waves.
-//  * wave 9 runs Sinkhorn-Knopp for the member's own tokens and writes H.
-// Exchange words are written with plain stores (through the CU's L1 into the
-// XCD's L2) and read with agent-scope loads (which skip the L1); a word whose
-// tag is not yet the tile's is read again.  A member clears its own slots at
-// the start and the team meets on words stamped with the call's sequence
-// number, so words of earlier calls never match.  Every sum runs in a fixed
-// order: results are bitwise reproducible.  All waits are bounded; one that
-// runs out marks the workgroup broken (no further waits; results invalid)
-// and the call's sequence number is stored into the workspace's error word.
-// The launch is cooperative (all workgroups co-resident).
+//    squares into an LDS ring; sums its eighth of tile k-1's record over the
+//    8 waves (wave order) and posts it with one 16-byte store; and, once
+//    tile k-OD's H_pre has come back, forms h = H_pre . X for its positions
+//    from the registers that still hold that tile, and stores it.  These
+//    waves issue no memory operation but their X loads, the record store and
+//    the h store, a fixed number per step (masked lanes use out-of-range
+//    buffer offsets, which move no data), so the in-order completion count
+//    only ever makes them wait for their oldest tile.
+//  * waves 8-9 exchange, tiles alternating between them.  For tile j, once
+//    the member's waves have posted its record:
+//      B  reduce-scatter: member s owns tokens s and s + S of the tile.  It
+//         reads every member's record of them, sums them by a fixed tree
+//         over the members (fp64), forms r, the logits and the gates, posts
+//         H_pre and hands the residual logits to wave 10.
+//      C  broadcast: reads H_pre of all 16 tokens into LDS for the
+//         streaming waves.
+//  * wave 10 runs Sinkhorn-Knopp for the member's own tokens (two tiles per
+//    pass) and writes H.
+// Exchange words are tagged 64-bit values (value | tag << 32) moved in
+// 16-byte pairs: written with plain stores (through the CU's L1 into the
+// XCD's L2), read with sc1 buffer loads (which skip the L1); a pair whose tag
+// is not yet the tile's is read again.  Each member clears its own slots
+// before any wave posts, and the team meets on words stamped with the call's
+// sequence number, so words of earlier calls never match.  Every sum runs in
+// a fixed order: results are bitwise reproducible.  All waits are bounded;
+// one that runs out marks the workgroup broken (no further waits; results
+// invalid) and the call's sequence number is stored into the workspace's
+// error word.  The launch is cooperative (all workgroups co-resident).
 #include <atomic>
 
 #include "launch.hpp"
