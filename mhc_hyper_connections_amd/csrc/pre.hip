@@ -33,9 +33,11 @@
 namespace mhc {
 namespace {
 
-constexpr int PRE_WAVES = 8;
+constexpr int PRE_WAVES = 8;                // waves per workgroup of the persistent form
 constexpr int PRE_THREADS = PRE_WAVES * 64;
-constexpr int PRE_SLICE = PRE_WAVES * 32;   // positions of d per slice (32 per wave)
+constexpr int SMALL_WAVES = 2;              // waves per workgroup of the small-T form
+// Slices of d: 32 positions per wave (all n streams of them).
+__host__ __device__ constexpr int slice_width(int waves) { return 32 * waves; }
 
 // Write-only slots after the partial records that absorb the stores of
 // items past the end (16 bytes per thread).
@@ -56,8 +58,13 @@ __host__ __device__ constexpr int part_width(int n, bool with_d = false) { retur
 //         formed with mhc_post's arithmetic, stored to Xout, and its
 //         projection partials (for the next layer) computed from the stored
 //         values.
-template <typename ST, int N, int MB, int MODE>
-__global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int d, int S, int64_t ntiles,
+//
+// PWV waves per workgroup, slices of 32 PWV positions.  ONE: every
+// workgroup takes exactly one tile (blockIdx / S), with no prefetch: the
+// small-T form, which spreads a few tiles over many workgroups; otherwise
+// the workgroups are persistent and walk tiles with two in flight.
+template <typename ST, int N, int MB, int MODE, int PWV = PRE_WAVES, bool ONE = false>
+__global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d, int S, int64_t ntiles,
                                                                   const typename ST::elem* X,
                                                                   const typename ST::elem* __restrict__ Dg,
                                                                   const float* __restrict__ phi,
@@ -74,8 +81,9 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
   constexpr int HV = FUSE_POST ? M / 4 : 1;                 // the maps row of the previous layer, as f32x4
   constexpr int PW = part_width(N, WITH_D);
   constexpr int SSO = ss_offset(N, WITH_D);
-  __shared__ float red[PRE_WAVES][R][M + ND];
-  __shared__ double red_ss[PRE_WAVES][R];
+  constexpr int NT = PWV * 64;                              // threads
+  __shared__ float red[PWV][R][M + ND];
+  __shared__ double red_ss[PWV][R];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -84,7 +92,7 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
   const int s = blockIdx.x % S;
   const int64_t ntg = gridDim.x / S;
   float* const trash = part + static_cast<int64_t>(S) * T * PW;     // kPartTrashBytes of write-only slots
-  const int j0 = s * PRE_SLICE + 32 * w + 8 * g;
+  const int j0 = s * slice_width(PWV) + 32 * w + 8 * g;
   const bool jv = j0 < d;
 
   // This lane's rows of phi: rows i*d + j0 .. +7 of column 16 nb + r16.
@@ -231,16 +239,16 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
     // tile's wait drain the prefetch).  Items past the tile or past T go to
     // the trash slots after the records.
     constexpr int NF = R * (M + ND);
-    constexpr int FPT = (NF + PRE_THREADS - 1) / PRE_THREADS;
+    constexpr int FPT = (NF + NT - 1) / NT;
 #pragma unroll
     for (int k = 0; k < FPT; ++k) {
-      const int q = threadIdx.x + k * PRE_THREADS;
+      const int q = threadIdx.x + k * NT;
       const int qq = q < NF ? q : 0;
       const int tok = qq / (M + ND);
       const int col = qq - tok * (M + ND);
       float sum = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < PRE_WAVES; ++ww) sum += red[ww][tok][col];
+      for (int ww = 0; ww < PWV; ++ww) sum += red[ww][tok][col];
       const int64_t t = tile * R + tok;
       float* dst = (q < NF && t < T) ? part + (static_cast<int64_t>(s) * T + t) * PW + col : trash + threadIdx.x;
       *dst = sum;
@@ -249,17 +257,26 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
       const int tok = static_cast<int>(threadIdx.x) < R ? static_cast<int>(threadIdx.x) : 0;
       double sum = 0.0;
 #pragma unroll
-      for (int ww = 0; ww < PRE_WAVES; ++ww) sum += red_ss[ww][tok];
+      for (int ww = 0; ww < PWV; ++ww) sum += red_ss[ww][tok];
       const int64_t t = tile * R + tok;
       double* dst = (static_cast<int>(threadIdx.x) < R && t < T)
                         ? reinterpret_cast<double*>(part + (static_cast<int64_t>(s) * T + t) * PW + SSO)
                         : reinterpret_cast<double*>(trash) + threadIdx.x;
       *dst = sum;
     }
-    __syncthreads();
-    load_tile(tile + 2 * ntg, cur, hv);
-    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch here: the scheduler would sink it to its use
+    if constexpr (!ONE) {
+      __syncthreads();
+      load_tile(tile + 2 * ntg, cur, hv);
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch here: the scheduler would sink it to its use
+    }
   };
+
+  if constexpr (ONE) {
+    const int64_t tile = blockIdx.x / S;
+    load_tile(tile, xa, ha);
+    step(tile, xa, ha);
+    return;
+  }
 
   // Every workgroup walks the same number of tiles, an even number, and
   // every prefetch is issued unconditionally (tiles past the end read token
@@ -290,7 +307,9 @@ __global__ __launch_bounds__(PRE_THREADS) void pre_partial_kernel(int64_t T, int
 // group 0 writes H.  Lanes past d work on the last chunk again and store
 // the same values to the same place, so no load or store sits behind a
 // branch and the compiler keeps both passes in flight.
-template <typename ST, int N, bool HC>
+// SPG: slices per 16-lane group held in registers (the group sums slices
+// q, q+4, ...; S <= 4 SPG take no further loop).
+template <typename ST, int N, bool HC, int SPG>
 __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S,
                                                          const typename ST::elem* __restrict__ X,
                                                          const float* __restrict__ part,
@@ -331,7 +350,6 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
   const int q = lane >> 4;
   const bool er = e < NN, eg = e < 2 * N;
   const int cr = er ? colr : 0, cg = eg ? colg : 0;
-  constexpr int SPG = 4;                      // slices per group in registers: S <= 16
   double pss[SPG];
   float pzr[SPG], pzg[SPG];
 #pragma unroll
@@ -354,7 +372,7 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
     zr += sv ? static_cast<double>(pzr[k]) : 0.0;
     zg += sv ? static_cast<double>(pzg[k]) : 0.0;
   }
-  for (int s = q + 4 * SPG; s < S; s += 4) {     // d > 4096 only
+  for (int s = q + 4 * SPG; s < S; s += 4) {     // more slices than the registers hold (large d)
     const float* P = part + (static_cast<int64_t>(s) * T + t) * PW;
     ss += *reinterpret_cast<const double*>(P + SSO);
     zr += P[cr];
@@ -428,35 +446,62 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
   if (p + 1 < npass) emit(p + 1, xb);
 }
 
-int num_slices(int d) { return (d + PRE_SLICE - 1) / PRE_SLICE; }
+int num_slices(int d, int waves = PRE_WAVES) { return (d + slice_width(waves) - 1) / slice_width(waves); }
+
+// The forward's small-T form: when the persistent form would launch fewer
+// than 128 workgroups (32-token tiles x slices of 256), slices of 64
+// positions and one 16-token tile per workgroup.  A function of T and d
+// only, so the workspace size is too.
+bool small_t_form(int64_t T, int d) { return ((T + 31) / 32) * num_slices(d) < 128; }
+int forward_slices(int64_t T, int d) { return small_t_form(T, d) ? num_slices(d, SMALL_WAVES) : num_slices(d); }
 
 // The finishing pass, in the form of the maps p asks for.
-template <typename ST, int N>
-hipError_t launch_finish(const mhc_params& p, const void* X, const float* part, const float* bias, void* h, float* H,
-                         hipStream_t stream) {
+template <typename ST, int N, bool HC>
+hipError_t launch_finish_t(const mhc_params& p, int S, const void* X, const float* part, const float* bias, void* h,
+                           float* H, hipStream_t stream) {
   typedef typename ST::elem E;
-  const int S = num_slices(p.d);
-  const int64_t blocks = (p.T + 3) / 4;
-  if (p.maps == MHC_MAPS_HC)
-    hipLaunchKernelGGL((pre_finish_kernel<ST, N, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       p.T, p.d, S, static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post,
-                       p.eps, p.t_max, static_cast<E*>(h), H);
+  const dim3 grid(static_cast<unsigned>((p.T + 3) / 4));
+  if (S <= 16)
+    hipLaunchKernelGGL((pre_finish_kernel<ST, N, HC, 4>), grid, dim3(256), 0, stream, p.T, p.d, S,
+                       static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post, p.eps, p.t_max,
+                       static_cast<E*>(h), H);
   else
-    hipLaunchKernelGGL((pre_finish_kernel<ST, N, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       p.T, p.d, S, static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post,
-                       p.eps, p.t_max, static_cast<E*>(h), H);
+    hipLaunchKernelGGL((pre_finish_kernel<ST, N, HC, 16>), grid, dim3(256), 0, stream, p.T, p.d, S,
+                       static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post, p.eps, p.t_max,
+                       static_cast<E*>(h), H);
   return hipGetLastError();
+}
+
+// The finishing pass over S slices' records, in the form of the maps p asks for.
+template <typename ST, int N>
+hipError_t launch_finish(const mhc_params& p, int S, const void* X, const float* part, const float* bias, void* h,
+                         float* H, hipStream_t stream) {
+  return p.maps == MHC_MAPS_HC ? launch_finish_t<ST, N, true>(p, S, X, part, bias, h, H, stream)
+                               : launch_finish_t<ST, N, false>(p, S, X, part, bias, h, H, stream);
 }
 
 template <typename ST, int N>
 hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
                         void* workspace, const DeviceInfo& dev, hipStream_t stream) {
   typedef typename ST::elem E;
+  float* part = static_cast<float*>(workspace);
+  if (small_t_form(p.T, p.d)) {
+    // Few tokens: one 16-token tile per workgroup, slices of 64 positions.
+    constexpr int MB = 1;
+    const int S = num_slices(p.d, SMALL_WAVES);
+    const int64_t ntiles = (p.T + 16 * MB - 1) / (16 * MB);
+    hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 0, SMALL_WAVES, true>), dim3(static_cast<unsigned>(S * ntiles)),
+                       dim3(SMALL_WAVES * 64), 0, stream, p.T, p.d, S, ntiles, static_cast<const E*>(X),
+                       static_cast<const E*>(nullptr), phi, part, static_cast<const float*>(nullptr),
+                       static_cast<E*>(nullptr));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_finish<ST, N>(p, S, X, part, bias, h, H, stream);
+  }
   constexpr int MB = 2;                  // 32-token tiles: two in flight fit the registers
   constexpr int R = 16 * MB;
   const int S = num_slices(p.d);
   const int64_t ntiles = (p.T + R - 1) / R;
-  float* part = static_cast<float*>(workspace);
   int64_t groups = dev.num_cus / S;
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
@@ -466,7 +511,7 @@ hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, co
                      static_cast<const float*>(nullptr), static_cast<E*>(nullptr));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_finish<ST, N>(p, X, part, bias, h, H, stream);
+  return launch_finish<ST, N>(p, S, X, part, bias, h, H, stream);
 }
 
 // mhc_post of the previous layer fused into the partial pass (MODE 2), then
@@ -479,9 +524,21 @@ hipError_t launch_post_pre_t(const mhc_params& p, const void* X, const void* Y, 
   typedef typename ST::elem E;
   constexpr int MB = 1;
   constexpr int R = 16 * MB;
+  float* part = static_cast<float*>(workspace);
+  if (small_t_form(p.T, p.d)) {
+    // The small-T form, as mhc_pre takes it: the same slices and records, so
+    // the results stay bitwise those of the separate calls.
+    const int S = num_slices(p.d, SMALL_WAVES);
+    const int64_t ntiles = (p.T + R - 1) / R;
+    hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 2, SMALL_WAVES, true>), dim3(static_cast<unsigned>(S * ntiles)),
+                       dim3(SMALL_WAVES * 64), 0, stream, p.T, p.d, S, ntiles, static_cast<const E*>(X),
+                       static_cast<const E*>(Y), phi, part, Hprev, static_cast<E*>(Xout));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_finish<ST, N>(p, S, Xout, part, bias, h, H, stream);
+  }
   const int S = num_slices(p.d);
   const int64_t ntiles = (p.T + R - 1) / R;
-  float* part = static_cast<float*>(workspace);
   int64_t groups = dev.num_cus / S;
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
@@ -491,7 +548,7 @@ hipError_t launch_post_pre_t(const mhc_params& p, const void* X, const void* Y, 
                      Hprev, static_cast<E*>(Xout));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_finish<ST, N>(p, Xout, part, bias, h, H, stream);
+  return launch_finish<ST, N>(p, S, Xout, part, bias, h, H, stream);
 }
 
 template <typename ST>
@@ -570,7 +627,12 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
 }
 
 size_t pre_workspace_bytes(int64_t T, int n, int d) {
-  const size_t two_pass = pre_partial_bytes(T, n, d, false);
+  size_t two_pass = pre_partial_bytes(T, n, d, false);   // persistent form (also mhc_post_pre's)
+  if (small_t_form(T, d)) {
+    const size_t small = static_cast<size_t>(num_slices(d, SMALL_WAVES)) * static_cast<size_t>(T) *
+                             static_cast<size_t>(part_width(n)) * sizeof(float) + kPartTrashBytes;
+    if (small > two_pass) two_pass = small;
+  }
   const size_t one_pass = pre_fused_workspace_bytes(T, n, d);
   return two_pass > one_pass ? two_pass : one_pass;
 }

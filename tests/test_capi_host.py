@@ -100,6 +100,8 @@ def test_workspace_size_formula(lib):
         slices = -(-d // 256)
         width = ((n * n + 2 * n + 1) & ~1) + 2          # m fp32 partials, then an aligned fp64
         two_pass = slices * T * width * 4 + 512 * 16    # records + write-only trash slots (16 B per thread)
+        if -(-T // 32) * slices < 128:                  # small-T form: slices of 64 positions
+            two_pass = max(two_pass, -(-d // 64) * T * width * 4 + 512 * 16)
         # one pass: header, 16 start words per team, then per team 4 ring slots of 16-token
         # records (m + 2 words per member and token) and n H_pre words per token, 8 B a word;
         # room for 8 XCDs x floor(48 / slices) teams
