@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmhc.so")
-SOURCES = ["capi.cpp", "pre.hip", "pre_fused.hip", "post.hip", "amax.hip", "bwd.hip"]
+SOURCES = ["capi.cpp", "pre.hip", "pre8.hip", "pre_fused.hip", "post.hip", "amax.hip", "bwd.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

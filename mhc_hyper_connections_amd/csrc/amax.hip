@@ -107,6 +107,7 @@ hipError_t launch_amax(int64_t T, int n, int L, const float* Hs, float* amax, fl
     case 1: hipLaunchKernelGGL(amax_kernel<1>, dim3(blocks), dim3(256), 0, stream, T, L, Hs, amax, gfwd, gbwd, comp); break;
     case 2: hipLaunchKernelGGL(amax_kernel<2>, dim3(blocks), dim3(256), 0, stream, T, L, Hs, amax, gfwd, gbwd, comp); break;
     case 4: hipLaunchKernelGGL(amax_kernel<4>, dim3(blocks), dim3(256), 0, stream, T, L, Hs, amax, gfwd, gbwd, comp); break;
+    case 8: hipLaunchKernelGGL(amax_kernel<8>, dim3(blocks), dim3(256), 0, stream, T, L, Hs, amax, gfwd, gbwd, comp); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -39,7 +39,7 @@ mhc_status check_params(const mhc_params* p) {
     return MHC_ERR_SHAPE;
   if (p->dtype != MHC_FP32 && p->dtype != MHC_BF16) return MHC_ERR_DTYPE;
   if (p->maps != MHC_MAPS_MHC && p->maps != MHC_MAPS_HC) return MHC_ERR_SHAPE;
-  if (p->n != 1 && p->n != 2 && p->n != 4) return MHC_ERR_UNSUPPORTED;
+  if (p->n != 1 && p->n != 2 && p->n != 4 && p->n != 8) return MHC_ERR_UNSUPPORTED;
   if (p->d % 8 != 0) return MHC_ERR_UNSUPPORTED;
   // Element counts must fit comfortably in 64-bit byte offsets.
   const double elems = static_cast<double>(p->T) * p->n * p->d;
@@ -87,7 +87,7 @@ const char* mhc_status_string(mhc_status s) {
     case MHC_ERR_SHAPE: return "a size or hyperparameter is out of range";
     case MHC_ERR_DTYPE: return "unknown state dtype (expected MHC_FP32 or MHC_BF16)";
     case MHC_ERR_ALIGN: return "a tensor base pointer is not 16-byte aligned";
-    case MHC_ERR_UNSUPPORTED: return "shape not supported on the device (n must be 1, 2 or 4; d a multiple of 8)";
+    case MHC_ERR_UNSUPPORTED: return "shape not supported (n must be 1, 2, 4 or 8, the backward n <= 4; d a multiple of 8)";
     case MHC_ERR_ALIAS: return "an output overlaps an input";
     case MHC_ERR_WORKSPACE: return "workspace missing or too small";
     case MHC_ERR_HIP: return "a HIP call or kernel launch failed";
@@ -194,6 +194,7 @@ mhc_status mhc_post_bwd(const mhc_params* p, const void* X, const void* Y, const
   mhc_status st = check_params(p);
   if (st != MHC_OK) return st;
   if (p->T == 0) return MHC_OK;
+  if (p->n > 4) return MHC_ERR_UNSUPPORTED;
   if (!X || !Y || !H || !G || !dX || !dY || !dH) return MHC_ERR_NULL;
   if (!aligned16(X) || !aligned16(Y) || !aligned16(H) || !aligned16(G) || !aligned16(dX) || !aligned16(dY) ||
       !aligned16(dH))
@@ -215,7 +216,7 @@ mhc_status mhc_post_bwd(const mhc_params* p, const void* X, const void* Y, const
 }
 
 size_t mhc_pre_bwd_workspace_size(const mhc_params* p) {
-  if (check_params(p) != MHC_OK) return 0;
+  if (check_params(p) != MHC_OK || p->n > 4) return 0;
   return mhc::pre_bwd_workspace_bytes(p->T, p->n, p->d, p->dtype);
 }
 
@@ -224,7 +225,7 @@ mhc_status mhc_pre_bwd(const mhc_params* p, const void* X, const float* phi, con
                        size_t workspace_bytes, void* stream) {
   mhc_status st = check_params(p);
   if (st != MHC_OK) return st;
-  if (p->t_max > mhc::pre_bwd_max_tmax() || p->maps != MHC_MAPS_MHC) return MHC_ERR_UNSUPPORTED;
+  if (p->n > 4 || p->t_max > mhc::pre_bwd_max_tmax() || p->maps != MHC_MAPS_MHC) return MHC_ERR_UNSUPPORTED;
   if (!dphi || !dbias || !dalpha) return MHC_ERR_NULL;
   if (p->T > 0 && (!X || !phi || !bias || !D || !dH || !dX)) return MHC_ERR_NULL;
   const size_t need = mhc::pre_bwd_workspace_bytes(p->T, p->n, p->d, p->dtype);
@@ -257,7 +258,7 @@ mhc_status mhc_pre_bwd(const mhc_params* p, const void* X, const float* phi, con
 mhc_status mhc_amax(int64_t T, int32_t n, int32_t L, const float* H_stack, float* amax, float* gain_fwd,
                     float* gain_bwd, float* composite, void* stream) {
   if (T < 0 || T > kMaxT || n < 1 || n > 16 || L < 0) return MHC_ERR_SHAPE;
-  if (n != 1 && n != 2 && n != 4) return MHC_ERR_UNSUPPORTED;
+  if (n != 1 && n != 2 && n != 4 && n != 8) return MHC_ERR_UNSUPPORTED;
   if (T == 0) return MHC_OK;
   if (L > 0 && !H_stack) return MHC_ERR_NULL;
   if (!amax && !gain_fwd && !gain_bwd && !composite) return MHC_ERR_NULL;

@@ -32,6 +32,12 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
                            const float* phi, const float* bias, void* h, float* H, void* workspace, const DeviceInfo& dev,
                            hipStream_t stream);
 
+// mhc_pre for n = 8 (pre8.hip): split-K over 64-position slices, then one
+// token per wave.
+size_t pre8_workspace_bytes(int64_t T, int d);
+hipError_t launch_pre8(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
+                       void* workspace, const DeviceInfo& dev, hipStream_t stream);
+
 // The single-pass form (pre_fused.hip): hipErrorNotSupported when it does not apply.
 size_t pre_fused_workspace_bytes(int64_t T, int n, int d);
 bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev);   // what MHC_PRE_AUTO picks

@@ -84,7 +84,7 @@ template <typename ST, int N>
 hipError_t launch_post_t(const mhc_params& p, const void* X, const void* Y, const float* H, void* Xo,
                          hipStream_t stream) {
   typedef typename ST::elem E;
-  constexpr int IPT = 2;
+  constexpr int IPT = N >= 8 ? 1 : 2;   // chunks per thread in flight
   const int d8 = p.d / 8;
   const int64_t nchunks = p.T * d8;
   const int64_t per_block = static_cast<int64_t>(POST_THREADS) * IPT;
@@ -110,6 +110,7 @@ hipError_t launch_post_n(const mhc_params& p, const void* X, const void* Y, cons
     case 1: return launch_post_t<ST, 1>(p, X, Y, H, Xo, stream);
     case 2: return launch_post_t<ST, 2>(p, X, Y, H, Xo, stream);
     case 4: return launch_post_t<ST, 4>(p, X, Y, H, Xo, stream);
+    case 8: return launch_post_t<ST, 8>(p, X, Y, H, Xo, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -43,14 +43,6 @@ __host__ __device__ constexpr int slice_width(int waves) { return 32 * waves; }
 // items past the end (16 bytes per thread).
 constexpr size_t kPartTrashBytes = PRE_THREADS * 16;
 
-// Per-token record of one slice in the workspace: m fp32 partial dot
-// products (then, for the backward, n more: <D, X_i> over the slice), then
-// the partial sum of squares as an fp64 at an 8-byte aligned float offset.
-__host__ __device__ constexpr int ss_offset(int n, bool with_d = false) {
-  return (num_maps(n) + (with_d ? n : 0) + 1) & ~1;
-}
-__host__ __device__ constexpr int part_width(int n, bool with_d = false) { return ss_offset(n, with_d) + 2; }
-
 // MODE 0: the forward's projection partials of X.
 // MODE 1: the backward's: also <D, X_i> per stream (Dg = D).
 // MODE 2: the previous layer's mhc_post fused in front: X is X_l, Dg is
@@ -558,6 +550,7 @@ hipError_t launch_pre_n(const mhc_params& p, const void* X, const float* phi, co
     case 1: return launch_pre_t<ST, 1>(p, X, phi, bias, h, H, ws, dev, stream);
     case 2: return launch_pre_t<ST, 2>(p, X, phi, bias, h, H, ws, dev, stream);
     case 4: return launch_pre_t<ST, 4>(p, X, phi, bias, h, H, ws, dev, stream);
+    case 8: return launch_pre8(p, X, phi, bias, h, H, ws, dev, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -616,7 +609,7 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
                       : launch_post_pre_t<F32, 2>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream);
     case 4: return bf ? launch_post_pre_t<BF16, 4>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream)
                       : launch_post_pre_t<F32, 4>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream);
-    default: {   // n = 1: m = 3 maps per token; the two entry points one after the other
+    default: {   // n = 1 (m = 3 maps per token) and n = 8: the two entry points one after the other
       hipError_t e = launch_post(p, X, Y, Hprev, Xout, stream);
       if (e != hipSuccess) return e;
       int used = 0;
@@ -627,6 +620,7 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
 }
 
 size_t pre_workspace_bytes(int64_t T, int n, int d) {
+  if (n == 8) return pre8_workspace_bytes(T, d);
   size_t two_pass = pre_partial_bytes(T, n, d, false);   // persistent form (also mhc_post_pre's)
   if (small_t_form(T, d)) {
     const size_t small = static_cast<size_t>(num_slices(d, SMALL_WAVES)) * static_cast<size_t>(T) *

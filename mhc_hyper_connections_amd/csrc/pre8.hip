@@ -1,0 +1,334 @@
+// mhc_pre for n = 8 streams: m = n^2 + 2n = 80 maps per token and a 64-entry
+// Sinkhorn-Knopp.  Same method as pre.hip ("mHC" notes on DeepSeek-V4, eqs.
+// dsv4-mhc-rmsnorm, a/b/c-tilde, sinkhorn-init, sinkhorn, gate; Dubrov,
+// "DeepSeek mHC: Manifold-Constrained Hyper-Connections", Eq. 3 and section
+// "Kernmechanismen" for the unconstrained HC maps), in two passes:
+//  1. pre_partial8_kernel -- persistent split-K projection.  At n = 8 a
+//     lane cannot hold its rows of phi for all 80 columns and all streams
+//     (8 streams x 5 column blocks x hi/lo = 320 registers), so a
+//     workgroup's eight waves split the contraction by stream: wave w takes
+//     streams 2 (w % 4) and 2 (w % 4) + 1 of position group w / 4 (32
+//     positions) of the workgroup's 64-position slice and keeps those rows
+//     of phi for all 80 columns in registers (80).  Every wave reads its own
+//     part of the X tile (16 tokens x 2 streams x 32 positions).  The eight
+//     waves' partials are added in LDS in wave order and written as the same
+//     per-token records as n <= 4 (m partials, fp64 sum of squares).
+//  2. pre_finish8_kernel -- one token per wave, one Sinkhorn entry per lane:
+//     sums the slices in order (fp64), forms r, the logits, the gates and
+//     Sinkhorn (column sums over lanes e ^ 8, 16, 32; row sums over e ^ 1,
+//     2, 4), writes H and streams h = H_pre . X.
+#include "launch.hpp"
+#include "pre_common.hpp"
+
+namespace mhc {
+namespace {
+
+constexpr int P8_N = 8;
+constexpr int P8_M = num_maps(P8_N);          // 80
+constexpr int P8_CB = P8_M / 16;              // 16-column blocks
+constexpr int P8_SP = P8_N / 2;               // stream pairs
+constexpr int P8_PG = 2;                      // position groups of 32
+constexpr int P8_WAVES = P8_SP * P8_PG;       // 8
+constexpr int P8_THREADS = P8_WAVES * 64;
+constexpr int P8_SLICE = 32 * P8_PG;          // positions of d per slice
+constexpr int P8_R = 16;                      // tokens per tile
+constexpr size_t kP8TrashBytes = P8_THREADS * 16;   // write-only slots after the records
+
+// DB: two tile buffers in flight (bf16 state); fp32 state keeps one buffer.
+// Either way a buffer is reloaded as soon as it has been multiplied.
+template <typename ST, bool DB>
+__global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int d, int S, int64_t ntiles,
+                                                                  const typename ST::elem* X,
+                                                                  const float* __restrict__ phi,
+                                                                  float* __restrict__ part) {
+  constexpr int N = P8_N, M = P8_M;
+  constexpr int PW = part_width(N);
+  constexpr int SSO = ss_offset(N);
+  __shared__ float red[P8_WAVES][P8_R][M];
+  __shared__ double red_ss[P8_WAVES][P8_R];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int sp = w % P8_SP;
+  const int pg = w / P8_SP;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int s = blockIdx.x % S;
+  const int64_t ntg = gridDim.x / S;
+  float* const trash = part + static_cast<int64_t>(S) * T * PW;
+  const int j0 = s * P8_SLICE + 32 * pg + 8 * g;
+  const bool jv = j0 < d;
+  const int jl = jv ? j0 : 0;
+
+  // This lane's rows of phi: rows i*d + j0 .. +7 (streams i = 2 sp, 2 sp + 1)
+  // of column 16 b + r16, every column block b.
+  PhiOp<ST> bop[2][P8_CB];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = 2 * sp + q;
+#pragma unroll
+    for (int b = 0; b < P8_CB; ++b) {
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        f[e] = jv ? phi[static_cast<int64_t>(i * d + j0 + e) * M + 16 * b + r16] : 0.0f;
+      bop[q][b] = make_phi_op(f, ST{});
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Unconditional loads from valid addresses: tokens past T read token 0,
+  // lanes past d read position 0 (zero phi rows; squares dropped).
+  auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[2]) {
+    const int64_t t = tile * P8_R + r16;
+    const int64_t tt = t < T ? t : 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) x[q] = load_raw8<ST>(X + (tt * N + 2 * sp + q) * d + jl);
+  };
+
+  auto step = [&](int64_t tile, Raw8<ST> (&cur)[2], int64_t next) {
+    f32x4 acc[P8_CB];
+#pragma unroll
+    for (int b = 0; b < P8_CB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int b = 0; b < P8_CB; ++b) acc[b] = mfma_block(cur[q], bop[q][b], acc[b]);
+    // Sum of squares of this lane's 2 x 8 values; lanes r16 + 16 g hold token r16.
+    double sq = 0.0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float x[8];
+      unpack8(cur[q], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), sq);
+    }
+    sq = jv ? sq : 0.0;
+    sq += __shfl_xor(sq, 16);
+    sq += __shfl_xor(sq, 32);
+    // The buffer is free once multiplied: the next tile's loads go out now.
+    load_tile(next, cur);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < P8_CB; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[w][4 * g + v][16 * b + r16] = acc[b][v];
+    if (g == 0) red_ss[w][r16] = sq;
+    __syncthreads();
+    // Records out: the eight waves' partials added in wave order, a fixed
+    // number of stores per thread (items past the tile or past T go to the
+    // write-only slots).
+    constexpr int NF = P8_R * M;
+    constexpr int FPT = (NF + P8_THREADS - 1) / P8_THREADS;
+#pragma unroll
+    for (int k = 0; k < FPT; ++k) {
+      const int q = threadIdx.x + k * P8_THREADS;
+      const int qq = q < NF ? q : 0;
+      const int tok = qq / M;
+      const int c = qq - tok * M;
+      float sum = red[0][tok][c];
+#pragma unroll
+      for (int ww = 1; ww < P8_WAVES; ++ww) sum += red[ww][tok][c];
+      const int64_t t = tile * P8_R + tok;
+      float* dst = (q < NF && t < T) ? part + (static_cast<int64_t>(s) * T + t) * PW + c : trash + threadIdx.x;
+      *dst = sum;
+    }
+    {
+      const int tok = static_cast<int>(threadIdx.x) < P8_R ? static_cast<int>(threadIdx.x) : 0;
+      double sum = red_ss[0][tok];
+#pragma unroll
+      for (int ww = 1; ww < P8_WAVES; ++ww) sum += red_ss[ww][tok];
+      const int64_t t = tile * P8_R + tok;
+      double* dst = (static_cast<int>(threadIdx.x) < P8_R && t < T)
+                        ? reinterpret_cast<double*>(part + (static_cast<int64_t>(s) * T + t) * PW + SSO)
+                        : reinterpret_cast<double*>(trash) + threadIdx.x;
+      *dst = sum;
+    }
+    __syncthreads();
+  };
+
+  // Every workgroup walks the same, even number of tiles; prefetches past
+  // the end read token 0 and write nothing (see pre.hip).
+  const int64_t tile0 = blockIdx.x / S;
+  const int64_t per_wg = (ntiles + ntg - 1) / ntg;
+  Raw8<ST> xa[2];
+  load_tile(tile0, xa);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (DB) {
+    Raw8<ST> xb[2];
+    load_tile(tile0 + ntg, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    int64_t k = 0;
+    do {
+      step(tile0 + k * ntg, xa, tile0 + (k + 2) * ntg);
+      step(tile0 + (k + 1) * ntg, xb, tile0 + (k + 3) * ntg);
+      k += 2;
+    } while (k < per_wg);
+  } else {
+    int64_t k = 0;
+    do {
+      step(tile0 + k * ntg, xa, tile0 + (k + 1) * ntg);
+      k += 1;
+    } while (k < per_wg);
+  }
+}
+
+// Sinkhorn-Knopp on one token's 8 x 8 map held by a whole wave: lane e owns
+// entry (e / 8, e % 8).  Column sums add lanes e ^ 8, 16, 32, row sums
+// e ^ 1, 2, 4 (a butterfly: every lane of a line holds the same bits).  The
+// token's largest logit is subtracted first (unchanged iterates, finite exp).
+__device__ __forceinline__ float sinkhorn64(float lr, int t_max) {
+  float mx = lr;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (t_max == 0) mx = 0.0f;
+  float mv = expf(lr - mx);
+  for (int it = 0; it < t_max; ++it) {
+    float cs = mv;
+    cs += __shfl_xor(cs, 8);
+    cs += __shfl_xor(cs, 16);
+    cs += __shfl_xor(cs, 32);
+    mv = mv / cs;
+    float rs = mv;
+    rs += __shfl_xor(rs, 1);
+    rs += __shfl_xor(rs, 2);
+    rs += __shfl_xor(rs, 4);
+    mv = mv / rs;
+  }
+  return mv;
+}
+
+// One token per wave.  Lane e: residual entry e (column 8 + e); lanes e < 16
+// also the gate of column e (pre) or 72 + e - 8 (post).
+template <typename ST, bool HC>
+__global__ __launch_bounds__(256) void pre_finish8_kernel(int64_t T, int d, int S, const typename ST::elem* __restrict__ X,
+                                                          const float* __restrict__ part,
+                                                          const float* __restrict__ bias, float a_pre, float a_res,
+                                                          float a_post, float eps, int t_max,
+                                                          typename ST::elem* __restrict__ h, float* __restrict__ H) {
+  constexpr int N = P8_N, M = P8_M, NN = N * N;
+  constexpr int PW = part_width(N);
+  constexpr int SSO = ss_offset(N);
+  const int e = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                                        // wave-uniform
+  const int colr = N + e;
+  const bool eg = e < 2 * N;
+  const int colg = (e < N) ? e : (eg ? N + NN + (e - N) : 0);
+
+  // Sums over the slices in order, 8 slices' loads at a time.
+  double ss = 0.0, zr = 0.0, zg = 0.0;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    double pss[8];
+    float pzr[8], pzg[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = s0 + k < S ? s0 + k : 0;
+      const float* P = part + (static_cast<int64_t>(s) * T + t) * PW;
+      pss[k] = *reinterpret_cast<const double*>(P + SSO);
+      pzr[k] = P[colr];
+      pzg[k] = P[colg];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k < S) {
+        ss += pss[k];
+        zr += static_cast<double>(pzr[k]);
+        zg += static_cast<double>(pzg[k]);
+      }
+    }
+  }
+  const double inv_r = inv_rms(ss, N * d, eps);
+  float gv = 0.0f, mv;
+  if constexpr (HC) {
+    if (eg)
+      gv = static_cast<float>(static_cast<double>(bias[colg]) +
+                              static_cast<double>((e < N) ? a_pre : a_post) * tanh(zg * inv_r));
+    mv = static_cast<float>(static_cast<double>(bias[colr]) + static_cast<double>(a_res) * tanh(zr * inv_r));
+  } else {
+    if (eg) {
+      const float l = logit_of(zg, inv_r, (e < N) ? a_pre : a_post, bias[colg]);
+      gv = (e < N) ? sigmoidf_(l) : 2.0f * sigmoidf_(l);
+    }
+    mv = sinkhorn64(logit_of(zr, inv_r, a_res, bias[colr]), t_max);
+  }
+  float* Ht = H + t * M;
+  Ht[colr] = mv;
+  if (eg) Ht[colg] = gv;
+  float hp[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) hp[i] = __shfl(gv, i);
+
+  // h = H_pre . X over passes of 64 lanes x 8 positions.
+  const typename ST::elem* Xt = X + t * N * static_cast<int64_t>(d);
+  typename ST::elem* ht = h + t * static_cast<int64_t>(d);
+  for (int j = e * 8; j < d; j += 512) {
+    Raw8<ST> x[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = load_raw8<ST, true>(Xt + static_cast<int64_t>(i) * d + j);
+    float o[8];
+    {
+      float v[8];
+      unpack8(x[0], v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = hp[0] * v[k];
+    }
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+      float v[8];
+      unpack8(x[i], v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = fmaf(hp[i], v[k], o[k]);
+    }
+    store8<ST, true>(ht + j, o);
+  }
+}
+
+int slices8(int d) { return (d + P8_SLICE - 1) / P8_SLICE; }
+
+template <typename ST>
+hipError_t launch_pre8_t(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
+                         void* workspace, const DeviceInfo& dev, hipStream_t stream) {
+  typedef typename ST::elem E;
+  constexpr bool DB = sizeof(E) == 2;
+  const int S = slices8(p.d);
+  const int64_t ntiles = (p.T + P8_R - 1) / P8_R;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(pre_partial8_kernel<ST, DB>),
+                                                   P8_THREADS, 0) != hipSuccess || occ < 1)
+    occ = 1;
+  int64_t groups = static_cast<int64_t>(dev.num_cus) * occ / S;
+  if (groups < 1) groups = 1;
+  if (groups > ntiles) groups = ntiles;
+  float* part = static_cast<float*>(workspace);
+  hipLaunchKernelGGL((pre_partial8_kernel<ST, DB>), dim3(static_cast<unsigned>(groups * S)), dim3(P8_THREADS), 0,
+                     stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), phi, part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const dim3 grid(static_cast<unsigned>((p.T + 3) / 4));
+  if (p.maps == MHC_MAPS_HC)
+    hipLaunchKernelGGL((pre_finish8_kernel<ST, true>), grid, dim3(256), 0, stream, p.T, p.d, S,
+                       static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post, p.eps, p.t_max,
+                       static_cast<E*>(h), H);
+  else
+    hipLaunchKernelGGL((pre_finish8_kernel<ST, false>), grid, dim3(256), 0, stream, p.T, p.d, S,
+                       static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post, p.eps, p.t_max,
+                       static_cast<E*>(h), H);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t pre8_workspace_bytes(int64_t T, int d) {
+  return static_cast<size_t>(slices8(d)) * static_cast<size_t>(T) * static_cast<size_t>(part_width(P8_N)) *
+             sizeof(float) + kP8TrashBytes;
+}
+
+hipError_t launch_pre8(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
+                       void* workspace, const DeviceInfo& dev, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  if (p.dtype == MHC_BF16) return launch_pre8_t<BF16>(p, X, phi, bias, h, H, workspace, dev, stream);
+  return launch_pre8_t<F32>(p, X, phi, bias, h, H, workspace, dev, stream);
+}
+
+}  // namespace mhc

@@ -9,6 +9,14 @@ namespace mhc {
 
 __host__ __device__ constexpr int num_maps(int n) { return n * n + 2 * n; }
 
+// Per-token record of one slice of d in a split-K workspace: m fp32 partial
+// dot products (then, for the backward, n more: <D, X_i> over the slice),
+// then the partial sum of squares as an fp64 at an 8-byte aligned float offset.
+__host__ __device__ constexpr int ss_offset(int n, bool with_d = false) {
+  return (num_maps(n) + (with_d ? n : 0) + 1) & ~1;
+}
+__host__ __device__ constexpr int part_width(int n, bool with_d = false) { return ss_offset(n, with_d) + 2; }
+
 // MFMA B operand for one (stream, 16-column block): 8 rows of phi per lane.
 // bf16 state: phi = hi + lo, two bf16 halves (~16 significant bits); fp32
 // state: phi itself for the fp32 MFMA.

@@ -286,7 +286,7 @@ def _naive_layer(X, Y, phi, bias, alpha, eps, t_max):
 def pin_bruteforce_tiny_layers(o):
     """Whole layer on tiny shapes against the independent formulation."""
     rng = np.random.default_rng(17)
-    for n in (1, 2, 3, 4):
+    for n in (1, 2, 3, 4, 8):
         for d in (1, 3, 8):
             for alpha in ((0.01, 0.01, 0.01), (1.0, 0.7, -0.4)):
                 T = 3

@@ -110,6 +110,10 @@ def test_workspace_size_formula(lib):
         slot = slices * 16 * record + 16 * n
         one_pass = 256 + teams * 16 * 8 + teams * 4 * slot * 8 if 8 <= slices <= 16 else 0
         assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == max(two_pass, one_pass)
+    for (T, d) in ((64, 256), (1, 8), (4096, 4104)):
+        # n = 8: records of 80 partials + an fp64 over slices of 64 positions, plus trash slots
+        p = _params(T=T, n=8, d=d)
+        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == -(-d // 64) * T * 82 * 4 + 512 * 16
     assert lib.mhc_pre_workspace_size(None) == 0
     assert lib.mhc_pre_workspace_size(ctypes.byref(_params(n=3))) == 0
 
@@ -128,6 +132,8 @@ def test_post_argument_checks(lib):
 
 def test_amax_and_gelu_argument_checks(lib):
     assert lib.mhc_amax(10, 3, 5, A[0], A[1], None, None, None, None) == 5
+    assert lib.mhc_amax(10, 16, 5, A[0], A[1], None, None, None, None) == 5
+    assert lib.mhc_amax(10, 8, 5, A[0], A[0], None, None, None, None) == 6   # n = 8 passes the shape checks
     assert lib.mhc_amax(-1, 4, 5, A[0], A[1], None, None, None, None) == 2
     assert lib.mhc_amax(10, 4, -1, A[0], A[1], None, None, None, None) == 2
     assert lib.mhc_amax(10, 4, 5, None, A[1], None, None, None, None) == 1
@@ -157,6 +163,7 @@ def test_post_bwd_argument_checks(lib):
         lib.mhc_post_bwd(ctypes.byref(p), X, Y, H, G, dX, dY, dH, None)
     assert lib.mhc_post_bwd(None, *A[:7], None) == 1
     assert f(_params(n=3)) == 5
+    assert f(_params(n=8)) == 5                        # the backward covers n <= 4
     assert f(p, G=None) == 1
     assert f(p, dH=A[6] + 4) == 4
     assert f(p, dX=A[3]) == 6                         # dX onto G
@@ -175,6 +182,8 @@ def test_pre_bwd_argument_checks(lib):
         nb = lib.mhc_pre_bwd_workspace_size(ctypes.byref(p)) if ws_bytes is None else ws_bytes
         return lib.mhc_pre_bwd(ctypes.byref(p), X, phi, bias, D, dH, dX, dphi, dbias, dalpha, ws, nb, None)
     assert f(_params(n=3)) == 5
+    assert f(_params(n=8)) == 5                        # the backward covers n <= 4
+    assert lib.mhc_pre_bwd_workspace_size(ctypes.byref(_params(n=8))) == 0
     assert f(_params(t_max=129)) == 5                  # Sinkhorn iterates beyond the backward's LDS budget
     assert f(p, D=None) == 1
     assert f(p, ws=None) == 7
