@@ -208,6 +208,36 @@ def traffic_bytes(path, workload, entry):
         return None
 
 
+def time_small_t(mhc, torch, reps=100):
+    """Per-call latency of mhc_pre at decode-sized T (the small-T split-K
+    form), on random inputs of the layer shapes: n = 4 bf16 at d = 4096 and
+    d = 2048, and the fp32 T = 64, d = 256 workload."""
+    out = []
+    for d, dt, T in ((4096, torch.bfloat16, 1), (4096, torch.bfloat16, 16), (4096, torch.bfloat16, 64),
+                     (2048, torch.bfloat16, 64), (256, torch.float32, 64)):
+        n, m = 4, 24
+        g = torch.Generator(device="cuda").manual_seed(T * 7 + d)
+        X = torch.randn(T, n, d, device="cuda", generator=g).to(dt)
+        phi = torch.randn(n * d, m, device="cuda", generator=g) * 0.02
+        bias = torch.randn(m, device="cuda", generator=g) * 0.1
+        code = 1 if dt == torch.bfloat16 else 0
+        ws = torch.empty(mhc.pre_workspace_size(T, n, d, code), dtype=torch.uint8, device="cuda")
+        h = torch.empty((T, d), dtype=dt, device="cuda")
+        H = torch.empty((T, m), device="cuda")
+        for _ in range(10):
+            mhc.pre_ex(X, phi, bias, 0, h=h, H=H, workspace=ws)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            mhc.pre_ex(X, phi, bias, 0, h=h, H=H, workspace=ws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        out.append({"shape": f"T={T} n=4 d={d} {'bf16' if code else 'fp32'}",
+                    "us": ev[0].elapsed_time(ev[1]) / reps * 1e3})
+    return out
+
+
 def cpu_baseline(w, seconds_target=15.0):
     """The oracle (single-threaded C++, double) on the first tokens of the
     same workload: mhc_pre + mhc_post per token."""
@@ -485,6 +515,10 @@ def main():
             forms[name] = None
     log("mhc_pre forms: " + ", ".join(f"{k} {v['avg_us']:.1f} us" for k, v in forms.items() if v))
 
+    small_t = time_small_t(mhc, torch)
+    log("mhc_pre at small T (split-K form, per call): " +
+        ", ".join(f"{r['shape']} {r['us']:.1f} us" for r in small_t))
+
     backward = None
     if not args.no_backward:
         log("timing the backward (mhc_post_bwd + mhc_pre_bwd)")
@@ -537,6 +571,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "mhc_pre_forms": forms,
+        "small_t": small_t,
         "backward": backward,
         "stack": stack,
         "cpu_baseline": cpu,

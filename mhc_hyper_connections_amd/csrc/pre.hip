@@ -168,30 +168,69 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
       }
     }
 
-    // Sum of squares in fp64: never overflows for a finite fp32 / bf16 state
-    // (fp32 overflows once the state's RMS passes ~1.8e19 / sqrt(n d)).
+    // Sum of squares.  bf16 state without D: the diagonal of the tile's
+    // 16 x 16 Gram matrix on MFMA (bf16 products are exact in fp32; fp32
+    // accumulation over the wave's 32 positions x n streams), redone in fp64
+    // for a token whose fp32 sum overflows; entry (t, t) sits in lane
+    // 16 (t / 4) + t, element t % 4, and covers the wave's 4 lane groups.
+    // Otherwise fp64 per lane, added over the 4 groups below.  Either never
+    // overflows for a finite state.
+    constexpr bool GRAM = std::is_same<ST, BF16>::value && !WITH_D;
     double ss[MB];
     float dd[MB][ND > 0 ? ND : 1];
     f32x4 acc[MB][NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       double sq = 0.0;
-      float dv[8];
-      if (WITH_D) unpack8(cur[mb][N], dv);
+      if constexpr (GRAM) {
+        f32x4 gram = {0.0f, 0.0f, 0.0f, 0.0f};
+        Raw8<ST> xm[N];
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        float x[8];
-        unpack8(cur[mb][i], x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sq = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), sq);
-        if (WITH_D) {
-          float a = 0.0f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a = fmaf(dv[e], x[e], a);
-          dd[mb][i] = jv ? a : 0.0f;
+        for (int i = 0; i < N; ++i) {
+          xm[i] = jv ? cur[mb][i] : zero_raw8<ST>();   // lanes past d hold position 0's values
+          gram = mfma_block_gram(xm[i], gram);
         }
+        const int dv = r16 & 3;
+        const float sqf = dv == 0 ? gram[0] : dv == 1 ? gram[1] : dv == 2 ? gram[2] : gram[3];
+        sq = static_cast<double>(sqf);
+        const bool ovf = g == (r16 >> 2) && !__builtin_isfinite(sqf);
+        if (__any(ovf)) {            // wave-uniform: every lane takes part in the permutes
+          double s64 = 0.0;
+          for (int q = 0; q < 4; ++q) {
+            const int src = 16 * q + r16;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+              Raw8<ST> xq;
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                xq.v[c] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * src, static_cast<int>(xm[i].v[c])));
+              float x[8];
+              unpack8(xq, x);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) s64 = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), s64);
+            }
+          }
+          if (ovf) sq = s64;
+        }
+        ss[mb] = (g == (r16 >> 2)) ? sq : 0.0;
+      } else {
+        float dv[8];
+        if (WITH_D) unpack8(cur[mb][N], dv);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          float x[8];
+          unpack8(cur[mb][i], x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sq = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), sq);
+          if (WITH_D) {
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaf(dv[e], x[e], a);
+            dd[mb][i] = jv ? a : 0.0f;
+          }
+        }
+        ss[mb] = jv ? sq : 0.0;
       }
-      ss[mb] = jv ? sq : 0.0;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -211,10 +250,14 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
           for (int v = 0; v < 4; ++v) red[w][mb * 16 + 4 * g + v][col] = acc[mb][nb][v];
         }
       }
-      double sq = ss[mb];
-      sq += __shfl_xor(sq, 16);
-      sq += __shfl_xor(sq, 32);
-      if (g == 0) red_ss[w][mb * 16 + r16] = sq;
+      if constexpr (GRAM) {
+        if (g == (r16 >> 2)) red_ss[w][mb * 16 + r16] = ss[mb];
+      } else {
+        double sq = ss[mb];
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        if (g == 0) red_ss[w][mb * 16 + r16] = sq;
+      }
       if (WITH_D) {
 #pragma unroll
         for (int i = 0; i < ND; ++i) {

@@ -51,6 +51,12 @@ __device__ __forceinline__ f32x4 mfma_block(const Raw8<BF16>& a, const PhiOp<BF1
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b.lo, acc, 0, 0, 0);
   return acc;
 }
+// acc += A . A^T for a 16 (tokens) x 32 (positions) bf16 block in the A
+// layout above: entry (t, t) is token t's sum of squares over the block.
+__device__ __forceinline__ f32x4 mfma_block_gram(const Raw8<BF16>& a, f32x4 acc) {
+  const bf16x8 av = __builtin_bit_cast(bf16x8, a.v);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, av, acc, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma_block(const Raw8<F32>& a, const PhiOp<F32>& b, f32x4 acc) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[e], b.v[e], acc, 0, 0, 0);

@@ -18,8 +18,9 @@
 //    member's slice for a tile's 16 tokens in registers (lane = token row
 //    and 8 positions, the MFMA A layout; one 16-byte load per stream).  In
 //    step k it forms tile k's m partial dot products with phi on MFMA (phi
-//    as bf16 hi + lo halves, kept in LDS) and the fp64 partial sum of
-//    squares into an LDS ring; sums its eighth of tile k-1's record over the
+//    as bf16 hi + lo halves, kept in LDS) and the partial sums of squares
+//    (the diagonal of the tile's 16 x 16 Gram matrix, also on MFMA) into an
+//    LDS ring; sums its eighth of tile k-1's record over the
 //    8 waves (wave order) and posts it with one 16-byte store; and, once
 //    tile k-OD's H_pre has come back, forms h = H_pre . X for its positions
 //    from the registers that still hold that tile, and stores it.  These
@@ -46,7 +47,9 @@
 // a fixed order: results are bitwise reproducible.  All waits are bounded;
 // one that runs out marks the workgroup broken (no further waits; results
 // invalid) and the call's sequence number is stored into the workspace's
-// error word.  The launch is cooperative (all workgroups co-resident).
+// error word.  The launch is cooperative (all workgroups co-resident).  The
+// exchange and Sinkhorn waves run at a raised issue priority: the streaming
+// waves have slack, the exchange is on every tile's critical path.
 #include <atomic>
 
 #include "launch.hpp"
@@ -65,12 +68,12 @@ constexpr int OR = 16;                  // tokens per tile
 constexpr int OS_MIN = 8;               // team size range (ceil(d / OSLICE))
 constexpr int OS_MAX = 16;
 constexpr int OTPR = (OR + OS_MIN - 1) / OS_MIN;   // most tokens a member owns per tile
-constexpr int OSLOTS = 4;               // exchange ring depth (tiles); see below
+constexpr int OSLOTS = 5;               // exchange ring depth (tiles); see below
 constexpr int ORR = 3;                  // LDS ring of partials (tiles)
-constexpr int OMR = 4;                  // LDS ring of H_pre (tiles; a slot is rewritten once its tile's h is out)
+constexpr int OMR = 5;                  // LDS ring of H_pre (tiles; a slot is rewritten once its tile's h is out)
 constexpr int OKR = 4;                  // LDS ring of Sinkhorn inputs (tiles; taken two at a time)
-constexpr int OD = 4;                   // tiles between a tile's partials and its h; see below
-constexpr int OP = 3;                   // X tiles in flight ahead of the one being multiplied
+constexpr int OD = 5;                   // tiles between a tile's partials and its h; see below
+constexpr int OP = 2;                   // X tiles in flight ahead of the one being multiplied
 constexpr int ONB = OD + OP;            // X tile buffers per lane
 constexpr size_t OHDR = 256;            // workspace header: the error word
 constexpr int OXCD = 8;                 // XCDs of the device (MI355X)
@@ -350,17 +353,20 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
     const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(a.h, 0, a.hbytes, 0x00020000);
 
     // Tile jt's partials over this wave's 32 positions into the LDS ring.
+    // Sum of squares: with A = B = the tile (16 tokens x 32 positions), the
+    // MFMA's diagonal entry (t, t) is token t's sum of squares over the
+    // wave's positions; bf16 products are exact in fp32, the accumulation
+    // over the 4 streams' 128 values is fp32, the sums across waves and
+    // members fp64.  Entry (t, t) sits in lane 16 (t / 4) + t, element t % 4.
     auto partials = [&](int jt, const u32x4 (&x)[N]) {
-      double sq = 0.0;
+      f32x4 gram = {0.0f, 0.0f, 0.0f, 0.0f};
       f32x4 acc[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < N; ++i) {
-        float v[8];
-        unpack8(Raw8<BF16>{x[i]}, v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sq = fma(static_cast<double>(v[e]), static_cast<double>(v[e]), sq);
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, x[i]);
+        gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, xv, gram, 0, 0, 0);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int cn = (M - 16 * nb < 16) ? M - 16 * nb : 16;
@@ -375,8 +381,32 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);   // read phi per stream, next to its MFMAs (registers)
       }
-      sq += __shfl_xor(sq, 16);
-      sq += __shfl_xor(sq, 32);
+      const int dv = r16 & 3;
+      const float sqf = dv == 0 ? gram[0] : dv == 1 ? gram[1] : dv == 2 ? gram[2] : gram[3];
+      double sq = static_cast<double>(sqf);
+      const bool ovf = g == (r16 >> 2) && !__builtin_isfinite(sqf);
+      if (__any(ovf)) {
+        // fp32 overflow (|x| beyond ~1e18): the token's sum again in fp64
+        // from the 4 lanes that hold its positions (lane 16 q + t holds
+        // positions 8 q .. 8 q + 7).  Wave-uniform branch: every lane
+        // takes part in the permutes.
+        double s64 = 0.0;
+        for (int q = 0; q < 4; ++q) {
+          const int src = 16 * q + r16;
+#pragma unroll
+          for (int i = 0; i < N; ++i) {
+            u32x4 xq;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              xq[c] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * src, static_cast<int>(x[i][c])));
+            float v[8];
+            unpack8(Raw8<BF16>{xq}, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s64 = fma(static_cast<double>(v[e]), static_cast<double>(v[e]), s64);
+          }
+        }
+        if (ovf) sq = s64;
+      }
       const int slot = jt % ORR;
       wait_all_ge(posted, jt - ORR + 1, vbroken, lane);   // every wave has posted the slot's last tile
 #pragma unroll
@@ -387,7 +417,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
           for (int v = 0; v < 4; ++v) red[slot][w][4 * g + v][col >> 2][col & 3] = acc[nb][v];
         }
       }
-      if (g == 0) red_ss[slot][w][r16] = sq;
+      if (g == (r16 >> 2)) red_ss[slot][w][r16] = sq;
       lds_done();
       if (lane == 0) flag_set(&part_ready[w], jt + 1);
     };
@@ -495,6 +525,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
     // Exchange wave x takes the tiles t with t % OX == x.  Meet the team
     // first: every member's slots are clear once its start word holds this
     // call's sequence number.
+    __builtin_amdgcn_s_setprio(2);
     const int xw = wave - OW;
     u64* st = a.start + static_cast<int64_t>(team) * OS_MAX;
     if (lane == 0 && xw == 0) st[s] = a.epoch;
@@ -544,6 +575,15 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
       return v;
     };
     u32x4 rsv[OTPR][NRB];
+    // Lane (o, e) of the maps: entry e of owned token o.  Its bias values are
+    // fixed per lane: loaded once, not behind the streaming loads every tile.
+    const int o = lane >> 4;
+    const int e = lane & 15;
+    const int colr = N + e;
+    const int colg = (e < N) ? e : (N + NN + (e - N));
+    const int cr = e < NN ? colr : 0, cg = e < 2 * N ? colg : 0;
+    const float bias_r = a.bias[cr], bias_g = a.bias[cg];
+    const float alpha_g = (e < N) ? a.a_pre : a.a_post;
     // Tile jb: once this member's waves have posted their record of it (the
     // other members post theirs at about the same time), the reduce-scatter
     // (B) and then the broadcast of the owners' H_pre (C).
@@ -586,15 +626,9 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
         }
       }
       lds_done();
-      // Lane (o, e) of the maps: entry e of owned token o.
-      const int o = lane >> 4;
-      const int e = lane & 15;
       const int tok = s + o * S;
       const bool own = o < tpr && tok < OR;
       const int oo = o < OTPR ? o : 0;
-      const int colr = N + e;
-      const int colg = (e < N) ? e : (N + NN + (e - N));
-      const int cr = e < NN ? colr : 0, cg = e < 2 * N ? colg : 0;
       const double ss = xs[xw][oo][SSO];
       const double zr = xs[xw][oo][cr];
       const double zg = xs[xw][oo][cg];
@@ -602,17 +636,16 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
       float gv = 0.0f, rv = -INFINITY;
       if constexpr (HC) {
         if (e < 2 * N)
-          gv = static_cast<float>(static_cast<double>(a.bias[cg]) +
-                                  static_cast<double>((e < N) ? a.a_pre : a.a_post) * tanh(zg * inv_r));
-        rv = (e < NN) ? static_cast<float>(static_cast<double>(a.bias[cr]) +
+          gv = static_cast<float>(static_cast<double>(bias_g) + static_cast<double>(alpha_g) * tanh(zg * inv_r));
+        rv = (e < NN) ? static_cast<float>(static_cast<double>(bias_r) +
                                            static_cast<double>(a.a_res) * tanh(zr * inv_r))
                       : 0.0f;
       } else {
         if (e < 2 * N) {
-          const float l = logit_of(zg, inv_r, (e < N) ? a.a_pre : a.a_post, a.bias[cg]);
+          const float l = logit_of(zg, inv_r, alpha_g, bias_g);
           gv = (e < N) ? sigmoidf_(l) : 2.0f * sigmoidf_(l);
         }
-        if (e < NN) rv = logit_of(zr, inv_r, a.a_res, a.bias[cr]);
+        if (e < NN) rv = logit_of(zr, inv_r, a.a_res, bias_r);
       }
       u64* slot = tring + (jb % OSLOTS) * a.slotw;
       if (own && e < N) slot[recw + tok * N + e] = xword(__float_as_uint(gv), tag);
@@ -644,6 +677,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
     // ----------------------------------------------------------------- Sinkhorn
     // Two tiles per pass: lanes 32 q .. 32 q + 31 take tile jt + q, 16 lanes
     // per owned token.
+    __builtin_amdgcn_s_setprio(2);
     const int q = lane >> 5;
     const int o = (lane >> 4) & 1;
     const int e = lane & 15;

@@ -102,13 +102,13 @@ def test_workspace_size_formula(lib):
         two_pass = slices * T * width * 4 + 512 * 16    # records + write-only trash slots (16 B per thread)
         if -(-T // 32) * slices < 128:                  # small-T form: slices of 64 positions
             two_pass = max(two_pass, -(-d // 64) * T * width * 4 + 512 * 16)
-        # one pass: header, 16 start words per team, then per team 4 ring slots of 16-token
+        # one pass: header, 16 start words per team, then per team 5 ring slots of 16-token
         # records (m + 2 words per member and token) and n H_pre words per token, 8 B a word;
         # room for 8 XCDs x floor(48 / slices) teams
         teams = 8 * (48 // slices)
         record = ((n * n + 2 * n + 1) & ~1) + 2            # m partials, even padding, fp64 sum of squares
         slot = slices * 16 * record + 16 * n
-        one_pass = 256 + teams * 16 * 8 + teams * 4 * slot * 8 if 8 <= slices <= 16 else 0
+        one_pass = 256 + teams * 16 * 8 + teams * 5 * slot * 8 if 8 <= slices <= 16 else 0
         assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == max(two_pass, one_pass)
     for (T, d) in ((64, 256), (1, 8), (4096, 4104)):
         # n = 8: records of 80 partials + an fp64 over slices of 64 positions, plus trash slots

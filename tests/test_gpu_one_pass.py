@@ -137,3 +137,26 @@ def test_one_pass_repeated_calls_same_workspace(mhc):
     assert int(ws[:8].view(torch.int64).item()) == 0
     for o in outs[1:]:
         assert np.array_equal(o[0], outs[0][0]) and np.array_equal(o[1], outs[0][1])
+
+
+def test_large_state_sum_of_squares(mhc, oracle_lib):
+    """Tokens scaled by 2^64 (|x| ~ 1e19, exact in bf16): their squares
+    overflow fp32, so the single pass's fp32 sum of squares must fall back to
+    fp64 like the two-pass form; every token still matches the oracle."""
+    w = synth.scaled(synth.WORKLOADS["layer_bf16_T16384_d4096"], T=1024)
+    X = synth.make_state(w)
+    f = synth.bf16_bits_to_f32(X)
+    big = [3, 100, 517, 1023]
+    f[big] *= np.float32(2.0 ** 64)
+    f[200] *= np.float32(2.0 ** -64)
+    X = (f.view(np.uint32) >> 16).astype(np.uint16)
+    phi, bias = synth.make_params(w)
+    alpha = (1.0, 1.0, 1.0)
+    ref = oracle_lib.pre(X, phi, bias, alpha, eps=w.eps, t_max=w.t_max)
+    for algo in (mhc.PRE_ONE_PASS, mhc.PRE_TWO_PASS):
+        h, H, used, err = _run(mhc, w, X, phi, bias, alpha, algo)
+        assert used == algo
+        assert err == 0 or algo == mhc.PRE_TWO_PASS      # the two-pass form keeps records there
+        assert np.all(np.isfinite(H))
+        assert_close(H, ref["H"], *TOL[("bf16", "maps")], what=f"large state H ({algo})")
+        assert_close(h, ref["h"], *TOL[("bf16", "state")], what=f"large state h ({algo})")
