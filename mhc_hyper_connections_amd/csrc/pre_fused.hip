@@ -370,13 +370,13 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int cn = (M - 16 * nb < 16) ? M - 16 * nb : 16;
-          const bool cv = r16 < cn;
-          const int ent = 64 * nb + g * cn + (cv ? r16 : 0);
-          const u32x4 zero = {0u, 0u, 0u, 0u};
-          const u32x4 hi = phi_l[w][i][0][ent], lo = phi_l[w][i][1][ent];
+          // A block narrower than 16 columns (the last one) repeats valid
+          // entries in its unused columns: output column c depends only on
+          // B column c, and columns >= m are never written out.
+          const int ent = 64 * nb + g * cn + (r16 < cn ? r16 : r16 - cn);
           PhiOp<BF16> b;
-          b.hi = __builtin_bit_cast(bf16x8, cv ? hi : zero);
-          b.lo = __builtin_bit_cast(bf16x8, cv ? lo : zero);
+          b.hi = __builtin_bit_cast(bf16x8, phi_l[w][i][0][ent]);
+          b.lo = __builtin_bit_cast(bf16x8, phi_l[w][i][1][ent]);
           acc[nb] = mfma_block(Raw8<BF16>{x[i]}, b, acc[nb]);
         }
         __builtin_amdgcn_sched_barrier(0);   // read phi per stream, next to its MFMAs (registers)
@@ -476,15 +476,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
 #pragma unroll
         for (int i = 0; i < N; ++i) hp[i] = maps[jt % OMR][r16][i];
       }
-      // Unpack the held tile afresh: reusing the values unpacked D steps
-      // earlier for the sum of squares would keep 32 floats per held tile
-      // live instead of 16 packed registers.
-      u32x4 y[N];
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        y[i] = x[i];
-        asm volatile("" : "+v"(y[i]));
-      }
+      const u32x4 (&y)[N] = x;
       float o[8];
       {
         float v[8];
