@@ -168,14 +168,14 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
       }
     }
 
-    // Sum of squares.  bf16 state without D: the diagonal of the tile's
-    // 16 x 16 Gram matrix on MFMA (bf16 products are exact in fp32; fp32
-    // accumulation over the wave's 32 positions x n streams), redone in fp64
-    // for a token whose fp32 sum overflows; entry (t, t) sits in lane
-    // 16 (t / 4) + t, element t % 4, and covers the wave's 4 lane groups.
-    // Otherwise fp64 per lane, added over the 4 groups below.  Either never
-    // overflows for a finite state.
-    constexpr bool GRAM = std::is_same<ST, BF16>::value && !WITH_D;
+    // Sum of squares.  bf16 state: the diagonal of the tile's 16 x 16 Gram
+    // matrix on MFMA (bf16 products are exact in fp32; fp32 accumulation
+    // over the wave's 32 positions x n streams), redone in fp64 for a token
+    // whose fp32 sum overflows; entry (t, t) sits in lane 16 (t / 4) + t,
+    // element t % 4, and covers the wave's 4 lane groups.  fp32 state: fp64
+    // per lane, added over the 4 groups below.  Either never overflows for
+    // a finite state.  <D, X_i> (with D) is fp32 per lane either way.
+    constexpr bool GRAM = std::is_same<ST, BF16>::value;
     double ss[MB];
     float dd[MB][ND > 0 ? ND : 1];
     f32x4 acc[MB][NB];
@@ -213,6 +213,19 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
           if (ovf) sq = s64;
         }
         ss[mb] = (g == (r16 >> 2)) ? sq : 0.0;
+        if constexpr (WITH_D) {
+          float dv[8];
+          unpack8(cur[mb][N], dv);
+#pragma unroll
+          for (int i = 0; i < N; ++i) {
+            float x[8];
+            unpack8(cur[mb][i], x);
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaf(dv[e], x[e], a);
+            dd[mb][i] = jv ? a : 0.0f;
+          }
+        }
       } else {
         float dv[8];
         if (WITH_D) unpack8(cur[mb][N], dv);
