@@ -238,6 +238,37 @@ def time_small_t(mhc, torch, reps=100):
     return out
 
 
+def time_n8(mhc, torch, T=16384, d=4096, reps=10):
+    """mhc_pre and mhc_post at n = 8 streams (m = 80, bf16, random inputs of
+    the layer's distributions), per call, with their algorithmic GB/s."""
+    n, m = 8, 80
+    g = torch.Generator(device="cuda").manual_seed(88)
+    X = torch.randn(T, n, d, device="cuda", generator=g).to(torch.bfloat16)
+    Y = torch.randn(T, d, device="cuda", generator=g).to(torch.bfloat16)
+    phi = torch.randn(n * d, m, device="cuda", generator=g) * 0.02
+    bias = torch.randn(m, device="cuda", generator=g) * 0.1
+    ws = torch.empty(mhc.pre_workspace_size(T, n, d, 1), dtype=torch.uint8, device="cuda")
+    h = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    H = torch.empty((T, m), device="cuda")
+    Xo = torch.empty_like(X)
+    out = {"shape": f"T={T} n=8 d={d} bf16"}
+    calls = (("mhc_pre", lambda: mhc.pre(X, phi, bias, h=h, H=H, workspace=ws), T * n * d * 2 + T * d * 2 + T * m * 4),
+             ("mhc_post", lambda: mhc.post(X, Y, H, out=Xo), 2 * T * n * d * 2 + T * d * 2 + T * (n * n + n) * 4))
+    for name, fn, nbytes in calls:
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) / reps * 1e3
+        out[name] = {"avg_us": us, "GBps": nbytes / us / 1e3}
+    return out
+
+
 def cpu_baseline(w, seconds_target=15.0):
     """The oracle (single-threaded C++, double) on the first tokens of the
     same workload: mhc_pre + mhc_post per token."""
@@ -516,6 +547,9 @@ def main():
     log("mhc_pre forms: " + ", ".join(f"{k} {v['avg_us']:.1f} us" for k, v in forms.items() if v))
 
     small_t = time_small_t(mhc, torch)
+    n8 = time_n8(mhc, torch)
+    log(f"n = 8 ({n8['shape']}): mhc_pre {n8['mhc_pre']['avg_us']:.1f} us ({n8['mhc_pre']['GBps']:.0f} GB/s), "
+        f"mhc_post {n8['mhc_post']['avg_us']:.1f} us ({n8['mhc_post']['GBps']:.0f} GB/s)")
     log("mhc_pre at small T (split-K form, per call): " +
         ", ".join(f"{r['shape']} {r['us']:.1f} us" for r in small_t))
 
@@ -572,6 +606,7 @@ def main():
         "kernels": kernels,
         "mhc_pre_forms": forms,
         "small_t": small_t,
+        "n8": n8,
         "backward": backward,
         "stack": stack,
         "cpu_baseline": cpu,

@@ -356,9 +356,11 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
 // the same values to the same place, so no load or store sits behind a
 // branch and the compiler keeps both passes in flight.
 // SPG: slices per 16-lane group held in registers (the group sums slices
-// q, q+4, ...; S <= 4 SPG take no further loop).
+// q, q+4, ...; S <= 4 SPG take no further loop).  With few tokens the
+// token's passes are split over `ppp`-pass parts (grid y): every part's wave
+// forms the same maps, part 0 writes H.
 template <typename ST, int N, bool HC, int SPG>
-__global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S,
+__global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S, int ppp,
                                                          const typename ST::elem* __restrict__ X,
                                                          const float* __restrict__ part,
                                                          const float* __restrict__ bias, float a_pre,
@@ -378,9 +380,11 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
 
   const typename ST::elem* Xt = X + t * N * static_cast<int64_t>(d);
   typename ST::elem* ht = h + t * static_cast<int64_t>(d);
-  const int npass = (d + 511) / 512;
+  const int p_first = static_cast<int>(blockIdx.y) * ppp;      // this part's passes: p_first .. + npass - 1
+  const int npass_all = (d + 511) / 512;
+  const int npass = (npass_all - p_first < ppp) ? npass_all - p_first : ppp;
   auto pos = [&](int p) {
-    const int j = p * 512 + lane * 8;
+    const int j = (p_first + p) * 512 + lane * 8;
     return j < d ? j : d - 8;
   };
   Raw8<ST> xa[N], xb[N];
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
     if (e < NN) lr = logit_of(zr, inv_r, a_res, bias_r);
     mv = sinkhorn16<N>(lr, e, t_max);
   }
-  if (lane < 16) {
+  if (lane < 16 && blockIdx.y == 0) {
     float* Ht = H + t * M;
     if (e < NN) Ht[colr] = mv;
     if (e < 2 * N) Ht[colg] = gv;
@@ -508,13 +512,20 @@ template <typename ST, int N, bool HC>
 hipError_t launch_finish_t(const mhc_params& p, int S, const void* X, const float* part, const float* bias, void* h,
                            float* H, hipStream_t stream) {
   typedef typename ST::elem E;
-  const dim3 grid(static_cast<unsigned>((p.T + 3) / 4));
+  // Parts per token: enough waves for the device (~1024) when T is small.
+  const int npass = (p.d + 511) / 512;
+  int64_t want = (1024 + p.T - 1) / p.T;
+  if (want > npass) want = npass;
+  if (want < 1) want = 1;
+  const int ppp = static_cast<int>((npass + want - 1) / want);
+  const int parts = (npass + ppp - 1) / ppp;                  // every part has at least one pass
+  const dim3 grid(static_cast<unsigned>((p.T + 3) / 4), static_cast<unsigned>(parts));
   if (S <= 16)
-    hipLaunchKernelGGL((pre_finish_kernel<ST, N, HC, 4>), grid, dim3(256), 0, stream, p.T, p.d, S,
+    hipLaunchKernelGGL((pre_finish_kernel<ST, N, HC, 4>), grid, dim3(256), 0, stream, p.T, p.d, S, ppp,
                        static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post, p.eps, p.t_max,
                        static_cast<E*>(h), H);
   else
-    hipLaunchKernelGGL((pre_finish_kernel<ST, N, HC, 16>), grid, dim3(256), 0, stream, p.T, p.d, S,
+    hipLaunchKernelGGL((pre_finish_kernel<ST, N, HC, 16>), grid, dim3(256), 0, stream, p.T, p.d, S, ppp,
                        static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post, p.eps, p.t_max,
                        static_cast<E*>(h), H);
   return hipGetLastError();
