@@ -39,8 +39,9 @@
  *    A failed launch returns MHC_ERR_HIP.  Faults during execution surface at
  *    the caller's next synchronisation.  NaN and Inf propagate; they are not
  *    checked.  No entry point throws or aborts.
- *  - Device support: n in {1, 2, 4}; d a multiple of 8; tensor base pointers
- *    16-byte aligned.  T = 0 is a valid no-op.
+ *  - Device support: n in {1, 2, 4, 8} (the backward: n in {1, 2, 4}); d a
+ *    multiple of 8; tensor base pointers 16-byte aligned.  T = 0 is a valid
+ *    no-op.
  *  - Results are bitwise reproducible for fixed inputs and shapes: every
  *    reduction runs in a fixed order and no floating-point atomics are used.
  *  - The library keeps no mutable state between calls apart from a cache of
@@ -78,7 +79,7 @@ typedef enum mhc_dtype { MHC_FP32 = 0, MHC_BF16 = 1 } mhc_dtype;
  * workloads here use 1e-6). */
 typedef struct mhc_params {
   int64_t T;          /* tokens, >= 0 */
-  int32_t n;          /* streams: 1, 2 or 4 */
+  int32_t n;          /* streams: 1, 2, 4 or 8 (backward: 1, 2 or 4) */
   int32_t d;          /* values per stream, multiple of 8 */
   int32_t dtype;      /* mhc_dtype of X, h, Y, X_out */
   int32_t t_max;      /* Sinkhorn-Knopp passes, 0 .. 1000 */
@@ -133,7 +134,7 @@ size_t mhc_pre_workspace_size(const mhc_params* p);
  * how many times they read X from HBM:
  *   MHC_PRE_TWO_PASS  a split-K projection pass, then a maps + aggregation
  *                     pass that reads X again; any valid shape.
- *   MHC_PRE_ONE_PASS  bf16 state with 1793 <= d <= 4096 and at least one
+ *   MHC_PRE_ONE_PASS  bf16 state, n <= 4, 1793 <= d <= 4096 and at least one
  *                     16-token tile per team: teams of S = ceil(d / 256)
  *                     workgroups (one per compute unit, all on one XCD)
  *                     split d, exchange per-token sums through the XCD's L2
@@ -188,7 +189,7 @@ mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const flo
  *   h       out  [T, d] layer l+1's sublayer input
  *   H_next  out  [T, m] layer l+1's maps
  *   workspace    at least mhc_pre_workspace_size(p) bytes
- * n = 1 runs the two entry points one after the other. */
+ * n = 1 and n = 8 run the two entry points one after the other. */
 mhc_status mhc_post_pre(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out,
                         const float* phi, const float* bias, void* h, float* H_next, void* workspace,
                         size_t workspace_bytes, void* stream);
