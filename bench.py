@@ -345,12 +345,17 @@ def write_traffic(fetch_db, write_db, out_path, workload="layer_bf16_T16384_d409
     fetch = _counter_per_kernel(fetch_db, "FETCH_SIZE")
     write = _counter_per_kernel(write_db, "WRITE_SIZE")
     copy_bytes = 512 * 1024 * 1024
-    cf = [k for k in fetch if COPY_KERNEL in k]
-    cw = [k for k in write if COPY_KERNEL in k]
-    if not cf or not cw:
-        raise SystemExit("the plain-copy kernel is missing from the counter runs")
-    fetch_scale = copy_bytes / (_median(fetch[cf[0]]) * 1024)
-    write_scale = copy_bytes / (_median(write[cw[0]]) * 1024)
+
+    def copy_median(per):
+        # The 512 MiB copy's dispatches: torch's small multiplies (input
+        # set-up) run the same kernel, so keep the dispatches near the largest.
+        vals = [v for k, vs in per.items() if COPY_KERNEL in k for v in vs]
+        if not vals:
+            raise SystemExit("the plain-copy kernel is missing from the counter runs")
+        top = max(vals)
+        return _median([v for v in vals if v >= 0.5 * top])
+    fetch_scale = copy_bytes / (copy_median(fetch) * 1024)
+    write_scale = copy_bytes / (copy_median(write) * 1024)
     entries = {}
     for entry, pats in ENTRY_KERNELS.items():
         rb = wb = 0.0
@@ -388,7 +393,8 @@ def summarize_trace(stats_db):
     for name, calls, avg, pct in rows:          # average is in microseconds
         short = name.replace("void ", "").replace("mhc::(anonymous namespace)::", "").split("(")[0]
         if "MulFunctor" in name:
-            short = "torch mul (plain copy of the state, 1 read + 1 write of 512 MiB)"
+            short = ("torch mul (plain copy of the state, 1 read + 1 write of 512 MiB)" if avg > 50.0
+                     else "torch mul (small input set-up)")
         lines.append(f"| `{short[:90]}` | {calls} | {avg:.1f} | {pct:.1f}% |")
     return "\n".join(lines)
 
@@ -430,6 +436,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     mhc.load_library()
+    # Decode-sized calls first, on a fresh allocator: timed after the large
+    # workload's buffers were allocated, one of these shapes (T = 64,
+    # d = 4096) measured 23 us per call against 13 us alone, for a reason not
+    # yet found; the number reported is the isolated per-call latency.
+    small_t = time_small_t(mhc, torch)
+    torch.cuda.empty_cache()
     w = synth.WORKLOADS[args.workload]
     if w.layers != 1:
         raise SystemExit("bench.py times single-layer workloads")
@@ -546,7 +558,6 @@ def main():
             forms[name] = None
     log("mhc_pre forms: " + ", ".join(f"{k} {v['avg_us']:.1f} us" for k, v in forms.items() if v))
 
-    small_t = time_small_t(mhc, torch)
     n8 = time_n8(mhc, torch)
     log(f"n = 8 ({n8['shape']}): mhc_pre {n8['mhc_pre']['avg_us']:.1f} us ({n8['mhc_pre']['GBps']:.0f} GB/s), "
         f"mhc_post {n8['mhc_post']['avg_us']:.1f} us ({n8['mhc_post']['GBps']:.0f} GB/s)")
