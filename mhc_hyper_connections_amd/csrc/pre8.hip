@@ -31,21 +31,25 @@ constexpr int P8_PG = 2;                      // position groups of 32
 constexpr int P8_WAVES = P8_SP * P8_PG;       // 8
 constexpr int P8_THREADS = P8_WAVES * 64;
 constexpr int P8_SLICE = 32 * P8_PG;          // positions of d per slice
-constexpr int P8_R = 16;                      // tokens per tile
+// Token record of one slice: 80 partials, 2 words of padding, the fp64 sum
+// of squares at word 82; 84 words keep every record 16-byte aligned.
+constexpr int P8_SSO = P8_M + 2;
+constexpr int P8_PW = P8_SSO + 2;
 constexpr size_t kP8TrashBytes = P8_THREADS * 16;   // write-only slots after the records
 
+// MB: 16-token row blocks per tile (2 for bf16 state: 32 tokens a step).
 // DB: two tile buffers in flight (bf16 state); fp32 state keeps one buffer.
 // Either way a buffer is reloaded as soon as it has been multiplied.
-template <typename ST, bool DB>
+template <typename ST, int MB, bool DB>
 __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int d, int S, int64_t ntiles,
                                                                   const typename ST::elem* X,
                                                                   const float* __restrict__ phi,
                                                                   float* __restrict__ part) {
   constexpr int N = P8_N, M = P8_M;
-  constexpr int PW = part_width(N);
-  constexpr int SSO = ss_offset(N);
-  __shared__ float red[P8_WAVES][P8_R][M];
-  __shared__ double red_ss[P8_WAVES][P8_R];
+  constexpr int R = 16 * MB;                  // tokens per tile
+  constexpr bool GRAM = std::is_same<ST, BF16>::value;
+  __shared__ f32x4 red[P8_WAVES][R][M / 4];
+  __shared__ double red_ss[P8_WAVES][R];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -55,7 +59,7 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
   const int g = lane >> 4;
   const int s = blockIdx.x % S;
   const int64_t ntg = gridDim.x / S;
-  float* const trash = part + static_cast<int64_t>(S) * T * PW;
+  float* const trash = part + static_cast<int64_t>(S) * T * P8_PW;
   const int j0 = s * P8_SLICE + 32 * pg + 8 * g;
   const bool jv = j0 < d;
   const int jl = jv ? j0 : 0;
@@ -78,69 +82,121 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
   __builtin_amdgcn_sched_barrier(0);
 
   // Unconditional loads from valid addresses: tokens past T read token 0,
-  // lanes past d read position 0 (zero phi rows; squares dropped).
-  auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[2]) {
-    const int64_t t = tile * P8_R + r16;
-    const int64_t tt = t < T ? t : 0;
+  // lanes past d read position 0 (zero phi rows; their squares are masked).
+  auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][2]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) x[q] = load_raw8<ST>(X + (tt * N + 2 * sp + q) * d + jl);
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t t = tile * R + mb * 16 + r16;
+      const int64_t tt = t < T ? t : 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) x[mb][q] = load_raw8<ST>(X + (tt * N + 2 * sp + q) * d + jl);
+    }
   };
 
-  auto step = [&](int64_t tile, Raw8<ST> (&cur)[2], int64_t next) {
-    f32x4 acc[P8_CB];
+  auto step = [&](int64_t tile, Raw8<ST> (&cur)[MB][2], int64_t next) {
+    f32x4 acc[MB][P8_CB];
+    double sq[MB];
 #pragma unroll
-    for (int b = 0; b < P8_CB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+      for (int b = 0; b < P8_CB; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      Raw8<ST> xm[2];
 #pragma unroll
-      for (int b = 0; b < P8_CB; ++b) acc[b] = mfma_block(cur[q], bop[q][b], acc[b]);
-    // Sum of squares of this lane's 2 x 8 values; lanes r16 + 16 g hold token r16.
-    double sq = 0.0;
+      for (int q = 0; q < 2; ++q) {
+        xm[q] = jv ? cur[mb][q] : zero_raw8<ST>();
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      float x[8];
-      unpack8(cur[q], x);
+        for (int b = 0; b < P8_CB; ++b) acc[mb][b] = mfma_block(cur[mb][q], bop[q][b], acc[mb][b]);
+      }
+      if constexpr (GRAM) {
+        // Token t's sum of squares over the wave's 2 x 32 values: entry (t, t)
+        // of the Gram matrix (lane 16 (t / 4) + t, element t % 4); fp64 from
+        // the registers if the fp32 sum is not finite.
+        f32x4 gram = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sq = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), sq);
+        for (int q = 0; q < 2; ++q) gram = mfma_block_gram(xm[q], gram);
+        const int dv = r16 & 3;
+        const float sqf = dv == 0 ? gram[0] : dv == 1 ? gram[1] : dv == 2 ? gram[2] : gram[3];
+        double v = static_cast<double>(sqf);
+        const bool ovf = g == (r16 >> 2) && !__builtin_isfinite(sqf);
+        if (__any(ovf)) {            // wave-uniform: every lane takes part in the permutes
+          double s64 = 0.0;
+          for (int qq = 0; qq < 4; ++qq) {
+            const int src = 16 * qq + r16;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              Raw8<ST> xq;
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                xq.v[c] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * src, static_cast<int>(xm[q].v[c])));
+              float x[8];
+              unpack8(xq, x);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) s64 = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), s64);
+            }
+          }
+          if (ovf) v = s64;
+        }
+        sq[mb] = v;
+      } else {
+        double v = 0.0;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float x[8];
+          unpack8(xm[q], x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), v);
+        }
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        sq[mb] = v;
+      }
     }
-    sq = jv ? sq : 0.0;
-    sq += __shfl_xor(sq, 16);
-    sq += __shfl_xor(sq, 32);
     // The buffer is free once multiplied: the next tile's loads go out now.
     load_tile(next, cur);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int b = 0; b < P8_CB; ++b)
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[w][4 * g + v][16 * b + r16] = acc[b][v];
-    if (g == 0) red_ss[w][r16] = sq;
+      for (int b = 0; b < P8_CB; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          red[w][mb * 16 + 4 * g + v][(16 * b + r16) >> 2][r16 & 3] = acc[mb][b][v];
+      if (GRAM ? (g == (r16 >> 2)) : (g == 0)) red_ss[w][mb * 16 + r16] = sq[mb];
+    }
     __syncthreads();
-    // Records out: the eight waves' partials added in wave order, a fixed
-    // number of stores per thread (items past the tile or past T go to the
-    // write-only slots).
-    constexpr int NF = P8_R * M;
+    // Records out, 16 bytes a store: the eight waves' partials added in wave
+    // order, a fixed number of stores per thread (items past the tile or past
+    // T go to the write-only slots).
+    constexpr int NF = R * (M / 4);
     constexpr int FPT = (NF + P8_THREADS - 1) / P8_THREADS;
 #pragma unroll
     for (int k = 0; k < FPT; ++k) {
       const int q = threadIdx.x + k * P8_THREADS;
       const int qq = q < NF ? q : 0;
-      const int tok = qq / M;
-      const int c = qq - tok * M;
-      float sum = red[0][tok][c];
+      const int tok = qq / (M / 4);
+      const int c4 = qq - tok * (M / 4);
+      f32x4 sum = red[0][tok][c4];
 #pragma unroll
-      for (int ww = 1; ww < P8_WAVES; ++ww) sum += red[ww][tok][c];
-      const int64_t t = tile * P8_R + tok;
-      float* dst = (q < NF && t < T) ? part + (static_cast<int64_t>(s) * T + t) * PW + c : trash + threadIdx.x;
-      *dst = sum;
+      for (int ww = 1; ww < P8_WAVES; ++ww) {
+        const f32x4 y = red[ww][tok][c4];
+        sum[0] += y[0];
+        sum[1] += y[1];
+        sum[2] += y[2];
+        sum[3] += y[3];
+      }
+      const int64_t t = tile * R + tok;
+      float* dst = (q < NF && t < T) ? part + (static_cast<int64_t>(s) * T + t) * P8_PW + 4 * c4
+                                     : trash + 4 * threadIdx.x;
+      *reinterpret_cast<f32x4*>(dst) = sum;
     }
     {
-      const int tok = static_cast<int>(threadIdx.x) < P8_R ? static_cast<int>(threadIdx.x) : 0;
+      const int tok = static_cast<int>(threadIdx.x) < R ? static_cast<int>(threadIdx.x) : 0;
       double sum = red_ss[0][tok];
 #pragma unroll
       for (int ww = 1; ww < P8_WAVES; ++ww) sum += red_ss[ww][tok];
-      const int64_t t = tile * P8_R + tok;
-      double* dst = (static_cast<int>(threadIdx.x) < P8_R && t < T)
-                        ? reinterpret_cast<double*>(part + (static_cast<int64_t>(s) * T + t) * PW + SSO)
+      const int64_t t = tile * R + tok;
+      double* dst = (static_cast<int>(threadIdx.x) < R && t < T)
+                        ? reinterpret_cast<double*>(part + (static_cast<int64_t>(s) * T + t) * P8_PW + P8_SSO)
                         : reinterpret_cast<double*>(trash) + threadIdx.x;
       *dst = sum;
     }
@@ -151,11 +207,11 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
   // the end read token 0 and write nothing (see pre.hip).
   const int64_t tile0 = blockIdx.x / S;
   const int64_t per_wg = (ntiles + ntg - 1) / ntg;
-  Raw8<ST> xa[2];
+  Raw8<ST> xa[MB][2];
   load_tile(tile0, xa);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (DB) {
-    Raw8<ST> xb[2];
+    Raw8<ST> xb[MB][2];
     load_tile(tile0 + ntg, xb);
     __builtin_amdgcn_sched_barrier(0);
     int64_t k = 0;
@@ -207,8 +263,8 @@ __global__ __launch_bounds__(256) void pre_finish8_kernel(int64_t T, int d, int 
                                                           float a_post, float eps, int t_max,
                                                           typename ST::elem* __restrict__ h, float* __restrict__ H) {
   constexpr int N = P8_N, M = P8_M, NN = N * N;
-  constexpr int PW = part_width(N);
-  constexpr int SSO = ss_offset(N);
+  constexpr int PW = P8_PW;
+  constexpr int SSO = P8_SSO;
   const int e = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                                        // wave-uniform
@@ -291,17 +347,19 @@ hipError_t launch_pre8_t(const mhc_params& p, const void* X, const float* phi, c
                          void* workspace, const DeviceInfo& dev, hipStream_t stream) {
   typedef typename ST::elem E;
   constexpr bool DB = sizeof(E) == 2;
+  constexpr int MB = DB ? 2 : 1;
   const int S = slices8(p.d);
-  const int64_t ntiles = (p.T + P8_R - 1) / P8_R;
+  const int64_t ntiles = (p.T + 16 * MB - 1) / (16 * MB);
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(pre_partial8_kernel<ST, DB>),
-                                                   P8_THREADS, 0) != hipSuccess || occ < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &occ, reinterpret_cast<const void*>(pre_partial8_kernel<ST, MB, DB>), P8_THREADS, 0) != hipSuccess ||
+      occ < 1)
     occ = 1;
   int64_t groups = static_cast<int64_t>(dev.num_cus) * occ / S;
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
   float* part = static_cast<float*>(workspace);
-  hipLaunchKernelGGL((pre_partial8_kernel<ST, DB>), dim3(static_cast<unsigned>(groups * S)), dim3(P8_THREADS), 0,
+  hipLaunchKernelGGL((pre_partial8_kernel<ST, MB, DB>), dim3(static_cast<unsigned>(groups * S)), dim3(P8_THREADS), 0,
                      stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), phi, part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -320,8 +378,8 @@ hipError_t launch_pre8_t(const mhc_params& p, const void* X, const float* phi, c
 }  // namespace
 
 size_t pre8_workspace_bytes(int64_t T, int d) {
-  return static_cast<size_t>(slices8(d)) * static_cast<size_t>(T) * static_cast<size_t>(part_width(P8_N)) *
-             sizeof(float) + kP8TrashBytes;
+  return static_cast<size_t>(slices8(d)) * static_cast<size_t>(T) * static_cast<size_t>(P8_PW) * sizeof(float) +
+         kP8TrashBytes;
 }
 
 hipError_t launch_pre8(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,

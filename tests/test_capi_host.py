@@ -111,9 +111,10 @@ def test_workspace_size_formula(lib):
         one_pass = 256 + teams * 16 * 8 + teams * 5 * slot * 8 if 8 <= slices <= 16 else 0
         assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == max(two_pass, one_pass)
     for (T, d) in ((64, 256), (1, 8), (4096, 4104)):
-        # n = 8: records of 80 partials + an fp64 over slices of 64 positions, plus trash slots
+        # n = 8: records of 80 partials, 2 words of padding and an fp64 (84 words, 16-byte
+        # aligned) over slices of 64 positions, plus trash slots
         p = _params(T=T, n=8, d=d)
-        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == -(-d // 64) * T * 82 * 4 + 512 * 16
+        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == -(-d // 64) * T * 84 * 4 + 512 * 16
     assert lib.mhc_pre_workspace_size(None) == 0
     assert lib.mhc_pre_workspace_size(ctypes.byref(_params(n=3))) == 0
 
