@@ -139,19 +139,22 @@ size_t mhc_pre_workspace_size(const mhc_params* p);
  *                     workgroups (one per compute unit, all on one XCD)
  *                     split d, exchange per-token sums through the XCD's L2
  *                     and keep their slice of X in registers until H_pre is
- *                     known, so X is read once.  Uses a cooperative launch.
+ *                     known, so X is read once.  Uses a cooperative launch,
+ *                     so not on a stream being captured into a HIP graph.
  *                     Returns MHC_ERR_UNSUPPORTED when it does not apply.
  *   MHC_PRE_AUTO      the one-pass form where it measures faster on MI355X
  *                     (n = 4, teams that fill whole XCDs, at least 40 tiles
- *                     per team: T >= 10240 at d = 4096), else the two-pass.
+ *                     per team: T >= 10240 at d = 4096) and the stream is not
+ *                     capturing, else the two-pass form.  Every other entry
+ *                     point may be captured into a HIP graph.
  * Both sum every partial in a fixed order (results are bitwise reproducible
  * for a given form); the two forms agree to rounding.
  * algo_used (nullable, host pointer) receives the form that ran.  After a
  * one-pass call, the first 8 bytes of the workspace hold 0, or the
  * sequence number of a one-pass call whose internal wait ran out (its
  * results are invalid); the library never clears it.  A wait can only run
- * out if the workgroups of the launch are not all resident or not placed on
- * the XCDs round-robin, which the cooperative launch on MI355X rules out. */
+ * out if the workgroups of the launch are not all resident at once, which
+ * the cooperative launch rules out. */
 #define MHC_PRE_AUTO 0
 #define MHC_PRE_TWO_PASS 1
 #define MHC_PRE_ONE_PASS 2

@@ -11,9 +11,13 @@
 // team of S = ceil(d / 256) workgroups (8 <= S <= 16), one per CU, all on one
 // XCD: they exchange per-token sums through that XCD's L2.  Member s owns
 // positions [256 s, 256 s + 256) of every stream; the team walks 16-token
-// tiles.  Workgroups are dispatched to the XCDs round-robin, so team and
-// member follow from the workgroup index (checked against the hardware XCD
-// id).  A workgroup runs eleven waves with fixed roles:
+// tiles.  Workgroups are dispatched to the XCDs round-robin, not always
+// starting at XCD 0 (after a HIP graph has been captured in the process the
+// start moved): a workgroup takes its team from its hardware XCD id and its
+// place on that XCD from its index / 8.  Were the placement ever not a
+// rotation, a team's members would sit on different XCDs, their exchange
+// words would not meet in one L2, and the bounded waits would report it.
+// A workgroup runs eleven waves with fixed roles:
 //  * waves 0-7 stream.  Wave w holds positions 32 w .. 32 w + 31 of the
 //    member's slice for a tile's 16 tokens in registers (lane = token row
 //    and 8 positions, the MFMA A layout; one 16-byte load per stream).  In
@@ -214,24 +218,22 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
   __shared__ int maps_tag[OMR];            // H_pre of tile t is in slot t % OMR once maps_tag[slot] > t
   __shared__ int sk_tag[OKR];              // likewise for the Sinkhorn inputs
   __shared__ int sk_free, broken;
-  __shared__ int misplaced;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   int* const vbroken = &broken;
 
-  // Team membership.  Workgroups are dispatched to the XCDs round-robin
-  // (workgroup b runs on XCD b % 8), so teams follow from the index; the
-  // hardware's XCD id is checked, and a workgroup placed otherwise marks the
-  // call broken (its team's waits then run out and report, never hang).
+  // Team membership: the team from the hardware XCD id, the place on the
+  // XCD from the workgroup index (round-robin dispatch puts workgroups b,
+  // b + 8, b + 16, ... on one XCD, whichever XCD the rotation starts at).
+  __shared__ int xcc_l;
   if (tid == 0) {
-    const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;   // HW_REG_XCC_ID
-    misplaced = (xcc == (blockIdx.x & (OXCD - 1))) ? 0 : 1;
+    xcc_l = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7);   // HW_REG_XCC_ID
     for (int q = 0; q < OMR; ++q) maps_tag[q] = 0;
     for (int q = 0; q < OKR; ++q) sk_tag[q] = 0;
     sk_free = 0;
-    broken = misplaced;
+    broken = 0;
   }
   if (tid < OW) {
     part_ready[tid] = 0;
@@ -241,8 +243,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
   const int S = a.S;
   const int idx = static_cast<int>(blockIdx.x) / OXCD;
   if (idx >= a.tpx * S) return;   // not part of a team (whole workgroup)
-  if (misplaced != 0 && tid == 0) __hip_atomic_store(a.hdr, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int team = static_cast<int>(blockIdx.x & (OXCD - 1)) * a.tpx + idx / S;
+  const int team = xcc_l * a.tpx + idx / S;
   const int s = idx % S;
   const int d = a.d;
   const int64_t T = a.T;
@@ -741,6 +742,13 @@ bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev) {
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
                             float* H, void* workspace, size_t ws_bytes, const DeviceInfo& dev, hipStream_t stream) {
   if (p.dtype != MHC_BF16 || (p.n != 4 && p.n != 2 && p.n != 1)) return hipErrorNotSupported;
+  // Not under stream capture: a graph replays the kernel without the
+  // cooperative launch's residency guarantee and with the captured call's
+  // sequence number, so the team's meeting could not be trusted (measured:
+  // every replay's waits ran out).
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone)
+    return hipErrorNotSupported;
   const int S = one_pass_slices(p.d);
   if (S < OS_MIN || S > OS_MAX || !dev.cooperative || dev.num_cus % OXCD != 0) return hipErrorNotSupported;
   const int per_xcd = dev.num_cus / OXCD;

@@ -1,0 +1,71 @@
+"""The forward step captured into a HIP graph (torch.cuda.CUDAGraph).
+
+mhc_pre's single pass relies on a cooperative launch and a per-call sequence
+number, which a graph cannot reproduce, so on a capturing stream MHC_PRE_AUTO
+takes the two-pass form and MHC_PRE_ONE_PASS is refused.  The captured step
+(mhc_pre, mhc_post, mhc_amax) is replayed several times with eager work and
+synchronisations in between; every replay must give the eager two-pass
+results bit for bit.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def mhc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mhc_hyper_connections_amd as m
+    m.load_library()
+    return m
+
+
+def test_forward_step_in_a_graph(mhc):
+    T, n, d, m = 12288, 4, 4096, 24            # AUTO takes the single pass here when not capturing
+    g = torch.Generator(device="cuda").manual_seed(31)
+    X = torch.randn(T, n, d, device="cuda", generator=g).to(torch.bfloat16)
+    Y = torch.randn(T, d, device="cuda", generator=g).to(torch.bfloat16)
+    phi = torch.randn(n * d, m, device="cuda", generator=g) * 0.02
+    bias = torch.randn(m, device="cuda", generator=g) * 0.1
+    alpha = (1.0, 1.0, 1.0)
+    ws = torch.zeros(mhc.pre_workspace_size(T, n, d, mhc.MHC_BF16), dtype=torch.uint8, device="cuda")
+    h = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    H = torch.empty((T, m), device="cuda")
+    Xo = torch.empty_like(X)
+    amax = torch.empty(T, device="cuda")
+
+    _, _, used_eager = mhc.pre_ex(X, phi, bias, mhc.PRE_AUTO, alpha=alpha, workspace=ws)
+    assert used_eager == mhc.PRE_ONE_PASS
+    h_ref, H_ref, _ = mhc.pre_ex(X, phi, bias, mhc.PRE_TWO_PASS, alpha=alpha, workspace=ws)
+    Xo_ref = mhc.post(X, Y, H_ref)
+    a_ref = mhc.amax(H_ref.unsqueeze(0).contiguous(), n, want_all=False)["amax"]
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in (h_ref, H_ref, Xo_ref, a_ref)]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    used = {}
+    with torch.cuda.graph(graph, stream=s):
+        _, _, used["auto"] = mhc.pre_ex(X, phi, bias, mhc.PRE_AUTO, alpha=alpha, h=h, H=H, workspace=ws)
+        mhc.post(X, Y, H, out=Xo)
+        mhc.amax(H.unsqueeze(0), n, out_amax=amax, want_all=False)
+        with pytest.raises(mhc.MhcError) as ei:
+            mhc.pre_ex(X, phi, bias, mhc.PRE_ONE_PASS, alpha=alpha, h=h, H=H, workspace=ws)
+        assert ei.value.status == 5                        # MHC_ERR_UNSUPPORTED, nothing captured
+    assert used["auto"] == mhc.PRE_TWO_PASS
+
+    for r in range(4):
+        for t in (h, H, Xo, amax):
+            t.zero_()
+        # eager work between replays: a single-pass call on the same workspace
+        mhc.pre_ex(X, phi, bias, mhc.PRE_ONE_PASS, alpha=(0.5, 0.5, 0.5), workspace=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((h, H, Xo, amax), refs, ("h", "H", "X'", "amax")):
+            assert torch.equal(got, want), f"replay {r}: {name} differs from the eager two-pass result"
