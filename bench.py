@@ -14,6 +14,7 @@ bounded sample.  Progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -101,9 +102,11 @@ def time_backward(mhc, torch, w, X, Y, phi, bias, H, steps, warmup, stream):
     algo = backward_bytes(T, n, d, sb)
     out = {"workload": wb.name, "steps": steps}
     for name, (a, b) in (("mhc_post_bwd", (0, 1)), ("mhc_pre_bwd", (1, 2))):
-        avg_ms = float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
-        out[name] = {"avg_us": avg_ms * 1e3, "algorithmic_bytes": algo[name],
-                     "GBps": algo[name] / (avg_ms * 1e-3) / 1e9}
+        per = [e[a].elapsed_time(e[b]) for e in evs]
+        avg_ms = float(np.mean(per))
+        out[name] = {"avg_us": avg_ms * 1e3, "median_us": float(np.median(per)) * 1e3,
+                     "min_us": float(np.min(per)) * 1e3, "max_us": float(np.max(per)) * 1e3,
+                     "algorithmic_bytes": algo[name], "GBps": algo[name] / (avg_ms * 1e-3) / 1e9}
     out["fwd_bwd_tokens_per_s"] = None
     return out
 
@@ -440,6 +443,12 @@ def main():
     # workload's buffers were allocated, one of these shapes (T = 64,
     # d = 4096) measured 23 us per call against 13 us alone, for a reason not
     # yet found; the number reported is the isolated per-call latency.
+    # No cyclic garbage collection while timing: a full collection with torch
+    # loaded took up to 34 ms of host time here, long enough to drain the
+    # GPU's queue and add a gap to one step's interval (one backward step
+    # measured 61 ms against a 590 us median).
+    gc.collect()
+    gc.disable()
     small_t = time_small_t(mhc, torch)
     torch.cuda.empty_cache()
     w = synth.WORKLOADS[args.workload]
@@ -573,7 +582,9 @@ def main():
             backward["fwd_bwd_tokens_per_s"] = T / ((ms_step * 1e3 + bwd_us) * 1e-6)
             log(f"backward: post_bwd {backward['mhc_post_bwd']['avg_us']:.1f} us "
                 f"({backward['mhc_post_bwd']['GBps']:.0f} GB/s), pre_bwd {backward['mhc_pre_bwd']['avg_us']:.1f} us "
-                f"({backward['mhc_pre_bwd']['GBps']:.0f} GB/s)")
+                f"({backward['mhc_pre_bwd']['GBps']:.0f} GB/s); per-step min/median/max post_bwd "
+                + "/".join(f"{backward['mhc_post_bwd'][k]:.0f}" for k in ("min_us", "median_us", "max_us"))
+                + ", pre_bwd " + "/".join(f"{backward['mhc_pre_bwd'][k]:.0f}" for k in ("min_us", "median_us", "max_us")))
 
     stack = None
     if not args.no_stack:
