@@ -303,7 +303,7 @@ def cpu_baseline(w, seconds_target=15.0):
 ENTRY_KERNELS = {
     "mhc_pre": ["pre_one_pass_kernel<4, false>"],                      # the form MHC_PRE_AUTO takes here
     "mhc_pre_two_pass": ["pre_partial_kernel<mhc::BF16, 4, 2, 0, 8, false>", "pre_finish_kernel<mhc::BF16, 4, false, 4>"],
-    "mhc_post": ["post_kernel<mhc::BF16, 4"],
+    "mhc_post": ["post_tile_kernel<mhc::BF16, 4>"],
     "mhc_amax": ["amax_kernel<4>"],
     "mhc_post_bwd": ["post_bwd_kernel<mhc::BF16, 4>"],
     "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 2, 1, 8, false>", "pre_bwd_token_kernel<4>",
