@@ -79,11 +79,12 @@ def time_backward(mhc, torch, w, X, Y, phi, bias, H, steps, warmup, stream):
     dbias = torch.empty(m, dtype=torch.float32, device="cuda")
     dalpha = torch.empty(3, dtype=torch.float32, device="cuda")
     ws = torch.empty(mhc.pre_bwd_workspace_size(T, n, d, w.dtype), dtype=torch.uint8, device="cuda")
+    ws_post = torch.empty(max(16, mhc.post_bwd_workspace_size(T, n, d, w.dtype)), dtype=torch.uint8, device="cuda")
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        mhc.post_bwd(X, Y, H, G, dX=dX, dY=dY, dH=dH, stream=stream)
+        mhc.post_bwd(X, Y, H, G, dX=dX, dY=dY, dH=dH, workspace=ws_post, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         mhc.pre_bwd(X, phi, bias, D, dH, dX, alpha=w.alpha, eps=w.eps, t_max=w.t_max, dphi=dphi, dbias=dbias,
@@ -107,6 +108,15 @@ def time_backward(mhc, torch, w, X, Y, phi, bias, H, steps, warmup, stream):
         out[name] = {"avg_us": avg_ms * 1e3, "median_us": float(np.median(per)) * 1e3,
                      "min_us": float(np.min(per)) * 1e3, "max_us": float(np.max(per)) * 1e3,
                      "algorithmic_bytes": algo[name], "GBps": algo[name] / (avg_ms * 1e-3) / 1e9}
+    # The scratch-free form of mhc_post_bwd (no workspace), for reference.
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    mhc.post_bwd(X, Y, H, G, dX=dX, dY=dY, dH=dH, tiled=False, stream=stream)
+    sev[0].record(stream)
+    for _ in range(steps):
+        mhc.post_bwd(X, Y, H, G, dX=dX, dY=dY, dH=dH, tiled=False, stream=stream)
+    sev[1].record(stream)
+    torch.cuda.synchronize()
+    out["mhc_post_bwd_scratch_free_us"] = sev[0].elapsed_time(sev[1]) / steps * 1e3
     out["fwd_bwd_tokens_per_s"] = None
     return out
 
@@ -305,7 +315,7 @@ ENTRY_KERNELS = {
     "mhc_pre_two_pass": ["pre_partial_kernel<mhc::BF16, 4, 2, 0, 8, false>", "pre_finish_kernel<mhc::BF16, 4, false, 4>"],
     "mhc_post": ["post_tile_kernel<mhc::BF16, 4>"],
     "mhc_amax": ["amax_kernel<4>"],
-    "mhc_post_bwd": ["post_bwd_kernel<mhc::BF16, 4>"],
+    "mhc_post_bwd": ["post_bwd_tile_kernel<mhc::BF16, 4>", "post_bwd_reduce_kernel<4>"],
     "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 2, 1, 8, false>", "pre_bwd_token_kernel<4>",
                     "pre_bwd_apply_mfma_kernel<4>", "reduce_chunks_kernel", "reduce_columns_kernel"],
 }
@@ -584,7 +594,8 @@ def main():
                 f"({backward['mhc_post_bwd']['GBps']:.0f} GB/s), pre_bwd {backward['mhc_pre_bwd']['avg_us']:.1f} us "
                 f"({backward['mhc_pre_bwd']['GBps']:.0f} GB/s); per-step min/median/max post_bwd "
                 + "/".join(f"{backward['mhc_post_bwd'][k]:.0f}" for k in ("min_us", "median_us", "max_us"))
-                + ", pre_bwd " + "/".join(f"{backward['mhc_pre_bwd'][k]:.0f}" for k in ("min_us", "median_us", "max_us")))
+                + ", pre_bwd " + "/".join(f"{backward['mhc_pre_bwd'][k]:.0f}" for k in ("min_us", "median_us", "max_us"))
+                + f"; post_bwd without workspace {backward['mhc_post_bwd_scratch_free_us']:.1f} us")
 
     stack = None
     if not args.no_stack:

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 4
+#define MHC_ABI_VERSION 5
 
 typedef enum mhc_status {
   MHC_OK = 0,
@@ -217,6 +217,21 @@ mhc_status mhc_post_pre(const mhc_params* p, const void* X, const void* Y, const
  * No output may overlap an input or another output. */
 mhc_status mhc_post_bwd(const mhc_params* p, const void* X, const void* Y, const float* H, const void* G,
                         void* dX, void* dY, float* dH, void* stream);
+
+/* mhc_post_bwd_ex: mhc_post_bwd with a workspace, which lets it run in a
+ * faster tiled form when d is a multiple of 512: a workgroup then covers 4
+ * tokens x 512 values of d, so each token's dot products are formed per
+ * 512-value slice, kept in the workspace and added in slice order.
+ *   workspace  NULL: the scratch-free form that mhc_post_bwd runs.  Else at
+ *              least mhc_post_bwd_workspace_size(p) bytes (fewer is
+ *              MHC_ERR_WORKSPACE), 16-byte aligned, overlapping no other
+ *              argument; contents on entry ignored, on return unspecified.
+ * mhc_post_bwd_workspace_size returns 0 where the tiled form does not apply
+ * (then the workspace is not used).  Both forms sum in a fixed order (bitwise
+ * reproducible) and agree to rounding. */
+size_t mhc_post_bwd_workspace_size(const mhc_params* p);
+mhc_status mhc_post_bwd_ex(const mhc_params* p, const void* X, const void* Y, const float* H, const void* G,
+                           void* dX, void* dY, float* dH, void* workspace, size_t workspace_bytes, void* stream);
 
 /* mhc_pre_bwd: for h = H_pre X and the maps of mhc_pre, recomputed from X:
  *   dX    += H_pre D + the RMSNorm / projection path      read-modify-write,

@@ -17,10 +17,10 @@ Tensors are torch device tensors: X [T, n, d] and h, Y [T, d] in float32 or
 bfloat16; phi [n*d, n*n+2n], bias [n*n+2n] and H [T, n*n+2n] in float32.
 """
 from ._binding import (EXPORTS, LIB_PATH, MAPS_HC, MAPS_MHC, MHC_BF16, MHC_FP32, PRE_AUTO, PRE_ONE_PASS, PRE_TWO_PASS, MhcError,
-                       Params, amax, gelu_half, load_library, make_params, post, post_bwd, post_pre, pre, pre_bwd,
-                       pre_bwd_workspace_size, pre_ex, pre_workspace_size)
+                       Params, amax, gelu_half, load_library, make_params, post, post_bwd, post_bwd_workspace_size, post_pre,
+                       pre, pre_bwd, pre_bwd_workspace_size, pre_ex, pre_workspace_size)
 
-__all__ = ["pre", "pre_ex", "post", "post_pre", "amax", "gelu_half", "pre_workspace_size", "post_bwd", "pre_bwd",
+__all__ = ["pre", "pre_ex", "post", "post_pre", "amax", "gelu_half", "pre_workspace_size", "post_bwd", "post_bwd_workspace_size", "pre_bwd",
            "pre_bwd_workspace_size", "load_library", "make_params",
            "Params", "MhcError", "MHC_FP32", "MHC_BF16", "MAPS_MHC", "MAPS_HC", "PRE_AUTO", "PRE_TWO_PASS", "PRE_ONE_PASS", "LIB_PATH",
            "EXPORTS"]

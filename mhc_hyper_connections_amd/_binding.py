@@ -17,7 +17,7 @@ MHC_FP32, MHC_BF16 = 0, 1
 STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_DTYPE", 4: "MHC_ERR_ALIGN",
           5: "MHC_ERR_UNSUPPORTED", 6: "MHC_ERR_ALIAS", 7: "MHC_ERR_WORKSPACE", 8: "MHC_ERR_HIP"}
 EXPORTS = ["mhc_pre", "mhc_pre_ex", "mhc_pre_workspace_size", "mhc_post", "mhc_amax", "mhc_gelu_half",
-           "mhc_post_pre", "mhc_post_bwd", "mhc_pre_bwd", "mhc_pre_bwd_workspace_size", "mhc_status_string",
+           "mhc_post_pre", "mhc_post_bwd", "mhc_post_bwd_ex", "mhc_post_bwd_workspace_size", "mhc_pre_bwd", "mhc_pre_bwd_workspace_size", "mhc_status_string",
            "mhc_abi_version"]
 PRE_AUTO, PRE_TWO_PASS, PRE_ONE_PASS = 0, 1, 2
 
@@ -68,6 +68,10 @@ def load_library(path: str = LIB_PATH):
     lib.mhc_post_pre.restype = ctypes.c_int
     lib.mhc_post_bwd.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P]
     lib.mhc_post_bwd.restype = ctypes.c_int
+    lib.mhc_post_bwd_ex.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.mhc_post_bwd_ex.restype = ctypes.c_int
+    lib.mhc_post_bwd_workspace_size.argtypes = [ctypes.POINTER(Params)]
+    lib.mhc_post_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mhc_pre_bwd_workspace_size.argtypes = [ctypes.POINTER(Params)]
     lib.mhc_pre_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mhc_pre_bwd.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -230,9 +234,16 @@ def gelu_half(h, out=None, stream=None):
     return out
 
 
-def post_bwd(X, Y, H, G, dX=None, dY=None, dH=None, stream=None):
-    """mhc_post_bwd: returns (dX [T, n, d], dY [T, d], dH [T, m]); dH's first
-    n columns (the read map's) are left as they were."""
+def post_bwd_workspace_size(T, n, d, dtype=MHC_BF16) -> int:
+    """Bytes of workspace that lets mhc_post_bwd_ex take its tiled form (0: none)."""
+    return int(load_library().mhc_post_bwd_workspace_size(ctypes.byref(make_params(T, n, d, dtype))))
+
+
+def post_bwd(X, Y, H, G, dX=None, dY=None, dH=None, workspace=None, tiled=True, stream=None):
+    """mhc_post_bwd_ex: returns (dX [T, n, d], dY [T, d], dH [T, m]); dH's first
+    n columns (the read map's) are left as they were.  With ``tiled`` (and d a
+    multiple of 512) the call runs the tiled form, on ``workspace`` or on a
+    buffer allocated here; ``tiled=False`` runs mhc_post_bwd, which needs none."""
     torch = _torch()
     T, n, d = X.shape
     m = n * n + 2 * n
@@ -242,8 +253,20 @@ def post_bwd(X, Y, H, G, dX=None, dY=None, dH=None, stream=None):
     dH = torch.zeros((T, m), dtype=torch.float32, device=X.device) if dH is None else dH
     _need_device(X, Y, H, G, dX, dY, dH)
     lib = load_library()
-    _check("mhc_post_bwd", lib.mhc_post_bwd(ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(H), _ptr(G), _ptr(dX), _ptr(dY),
-                                            _ptr(dH), _stream(stream, X.device)))
+    if not tiled:
+        _check("mhc_post_bwd", lib.mhc_post_bwd(ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(H), _ptr(G), _ptr(dX),
+                                                _ptr(dY), _ptr(dH), _stream(stream, X.device)))
+        return dX, dY, dH
+    need = int(lib.mhc_post_bwd_workspace_size(ctypes.byref(p)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _need_device(workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("mhc_post_bwd_ex", lib.mhc_post_bwd_ex(ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(H), _ptr(G), _ptr(dX),
+                                                  _ptr(dY), _ptr(dH), _ptr(workspace),
+                                                  ws_bytes, _stream(stream, X.device)))
     return dX, dY, dH
 
 

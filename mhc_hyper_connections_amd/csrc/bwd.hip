@@ -144,10 +144,152 @@ __global__ __launch_bounds__(256) void post_bwd_kernel(int64_t T, int d, const t
   }
 }
 
+// The tiled form (d a multiple of 512, with a workspace): a workgroup covers
+// 4 tokens x 512 values of d, one token per wave, and consecutive workgroups
+// walk along d, the order in which MI355X streams fastest (as for mhc_post).
+// A token's n*n + n dot products are then split over its d / 512 slices: each
+// wave reduces its slice's across its lanes and writes them to the workspace,
+// part[t][slice][a], and a second kernel adds the slices in order into dH.
+template <typename ST, int N>
+__global__ __launch_bounds__(256) void post_bwd_tile_kernel(int64_t T, int d8, int nslice,
+                                                            const typename ST::elem* __restrict__ X,
+                                                            const typename ST::elem* __restrict__ Y,
+                                                            const float* __restrict__ H,
+                                                            const typename ST::elem* __restrict__ G,
+                                                            typename ST::elem* __restrict__ dX,
+                                                            typename ST::elem* __restrict__ dY,
+                                                            float* __restrict__ part) {
+  constexpr int M = num_maps(N);
+  constexpr int NN = N * N;
+  constexpr int NA = NN + N;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int b = static_cast<int>(blockIdx.x);
+  const int tile = b / nslice;
+  const int slice = b - tile * nslice;
+  const int64_t t = static_cast<int64_t>(tile) * 4 + wave;          // wave-uniform
+  if (t >= T) return;
+  const int64_t d = static_cast<int64_t>(d8) * 8;
+  const int64_t off = (static_cast<int64_t>(slice) * 64 + lane) * 8;
+  const int64_t xrow = t * N * d;
+  Raw8<ST> xr[N], gr[N], yr;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    xr[i] = load_raw8<ST, true>(X + xrow + static_cast<int64_t>(i) * d + off);
+    gr[i] = load_raw8<ST, true>(G + xrow + static_cast<int64_t>(i) * d + off);
+  }
+  yr = load_raw8<ST, true>(Y + t * d + off);
+  const float* Ht = H + t * M;
+  float res[N][N], post[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) res[i][j] = Ht[N + i * N + j];
+    post[i] = Ht[N + NN + i];
+  }
+  float x[N][8], g[N][8], y[8];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    unpack8(xr[i], x[i]);
+    unpack8(gr[i], g[i]);
+  }
+  unpack8(yr, y);
+  float acc[NA];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      float a = g[i][0] * x[j][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) a = fmaf(g[i][e], x[j][e], a);
+      acc[i * N + j] = a;
+    }
+    float a = g[i][0] * y[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) a = fmaf(g[i][e], y[e], a);
+    acc[NN + i] = a;
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float sum = res[0][j] * g[0][e];
+#pragma unroll
+      for (int i = 1; i < N; ++i) sum = fmaf(res[i][j], g[i][e], sum);
+      o[e] = sum;
+    }
+    store8<ST, true>(dX + xrow + static_cast<int64_t>(j) * d + off, o);
+  }
+  {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float sum = post[0] * g[0][e];
+#pragma unroll
+      for (int i = 1; i < N; ++i) sum = fmaf(post[i], g[i][e], sum);
+      o[e] = sum;
+    }
+    store8<ST, true>(dY + t * d + off, o);
+  }
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    float v = acc[a];
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) v += __shfl_xor(v, sh);
+    acc[a] = v;
+  }
+  if (lane < NA) {
+    float v = acc[0];
+#pragma unroll
+    for (int a = 1; a < NA; ++a) v = (lane == a) ? acc[a] : v;
+    part[(t * nslice + slice) * NA + lane] = v;
+  }
+}
+
+// dH[t][n + a] = sum over slices, in slice order, of part[t][slice][a].
+template <int N>
+__global__ __launch_bounds__(256) void post_bwd_reduce_kernel(int64_t T, int nslice, const float* __restrict__ part,
+                                                              float* __restrict__ dH) {
+  constexpr int M = num_maps(N);
+  constexpr int NA = N * N + N;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (q >= T * NA) return;
+  const int64_t t = q / NA;
+  const int a = static_cast<int>(q - t * NA);
+  const float* src = part + t * nslice * NA + a;
+  float v = src[0];
+  for (int sl = 1; sl < nslice; ++sl) v += src[static_cast<int64_t>(sl) * NA];
+  dH[t * M + N + a] = v;
+}
+
+}  // namespace
+
+size_t post_bwd_workspace_bytes(int64_t T, int n, int d) {
+  if (T <= 0 || d % 512 != 0 || n > 4) return 0;
+  return static_cast<size_t>(T) * static_cast<size_t>(d / 512) * static_cast<size_t>(n * n + n) * sizeof(float);
+}
+
+namespace {
+
 template <typename ST, int N>
 hipError_t launch_post_bwd_t(const mhc_params& p, const void* X, const void* Y, const float* H, const void* G,
-                             void* dX, void* dY, float* dH, hipStream_t stream) {
+                             void* dX, void* dY, float* dH, void* workspace, hipStream_t stream) {
   typedef typename ST::elem E;
+  constexpr int NA = N * N + N;
+  if (workspace != nullptr && post_bwd_workspace_bytes(p.T, N, p.d) > 0) {
+    const int nslice = p.d / 512;
+    const int64_t blocks = (p.T + 3) / 4 * nslice;
+    const int64_t rblocks = (p.T * NA + 255) / 256;
+    if (blocks > 0x7FFFFFFF || rblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    float* part = static_cast<float*>(workspace);
+    hipLaunchKernelGGL((post_bwd_tile_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T,
+                       p.d / 8, nslice, static_cast<const E*>(X), static_cast<const E*>(Y), H,
+                       static_cast<const E*>(G), static_cast<E*>(dX), static_cast<E*>(dY), part);
+    hipLaunchKernelGGL((post_bwd_reduce_kernel<N>), dim3(static_cast<unsigned>(rblocks)), dim3(256), 0, stream, p.T,
+                       nslice, part, dH);
+    return hipGetLastError();
+  }
   const int64_t blocks = (p.T + 3) / 4;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((post_bwd_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T, p.d,
@@ -778,16 +920,16 @@ hipError_t launch_pre_bwd_n(const mhc_params& p, const void* X, const float* phi
 }  // namespace
 
 hipError_t launch_post_bwd(const mhc_params& p, const void* X, const void* Y, const float* H, const void* G, void* dX,
-                           void* dY, float* dH, hipStream_t stream) {
+                           void* dY, float* dH, void* workspace, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   const bool bf = p.dtype == MHC_BF16;
   switch (p.n) {
-    case 1: return bf ? launch_post_bwd_t<BF16, 1>(p, X, Y, H, G, dX, dY, dH, stream)
-                      : launch_post_bwd_t<F32, 1>(p, X, Y, H, G, dX, dY, dH, stream);
-    case 2: return bf ? launch_post_bwd_t<BF16, 2>(p, X, Y, H, G, dX, dY, dH, stream)
-                      : launch_post_bwd_t<F32, 2>(p, X, Y, H, G, dX, dY, dH, stream);
-    case 4: return bf ? launch_post_bwd_t<BF16, 4>(p, X, Y, H, G, dX, dY, dH, stream)
-                      : launch_post_bwd_t<F32, 4>(p, X, Y, H, G, dX, dY, dH, stream);
+    case 1: return bf ? launch_post_bwd_t<BF16, 1>(p, X, Y, H, G, dX, dY, dH, workspace, stream)
+                      : launch_post_bwd_t<F32, 1>(p, X, Y, H, G, dX, dY, dH, workspace, stream);
+    case 2: return bf ? launch_post_bwd_t<BF16, 2>(p, X, Y, H, G, dX, dY, dH, workspace, stream)
+                      : launch_post_bwd_t<F32, 2>(p, X, Y, H, G, dX, dY, dH, workspace, stream);
+    case 4: return bf ? launch_post_bwd_t<BF16, 4>(p, X, Y, H, G, dX, dY, dH, workspace, stream)
+                      : launch_post_bwd_t<F32, 4>(p, X, Y, H, G, dX, dY, dH, workspace, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -189,15 +189,23 @@ mhc_status mhc_post_pre(const mhc_params* p, const void* X, const void* Y, const
                                        static_cast<hipStream_t>(stream)));
 }
 
-mhc_status mhc_post_bwd(const mhc_params* p, const void* X, const void* Y, const float* H, const void* G, void* dX,
-                        void* dY, float* dH, void* stream) {
+size_t mhc_post_bwd_workspace_size(const mhc_params* p) {
+  if (check_params(p) != MHC_OK) return 0;
+  return mhc::post_bwd_workspace_bytes(p->T, p->n, p->d);
+}
+
+mhc_status mhc_post_bwd_ex(const mhc_params* p, const void* X, const void* Y, const float* H, const void* G,
+                           void* dX, void* dY, float* dH, void* workspace, size_t workspace_bytes, void* stream) {
   mhc_status st = check_params(p);
   if (st != MHC_OK) return st;
   if (p->T == 0) return MHC_OK;
   if (p->n > 4) return MHC_ERR_UNSUPPORTED;
   if (!X || !Y || !H || !G || !dX || !dY || !dH) return MHC_ERR_NULL;
+  const size_t need = mhc::post_bwd_workspace_bytes(p->T, p->n, p->d);
+  if (workspace && workspace_bytes < need) return MHC_ERR_WORKSPACE;
+  if (need == 0) workspace = nullptr;
   if (!aligned16(X) || !aligned16(Y) || !aligned16(H) || !aligned16(G) || !aligned16(dX) || !aligned16(dY) ||
-      !aligned16(dH))
+      !aligned16(dH) || !aligned16(workspace))
     return MHC_ERR_ALIGN;
   const int m = p->n * p->n + 2 * p->n;
   const size_t sb = state_bytes(p->dtype);
@@ -205,14 +213,20 @@ mhc_status mhc_post_bwd(const mhc_params* p, const void* X, const void* Y, const
   const size_t yb = static_cast<size_t>(p->T) * p->d * sb;
   const Range ins[4] = {range_of(X, xb), range_of(Y, yb), range_of(H, static_cast<size_t>(p->T) * m * 4),
                         range_of(G, xb)};
-  const Range outs[3] = {range_of(dX, xb), range_of(dY, yb), range_of(dH, static_cast<size_t>(p->T) * m * 4)};
-  for (int a = 0; a < 3; ++a) {
+  const Range outs[4] = {range_of(dX, xb), range_of(dY, yb), range_of(dH, static_cast<size_t>(p->T) * m * 4),
+                         range_of(workspace, workspace ? need : 0)};
+  for (int a = 0; a < 4; ++a) {
     for (int b = 0; b < 4; ++b)
       if (overlap(outs[a], ins[b])) return MHC_ERR_ALIAS;
-    for (int b = a + 1; b < 3; ++b)
+    for (int b = a + 1; b < 4; ++b)
       if (overlap(outs[a], outs[b])) return MHC_ERR_ALIAS;
   }
-  return from_hip(mhc::launch_post_bwd(*p, X, Y, H, G, dX, dY, dH, static_cast<hipStream_t>(stream)));
+  return from_hip(mhc::launch_post_bwd(*p, X, Y, H, G, dX, dY, dH, workspace, static_cast<hipStream_t>(stream)));
+}
+
+mhc_status mhc_post_bwd(const mhc_params* p, const void* X, const void* Y, const float* H, const void* G, void* dX,
+                        void* dY, float* dH, void* stream) {
+  return mhc_post_bwd_ex(p, X, Y, H, G, dX, dY, dH, nullptr, 0, stream);
 }
 
 size_t mhc_pre_bwd_workspace_size(const mhc_params* p) {

@@ -57,8 +57,11 @@ hipError_t launch_pre_partial_with_d(const mhc_params& p, const void* X, const v
                                      const DeviceInfo& dev, hipStream_t stream);
 
 // Backward (bwd.hip).
+// workspace: NULL for the scratch-free form, else post_bwd_workspace_bytes()
+// bytes (that size is 0 where only the scratch-free form applies).
+size_t post_bwd_workspace_bytes(int64_t T, int n, int d);
 hipError_t launch_post_bwd(const mhc_params& p, const void* X, const void* Y, const float* H, const void* G, void* dX,
-                           void* dY, float* dH, hipStream_t stream);
+                           void* dY, float* dH, void* workspace, hipStream_t stream);
 size_t pre_bwd_workspace_bytes(int64_t T, int n, int d, int dtype);
 int pre_bwd_max_tmax();
 hipError_t launch_pre_bwd(const mhc_params& p, const void* X, const float* phi, const float* bias, const void* D,

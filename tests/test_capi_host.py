@@ -173,6 +173,26 @@ def test_post_bwd_argument_checks(lib):
     assert f(_params(T=0), X=None, Y=None, H=None, G=None, dX=None, dY=None, dH=None) == 0
 
 
+def test_post_bwd_ex_workspace(lib):
+    """The tiled form's workspace: T x (d / 512) slices x (n*n + n) floats,
+    0 where d is not a multiple of 512; a short, misaligned or overlapping
+    workspace is refused."""
+    for T, n, d in ((64, 4, 512), (1000, 4, 4096), (7, 2, 1024), (3, 1, 1536)):
+        assert lib.mhc_post_bwd_workspace_size(ctypes.byref(_params(T=T, n=n, d=d))) == T * (d // 512) * (n * n + n) * 4
+    for d in (256, 520, 1000):
+        assert lib.mhc_post_bwd_workspace_size(ctypes.byref(_params(d=d))) == 0
+    assert lib.mhc_post_bwd_workspace_size(ctypes.byref(_params(n=8, d=512))) == 0
+    assert lib.mhc_post_bwd_workspace_size(None) == 0
+    p = _params(d=512)
+    need = lib.mhc_post_bwd_workspace_size(ctypes.byref(p))
+    f = lambda p, ws=A[7], nb=need, dX=A[4]: \
+        lib.mhc_post_bwd_ex(ctypes.byref(p), A[0], A[1], A[2], A[3], dX, A[5], A[6], ws, nb, None)
+    assert f(p, nb=need - 1) == 7                     # WORKSPACE
+    assert f(p, ws=A[7] + 8) == 4                     # ALIGN
+    assert f(p, ws=A[4] + 64) == 6                    # workspace inside dX
+    assert f(_params(n=8, d=512)) == 5
+
+
 def test_pre_bwd_argument_checks(lib):
     p = _params()
     need = lib.mhc_pre_bwd_workspace_size(ctypes.byref(p))
