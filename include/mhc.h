@@ -139,9 +139,18 @@ size_t mhc_pre_workspace_size(const mhc_params* p);
  *                     workgroups (one per compute unit, all on one XCD)
  *                     split d, exchange per-token sums through the XCD's L2
  *                     and keep their slice of X in registers until H_pre is
- *                     known, so X is read once.  Uses a cooperative launch,
- *                     so not on a stream being captured into a HIP graph.
- *                     Returns MHC_ERR_UNSUPPORTED when it does not apply.
+ *                     known, so X is read once.  The team's members wait for
+ *                     each other (bounded waits), so they must be resident
+ *                     together, which an idle device gives an ordinary
+ *                     launch of one workgroup per compute unit.  Should a
+ *                     wait run out (members not resident together), the
+ *                     launches that follow on the stream recompute the
+ *                     call's results with the two-pass form; they are
+ *                     gated on the error word below and otherwise return
+ *                     at once.  Not on a stream being captured into a HIP
+ *                     graph (a replay would reuse the captured call's
+ *                     sequence number).  Returns MHC_ERR_UNSUPPORTED when it
+ *                     does not apply.
  *   MHC_PRE_AUTO      the one-pass form where it measures faster on MI355X
  *                     (n = 4, teams that fill whole XCDs, at least 40 tiles
  *                     per team: T >= 10240 at d = 4096) and the stream is not
@@ -151,10 +160,11 @@ size_t mhc_pre_workspace_size(const mhc_params* p);
  * for a given form); the two forms agree to rounding.
  * algo_used (nullable, host pointer) receives the form that ran.  After a
  * one-pass call, the first 8 bytes of the workspace hold 0, or the
- * sequence number of a one-pass call whose internal wait ran out (its
- * results are invalid); the library never clears it.  A wait can only run
- * out if the workgroups of the launch are not all resident at once, which
- * the cooperative launch rules out. */
+ * sequence number of the last one-pass call whose wait ran out and whose
+ * results the two-pass form therefore recomputed; the library never clears
+ * it.  Testing aid: with the environment variable
+ * MHC_TEST_ONE_PASS_FALLBACK=1 at the call, every workgroup of the single
+ * pass starts as if a wait had run out, so the fallback runs. */
 #define MHC_PRE_AUTO 0
 #define MHC_PRE_TWO_PASS 1
 #define MHC_PRE_ONE_PASS 2

@@ -51,7 +51,6 @@ mhc::DeviceInfo device_info() {
   // Per-device attribute cache; the only state the library keeps.
   static std::mutex mu;
   static int cus[64] = {0};
-  static int coop[64] = {0};
   mhc::DeviceInfo info;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -61,13 +60,9 @@ mhc::DeviceInfo device_info() {
     if (cus[dev] == 0) {
       int v = 0;
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-      int c = 0;
-      if (hipDeviceGetAttribute(&c, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) c = 0;
-      coop[dev] = c ? 1 : -1;
       cus[dev] = v;
     }
     info.num_cus = cus[dev];
-    info.cooperative = coop[dev] > 0;
   }
   return info;
 }

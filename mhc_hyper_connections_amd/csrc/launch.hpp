@@ -13,7 +13,6 @@ namespace mhc {
 struct DeviceInfo {
   int device = 0;
   int num_cus = 256;       // compute units
-  bool cooperative = false;  // cooperative launches (all workgroups co-resident) supported
 };
 
 // mhc_post: stream mixing + broadcast-add.
@@ -39,10 +38,20 @@ hipError_t launch_pre8(const mhc_params& p, const void* X, const float* phi, con
                        void* workspace, const DeviceInfo& dev, hipStream_t stream);
 
 // The single-pass form (pre_fused.hip): hipErrorNotSupported when it does not apply.
+// The first kOnePassHeaderBytes of its workspace hold the error word; its
+// fallback (launch_pre_gated) keeps the two-pass records after them.
+constexpr size_t kOnePassHeaderBytes = 256;
 size_t pre_fused_workspace_bytes(int64_t T, int n, int d);
 bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev);   // what MHC_PRE_AUTO picks
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
                             float* H, void* workspace, size_t ws_bytes, const DeviceInfo& dev, hipStream_t stream);
+
+// The two-pass form on a bf16 state (n <= 4), each kernel gated: it runs
+// only if *gate == gate_value when it starts, else returns at once.  The
+// records go to workspace (pre_partial_bytes of it).
+hipError_t launch_pre_gated(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
+                            float* H, void* workspace, const DeviceInfo& dev, const unsigned long long* gate,
+                            unsigned long long gate_value, hipStream_t stream);
 
 // Split-K partials of mhc_pre's projection plus, per stream i, <D, X_i> over
 // the slice (pre.hip).  part: [S][T][pre_part_width(n, true)] floats with

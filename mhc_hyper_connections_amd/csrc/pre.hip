@@ -55,6 +55,12 @@ constexpr size_t kPartTrashBytes = PRE_THREADS * 16;
 // workgroup takes exactly one tile (blockIdx / S), with no prefetch: the
 // small-T form, which spreads a few tiles over many workgroups; otherwise
 // the workgroups are persistent and walk tiles with two in flight.
+// A gated launch runs only when its gate word holds the expected value; the
+// word was written by an earlier kernel on the stream (agent scope).
+__device__ __forceinline__ bool gate_open(const unsigned long long* gate, unsigned long long value) {
+  return __hip_atomic_load(const_cast<unsigned long long*>(gate), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == value;
+}
+
 template <typename ST, int N, int MB, int MODE, int PWV = PRE_WAVES, bool ONE = false>
 __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d, int S, int64_t ntiles,
                                                                   const typename ST::elem* X,
@@ -62,7 +68,11 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
                                                                   const float* __restrict__ phi,
                                                                   float* __restrict__ part,
                                                                   const float* __restrict__ Hin,
-                                                                  typename ST::elem* Xout) {
+                                                                  typename ST::elem* Xout,
+                                                                  const unsigned long long* gate,
+                                                                  unsigned long long gate_value) {
+  // Gated launch: run only if *gate holds gate_value (see launch_pre_gated).
+  if (gate != nullptr && gate_open(gate, gate_value) == false) return;
   constexpr bool WITH_D = MODE == 1;
   constexpr bool FUSE_POST = MODE == 2;
   constexpr int M = num_maps(N);
@@ -366,7 +376,9 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
                                                          const float* __restrict__ bias, float a_pre,
                                                          float a_res, float a_post, float eps, int t_max,
                                                          typename ST::elem* __restrict__ h,
-                                                         float* __restrict__ H) {
+                                                         float* __restrict__ H, const unsigned long long* gate,
+                                                         unsigned long long gate_value) {
+  if (gate != nullptr && gate_open(gate, gate_value) == false) return;
   constexpr int M = num_maps(N);
   constexpr int NN = N * N;
   constexpr int PW = part_width(N);
@@ -510,7 +522,8 @@ int forward_slices(int64_t T, int d) { return small_t_form(T, d) ? num_slices(d,
 // The finishing pass, in the form of the maps p asks for.
 template <typename ST, int N, bool HC>
 hipError_t launch_finish_t(const mhc_params& p, int S, const void* X, const float* part, const float* bias, void* h,
-                           float* H, hipStream_t stream) {
+                           float* H, hipStream_t stream, const unsigned long long* gate = nullptr,
+                           unsigned long long gate_value = 0) {
   typedef typename ST::elem E;
   // Parts per token: enough waves for the device (~1024) when T is small.
   const int npass = (p.d + 511) / 512;
@@ -523,25 +536,27 @@ hipError_t launch_finish_t(const mhc_params& p, int S, const void* X, const floa
   if (S <= 16)
     hipLaunchKernelGGL((pre_finish_kernel<ST, N, HC, 4>), grid, dim3(256), 0, stream, p.T, p.d, S, ppp,
                        static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post, p.eps, p.t_max,
-                       static_cast<E*>(h), H);
+                       static_cast<E*>(h), H, gate, gate_value);
   else
     hipLaunchKernelGGL((pre_finish_kernel<ST, N, HC, 16>), grid, dim3(256), 0, stream, p.T, p.d, S, ppp,
                        static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post, p.eps, p.t_max,
-                       static_cast<E*>(h), H);
+                       static_cast<E*>(h), H, gate, gate_value);
   return hipGetLastError();
 }
 
 // The finishing pass over S slices' records, in the form of the maps p asks for.
 template <typename ST, int N>
 hipError_t launch_finish(const mhc_params& p, int S, const void* X, const float* part, const float* bias, void* h,
-                         float* H, hipStream_t stream) {
-  return p.maps == MHC_MAPS_HC ? launch_finish_t<ST, N, true>(p, S, X, part, bias, h, H, stream)
-                               : launch_finish_t<ST, N, false>(p, S, X, part, bias, h, H, stream);
+                         float* H, hipStream_t stream, const unsigned long long* gate = nullptr,
+                         unsigned long long gate_value = 0) {
+  return p.maps == MHC_MAPS_HC ? launch_finish_t<ST, N, true>(p, S, X, part, bias, h, H, stream, gate, gate_value)
+                               : launch_finish_t<ST, N, false>(p, S, X, part, bias, h, H, stream, gate, gate_value);
 }
 
 template <typename ST, int N>
 hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
-                        void* workspace, const DeviceInfo& dev, hipStream_t stream) {
+                        void* workspace, const DeviceInfo& dev, hipStream_t stream,
+                        const unsigned long long* gate = nullptr, unsigned long long gate_value = 0) {
   typedef typename ST::elem E;
   float* part = static_cast<float*>(workspace);
   if (small_t_form(p.T, p.d)) {
@@ -552,10 +567,10 @@ hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, co
     hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 0, SMALL_WAVES, true>), dim3(static_cast<unsigned>(S * ntiles)),
                        dim3(SMALL_WAVES * 64), 0, stream, p.T, p.d, S, ntiles, static_cast<const E*>(X),
                        static_cast<const E*>(nullptr), phi, part, static_cast<const float*>(nullptr),
-                       static_cast<E*>(nullptr));
+                       static_cast<E*>(nullptr), gate, gate_value);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_finish<ST, N>(p, S, X, part, bias, h, H, stream);
+    return launch_finish<ST, N>(p, S, X, part, bias, h, H, stream, gate, gate_value);
   }
   constexpr int MB = 2;                  // 32-token tiles: two in flight fit the registers
   constexpr int R = 16 * MB;
@@ -567,10 +582,10 @@ hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, co
   const int64_t grid = groups * S;
   hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 0>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
                      stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(nullptr), phi, part,
-                     static_cast<const float*>(nullptr), static_cast<E*>(nullptr));
+                     static_cast<const float*>(nullptr), static_cast<E*>(nullptr), gate, gate_value);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_finish<ST, N>(p, S, X, part, bias, h, H, stream);
+  return launch_finish<ST, N>(p, S, X, part, bias, h, H, stream, gate, gate_value);
 }
 
 // mhc_post of the previous layer fused into the partial pass (MODE 2), then
@@ -591,7 +606,8 @@ hipError_t launch_post_pre_t(const mhc_params& p, const void* X, const void* Y, 
     const int64_t ntiles = (p.T + R - 1) / R;
     hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 2, SMALL_WAVES, true>), dim3(static_cast<unsigned>(S * ntiles)),
                        dim3(SMALL_WAVES * 64), 0, stream, p.T, p.d, S, ntiles, static_cast<const E*>(X),
-                       static_cast<const E*>(Y), phi, part, Hprev, static_cast<E*>(Xout));
+                       static_cast<const E*>(Y), phi, part, Hprev, static_cast<E*>(Xout),
+                       static_cast<const unsigned long long*>(nullptr), 0ull);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     return launch_finish<ST, N>(p, S, Xout, part, bias, h, H, stream);
@@ -604,7 +620,7 @@ hipError_t launch_post_pre_t(const mhc_params& p, const void* X, const void* Y, 
   const int64_t grid = groups * S;
   hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 2>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
                      stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(Y), phi, part,
-                     Hprev, static_cast<E*>(Xout));
+                     Hprev, static_cast<E*>(Xout), static_cast<const unsigned long long*>(nullptr), 0ull);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_finish<ST, N>(p, S, Xout, part, bias, h, H, stream);
@@ -636,7 +652,8 @@ hipError_t launch_partial_d_t(const mhc_params& p, const void* X, const void* D,
   const int64_t grid = groups * S;
   hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 1>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
                      stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(D), phi, part,
-                     static_cast<const float*>(nullptr), static_cast<E*>(nullptr));
+                     static_cast<const float*>(nullptr), static_cast<E*>(nullptr),
+                     static_cast<const unsigned long long*>(nullptr), 0ull);
   return hipGetLastError();
 }
 
@@ -686,6 +703,19 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
   }
 }
 
+hipError_t launch_pre_gated(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
+                            float* H, void* workspace, const DeviceInfo& dev, const unsigned long long* gate,
+                            unsigned long long gate_value, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  if (p.dtype != MHC_BF16) return hipErrorInvalidValue;
+  switch (p.n) {
+    case 1: return launch_pre_t<BF16, 1>(p, X, phi, bias, h, H, workspace, dev, stream, gate, gate_value);
+    case 2: return launch_pre_t<BF16, 2>(p, X, phi, bias, h, H, workspace, dev, stream, gate, gate_value);
+    case 4: return launch_pre_t<BF16, 4>(p, X, phi, bias, h, H, workspace, dev, stream, gate, gate_value);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 size_t pre_workspace_bytes(int64_t T, int n, int d) {
   if (n == 8) return pre8_workspace_bytes(T, d);
   size_t two_pass = pre_partial_bytes(T, n, d, false);   // persistent form (also mhc_post_pre's)
@@ -695,6 +725,9 @@ size_t pre_workspace_bytes(int64_t T, int n, int d) {
     if (small > two_pass) two_pass = small;
   }
   const size_t one_pass = pre_fused_workspace_bytes(T, n, d);
+  if (one_pass == 0) return two_pass;
+  // The single pass's fallback keeps its records after the error word.
+  two_pass += kOnePassHeaderBytes;
   return two_pass > one_pass ? two_pass : one_pass;
 }
 

@@ -49,12 +49,20 @@
 // before any wave posts, and the team meets on words stamped with the call's
 // sequence number, so words of earlier calls never match.  Every sum runs in
 // a fixed order: results are bitwise reproducible.  All waits are bounded;
-// one that runs out marks the workgroup broken (no further waits; results
-// invalid) and the call's sequence number is stored into the workspace's
-// error word.  The launch is cooperative (all workgroups co-resident).  The
-// exchange and Sinkhorn waves run at a raised issue priority: the streaming
-// waves have slack, the exchange is on every tile's critical path.
+// one that runs out marks the workgroup broken (no further waits; its
+// results are garbage, its writes stay in bounds) and the call's sequence
+// number is stored into the workspace's error word.
+// The launch is an ordinary one of one workgroup per CU, which on an idle
+// device makes every team resident together; a cooperative launch would
+// guarantee it but costs about 16 us more per call on MI355X.  The guarantee
+// is replaced by a fallback: the two-pass form is launched behind the single
+// pass, each of its kernels gated on the error word holding this call's
+// sequence number, so it recomputes every output when a wait ran out and
+// otherwise returns at once (about 3 us for the two launches).
+// The exchange and Sinkhorn waves run at a raised issue priority: the
+// streaming waves have slack, the exchange is on every tile's critical path.
 #include <atomic>
+#include <cstdlib>
 
 #include "launch.hpp"
 #include "pre_common.hpp"
@@ -79,10 +87,11 @@ constexpr int OKR = 4;                  // LDS ring of Sinkhorn inputs (tiles; t
 constexpr int OD = 5;                   // tiles between a tile's partials and its h; see below
 constexpr int OP = 2;                   // X tiles in flight ahead of the one being multiplied
 constexpr int ONB = OD + OP;            // X tile buffers per lane
-constexpr size_t OHDR = 256;            // workspace header: the error word
+constexpr size_t OHDR = kOnePassHeaderBytes;   // workspace header: the error word
 constexpr int OXCD = 8;                 // XCDs of the device (MI355X)
 constexpr unsigned kLdsSpin = 1u << 20; // bounded waits: far beyond any legitimate one
 constexpr unsigned kMemSpin = 1u << 16;
+constexpr unsigned kStartSpin = 1u << 12; // the team's meeting: members start within microseconds of each other
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: loads read 0, stores drop
 
 // Progress and slot reuse.  In step k a streaming wave writes tile k's
@@ -118,6 +127,7 @@ struct OneArgs {
   int64_t slotw;   // words per slot: S * OR * record words, then OR * n H_pre words
   u64 epoch;       // sequence number of the call (never 0)
   int xbytes, hbytes;
+  int force_break; // testing aid: every workgroup starts broken, so the call falls back
 };
 
 __device__ __forceinline__ u64 xword(uint32_t v, uint32_t tag) {
@@ -231,9 +241,12 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
   if (tid == 0) {
     xcc_l = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7);   // HW_REG_XCC_ID
     for (int q = 0; q < OMR; ++q) maps_tag[q] = 0;
-    for (int q = 0; q < OKR; ++q) sk_tag[q] = 0;
+    for (int q = 0; q < OKR; ++q) {
+      sk_tag[q] = 0;
+      for (int o = 0; o < OTPR; ++o) sktok[q][o] = -1;
+    }
     sk_free = 0;
-    broken = 0;
+    broken = a.force_break;
   }
   if (tid < OW) {
     part_ready[tid] = 0;
@@ -526,7 +539,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
       unsigned n = 0;
       while (agent_load(st + lane) != a.epoch) {
         if (flag_get(vbroken)) break;
-        if (++n > kMemSpin) {
+        if (++n > kStartSpin) {
           flag_set(vbroken, 1);
           break;
         }
@@ -688,7 +701,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
       if (lane == 0) flag_set(&sk_free, jn);
       float mv = in.x;
       if constexpr (!HC) mv = sinkhorn16<N>(e < NN ? in.x : -INFINITY, e, a.t_max);
-      if (t >= 0) {
+      if (t >= 0 && t < a.T) {             // (a broken workgroup may read a slot before it is written)
         float* Ht = a.H + t * M;
         if (e < NN) Ht[N + e] = mv;
         if (e < 2 * N) Ht[colg] = in.y;
@@ -729,7 +742,7 @@ size_t pre_fused_workspace_bytes(int64_t /*T*/, int n, int d) {
 // T = 16384, d = 4096: 194 us against 227 us); for n <= 2 a tile carries too
 // little data to hide the exchange.
 bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev) {
-  if (p.dtype != MHC_BF16 || p.n != 4 || !dev.cooperative || dev.num_cus % OXCD != 0) return false;
+  if (p.dtype != MHC_BF16 || p.n != 4 || dev.num_cus % OXCD != 0) return false;
   const int S = one_pass_slices(p.d);
   const int per_xcd = dev.num_cus / OXCD;
   if (S < OS_MIN || S > OS_MAX || per_xcd % S != 0) return false;
@@ -742,15 +755,13 @@ bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev) {
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
                             float* H, void* workspace, size_t ws_bytes, const DeviceInfo& dev, hipStream_t stream) {
   if (p.dtype != MHC_BF16 || (p.n != 4 && p.n != 2 && p.n != 1)) return hipErrorNotSupported;
-  // Not under stream capture: a graph replays the kernel without the
-  // cooperative launch's residency guarantee and with the captured call's
-  // sequence number, so the team's meeting could not be trusted (measured:
-  // every replay's waits ran out).
+  // Not under stream capture: a graph replays the captured call's sequence
+  // number, so words left by the previous replay would pass for this one's.
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone)
     return hipErrorNotSupported;
   const int S = one_pass_slices(p.d);
-  if (S < OS_MIN || S > OS_MAX || !dev.cooperative || dev.num_cus % OXCD != 0) return hipErrorNotSupported;
+  if (S < OS_MIN || S > OS_MAX || dev.num_cus % OXCD != 0) return hipErrorNotSupported;
   const int per_xcd = dev.num_cus / OXCD;
   const int tpx = per_xcd / S;
   if (tpx < 1) return hipErrorNotSupported;
@@ -800,8 +811,14 @@ hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi
   a.epoch = ++g_epoch;
   a.xbytes = static_cast<int>(xbytes);
   a.hbytes = static_cast<int>(hbytes);
+  const char* fb = std::getenv("MHC_TEST_ONE_PASS_FALLBACK");
+  a.force_break = (fb != nullptr && fb[0] == '1') ? 1 : 0;
   void* args[] = {&a};
-  return hipLaunchCooperativeKernel(fn, dim3(dev.num_cus), dim3(OT), args, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3(dev.num_cus), dim3(OT), args, 0, stream);
+  if (e != hipSuccess) return e;
+  // The fallback: the two-pass form, gated on this call's sequence number in
+  // the error word, so it runs only if a wait of the single pass ran out.
+  return launch_pre_gated(p, X, phi, bias, h, H, base + OHDR, dev, a.hdr, a.epoch, stream);
 }
 
 }  // namespace mhc

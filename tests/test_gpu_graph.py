@@ -1,8 +1,8 @@
 """The forward step captured into a HIP graph (torch.cuda.CUDAGraph).
 
-mhc_pre's single pass relies on a cooperative launch and a per-call sequence
-number, which a graph cannot reproduce, so on a capturing stream MHC_PRE_AUTO
-takes the two-pass form and MHC_PRE_ONE_PASS is refused.  The captured step
+mhc_pre's single pass stamps its exchange words with a per-call sequence
+number, which a graph replay would repeat, so on a capturing stream
+MHC_PRE_AUTO takes the two-pass form and MHC_PRE_ONE_PASS is refused.  The captured step
 (mhc_pre, mhc_post, mhc_amax) is replayed several times with eager work and
 synchronisations in between; every replay must give the eager two-pass
 results bit for bit.

@@ -160,3 +160,37 @@ def test_large_state_sum_of_squares(mhc, oracle_lib):
         assert np.all(np.isfinite(H))
         assert_close(H, ref["H"], *TOL[("bf16", "maps")], what=f"large state H ({algo})")
         assert_close(h, ref["h"], *TOL[("bf16", "state")], what=f"large state h ({algo})")
+
+
+@pytest.mark.parametrize("maps", ["mhc", "hc"])
+@pytest.mark.parametrize("T", [300, 4100])
+def test_one_pass_fallback(mhc, monkeypatch, T, maps):
+    """A single pass whose waits run out is recomputed by the gated two-pass
+    launches that follow it.  The library's testing switch makes every
+    workgroup start broken (the condition a team that is not all resident
+    meets): the call must still return the two-pass form's results bit for
+    bit, leave a non-zero sequence number in the error word, and the next
+    call without the switch must leave that word alone and give the same
+    results."""
+    w = synth.scaled(synth.WORKLOADS["layer_bf16_T16384_d4096"], T=T)
+    code = mhc.MAPS_HC if maps == "hc" else mhc.MAPS_MHC
+    X = to_device(synth.make_state(w))
+    phi, bias = (to_device(a) for a in synth.make_params(w))
+    alpha = (0.9, 1.1, 0.7)
+    ws = torch.full((mhc.pre_workspace_size(w.T, w.n, w.d, w.dtype),), 0xA5, dtype=torch.uint8, device="cuda")
+    ws[:8].zero_()
+    h2, H2, used2 = mhc.pre_ex(X, phi, bias, mhc.PRE_TWO_PASS, alpha=alpha, maps=code)
+    ref = (to_host(h2).copy(), to_host(H2).copy())
+    monkeypatch.setenv("MHC_TEST_ONE_PASS_FALLBACK", "1")
+    h1, H1, used1 = mhc.pre_ex(X, phi, bias, mhc.PRE_ONE_PASS, alpha=alpha, workspace=ws, maps=code)
+    torch.cuda.synchronize()
+    err = int(ws[:8].view(torch.int64).item())
+    assert used1 == mhc.PRE_ONE_PASS and err != 0
+    assert np.array_equal(to_host(h1), ref[0]) and np.array_equal(to_host(H1), ref[1])
+    monkeypatch.delenv("MHC_TEST_ONE_PASS_FALLBACK")
+    h3, H3, used3 = mhc.pre_ex(X, phi, bias, mhc.PRE_ONE_PASS, alpha=alpha, workspace=ws, maps=code)
+    torch.cuda.synchronize()
+    assert int(ws[:8].view(torch.int64).item()) == err          # never cleared by the library
+    h4, H4, _ = mhc.pre_ex(X, phi, bias, mhc.PRE_ONE_PASS, alpha=alpha, maps=code)
+    assert np.array_equal(to_host(h3), to_host(h4)) and np.array_equal(to_host(H3), to_host(H4))
+    assert np.max(np.abs(to_host(H3).astype(np.float64) - ref[1])) < 1e-5
