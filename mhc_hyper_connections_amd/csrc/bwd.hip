@@ -529,7 +529,11 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(int64_t count, float* __
 constexpr int AM_WAVES = 8;
 constexpr int AM_THREADS = AM_WAVES * 64;
 constexpr int AM_SLICE = AM_WAVES * 32;
-constexpr int XS_PITCH = 36;      // halfwords per token row of the LDS tile: the column reads hit distinct banks
+// The tile's X and D go through LDS: loaded with each instruction covering 2
+// token rows x 512 bytes (wave w: tokens 2w, 2w+1, lane = 16-byte chunk of
+// the slice; on MI355X that streams faster than 16 rows x 64 bytes), read
+// back in the MFMA layouts.  16 bytes of padding per token put the 16
+// tokens of a read on distinct banks.
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -573,7 +577,8 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
   constexpr int TW = tok_width(N);
   constexpr int NJB = (M + 15) / 16;
   constexpr int NGQ = (M + 7) / 8;                 // lane groups with any column j < m
-  __shared__ uint16_t xs[AM_WAVES][N][16][XS_PITCH];
+  constexpr int STS = (N + 1) * 512 + 16;          // LDS bytes per token: n streams, D, padding
+  __shared__ __attribute__((aligned(16))) unsigned char stage_l[16 * STS];
   __shared__ bf16x8 phl[AM_WAVES][N][2][NGQ * 16][2];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -583,6 +588,11 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
   const int j0 = c0w + 8 * g;
   const bool jv = j0 < d;
   const int jl = jv ? j0 : 0;
+  // Load layout: token row trow of the tile, 8 positions at jl0.
+  const int trow = 2 * w + (lane >> 5);
+  const int jl0 = blockIdx.x * AM_SLICE + 8 * (lane & 31);
+  const bool jvl = jl0 < d;
+  const int jll = jvl ? jl0 : 0;
   const bool gq = g < NGQ;
   const int lq = gq ? lane : 0;
 
@@ -618,11 +628,13 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
   const int64_t ntile = (t_end - t_begin + 15) / 16;
 
   auto load = [&](int64_t q, ApplyTile<N>& b) {
+    const int64_t tl = t_begin + q * 16 + trow;
+    const int64_t ttl = tl < t_end ? tl : 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) b.x[i] = load_raw8<BF16>(X + (ttl * N + i) * d + jll);
+    b.dv = load_raw8<BF16>(D + ttl * d + jll);
     const int64_t t = t_begin + q * 16 + r16;
     const int64_t tt = t < t_end ? t : 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i) b.x[i] = load_raw8<BF16>(X + (tt * N + i) * d + jl);
-    b.dv = load_raw8<BF16>(D + tt * d + jl);
     const float* rec = tok + tt * TW;
     b.ga = *reinterpret_cast<const f32x4*>(rec + 8 * g);
     b.gb = *reinterpret_cast<const f32x4*>(rec + 8 * g + 4);
@@ -651,6 +663,21 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
   auto step = [&](int64_t q, ApplyTile<N>& b) {
     const int64_t t = t_begin + q * 16 + r16;
     const bool ok = t < t_end && jv;
+    {
+      // Through LDS: zeros for tokens past the chunk and positions past d
+      // (the dphi contraction below reads them), then the A layout back.
+      const bool okl = t_begin + q * 16 + trow < t_end && jvl;
+      unsigned char* row = stage_l + trow * STS + (lane & 31) * 16;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        *reinterpret_cast<u32x4*>(row + i * 512) = okl ? b.x[i].v : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(row + N * 512) = okl ? b.dv.v : u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
+      const unsigned char* rd = stage_l + r16 * STS + (32 * w + 8 * g) * 2;
+#pragma unroll
+      for (int i = 0; i < N; ++i) b.x[i].v = *reinterpret_cast<const u32x4*>(rd + i * 512);
+      b.dv.v = *reinterpret_cast<const u32x4*>(rd + N * 512);
+    }
     float gf[8] = {b.ga[0], b.ga[1], b.ga[2], b.ga[3], b.gb[0], b.gb[1], b.gb[2], b.gb[3]};
     bf16x8 ghi, glo;
     split_bf16(gf, ghi, glo);
@@ -679,10 +706,6 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
         r[4 + e] = xo[4 + e] + fmaf(b.hp[i], dv[4 + e], o[1][e] - b.coef * x[4 + e]);
       }
       if (ok) store8<BF16>(dX + (t * N + i) * d + j0, r);     // the one branch around memory: a store
-      const u32x4 xv = ok ? b.x[i].v : u32x4{0u, 0u, 0u, 0u};
-      uint32_t* row = reinterpret_cast<uint32_t*>(&xs[w][i][r16][8 * g]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) row[k] = xv[k];
     }
     load_dx(q + 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -700,7 +723,8 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
         for (int bb = 0; bb < 2; ++bb) {
           s16x4 a;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) a[u] = static_cast<short>(xs[w][i][4 * g + u][16 * bb + r16]);
+          for (int u = 0; u < 4; ++u)
+            a[u] = *reinterpret_cast<const short*>(stage_l + (4 * g + u) * STS + i * 512 + (32 * w + 16 * bb + r16) * 2);
           f32x4 c = acc[2 * i + bb][jb];
           c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, blo, c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bhi, c, 0, 0, 0);
