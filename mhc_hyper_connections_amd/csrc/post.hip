@@ -12,7 +12,7 @@
 // When d/8 is a multiple of 64 (d a multiple of 512) the tiled kernel runs: a
 // workgroup covers 4 tokens x 512 values of d, one token per wave, and
 // consecutive workgroups walk along d before moving to the next 4 tokens.  The
-// token index is then wave-uniform and the 20 map values come in through
+// token index is then wave-uniform and the n*n + n map values come in through
 // scalar loads.  On MI355X this order streams faster than giving a
 // workgroup whole tokens (a layout probe moving the same bytes: 180 us
 // against 211 us at T = 16384, n = 4, d = 4096).

@@ -50,6 +50,14 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
   constexpr bool GRAM = std::is_same<ST, BF16>::value;
   __shared__ f32x4 red[P8_WAVES][R][M / 4];
   __shared__ double red_ss[P8_WAVES][R];
+  // bf16: the tile arrives with each load instruction covering one token's
+  // 8 stream rows x 128 bytes (the slice), goes through LDS and is read
+  // back in the MFMA A layout; 16 bytes of padding per token keep the 16
+  // tokens of a read on distinct banks.
+  constexpr bool STAGE = GRAM;
+  static_assert(!STAGE || MB == 2, "the staged layout gives each wave 4 of the tile's 32 tokens");
+  constexpr int STS = N * 128 + 16;
+  __shared__ __attribute__((aligned(16))) unsigned char stage_l[STAGE ? R * STS : 16];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -83,17 +91,48 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
 
   // Unconditional loads from valid addresses: tokens past T read token 0,
   // lanes past d read position 0 (zero phi rows; their squares are masked).
+  // Staged load layout: load k of wave w covers token 4 w + k of the tile
+  // (8 per mb block), stream lane / 8, 8 positions at jls.
+  const int sst = lane >> 3;
+  const int jls0 = s * P8_SLICE + 8 * (lane & 7);
+  const bool jvs = jls0 < d;
+  const int jls = jvs ? jls0 : 0;
   auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][2]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int64_t t = tile * R + mb * 16 + r16;
-      const int64_t tt = t < T ? t : 0;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) x[mb][q] = load_raw8<ST>(X + (tt * N + 2 * sp + q) * d + jl);
+      for (int q = 0; q < 2; ++q) {
+        if constexpr (STAGE) {
+          const int64_t t = tile * R + 4 * w + 2 * mb + q;
+          const int64_t tt = t < T ? t : 0;
+          x[mb][q] = load_raw8<ST>(X + (tt * N + sst) * d + jls);
+        } else {
+          const int64_t t = tile * R + mb * 16 + r16;
+          const int64_t tt = t < T ? t : 0;
+          x[mb][q] = load_raw8<ST>(X + (tt * N + 2 * sp + q) * d + jl);
+        }
+      }
     }
   };
 
   auto step = [&](int64_t tile, Raw8<ST> (&cur)[MB][2], int64_t next) {
+    if constexpr (STAGE) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          *reinterpret_cast<u32x4*>(stage_l + (4 * w + 2 * mb + q) * STS + sst * 128 + (lane & 7) * 16) =
+              cur[mb][q].v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          cur[mb][q].v = *reinterpret_cast<const u32x4*>(stage_l + (mb * 16 + r16) * STS + (2 * sp + q) * 128 +
+                                                         (32 * pg + 8 * g) * 2);
+      }
+    }
     f32x4 acc[MB][P8_CB];
     double sq[MB];
 #pragma unroll
