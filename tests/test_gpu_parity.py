@@ -79,7 +79,10 @@ def test_layer_full_size_sampled(mhc, oracle_lib, name):
     _layer(mhc, oracle_lib, w, tokens=tok)
 
 
-EDGE = [(n, d, T, dt) for n in (1, 2, 4) for (d, T) in ((8, 1), (24, 17), (264, 65), (520, 33), (2048 + 8, 5))
+# d = 512 and 1536: multiples of 512, where mhc_post takes its tiled kernel (4-token tiles; T = 3 and 9
+# leave a partial last tile).
+EDGE = [(n, d, T, dt) for n in (1, 2, 4)
+        for (d, T) in ((8, 1), (24, 17), (264, 65), (520, 33), (2048 + 8, 5), (512, 3), (1536, 9))
         for dt in (synth.FP32, synth.BF16)]
 
 
