@@ -69,6 +69,33 @@ def test_layer_every_token(mhc, oracle_lib, name, changes, alpha):
     _layer(mhc, oracle_lib, w, alpha=alpha)
 
 
+PERSISTENT = [
+    # (n, d, T): enough tokens for the persistent two-pass form (ceil(T / 32) * ceil(d / 256) >= 128),
+    # whose bf16 tiles go through LDS; ragged slices of d and ragged last tiles
+    (4, 2056, 600),
+    (2, 264, 2100),
+    (1, 4096, 300),
+    (4, 1024, 1100),
+]
+
+
+@pytest.mark.parametrize("n,d,T", PERSISTENT, ids=[f"n{c[0]}_d{c[1]}_T{c[2]}" for c in PERSISTENT])
+def test_two_pass_persistent_every_token(mhc, oracle_lib, n, d, T):
+    """The persistent two-pass mhc_pre (LDS-staged bf16 tiles) against the
+    oracle on every token, at alpha = 1."""
+    w = synth.Workload(f"persist_n{n}_d{d}", T=T, n=n, d=d, dtype=synth.BF16, seed=6100 + n + d)
+    X = synth.make_state(w)
+    phi, bias = synth.make_params(w)
+    alpha = (1.0, 1.0, 1.0)
+    h, H, used = mhc.pre_ex(to_device(X), to_device(phi), to_device(bias), mhc.PRE_TWO_PASS, alpha=alpha,
+                            eps=w.eps, t_max=w.t_max)
+    torch.cuda.synchronize()
+    assert used == mhc.PRE_TWO_PASS
+    ref = oracle_lib.pre(X, phi, bias, alpha, eps=w.eps, t_max=w.t_max)
+    assert_close(to_host(H), ref["H"], *TOL[("bf16", "maps")], what=f"{w.name} H")
+    assert_close(to_host(h), ref["h"], *TOL[("bf16", "state")], what=f"{w.name} h")
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["layer_bf16_T4096_d2048", "layer_bf16_T16384_d4096"])
 def test_layer_full_size_sampled(mhc, oracle_lib, name):
