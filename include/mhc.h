@@ -97,8 +97,8 @@ typedef struct mhc_params {
  * "Kernmechanismen": a static bias plus an input-dependent term through
  * tanh, any sign), read as H = bias + alpha_blk * tanh(z) for all three maps,
  * no Sinkhorn.  The same z = x_hat . phi feeds both.  mhc_pre, mhc_pre_ex
- * (two-pass form only) and mhc_post_pre accept both; mhc_pre_bwd takes the
- * mHC form only (MHC_ERR_UNSUPPORTED otherwise). */
+ * (either form) and mhc_post_pre accept both; mhc_pre_bwd takes the mHC form
+ * only (MHC_ERR_UNSUPPORTED otherwise). */
 #define MHC_MAPS_MHC 0
 #define MHC_MAPS_HC 1
 
@@ -191,7 +191,8 @@ mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const flo
  *   X_out = H_res X + H_post^T Y            (layer l's maps H, as mhc_post)
  * and, from the stored X_out, layer l+1's maps H_next and its sublayer input
  * h (as mhc_pre with phi, bias and p's alphas / eps / t_max).  The results
- * are bitwise those of mhc_post followed by mhc_pre; the second read of X_out
+ * are bitwise those of mhc_post followed by mhc_pre in its two-pass form
+ * (MHC_PRE_TWO_PASS; the single pass agrees to rounding); the second read of X_out
  * that the separate calls make for the projection is saved (the pages fuse
  * the layer's kernels for the same reason: [t6] tbl-dsv4-mhc-kernels).
  *   X       in   [T, n, d] layer l's input state
