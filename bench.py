@@ -316,7 +316,7 @@ ENTRY_KERNELS = {
     "mhc_post": ["post_tile_kernel<mhc::BF16, 4>"],
     "mhc_amax": ["amax_kernel<4>"],
     "mhc_post_bwd": ["post_bwd_tile_kernel<mhc::BF16, 4>", "post_bwd_reduce_kernel<4>"],
-    "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 2, 1, 8, false>", "pre_bwd_token_kernel<4>",
+    "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 2, 1, 8, false>", "pre_bwd_token_kernel<4, true>",
                     "pre_bwd_apply_mfma_kernel<4>", "reduce_chunks_kernel", "reduce_columns_kernel"],
 }
 ENTRY_SOURCES = {

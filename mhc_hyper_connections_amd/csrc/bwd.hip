@@ -302,7 +302,12 @@ hipError_t launch_post_bwd_t(const mhc_params& p, const void* X, const void* Y, 
 // Also writes g transposed in blocks of 32 tokens, gT[t / 32][j][t % 32]
 // (j < 32, zero for j >= m and for the padding tokens T <= t < Tpad), the
 // operand layout of the dphi contraction over tokens in launch C.
-template <int N>
+// REG: t_max <= kRegTmax, the iterates stay in registers (no LDS, so more
+// waves per CU hide the latency of the serial Sinkhorn chain); otherwise
+// they go to LDS.
+constexpr int kRegTmax = 20;
+
+template <int N, bool REG>
 __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tpad, int d, int S, int PW, int SSO,
                                                            const float* __restrict__ part,
                                                            const float* __restrict__ bias, float a_pre,
@@ -347,17 +352,33 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
   if (t_max == 0) mx = 0.0f;
   const float m0 = is_res ? expf(lr - mx) : 0.0f;
   float mv = m0;
-  for (int it = 0; it < t_max; ++it) {
-    iters[(2 * it) * 64 + lane] = mv;
+  float itr[REG ? 2 * kRegTmax : 1];
+  auto put = [&](int k, float v) {
+    if constexpr (REG) itr[k] = v;
+    else iters[k * 64 + lane] = v;
+  };
+  auto get = [&](int k) -> float {
+    if constexpr (REG) return itr[k];
+    else return iters[k * 64 + lane];
+  };
+  auto sk_pass = [&](int it) {
+    put(2 * it, mv);
     float cs = mv;
 #pragma unroll
     for (int off = N; off < NN; off <<= 1) cs += __shfl_xor(cs, off);
     mv = mv / cs;
-    iters[(2 * it + 1) * 64 + lane] = mv;
+    put(2 * it + 1, mv);
     float rs = mv;
 #pragma unroll
     for (int off = 1; off < N; off <<= 1) rs += __shfl_xor(rs, off);
     mv = mv / rs;
+  };
+  if constexpr (REG) {
+#pragma unroll
+    for (int it = 0; it < kRegTmax; ++it)
+      if (it < t_max) sk_pass(it);
+  } else {
+    for (int it = 0; it < t_max; ++it) sk_pass(it);
   }
 
   // Gradients arriving at the maps: res and post from mhc_post_bwd, pre from <D, X_i>.
@@ -367,8 +388,8 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
   else if (is_gate && tv) dgate = dH[t * M + colg];
 
   // Sinkhorn in reverse.  Step 2 it normalised columns, step 2 it + 1 rows.
-  for (int st = 2 * t_max - 1; st >= 0; --st) {
-    const float A = iters[st * 64 + lane];
+  auto sk_back = [&](int st) {
+    const float A = get(st);
     const bool col = (st & 1) == 0;
     float sum = A, dot;
     if (col) {
@@ -388,6 +409,13 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
       for (int off = 1; off < N; off <<= 1) dot += __shfl_xor(dot, off);
     }
     dm = (dm - dot) / sum;
+  };
+  if constexpr (REG) {
+#pragma unroll
+    for (int st = 2 * kRegTmax - 1; st >= 0; --st)
+      if (st < 2 * t_max) sk_back(st);
+  } else {
+    for (int st = 2 * t_max - 1; st >= 0; --st) sk_back(st);
   }
   // exp: the per-token max shift cancels (it scales M0 and dM0 inversely).
   const float dl_res = is_res ? dm * m0 : 0.0f;
@@ -898,9 +926,14 @@ hipError_t launch_pre_bwd_t(const mhc_params& p, const void* X, const float* phi
   if (tblocks > 0x7FFFFFFF || kblocks_of(K) > 0x7FFFFFFF) return hipErrorInvalidValue;
   const size_t lds = static_cast<size_t>(2 * (p.t_max > 0 ? p.t_max : 1)) * 64 * sizeof(float);
   if (tblocks > 0) {
-    hipLaunchKernelGGL((pre_bwd_token_kernel<N>), dim3(static_cast<unsigned>(tblocks)), dim3(64), lds, stream, p.T,
-                       L.Tpad, p.d, L.S, L.PW, L.SSO, static_cast<const float*>(part), bias, p.alpha_pre, p.alpha_res,
-                       p.alpha_post, p.eps, p.t_max, dH, tok, gT, pg);
+    if (p.t_max <= kRegTmax)
+      hipLaunchKernelGGL((pre_bwd_token_kernel<N, true>), dim3(static_cast<unsigned>(tblocks)), dim3(64), 0, stream,
+                         p.T, L.Tpad, p.d, L.S, L.PW, L.SSO, static_cast<const float*>(part), bias, p.alpha_pre,
+                         p.alpha_res, p.alpha_post, p.eps, p.t_max, dH, tok, gT, pg);
+    else
+      hipLaunchKernelGGL((pre_bwd_token_kernel<N, false>), dim3(static_cast<unsigned>(tblocks)), dim3(64), lds, stream,
+                         p.T, L.Tpad, p.d, L.S, L.PW, L.SSO, static_cast<const float*>(part), bias, p.alpha_pre,
+                         p.alpha_res, p.alpha_post, p.eps, p.t_max, dH, tok, gT, pg);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
