@@ -259,16 +259,18 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
         }
         ss[mb] = (g == (r16 >> 2)) ? sq : 0.0;
         if constexpr (WITH_D) {
-          float dv[8];
-          unpack8(cur[mb][N], dv);
+          // <D, X_i> over the wave's 32 positions: the diagonal of the 16 x 16
+          // product X_i D^T on MFMA (D's A-layout registers are the B operand
+          // of D^T), entry (t, t) in lane 16 (t / 4) + t, element t % 4, like
+          // the sum of squares; lanes past d hold zeros in xm.
+          const bf16x8 dvb = __builtin_bit_cast(bf16x8, cur[mb][N].v);
 #pragma unroll
           for (int i = 0; i < N; ++i) {
-            float x[8];
-            unpack8(cur[mb][i], x);
-            float a = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a = fmaf(dv[e], x[e], a);
-            dd[mb][i] = jv ? a : 0.0f;
+            const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xm[i].v), dvb,
+                                                                     f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            const int dvi = r16 & 3;
+            const float dg = dvi == 0 ? c[0] : dvi == 1 ? c[1] : dvi == 2 ? c[2] : c[3];
+            dd[mb][i] = (g == (r16 >> 2)) ? dg : 0.0f;
           }
         }
       } else {
@@ -319,10 +321,14 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
       if (WITH_D) {
 #pragma unroll
         for (int i = 0; i < ND; ++i) {
-          float a = dd[mb][i];
-          a += __shfl_xor(a, 16);
-          a += __shfl_xor(a, 32);
-          if (g == 0) red[w][mb * 16 + r16][M + i] = a;
+          if constexpr (GRAM) {
+            if (g == (r16 >> 2)) red[w][mb * 16 + r16][M + i] = dd[mb][i];
+          } else {
+            float a = dd[mb][i];
+            a += __shfl_xor(a, 16);
+            a += __shfl_xor(a, 32);
+            if (g == 0) red[w][mb * 16 + r16][M + i] = a;
+          }
         }
       }
     }
