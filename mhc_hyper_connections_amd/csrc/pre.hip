@@ -219,7 +219,8 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
     // whose fp32 sum overflows; entry (t, t) sits in lane 16 (t / 4) + t,
     // element t % 4, and covers the wave's 4 lane groups.  fp32 state: fp64
     // per lane, added over the 4 groups below.  Either never overflows for
-    // a finite state.  <D, X_i> (with D) is fp32 per lane either way.
+    // a finite state.  <D, X_i> (with D): bf16, the diagonal of X_i D^T on
+    // MFMA (fp32 accumulation); fp32, per lane.
     constexpr bool GRAM = std::is_same<ST, BF16>::value;
     double ss[MB];
     float dd[MB][ND > 0 ? ND : 1];
