@@ -163,8 +163,8 @@ def test_large_state_sum_of_squares(mhc, oracle_lib):
 
 
 @pytest.mark.parametrize("maps", ["mhc", "hc"])
-@pytest.mark.parametrize("T", [300, 4100])
-def test_one_pass_fallback(mhc, monkeypatch, T, maps):
+@pytest.mark.parametrize("T,n", [(300, 4), (4100, 4), (1024, 2), (1024, 1)])
+def test_one_pass_fallback(mhc, monkeypatch, T, n, maps):
     """A single pass whose waits run out is recomputed by the gated two-pass
     launches that follow it.  The library's testing switch makes every
     workgroup start broken (the condition a team that is not all resident
@@ -172,7 +172,7 @@ def test_one_pass_fallback(mhc, monkeypatch, T, maps):
     bit, leave a non-zero sequence number in the error word, and the next
     call without the switch must leave that word alone and give the same
     results."""
-    w = synth.scaled(synth.WORKLOADS["layer_bf16_T16384_d4096"], T=T)
+    w = synth.Workload(f"fallback_T{T}_n{n}", T=T, n=n, d=4096, dtype=synth.BF16, seed=7300 + T + n)
     code = mhc.MAPS_HC if maps == "hc" else mhc.MAPS_MHC
     X = to_device(synth.make_state(w))
     phi, bias = (to_device(a) for a in synth.make_params(w))
