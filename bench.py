@@ -315,6 +315,50 @@ def time_small_t(mhc, torch, reps=100):
     return out
 
 
+def time_small_configs(mhc, torch, reps=50):
+    """The forward step (mhc_pre -> Y given -> mhc_post -> mhc_amax) on the
+    two smaller single-layer workloads, T = 64, d = 256 fp32 and T = 4096,
+    d = 2048 bf16, with the generator's inputs: per step and tokens/s."""
+    import numpy as np
+
+    import synth
+    out = []
+    for name in ("layer_fp32_T64_d256", "layer_bf16_T4096_d2048"):
+        w = synth.WORKLOADS[name]
+
+        def dev(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+            return torch.from_numpy(a).cuda()
+
+        X, Y = dev(synth.make_state(w)), dev(synth.make_sublayer_out(w))
+        phi, bias = (dev(a) for a in synth.make_params(w))
+        T, n, d, m = w.T, w.n, w.d, w.m
+        h = torch.empty((T, d), dtype=X.dtype, device="cuda")
+        H = torch.empty((T, m), dtype=torch.float32, device="cuda")
+        Xo = torch.empty_like(X)
+        amax = torch.empty(T, dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(16, mhc.pre_workspace_size(T, n, d, w.dtype)), dtype=torch.uint8, device="cuda")
+
+        def step():
+            mhc.pre(X, phi, bias, alpha=w.alpha, eps=w.eps, t_max=w.t_max, h=h, H=H, workspace=ws)
+            mhc.post(X, Y, H, out=Xo)
+            mhc.amax(H.view(1, T, m), n, out_amax=amax, want_all=False)
+
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            step()
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) / reps * 1e3
+        out.append({"workload": name, "us_per_step": us, "tokens_per_s": T / (us * 1e-6)})
+    return out
+
+
 def time_n8(mhc, torch, T=16384, d=4096, reps=10):
     """mhc_pre and mhc_post at n = 8 streams (m = 80, bf16, random inputs of
     the layer's distributions), per call, with their algorithmic GB/s."""
@@ -690,6 +734,9 @@ def main():
     log("mhc_pre forms: " + ", ".join(f"{k} {v['avg_us']:.1f} us" for k, v in forms.items() if v))
 
     n8 = time_n8(mhc, torch)
+    small_cfg = time_small_configs(mhc, torch)
+    log("smaller layers (forward step): " + ", ".join(
+        f"{r['workload']} {r['us_per_step']:.1f} us ({r['tokens_per_s'] / 1e6:.2f} M tokens/s)" for r in small_cfg))
     log(f"n = 8 ({n8['shape']}): mhc_pre {n8['mhc_pre']['avg_us']:.1f} us ({n8['mhc_pre']['GBps']:.0f} GB/s), "
         f"mhc_post {n8['mhc_post']['avg_us']:.1f} us ({n8['mhc_post']['GBps']:.0f} GB/s)")
     log("mhc_pre at small T (split-K form, per call; in a HIP graph): " +
@@ -755,6 +802,7 @@ def main():
         "mhc_pre_forms": forms,
         "small_t": small_t,
         "n8": n8,
+        "smaller_layers": small_cfg,
         "backward": backward,
         "stack": stack,
         "cpu_baseline": cpu,
