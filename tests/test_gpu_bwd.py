@@ -172,6 +172,13 @@ def test_post_bwd_forms(mhc, oracle_lib, T, n, d, dtype):
         assert_scaled(dH[:, n:], ref["dH"][:, n:], 1e-4, 1e-5, f"{w.name} tiled={tiled} dH")
     # dX (checked through the whole chain elsewhere) and dY: the same arithmetic per element in both forms
     assert np.array_equal(runs[False][0], runs[True][0]) and np.array_equal(runs[False][1], runs[True][1])
+    if d % 512 != 0:
+        # a workspace passed where the tiled form does not apply is not used: the scratch-free results
+        dH = torch.full((T, w.m), 7.0, dtype=torch.float32, device="cuda")
+        gX, gY, dH = mhc.post_bwd(dX_, dY_, H, dG, dH=dH, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+        for a, b in zip((to_host(gX), to_host(gY), to_host(dH)), runs[False]):
+            assert np.array_equal(a, b)
 
 
 def test_backward_empty_and_deterministic(mhc):
