@@ -69,3 +69,51 @@ def test_forward_step_in_a_graph(mhc):
         torch.cuda.synchronize()
         for got, want, name in zip((h, H, Xo, amax), refs, ("h", "H", "X'", "amax")):
             assert torch.equal(got, want), f"replay {r}: {name} differs from the eager two-pass result"
+
+
+def test_backward_and_post_pre_in_a_graph(mhc):
+    """mhc_post_bwd_ex (tiled, with its workspace), mhc_pre_bwd and
+    mhc_post_pre captured into one graph, replayed several times with eager
+    work and synchronisations in between: every replay gives the eager
+    results bit for bit (no entry point records a memset)."""
+    T, n, d, m = 2048, 4, 2048, 24
+    g = torch.Generator(device="cuda").manual_seed(37)
+    X = torch.randn(T, n, d, device="cuda", generator=g).to(torch.bfloat16)
+    Y = torch.randn(T, d, device="cuda", generator=g).to(torch.bfloat16)
+    G = torch.randn(T, n, d, device="cuda", generator=g).to(torch.bfloat16)
+    D = torch.randn(T, d, device="cuda", generator=g).to(torch.bfloat16)
+    phi = torch.randn(n * d, m, device="cuda", generator=g) * 0.02
+    bias = torch.randn(m, device="cuda", generator=g) * 0.1
+    alpha = (0.7, 1.1, 0.4)
+    _, H = mhc.pre(X, phi, bias, alpha=alpha)
+    wsp = torch.empty(mhc.post_bwd_workspace_size(T, n, d, mhc.MHC_BF16), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(mhc.pre_bwd_workspace_size(T, n, d, mhc.MHC_BF16), dtype=torch.uint8, device="cuda")
+    wsf = torch.empty(mhc.pre_workspace_size(T, n, d, mhc.MHC_BF16), dtype=torch.uint8, device="cuda")
+    dX, dY = torch.empty_like(X), torch.empty_like(Y)
+    dH = torch.zeros((T, m), device="cuda")
+    dphi, dbias, dalpha = torch.empty((n * d, m), device="cuda"), torch.empty(m, device="cuda"), torch.empty(3, device="cuda")
+    Xn, hn, Hn = torch.empty_like(X), torch.empty_like(Y), torch.empty((T, m), device="cuda")
+
+    def run():
+        mhc.post_bwd(X, Y, H, G, dX=dX, dY=dY, dH=dH, workspace=wsp)
+        mhc.pre_bwd(X, phi, bias, D, dH, dX, alpha=alpha, dphi=dphi, dbias=dbias, dalpha=dalpha, workspace=wsb)
+        mhc.post_pre(X, Y, H, phi, bias, alpha=alpha, out=Xn, h=hn, H_next=Hn, workspace=wsf)
+
+    outs = (dX, dY, dH, dphi, dbias, dalpha, Xn, hn, Hn)
+    run()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        run()
+    for r in range(4):
+        for t in outs:
+            t.zero_()
+        mhc.pre(X, phi, bias, alpha=(0.5, 0.5, 0.5), workspace=wsf)     # eager work on a shared workspace
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, (got, want) in enumerate(zip(outs, refs)):
+            assert torch.equal(got, want), f"replay {r}: output {k} differs from the eager run"
