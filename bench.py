@@ -585,6 +585,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-stack", action="store_true", help="skip the 60-layer stack timing")
+    ap.add_argument("--stack-only", action="store_true",
+                    help="time only the 60-layer stack (for a kernel trace of it); prints its JSON and exits")
     ap.add_argument("--pre-algo", type=int, default=0, choices=[0, 1, 2],
                     help="mhc_pre form: 0 auto, 1 two-pass, 2 one-pass")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
@@ -604,6 +606,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.stack_only:
+        mhc.load_library()
+        print(json.dumps(time_stack(mhc, torch, reps=3, warmup=1)))
+        return 0
     mhc.load_library()
     # Decode-sized calls first, on a fresh allocator: timed after the large
     # workload's buffers were allocated, one of these shapes (T = 64,
