@@ -45,7 +45,11 @@
  *  - Results are bitwise reproducible for fixed inputs and shapes: every
  *    reduction runs in a fixed order and no floating-point atomics are used.
  *  - The library keeps no mutable state between calls apart from a cache of
- *    device attributes; calls from several host threads are safe.
+ *    device attributes; calls from several host threads are safe.  What
+ *    carries over from one call to the next lives in caller-owned memory:
+ *    mhc_pre's workspace header (see mhc_pre_ex).
+ *  - Scratch memory: entry points that need it take a workspace whose size
+ *    mhc_workspace_size(p, op) returns (0: none needed).
  */
 #ifndef MHC_H
 #define MHC_H
@@ -57,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 5
+#define MHC_ABI_VERSION 6
 
 typedef enum mhc_status {
   MHC_OK = 0,
@@ -116,9 +120,13 @@ typedef struct mhc_params {
  *   h         out  [T, d] state dtype; must not overlap any input
  *   H         out  [T, m] fp32; must not overlap any input or h
  *   workspace in/out scratch of at least mhc_pre_workspace_size(p) bytes,
- *             16-byte aligned, overlapping nothing else; its contents on entry
- *             are ignored and on return are unspecified.  May be NULL only if
- *             the size query returns 0.
+ *             16-byte aligned, overlapping nothing else.  Its first 256 bytes
+ *             (the header) carry the single pass's sequence number and error
+ *             word from one call to the next; any initial contents work
+ *             (zeroed memory included), and the library never needs it
+ *             cleared.  The rest is scratch, unspecified on return.  Calls
+ *             that share a workspace must not overlap in time (one stream, or
+ *             ordered streams).  May be NULL only if the size query returns 0.
  * Returns MHC_ERR_WORKSPACE when workspace_bytes is too small. */
 mhc_status mhc_pre(const mhc_params* p, const void* X, const float* phi, const float* bias,
                    void* h, float* H, void* workspace, size_t workspace_bytes, void* stream);
@@ -142,32 +150,37 @@ size_t mhc_pre_workspace_size(const mhc_params* p);
  *                     known, so X is read once.  The team's members wait for
  *                     each other (bounded waits), so they must be resident
  *                     together, which an idle device gives an ordinary
- *                     launch of one workgroup per compute unit.  Should a
- *                     wait run out (members not resident together), the
- *                     launches that follow on the stream recompute the
- *                     call's results with the two-pass form; they are
- *                     gated on the error word below and otherwise return
- *                     at once.  Not on a stream being captured into a HIP
- *                     graph (a replay would reuse the captured call's
- *                     sequence number).  Returns MHC_ERR_UNSUPPORTED when it
- *                     does not apply.
+ *                     launch of one workgroup per compute unit.  A second
+ *                     kernel always follows on the stream: it advances the
+ *                     sequence number in the workspace header and, should a
+ *                     wait have run out (members not resident together),
+ *                     recomputes every output with the single pass's own
+ *                     arithmetic and order but without the exchange, so the
+ *                     results are the same bits either way.  The call's tag
+ *                     comes from the workspace, not the host, so the form
+ *                     may be captured into a HIP graph and replayed.
+ *                     Returns MHC_ERR_UNSUPPORTED when it does not apply.
  *   MHC_PRE_AUTO      the one-pass form where it measures faster on MI355X
  *                     (n = 4, teams that fill whole XCDs, at least 40 tiles
- *                     per team: T >= 10240 at d = 4096) and the stream is not
- *                     capturing, else the two-pass form.  Every other entry
- *                     point may be captured into a HIP graph.
- * Both sum every partial in a fixed order (results are bitwise reproducible
- * for a given form); the two forms agree to rounding.
- * algo_used (nullable, host pointer) receives the form that ran.  After a
- * one-pass call, the first 8 bytes of the workspace hold 0, or the
- * sequence number of the last one-pass call whose wait ran out and whose
- * results the two-pass form therefore recomputed; the library never clears
- * it.  Testing aid: with the environment variable
- * MHC_TEST_ONE_PASS_FALLBACK=1 at the call, every workgroup of the single
- * pass starts as if a wait had run out, so the fallback runs. */
+ *                     per team: T >= 10240 at d = 4096), else the two-pass
+ *                     form.
+ *   MHC_PRE_ONE_PASS_FALLBACK_TEST
+ *                     testing aid: the one-pass form with every workgroup
+ *                     starting as if a wait had run out, so the recomputing
+ *                     kernel produces every output.
+ * Both forms sum every partial in a fixed order (results are bitwise
+ * reproducible for a given form); the two forms agree to rounding.
+ * algo_used (nullable, host pointer) receives the form that ran.
+ * Workspace header after a one-pass call (64-bit words): [0] the tag of the
+ * last one-pass call whose wait ran out, XORed with 0x5555555555555555
+ * (earlier contents if none did), [1] the next call's sequence number, [2]
+ * the tag of the call just made (its sequence number with the top bit set);
+ * [0] == [2] ^ 0x5555555555555555 therefore means this call was recomputed.
+ * The other forms leave the header alone. */
 #define MHC_PRE_AUTO 0
 #define MHC_PRE_TWO_PASS 1
 #define MHC_PRE_ONE_PASS 2
+#define MHC_PRE_ONE_PASS_FALLBACK_TEST 3
 mhc_status mhc_pre_ex(const mhc_params* p, const void* X, const float* phi, const float* bias, void* h,
                       float* H, void* workspace, size_t workspace_bytes, int32_t algo, int32_t* algo_used,
                       void* stream);
@@ -285,6 +298,25 @@ mhc_status mhc_amax(int64_t T, int32_t n, int32_t L, const float* H_stack, float
  * run without a GEMM; it is not part of the mHC method.
  *   h in [count], Y out [count]; Y may be exactly h, other overlap is an error. */
 mhc_status mhc_gelu_half(int64_t count, int32_t dtype, const void* h, void* Y, void* stream);
+
+/* ---- mhc_workspace_size: scratch bytes of an entry point ---------------------
+ * One query for every entry point (the interface's size query): bytes of
+ * device scratch the entry point named by op needs for the parameters p, or
+ * 0 when it needs none, p is invalid or op unknown.  The per-entry-point
+ * queries above return the same numbers.
+ *   MHC_OP_PRE       mhc_pre and mhc_pre_ex (both forms)
+ *   MHC_OP_POST      mhc_post (0)
+ *   MHC_OP_POST_PRE  mhc_post_pre (= MHC_OP_PRE)
+ *   MHC_OP_AMAX      mhc_amax (0)
+ *   MHC_OP_POST_BWD  mhc_post_bwd_ex's tiled form (0 where it does not apply)
+ *   MHC_OP_PRE_BWD   mhc_pre_bwd */
+#define MHC_OP_PRE 0
+#define MHC_OP_POST 1
+#define MHC_OP_POST_PRE 2
+#define MHC_OP_AMAX 3
+#define MHC_OP_POST_BWD 4
+#define MHC_OP_PRE_BWD 5
+size_t mhc_workspace_size(const mhc_params* p, int32_t op);
 
 /* Static description of a status code (never NULL). */
 const char* mhc_status_string(mhc_status status);

@@ -17,9 +17,10 @@ MHC_FP32, MHC_BF16 = 0, 1
 STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_DTYPE", 4: "MHC_ERR_ALIGN",
           5: "MHC_ERR_UNSUPPORTED", 6: "MHC_ERR_ALIAS", 7: "MHC_ERR_WORKSPACE", 8: "MHC_ERR_HIP"}
 EXPORTS = ["mhc_pre", "mhc_pre_ex", "mhc_pre_workspace_size", "mhc_post", "mhc_amax", "mhc_gelu_half",
-           "mhc_post_pre", "mhc_post_bwd", "mhc_post_bwd_ex", "mhc_post_bwd_workspace_size", "mhc_pre_bwd", "mhc_pre_bwd_workspace_size", "mhc_status_string",
-           "mhc_abi_version"]
-PRE_AUTO, PRE_TWO_PASS, PRE_ONE_PASS = 0, 1, 2
+           "mhc_post_pre", "mhc_post_bwd", "mhc_post_bwd_ex", "mhc_post_bwd_workspace_size", "mhc_pre_bwd",
+           "mhc_pre_bwd_workspace_size", "mhc_workspace_size", "mhc_status_string", "mhc_abi_version"]
+PRE_AUTO, PRE_TWO_PASS, PRE_ONE_PASS, PRE_ONE_PASS_FALLBACK_TEST = 0, 1, 2, 3
+OP_PRE, OP_POST, OP_POST_PRE, OP_AMAX, OP_POST_BWD, OP_PRE_BWD = 0, 1, 2, 3, 4, 5
 
 
 class MhcError(RuntimeError):
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     lib.mhc_pre_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mhc_pre_bwd.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.mhc_pre_bwd.restype = ctypes.c_int
+    lib.mhc_workspace_size.argtypes = [ctypes.POINTER(Params), ctypes.c_int32]
+    lib.mhc_workspace_size.restype = ctypes.c_size_t
     lib.mhc_status_string.argtypes = [ctypes.c_int]
     lib.mhc_status_string.restype = ctypes.c_char_p
     lib.mhc_abi_version.argtypes = []
@@ -134,6 +137,12 @@ def _need_device(*ts):
             raise ValueError("libmhc expects contiguous tensors")
 
 
+def workspace_size(op, T, n, d, dtype=MHC_BF16) -> int:
+    """mhc_workspace_size: scratch bytes entry point ``op`` (OP_*) needs (0: none)."""
+    p = make_params(T, n, d, dtype)
+    return int(load_library().mhc_workspace_size(ctypes.byref(p), int(op)))
+
+
 def pre_workspace_size(T, n, d, dtype=MHC_BF16) -> int:
     p = make_params(T, n, d, dtype)
     return int(load_library().mhc_pre_workspace_size(ctypes.byref(p)))
@@ -142,7 +151,8 @@ def pre_workspace_size(T, n, d, dtype=MHC_BF16) -> int:
 def pre(X, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, h=None, H=None, workspace=None,
         stream=None, algo=None, maps=MAPS_MHC):
     """mhc_pre: returns (h [T, d] state dtype, H [T, m] fp32).  With ``algo``
-    (PRE_AUTO / PRE_TWO_PASS / PRE_ONE_PASS) it calls mhc_pre_ex instead.
+    (PRE_AUTO / PRE_TWO_PASS / PRE_ONE_PASS / PRE_ONE_PASS_FALLBACK_TEST) it
+    calls mhc_pre_ex instead.
     ``maps``: MAPS_MHC (the method) or MAPS_HC (the unconstrained contrast)."""
     if algo is not None:
         h, H, _ = pre_ex(X, phi, bias, algo, alpha, eps, t_max, h, H, workspace, stream, maps=maps)

@@ -1,8 +1,10 @@
 """Build libmhc.so in-tree with hipcc for gfx950.
 
 Each source under ``csrc/`` is compiled to an object in parallel, then linked
-into ``mhc_hyper_connections_amd/libmhc.so``.  All device code is compiled
-with packed-fp32 instructions disabled.
+into ``mhc_hyper_connections_amd/libmhc.so``.  The benchmark's streaming-copy
+reference (``csrc/bench_copy.hip``) goes into a library of its own,
+``libmhc_bench.so``.  All device code is compiled with packed-fp32
+instructions disabled.
 """
 from __future__ import annotations
 
@@ -16,7 +18,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmhc.so")
+BENCH_LIB = os.path.join(HERE, "libmhc_bench.so")
 SOURCES = ["capi.cpp", "pre.hip", "pre8.hip", "pre_fused.hip", "post.hip", "amax.hip", "bwd.hip"]
+BENCH_SOURCES = ["bench_copy.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
@@ -48,14 +52,16 @@ def build(force: bool = True, verbose: bool = False) -> str:
     if not force and os.path.exists(LIB):
         return LIB
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB)
+    srcs = SOURCES + BENCH_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    for lib, names in ((LIB, SOURCES), (BENCH_LIB, BENCH_SOURCES)):
+        tmp = lib + ".tmp"
+        cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *(objs[n] for n in names)]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
+        os.replace(tmp, lib)
     if verbose:
         print(f"built {LIB}")
     return LIB

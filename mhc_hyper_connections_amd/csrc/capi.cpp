@@ -103,7 +103,9 @@ mhc_status mhc_pre(const mhc_params* p, const void* X, const float* phi, const f
 mhc_status mhc_pre_ex(const mhc_params* p, const void* X, const float* phi, const float* bias, void* h, float* H,
                       void* workspace, size_t workspace_bytes, int32_t algo, int32_t* algo_used, void* stream) {
   if (algo_used) *algo_used = MHC_PRE_TWO_PASS;
-  if (algo != MHC_PRE_AUTO && algo != MHC_PRE_TWO_PASS && algo != MHC_PRE_ONE_PASS) return MHC_ERR_SHAPE;
+  if (algo != MHC_PRE_AUTO && algo != MHC_PRE_TWO_PASS && algo != MHC_PRE_ONE_PASS &&
+      algo != MHC_PRE_ONE_PASS_FALLBACK_TEST)
+    return MHC_ERR_SHAPE;
   mhc_status st = check_params(p);
   if (st != MHC_OK) return st;
   if (p->T == 0) return MHC_OK;
@@ -130,7 +132,7 @@ mhc_status mhc_pre_ex(const mhc_params* p, const void* X, const float* phi, cons
   const hipError_t e = mhc::launch_pre(*p, X, phi, bias, h, H, workspace, workspace_bytes, algo, &used, dev,
                                        static_cast<hipStream_t>(stream));
   if (algo_used) *algo_used = used;
-  if (e == hipErrorNotSupported && algo == MHC_PRE_ONE_PASS) return MHC_ERR_UNSUPPORTED;
+  if (e == hipErrorNotSupported && algo != MHC_PRE_AUTO && algo != MHC_PRE_TWO_PASS) return MHC_ERR_UNSUPPORTED;
   return from_hip(e);
 }
 
@@ -262,6 +264,18 @@ mhc_status mhc_pre_bwd(const mhc_params* p, const void* X, const float* phi, con
   const mhc::DeviceInfo dev = device_info();
   return from_hip(mhc::launch_pre_bwd(*p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, workspace, dev,
                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t mhc_workspace_size(const mhc_params* p, int32_t op) {
+  switch (op) {
+    case MHC_OP_PRE:
+    case MHC_OP_POST_PRE: return mhc_pre_workspace_size(p);
+    case MHC_OP_POST_BWD: return mhc_post_bwd_workspace_size(p);
+    case MHC_OP_PRE_BWD: return mhc_pre_bwd_workspace_size(p);
+    case MHC_OP_POST:
+    case MHC_OP_AMAX:
+    default: return 0;
+  }
 }
 
 mhc_status mhc_amax(int64_t T, int32_t n, int32_t L, const float* H_stack, float* amax, float* gain_fwd,

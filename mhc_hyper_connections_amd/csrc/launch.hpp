@@ -37,21 +37,21 @@ size_t pre8_workspace_bytes(int64_t T, int d);
 hipError_t launch_pre8(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
                        void* workspace, const DeviceInfo& dev, hipStream_t stream);
 
-// The single-pass form (pre_fused.hip): hipErrorNotSupported when it does not apply.
-// The first kOnePassHeaderBytes of its workspace hold the error word; its
-// fallback (launch_pre_gated) keeps the two-pass records after them.
-constexpr size_t kOnePassHeaderBytes = 256;
-size_t pre_fused_workspace_bytes(int64_t T, int n, int d);
+// mhc_pre's workspace is a header, which only the single pass uses, then a
+// body for the records of whichever form runs.  Header words (u64): [0] the
+// tag of the last single-pass call whose waits ran out, [1] the sequence
+// number of the next call, [2] the tag of the current call.
+constexpr size_t kPreHeaderBytes = 256;
+
+// The single-pass form (pre_fused.hip): hipErrorNotSupported when it does not
+// apply.  It reads and writes the whole workspace, header included.
+// force_fallback (a testing aid) makes every workgroup start as if a wait had
+// run out, so the fallback kernel recomputes the call.
+size_t pre_fused_body_bytes(int n, int d);
 bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev);   // what MHC_PRE_AUTO picks
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
-                            float* H, void* workspace, size_t ws_bytes, const DeviceInfo& dev, hipStream_t stream);
-
-// The two-pass form on a bf16 state (n <= 4), each kernel gated: it runs
-// only if *gate == gate_value when it starts, else returns at once.  The
-// records go to workspace (pre_partial_bytes of it).
-hipError_t launch_pre_gated(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
-                            float* H, void* workspace, const DeviceInfo& dev, const unsigned long long* gate,
-                            unsigned long long gate_value, hipStream_t stream);
+                            float* H, void* workspace, size_t ws_bytes, bool force_fallback, const DeviceInfo& dev,
+                            hipStream_t stream);
 
 // Split-K partials of mhc_pre's projection plus, per stream i, <D, X_i> over
 // the slice (pre.hip).  part: [S][T][pre_part_width(n, true)] floats with

@@ -55,12 +55,6 @@ constexpr size_t kPartTrashBytes = PRE_THREADS * 16;
 // workgroup takes exactly one tile (blockIdx / S), with no prefetch: the
 // small-T form, which spreads a few tiles over many workgroups; otherwise
 // the workgroups are persistent and walk tiles with two in flight.
-// A gated launch runs only when its gate word holds the expected value; the
-// word was written by an earlier kernel on the stream (agent scope).
-__device__ __forceinline__ bool gate_open(const unsigned long long* gate, unsigned long long value) {
-  return __hip_atomic_load(const_cast<unsigned long long*>(gate), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == value;
-}
-
 template <typename ST, int N, int MB, int MODE, int PWV = PRE_WAVES, bool ONE = false>
 __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d, int S, int64_t ntiles,
                                                                   const typename ST::elem* X,
@@ -68,11 +62,7 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
                                                                   const float* __restrict__ phi,
                                                                   float* __restrict__ part,
                                                                   const float* __restrict__ Hin,
-                                                                  typename ST::elem* Xout,
-                                                                  const unsigned long long* gate,
-                                                                  unsigned long long gate_value) {
-  // Gated launch: run only if *gate holds gate_value (see launch_pre_gated).
-  if (gate != nullptr && gate_open(gate, gate_value) == false) return;
+                                                                  typename ST::elem* Xout) {
   constexpr bool WITH_D = MODE == 1;
   constexpr bool FUSE_POST = MODE == 2;
   constexpr int M = num_maps(N);
@@ -418,9 +408,7 @@ __global__ __launch_bounds__(256) void pre_finish_kernel(int64_t T, int d, int S
                                                          const float* __restrict__ bias, float a_pre,
                                                          float a_res, float a_post, float eps, int t_max,
                                                          typename ST::elem* __restrict__ h,
-                                                         float* __restrict__ H, const unsigned long long* gate,
-                                                         unsigned long long gate_value) {
-  if (gate != nullptr && gate_open(gate, gate_value) == false) return;
+                                                         float* __restrict__ H) {
   constexpr int M = num_maps(N);
   constexpr int NN = N * N;
   constexpr int PW = part_width(N);
@@ -564,8 +552,7 @@ int forward_slices(int64_t T, int d) { return small_t_form(T, d) ? num_slices(d,
 // The finishing pass, in the form of the maps p asks for.
 template <typename ST, int N, bool HC>
 hipError_t launch_finish_t(const mhc_params& p, int S, const void* X, const float* part, const float* bias, void* h,
-                           float* H, hipStream_t stream, const unsigned long long* gate = nullptr,
-                           unsigned long long gate_value = 0) {
+                           float* H, hipStream_t stream) {
   typedef typename ST::elem E;
   // Parts per token: enough waves for the device (~1024) when T is small.
   const int npass = (p.d + 511) / 512;
@@ -578,27 +565,25 @@ hipError_t launch_finish_t(const mhc_params& p, int S, const void* X, const floa
   if (S <= 16)
     hipLaunchKernelGGL((pre_finish_kernel<ST, N, HC, 4>), grid, dim3(256), 0, stream, p.T, p.d, S, ppp,
                        static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post, p.eps, p.t_max,
-                       static_cast<E*>(h), H, gate, gate_value);
+                       static_cast<E*>(h), H);
   else
     hipLaunchKernelGGL((pre_finish_kernel<ST, N, HC, 16>), grid, dim3(256), 0, stream, p.T, p.d, S, ppp,
                        static_cast<const E*>(X), part, bias, p.alpha_pre, p.alpha_res, p.alpha_post, p.eps, p.t_max,
-                       static_cast<E*>(h), H, gate, gate_value);
+                       static_cast<E*>(h), H);
   return hipGetLastError();
 }
 
 // The finishing pass over S slices' records, in the form of the maps p asks for.
 template <typename ST, int N>
 hipError_t launch_finish(const mhc_params& p, int S, const void* X, const float* part, const float* bias, void* h,
-                         float* H, hipStream_t stream, const unsigned long long* gate = nullptr,
-                         unsigned long long gate_value = 0) {
-  return p.maps == MHC_MAPS_HC ? launch_finish_t<ST, N, true>(p, S, X, part, bias, h, H, stream, gate, gate_value)
-                               : launch_finish_t<ST, N, false>(p, S, X, part, bias, h, H, stream, gate, gate_value);
+                         float* H, hipStream_t stream) {
+  return p.maps == MHC_MAPS_HC ? launch_finish_t<ST, N, true>(p, S, X, part, bias, h, H, stream)
+                               : launch_finish_t<ST, N, false>(p, S, X, part, bias, h, H, stream);
 }
 
 template <typename ST, int N>
 hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
-                        void* workspace, const DeviceInfo& dev, hipStream_t stream,
-                        const unsigned long long* gate = nullptr, unsigned long long gate_value = 0) {
+                        void* workspace, const DeviceInfo& dev, hipStream_t stream) {
   typedef typename ST::elem E;
   float* part = static_cast<float*>(workspace);
   if (small_t_form(p.T, p.d)) {
@@ -609,10 +594,10 @@ hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, co
     hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 0, SMALL_WAVES, true>), dim3(static_cast<unsigned>(S * ntiles)),
                        dim3(SMALL_WAVES * 64), 0, stream, p.T, p.d, S, ntiles, static_cast<const E*>(X),
                        static_cast<const E*>(nullptr), phi, part, static_cast<const float*>(nullptr),
-                       static_cast<E*>(nullptr), gate, gate_value);
+                       static_cast<E*>(nullptr));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_finish<ST, N>(p, S, X, part, bias, h, H, stream, gate, gate_value);
+    return launch_finish<ST, N>(p, S, X, part, bias, h, H, stream);
   }
   constexpr int MB = 2;                  // 32-token tiles: two in flight fit the registers
   constexpr int R = 16 * MB;
@@ -624,10 +609,10 @@ hipError_t launch_pre_t(const mhc_params& p, const void* X, const float* phi, co
   const int64_t grid = groups * S;
   hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 0>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
                      stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(nullptr), phi, part,
-                     static_cast<const float*>(nullptr), static_cast<E*>(nullptr), gate, gate_value);
+                     static_cast<const float*>(nullptr), static_cast<E*>(nullptr));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_finish<ST, N>(p, S, X, part, bias, h, H, stream, gate, gate_value);
+  return launch_finish<ST, N>(p, S, X, part, bias, h, H, stream);
 }
 
 // mhc_post of the previous layer fused into the partial pass (MODE 2), then
@@ -648,8 +633,7 @@ hipError_t launch_post_pre_t(const mhc_params& p, const void* X, const void* Y, 
     const int64_t ntiles = (p.T + R - 1) / R;
     hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 2, SMALL_WAVES, true>), dim3(static_cast<unsigned>(S * ntiles)),
                        dim3(SMALL_WAVES * 64), 0, stream, p.T, p.d, S, ntiles, static_cast<const E*>(X),
-                       static_cast<const E*>(Y), phi, part, Hprev, static_cast<E*>(Xout),
-                       static_cast<const unsigned long long*>(nullptr), 0ull);
+                       static_cast<const E*>(Y), phi, part, Hprev, static_cast<E*>(Xout));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     return launch_finish<ST, N>(p, S, Xout, part, bias, h, H, stream);
@@ -662,7 +646,7 @@ hipError_t launch_post_pre_t(const mhc_params& p, const void* X, const void* Y, 
   const int64_t grid = groups * S;
   hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 2>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
                      stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(Y), phi, part,
-                     Hprev, static_cast<E*>(Xout), static_cast<const unsigned long long*>(nullptr), 0ull);
+                     Hprev, static_cast<E*>(Xout));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_finish<ST, N>(p, S, Xout, part, bias, h, H, stream);
@@ -694,8 +678,7 @@ hipError_t launch_partial_d_t(const mhc_params& p, const void* X, const void* D,
   const int64_t grid = groups * S;
   hipLaunchKernelGGL((pre_partial_kernel<ST, N, MB, 1>), dim3(static_cast<unsigned>(grid)), dim3(PRE_THREADS), 0,
                      stream, p.T, p.d, S, ntiles, static_cast<const E*>(X), static_cast<const E*>(D), phi, part,
-                     static_cast<const float*>(nullptr), static_cast<E*>(nullptr),
-                     static_cast<const unsigned long long*>(nullptr), 0ull);
+                     static_cast<const float*>(nullptr), static_cast<E*>(nullptr));
   return hipGetLastError();
 }
 
@@ -730,11 +713,12 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
                            hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   const bool bf = p.dtype == MHC_BF16;
+  void* body = static_cast<char*>(workspace) + kPreHeaderBytes;
   switch (p.n) {
-    case 2: return bf ? launch_post_pre_t<BF16, 2>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream)
-                      : launch_post_pre_t<F32, 2>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream);
-    case 4: return bf ? launch_post_pre_t<BF16, 4>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream)
-                      : launch_post_pre_t<F32, 4>(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, dev, stream);
+    case 2: return bf ? launch_post_pre_t<BF16, 2>(p, X, Y, Hprev, Xout, phi, bias, h, H, body, dev, stream)
+                      : launch_post_pre_t<F32, 2>(p, X, Y, Hprev, Xout, phi, bias, h, H, body, dev, stream);
+    case 4: return bf ? launch_post_pre_t<BF16, 4>(p, X, Y, Hprev, Xout, phi, bias, h, H, body, dev, stream)
+                      : launch_post_pre_t<F32, 4>(p, X, Y, Hprev, Xout, phi, bias, h, H, body, dev, stream);
     default: {   // n = 1 (m = 3 maps per token) and n = 8: the two entry points one after the other
       hipError_t e = launch_post(p, X, Y, Hprev, Xout, stream);
       if (e != hipSuccess) return e;
@@ -745,32 +729,24 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
   }
 }
 
-hipError_t launch_pre_gated(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
-                            float* H, void* workspace, const DeviceInfo& dev, const unsigned long long* gate,
-                            unsigned long long gate_value, hipStream_t stream) {
-  if (p.T == 0) return hipSuccess;
-  if (p.dtype != MHC_BF16) return hipErrorInvalidValue;
-  switch (p.n) {
-    case 1: return launch_pre_t<BF16, 1>(p, X, phi, bias, h, H, workspace, dev, stream, gate, gate_value);
-    case 2: return launch_pre_t<BF16, 2>(p, X, phi, bias, h, H, workspace, dev, stream, gate, gate_value);
-    case 4: return launch_pre_t<BF16, 4>(p, X, phi, bias, h, H, workspace, dev, stream, gate, gate_value);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 size_t pre_workspace_bytes(int64_t T, int n, int d) {
-  if (n == 8) return pre8_workspace_bytes(T, d);
-  size_t two_pass = pre_partial_bytes(T, n, d, false);   // persistent form (also mhc_post_pre's)
-  if (small_t_form(T, d)) {
-    const size_t small = static_cast<size_t>(num_slices(d, SMALL_WAVES)) * static_cast<size_t>(T) *
-                             static_cast<size_t>(part_width(n)) * sizeof(float) + kPartTrashBytes;
-    if (small > two_pass) two_pass = small;
+  // [header][body]: the header is the single pass's alone (its error word,
+  // sequence number and the current call's tag); every other form keeps its
+  // records in the body, so it never disturbs them.
+  size_t body = 0;
+  if (n == 8) {
+    body = pre8_workspace_bytes(T, d);
+  } else {
+    body = pre_partial_bytes(T, n, d, false);   // persistent form (also mhc_post_pre's)
+    if (small_t_form(T, d)) {
+      const size_t small = static_cast<size_t>(num_slices(d, SMALL_WAVES)) * static_cast<size_t>(T) *
+                               static_cast<size_t>(part_width(n)) * sizeof(float) + kPartTrashBytes;
+      if (small > body) body = small;
+    }
+    const size_t one_pass = pre_fused_body_bytes(n, d);
+    if (one_pass > body) body = one_pass;
   }
-  const size_t one_pass = pre_fused_workspace_bytes(T, n, d);
-  if (one_pass == 0) return two_pass;
-  // The single pass's fallback keeps its records after the error word.
-  two_pass += kOnePassHeaderBytes;
-  return two_pass > one_pass ? two_pass : one_pass;
+  return kPreHeaderBytes + body;
 }
 
 hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,
@@ -779,14 +755,15 @@ hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, cons
   if (used) *used = MHC_PRE_TWO_PASS;
   if (p.T == 0) return hipSuccess;
   if (algo == MHC_PRE_AUTO && pre_fused_preferred(p, dev)) {
-    if (launch_pre_fused(p, X, phi, bias, h, H, workspace, ws_bytes, dev, stream) == hipSuccess) {
+    if (launch_pre_fused(p, X, phi, bias, h, H, workspace, ws_bytes, false, dev, stream) == hipSuccess) {
       if (used) *used = MHC_PRE_ONE_PASS;
       return hipSuccess;
     }
     (void)hipGetLastError();                 // refused: the two-pass form below
   }
-  if (algo == MHC_PRE_ONE_PASS) {
-    const hipError_t e = launch_pre_fused(p, X, phi, bias, h, H, workspace, ws_bytes, dev, stream);
+  if (algo == MHC_PRE_ONE_PASS || algo == MHC_PRE_ONE_PASS_FALLBACK_TEST) {
+    const hipError_t e = launch_pre_fused(p, X, phi, bias, h, H, workspace, ws_bytes,
+                                          algo == MHC_PRE_ONE_PASS_FALLBACK_TEST, dev, stream);
     if (e == hipSuccess) {
       if (used) *used = MHC_PRE_ONE_PASS;
       return hipSuccess;
@@ -794,8 +771,9 @@ hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, cons
     (void)hipGetLastError();                 // clear a refused launch
     return e;
   }
-  if (p.dtype == MHC_BF16) return launch_pre_n<BF16>(p, X, phi, bias, h, H, workspace, dev, stream);
-  return launch_pre_n<F32>(p, X, phi, bias, h, H, workspace, dev, stream);
+  void* body = static_cast<char*>(workspace) + kPreHeaderBytes;
+  if (p.dtype == MHC_BF16) return launch_pre_n<BF16>(p, X, phi, bias, h, H, body, dev, stream);
+  return launch_pre_n<F32>(p, X, phi, bias, h, H, body, dev, stream);
 }
 
 }  // namespace mhc

@@ -46,24 +46,27 @@
 // 16-byte pairs: written with plain stores (through the CU's L1 into the
 // XCD's L2), read with sc1 buffer loads (which skip the L1); a pair whose tag
 // is not yet the tile's is read again.  Each member clears its own slots
-// before any wave posts, and the team meets on words stamped with the call's
-// sequence number, so words of earlier calls never match.  Every sum runs in
-// a fixed order: results are bitwise reproducible.  All waits are bounded;
-// one that runs out marks the workgroup broken (no further waits; its
-// results are garbage, its writes stay in bounds) and the call's sequence
-// number is stored into the workspace's error word.
+// before any wave posts, and the team meets on start words stamped with the
+// call's tag, so words of earlier calls never match.  The tag comes from a
+// sequence number kept in the workspace's header, which the kernel after the
+// single pass advances; nothing on the host counts calls, so a call captured
+// into a HIP graph gets a fresh tag at every replay.  Every sum runs in a
+// fixed order: results are bitwise reproducible.  All waits are bounded; one
+// that runs out marks the workgroup broken (no further waits; its results are
+// garbage, its writes stay in bounds) and the call's tag, XORed with a fixed
+// pattern, is stored into the header's error word (the pattern keeps a header
+// whose words all hold the same initial bytes from reading as a failure).
 // The launch is an ordinary one of one workgroup per CU, which on an idle
 // device makes every team resident together; a cooperative launch would
 // guarantee it but costs about 16 us more per call on MI355X.  The guarantee
-// is replaced by a fallback: the two-pass form is launched behind the single
-// pass, each of its kernels gated on the error word holding this call's
-// sequence number, so it recomputes every output when a wait ran out and
-// otherwise returns at once (about 3 us for the two launches).
+// is replaced by a fallback: pre_one_pass_fallback_kernel follows the single
+// pass on the stream.  Its workgroups return at once unless the error word
+// holds this call's tag; then they recompute every output with the single
+// pass's own arithmetic and summation order but no exchange (each workgroup
+// takes whole tiles and walks the members' slices itself), so the results
+// are bitwise those of an undisturbed single pass.
 // The exchange and Sinkhorn waves run at a raised issue priority: the
 // streaming waves have slack, the exchange is on every tile's critical path.
-#include <atomic>
-#include <cstdlib>
-
 #include "launch.hpp"
 #include "pre_common.hpp"
 
@@ -87,7 +90,9 @@ constexpr int OKR = 4;                  // LDS ring of Sinkhorn inputs (tiles; t
 constexpr int OD = 5;                   // tiles between a tile's partials and its h; see below
 constexpr int OP = 2;                   // X tiles in flight ahead of the one being multiplied
 constexpr int ONB = OD + OP;            // X tile buffers per lane
-constexpr size_t OHDR = kOnePassHeaderBytes;   // workspace header: the error word
+constexpr size_t OHDR = kPreHeaderBytes;       // workspace header (error word, sequence number, current tag)
+constexpr u64 kTagBit = 1ull << 63;     // set in every call's tag: a cleared or zeroed word never matches one
+constexpr u64 kErrFlip = 0x5555555555555555ull;   // error word = tag ^ kErrFlip: never the raw sequence word
 constexpr int OXCD = 8;                 // XCDs of the device (MI355X)
 constexpr unsigned kLdsSpin = 1u << 20; // bounded waits: far beyond any legitimate one
 constexpr unsigned kMemSpin = 1u << 16;
@@ -121,11 +126,11 @@ struct OneArgs {
   int t_max;
   uint16_t* h;
   float* H;
-  u64* hdr;        // [0] error word
+  u64* hdr;        // [0] error word, [1] sequence number, [2] the current call's tag
   u64* start;      // [team][OS_MAX] start words
   u64* ring;       // [team][OSLOTS][slot words]
   int64_t slotw;   // words per slot: S * OR * record words, then OR * n H_pre words
-  u64 epoch;       // sequence number of the call (never 0)
+  int nstart;      // start words in the workspace (max_teams(S) * OS_MAX)
   int xbytes, hbytes;
   int force_break; // testing aid: every workgroup starts broken, so the call falls back
 };
@@ -136,6 +141,9 @@ __device__ __forceinline__ u64 xword(uint32_t v, uint32_t tag) {
 __device__ __forceinline__ u64 agent_load(const u64* p) {
   return __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The call's tag: the header's sequence number (advanced by the kernel that
+// follows the single pass) with the top bit set.
+__device__ __forceinline__ u64 call_tag(const OneArgs& a) { return agent_load(a.hdr + 1) | kTagBit; }
 // Flags in LDS, shared by the workgroup's waves.  Atomic accesses (never
 // cached in registers, never merged) on the variables themselves, so the
 // compiler keeps them LDS operations: a generic (flat) access would also
@@ -247,6 +255,8 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
     }
     sk_free = 0;
     broken = a.force_break;
+    if (blockIdx.x == 0)   // the tag the fallback kernel compares the error word with
+      __hip_atomic_store(a.hdr + 2, call_tag(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (tid < OW) {
     part_ready[tid] = 0;
@@ -387,7 +397,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
           // A block narrower than 16 columns (the last one) repeats valid
           // entries in its unused columns: output column c depends only on
           // B column c, and columns >= m are never written out.
-          const int ent = 64 * nb + g * cn + (r16 < cn ? r16 : r16 - cn);
+          const int ent = 64 * nb + g * cn + r16 % cn;
           PhiOp<BF16> b;
           b.hi = __builtin_bit_cast(bf16x8, phi_l[w][i][0][ent]);
           b.lo = __builtin_bit_cast(bf16x8, phi_l[w][i][1][ent]);
@@ -533,11 +543,12 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
     // call's sequence number.
     __builtin_amdgcn_s_setprio(2);
     const int xw = wave - OW;
+    const u64 tag = call_tag(a);
     u64* st = a.start + static_cast<int64_t>(team) * OS_MAX;
-    if (lane == 0 && xw == 0) st[s] = a.epoch;
+    if (lane == 0 && xw == 0) st[s] = tag;
     if (lane < S) {
       unsigned n = 0;
-      while (agent_load(st + lane) != a.epoch) {
+      while (agent_load(st + lane) != tag) {
         if (flag_get(vbroken)) break;
         if (++n > kStartSpin) {
           flag_set(vbroken, 1);
@@ -678,7 +689,8 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
       lds_done();
       if (lane == 0) flag_set(&maps_tag[jb % OMR], jb + 1);
     }
-    if (flag_get(vbroken) && lane == 0) __hip_atomic_store(a.hdr, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (flag_get(vbroken) && lane == 0)
+      __hip_atomic_store(a.hdr, tag ^ kErrFlip, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     // ----------------------------------------------------------------- Sinkhorn
     // Two tiles per pass: lanes 32 q .. 32 q + 31 take tile jt + q, 16 lanes
@@ -710,6 +722,211 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
   }
 }
 
+// The single pass's fallback, and the bookkeeping that follows every call.
+// Workgroup 0 advances the header's sequence number (the next call's tag)
+// and clears the start words.  Every workgroup then compares the error word
+// with the current call's tag and returns unless a wait of the single pass ran
+// out; if one did, the workgroups take whole 16-token tiles and recompute h
+// and H with the single pass's arithmetic in its order:
+//  - member slice s, wave w: positions 256 s + 32 w .. +31, the same MFMA
+//    sequence (per stream: the Gram diagonal, then phi hi and lo per
+//    16-column block) on the same operands (phi split into bf16 halves the
+//    same way), the same fp64 redo of an overflowing sum of squares;
+//  - the member's record: the 8 waves' partials added in wave order (fp32;
+//    the sum of squares in fp64);
+//  - the team's sums: the same fixed tree over 16 lanes (member = lane % 16,
+//    members past S add 0) in fp64;
+//  - logits, gates, Sinkhorn and h = H_pre . X by the same functions.
+// No exchange, so nothing here waits for another workgroup.
+template <int N, bool HC>
+__global__ __launch_bounds__(OW * 64) void pre_one_pass_fallback_kernel(OneArgs a) {
+  constexpr int M = num_maps(N);
+  constexpr int NB = (M + 15) / 16;
+  constexpr int NN = N * N;
+  constexpr int NWD = M + 1;                 // team sums per token: m projections, then the sum of squares
+  constexpr int NTH = OW * 64;
+  __shared__ float fred[OW][OR][M];
+  __shared__ double fred_ss[OW][OR];
+  __shared__ float mrec[OS_MAX][OR][M];
+  __shared__ double mss[OS_MAX][OR];
+  __shared__ double team[OR][NWD];
+  __shared__ float fmaps[OR][N];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const u64 err = agent_load(a.hdr);
+  const u64 cur = agent_load(a.hdr + 2);
+  if (blockIdx.x == 0) {
+    if (tid == 0) {
+      const u64 next = ((agent_load(a.hdr + 1) & ~kTagBit) + 1) & ~kTagBit;
+      __hip_atomic_store(a.hdr + 1, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int q = tid; q < a.nstart; q += NTH) a.start[q] = 0ull;
+  }
+  if (err != (cur ^ kErrFlip)) return;
+
+  const int S = a.S;
+  const int d = a.d;
+  const int64_t T = a.T;
+  for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int64_t t = tile * OR + r16;
+    const bool tv = t < T;
+    for (int s = 0; s < S; ++s) {
+      const int j0 = s * OSLICE + 32 * w + 8 * g;
+      const bool jv = j0 < d;
+      u32x4 x[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        x[i] = (tv && jv) ? *reinterpret_cast<const u32x4*>(a.X + (t * N + i) * d + j0) : u32x4{0u, 0u, 0u, 0u};
+      f32x4 gram = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 acc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, x[i]);
+        gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, xv, gram, 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int cn = (M - 16 * nb < 16) ? M - 16 * nb : 16;
+          const int col = 16 * nb + r16 % cn;
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = jv ? a.phi[static_cast<int64_t>(i * d + j0 + e) * M + col] : 0.0f;
+          acc[nb] = mfma_block(Raw8<BF16>{x[i]}, make_phi_op(f, BF16{}), acc[nb]);
+        }
+      }
+      const int dv = r16 & 3;
+      const float sqf = dv == 0 ? gram[0] : dv == 1 ? gram[1] : dv == 2 ? gram[2] : gram[3];
+      double sq = static_cast<double>(sqf);
+      const bool ovf = g == (r16 >> 2) && !__builtin_isfinite(sqf);
+      if (__any(ovf)) {
+        double s64 = 0.0;
+        for (int q = 0; q < 4; ++q) {
+          const int src = 16 * q + r16;
+#pragma unroll
+          for (int i = 0; i < N; ++i) {
+            u32x4 xq;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              xq[c] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * src, static_cast<int>(x[i][c])));
+            float v[8];
+            unpack8(Raw8<BF16>{xq}, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s64 = fma(static_cast<double>(v[e]), static_cast<double>(v[e]), s64);
+          }
+        }
+        if (ovf) sq = s64;
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = 16 * nb + r16;
+        if (col < M) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) fred[w][4 * g + v][col] = acc[nb][v];
+        }
+      }
+      if (g == (r16 >> 2)) fred_ss[w][r16] = sq;
+      __syncthreads();
+      for (int q = tid; q < OR * M; q += NTH) {
+        const int tok = q / M;
+        const int c = q - tok * M;
+        float v = fred[0][tok][c];
+#pragma unroll
+        for (int ww = 1; ww < OW; ++ww) v += fred[ww][tok][c];
+        mrec[s][tok][c] = v;
+      }
+      if (tid < OR) {
+        double sd = fred_ss[0][tid];
+#pragma unroll
+        for (int ww = 1; ww < OW; ++ww) sd += fred_ss[ww][tid];
+        mss[s][tid] = sd;
+      }
+      __syncthreads();
+    }
+    // The team's sums: one (token, word) per 16-lane row.
+    for (int base = 4 * w; base < OR * NWD; base += 4 * OW) {
+      const int pi = base + (lane >> 4);
+      const int rm = lane & 15;
+      const bool pv = pi < OR * NWD;
+      const int tok = pv ? pi / NWD : 0;
+      const int wd = pv ? pi - tok * NWD : 0;
+      double v = 0.0;
+      if (pv && rm < S) v = wd < M ? static_cast<double>(mrec[rm][tok][wd]) : mss[rm][tok];
+      v = row16_sum(v);
+      if (pv && rm == 0) team[tok][wd] = v;
+    }
+    __syncthreads();
+    // Maps: 16 lanes per token, four tokens per wave.
+    if (w < OR / 4) {
+      const int tok = 4 * w + (lane >> 4);
+      const int e = lane & 15;
+      const int colr = N + e;
+      const int colg = (e < N) ? e : (N + NN + (e - N));
+      const int cr = e < NN ? colr : 0, cg = e < 2 * N ? colg : 0;
+      const float bias_r = a.bias[cr], bias_g = a.bias[cg];
+      const float alpha_g = (e < N) ? a.a_pre : a.a_post;
+      const double inv_r = inv_rms(team[tok][M], N * d, a.eps);
+      const double zr = team[tok][cr];
+      const double zg = team[tok][cg];
+      float gv = 0.0f, rv = -INFINITY;
+      if constexpr (HC) {
+        if (e < 2 * N)
+          gv = static_cast<float>(static_cast<double>(bias_g) + static_cast<double>(alpha_g) * tanh(zg * inv_r));
+        rv = (e < NN) ? static_cast<float>(static_cast<double>(bias_r) +
+                                           static_cast<double>(a.a_res) * tanh(zr * inv_r))
+                      : 0.0f;
+      } else {
+        if (e < 2 * N) {
+          const float l = logit_of(zg, inv_r, alpha_g, bias_g);
+          gv = (e < N) ? sigmoidf_(l) : 2.0f * sigmoidf_(l);
+        }
+        if (e < NN) rv = logit_of(zr, inv_r, a.a_res, bias_r);
+      }
+      float mv = rv;
+      if constexpr (!HC) mv = sinkhorn16<N>(e < NN ? rv : -INFINITY, e, a.t_max);
+      const int64_t tt = tile * OR + tok;
+      if (tt < T) {
+        float* Ht = a.H + tt * M;
+        if (e < NN) Ht[N + e] = mv;
+        if (e < 2 * N) Ht[colg] = gv;
+      }
+      if (e < N) fmaps[tok][e] = gv;
+    }
+    __syncthreads();
+    // h = H_pre . X, from a second read of the tile.
+    float hp[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) hp[i] = fmaps[r16][i];
+    for (int s = 0; s < S; ++s) {
+      const int j0 = s * OSLICE + 32 * w + 8 * g;
+      if (!tv || j0 >= d) continue;
+      u32x4 x[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) x[i] = *reinterpret_cast<const u32x4*>(a.X + (t * N + i) * d + j0);
+      float o[8];
+      {
+        float v[8];
+        unpack8(Raw8<BF16>{x[0]}, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = hp[0] * v[e];
+      }
+#pragma unroll
+      for (int i = 1; i < N; ++i) {
+        float v[8];
+        unpack8(Raw8<BF16>{x[i]}, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(hp[i], v[e], o[e]);
+      }
+      *reinterpret_cast<u32x4*>(a.h + t * d + j0) = pack8(o, BF16{}).v;
+    }
+    __syncthreads();   // the next tile reuses the LDS arrays
+  }
+}
+
 int one_pass_slices(int d) { return (d + OSLICE - 1) / OSLICE; }
 
 // Token record: m partials, padding to an even word, the fp64 sum of squares.
@@ -719,21 +936,20 @@ int64_t slot_words(int S, int n) { return static_cast<int64_t>(S) * OR * record_
 int max_teams(int S) { return OXCD * (48 / S); }   // devices with up to 48 CUs per XCD
 
 template <int N, bool HC>
-const void* one_pass_kernel_ptr() {
-  return reinterpret_cast<const void*>(&pre_one_pass_kernel<N, HC>);
+void one_pass_kernels(const void** fn, const void** fb) {
+  *fn = reinterpret_cast<const void*>(&pre_one_pass_kernel<N, HC>);
+  *fb = reinterpret_cast<const void*>(&pre_one_pass_fallback_kernel<N, HC>);
 }
-
-std::atomic<u64> g_epoch{0};
 
 }  // namespace
 
-// Bytes the single-pass form needs: header, start words and the exchange
-// ring, for devices with up to 48 CUs per XCD.
-size_t pre_fused_workspace_bytes(int64_t /*T*/, int n, int d) {
+// Body bytes the single-pass form needs after the header: start words and
+// the exchange ring, for devices with up to 48 CUs per XCD.
+size_t pre_fused_body_bytes(int n, int d) {
   const int S = one_pass_slices(d);
-  if (S < OS_MIN || S > OS_MAX) return 0;
+  if (n > 4 || S < OS_MIN || S > OS_MAX) return 0;
   const int teams = max_teams(S);
-  return OHDR + static_cast<size_t>(teams) * OS_MAX * sizeof(u64) +
+  return static_cast<size_t>(teams) * OS_MAX * sizeof(u64) +
          static_cast<size_t>(teams) * OSLOTS * static_cast<size_t>(slot_words(S, n)) * sizeof(u64);
 }
 
@@ -750,16 +966,13 @@ bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev) {
   return (p.T + OR - 1) / OR >= 40 * teams;
 }
 
-// Launch the single-pass form when it applies; returns hipErrorNotSupported
-// (without launching anything) when it does not, so the caller can fall back.
+// Launch the single-pass form and its fallback kernel when it applies;
+// returns hipErrorNotSupported (without launching anything) when it does
+// not, so the caller can take the two-pass form.
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
-                            float* H, void* workspace, size_t ws_bytes, const DeviceInfo& dev, hipStream_t stream) {
+                            float* H, void* workspace, size_t ws_bytes, bool force_fallback, const DeviceInfo& dev,
+                            hipStream_t stream) {
   if (p.dtype != MHC_BF16 || (p.n != 4 && p.n != 2 && p.n != 1)) return hipErrorNotSupported;
-  // Not under stream capture: a graph replays the captured call's sequence
-  // number, so words left by the previous replay would pass for this one's.
-  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone)
-    return hipErrorNotSupported;
   const int S = one_pass_slices(p.d);
   if (S < OS_MIN || S > OS_MAX || dev.num_cus % OXCD != 0) return hipErrorNotSupported;
   const int per_xcd = dev.num_cus / OXCD;
@@ -773,13 +986,14 @@ hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi
   const int64_t xbytes = p.T * p.n * static_cast<int64_t>(p.d) * 2;
   const int64_t hbytes = p.T * static_cast<int64_t>(p.d) * 2;
   if (xbytes >= (int64_t{1} << 31) || p.T < 1) return hipErrorNotSupported;
-  if (pre_fused_workspace_bytes(p.T, p.n, p.d) > ws_bytes) return hipErrorNotSupported;
+  if (OHDR + pre_fused_body_bytes(p.n, p.d) > ws_bytes) return hipErrorNotSupported;
   const bool hc = p.maps == MHC_MAPS_HC;
   const void* fn = nullptr;
+  const void* fb = nullptr;
   switch (p.n) {
-    case 1: fn = hc ? one_pass_kernel_ptr<1, true>() : one_pass_kernel_ptr<1, false>(); break;
-    case 2: fn = hc ? one_pass_kernel_ptr<2, true>() : one_pass_kernel_ptr<2, false>(); break;
-    default: fn = hc ? one_pass_kernel_ptr<4, true>() : one_pass_kernel_ptr<4, false>(); break;
+    case 1: hc ? one_pass_kernels<1, true>(&fn, &fb) : one_pass_kernels<1, false>(&fn, &fb); break;
+    case 2: hc ? one_pass_kernels<2, true>(&fn, &fb) : one_pass_kernels<2, false>(&fn, &fb); break;
+    default: hc ? one_pass_kernels<4, true>(&fn, &fb) : one_pass_kernels<4, false>(&fn, &fb); break;
   }
   int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, OT, 0) != hipSuccess || occ < 1)
@@ -806,19 +1020,18 @@ hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi
   a.H = H;
   a.hdr = reinterpret_cast<u64*>(base);
   a.start = reinterpret_cast<u64*>(base + OHDR);
-  a.ring = a.start + static_cast<size_t>(max_teams(S)) * OS_MAX;
+  a.nstart = max_teams(S) * OS_MAX;
+  a.ring = a.start + a.nstart;
   a.slotw = slot_words(S, p.n);
-  a.epoch = ++g_epoch;
   a.xbytes = static_cast<int>(xbytes);
   a.hbytes = static_cast<int>(hbytes);
-  const char* fb = std::getenv("MHC_TEST_ONE_PASS_FALLBACK");
-  a.force_break = (fb != nullptr && fb[0] == '1') ? 1 : 0;
+  a.force_break = force_fallback ? 1 : 0;
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel(fn, dim3(dev.num_cus), dim3(OT), args, 0, stream);
   if (e != hipSuccess) return e;
-  // The fallback: the two-pass form, gated on this call's sequence number in
-  // the error word, so it runs only if a wait of the single pass ran out.
-  return launch_pre_gated(p, X, phi, bias, h, H, base + OHDR, dev, a.hdr, a.epoch, stream);
+  // Always launched: it advances the sequence number, and recomputes the
+  // call only if a wait of the single pass ran out.
+  return hipLaunchKernel(fb, dim3(dev.num_cus), dim3(OW * 64), args, 0, stream);
 }
 
 }  // namespace mhc

@@ -19,7 +19,10 @@ int main(void) {
   p.n = 4;
   mhc_status b = mhc_post(&p, 0, 0, 0, 0, 0);             /* NULL tensors */
   size_t ws = mhc_pre_workspace_size(&p);
-  printf("%d %d %d %d\n", mhc_abi_version(), (int)a, (int)b, ws > 0);
+  size_t wq = mhc_workspace_size(&p, MHC_OP_PRE);
+  size_t wb = mhc_workspace_size(&p, MHC_OP_PRE_BWD);
+  printf("%d %d %d %d %d %d\n", mhc_abi_version(), (int)a, (int)b, ws > 0, wq == ws,
+         wb == mhc_pre_bwd_workspace_size(&p) && wb > 0);
   return 0;
 }
 """
@@ -42,4 +45,4 @@ def test_header_compiles_and_links_as_c(tmp_path):
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, timeout=60).stdout.split()
     import re
     ver = int(re.search(r"#define MHC_ABI_VERSION (\d+)", open(os.path.join(ROOT, "include", "mhc.h")).read()).group(1))
-    assert out == [str(ver), "5", "1", "1"]
+    assert out == [str(ver), "5", "1", "1", "1", "1"]

@@ -95,30 +95,51 @@ def test_pre_ex_argument_checks(lib):
 
 
 def test_workspace_size_formula(lib):
+    # [256-byte header, which only the single pass uses][body: the largest of the forms' records]
     for (T, n, d) in ((64, 4, 256), (16384, 4, 4096), (5, 2, 264), (1, 1, 8), (4096, 4, 2560)):
         p = _params(T=T, n=n, d=d)
         slices = -(-d // 256)
         width = ((n * n + 2 * n + 1) & ~1) + 2          # m fp32 partials, then an aligned fp64
-        two_pass = slices * T * width * 4 + 512 * 16    # records + write-only trash slots (16 B per thread)
+        body = slices * T * width * 4 + 512 * 16        # records + write-only trash slots (16 B per thread)
         if -(-T // 32) * slices < 128:                  # small-T form: slices of 64 positions
-            two_pass = max(two_pass, -(-d // 64) * T * width * 4 + 512 * 16)
-        # one pass: header, 16 start words per team, then per team 5 ring slots of 16-token
+            body = max(body, -(-d // 64) * T * width * 4 + 512 * 16)
+        # one pass: 16 start words per team, then per team 5 ring slots of 16-token
         # records (m + 2 words per member and token) and n H_pre words per token, 8 B a word;
         # room for 8 XCDs x floor(48 / slices) teams
         teams = 8 * (48 // slices)
         record = ((n * n + 2 * n + 1) & ~1) + 2            # m partials, even padding, fp64 sum of squares
         slot = slices * 16 * record + 16 * n
-        one_pass = 256 + teams * 16 * 8 + teams * 5 * slot * 8 if 8 <= slices <= 16 else 0
-        if one_pass:
-            two_pass += 256                             # the single pass's fallback keeps its records after the header
-        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == max(two_pass, one_pass)
+        one_pass = teams * 16 * 8 + teams * 5 * slot * 8 if 8 <= slices <= 16 else 0
+        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == 256 + max(body, one_pass)
     for (T, d) in ((64, 256), (1, 8), (4096, 4104)):
         # n = 8: records of 80 partials, 2 words of padding and an fp64 (84 words, 16-byte
         # aligned) over slices of 64 positions, plus trash slots
         p = _params(T=T, n=8, d=d)
-        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == -(-d // 64) * T * 84 * 4 + 512 * 16
+        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == 256 + -(-d // 64) * T * 84 * 4 + 512 * 16
     assert lib.mhc_pre_workspace_size(None) == 0
     assert lib.mhc_pre_workspace_size(ctypes.byref(_params(n=3))) == 0
+
+
+def test_workspace_size_query_by_op(lib):
+    """mhc_workspace_size(p, op) answers for every entry point: the same
+    numbers as the per-entry-point queries, 0 for those that need no scratch,
+    for invalid parameters and for unknown op codes."""
+    import mhc_hyper_connections_amd as m
+    for (T, n, d, dt) in ((64, 4, 256, 0), (16384, 4, 4096, 1), (5, 2, 264, 1), (100, 8, 512, 1), (33, 1, 1024, 0)):
+        p = _params(T=T, n=n, d=d, dtype=dt)
+        q = ctypes.byref(p)
+        assert lib.mhc_workspace_size(q, m.OP_PRE) == lib.mhc_pre_workspace_size(q) > 0
+        assert lib.mhc_workspace_size(q, m.OP_POST_PRE) == lib.mhc_pre_workspace_size(q)
+        assert lib.mhc_workspace_size(q, m.OP_POST_BWD) == lib.mhc_post_bwd_workspace_size(q)
+        assert lib.mhc_workspace_size(q, m.OP_PRE_BWD) == lib.mhc_pre_bwd_workspace_size(q)
+        assert lib.mhc_workspace_size(q, m.OP_POST) == 0
+        assert lib.mhc_workspace_size(q, m.OP_AMAX) == 0
+        for bad in (-1, 6, 1000):
+            assert lib.mhc_workspace_size(q, bad) == 0
+    for op in range(6):
+        assert lib.mhc_workspace_size(None, op) == 0
+        assert lib.mhc_workspace_size(ctypes.byref(_params(n=3)), op) == 0
+    assert m.workspace_size(m.OP_PRE_BWD, 16384, 4, 4096) == m.pre_bwd_workspace_size(16384, 4, 4096)
 
 
 def test_post_argument_checks(lib):

@@ -1,11 +1,10 @@
-"""The forward step captured into a HIP graph (torch.cuda.CUDAGraph).
+"""Entry points captured into a HIP graph (torch.cuda.CUDAGraph).
 
-mhc_pre's single pass stamps its exchange words with a per-call sequence
-number, which a graph replay would repeat, so on a capturing stream
-MHC_PRE_AUTO takes the two-pass form and MHC_PRE_ONE_PASS is refused.  The captured step
-(mhc_pre, mhc_post, mhc_amax) is replayed several times with eager work and
-synchronisations in between; every replay must give the eager two-pass
-results bit for bit.
+mhc_pre's single pass takes its exchange tag from a sequence number in the
+workspace header, which the kernel after it advances, so a replayed capture
+gets a fresh tag every time.  Captured work is replayed several times with
+eager calls on the same workspace and synchronisations in between; every
+replay must give the eager results bit for bit.
 """
 import numpy as np
 import pytest
@@ -13,6 +12,8 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
+
+ERR_FLIP = 0x5555555555555555
 
 
 @pytest.fixture(scope="module")
@@ -24,8 +25,16 @@ def mhc():
     return m
 
 
-def test_forward_step_in_a_graph(mhc):
-    T, n, d, m = 12288, 4, 4096, 24            # AUTO takes the single pass here when not capturing
+def _header(ws):
+    return [int(v) & 0xFFFFFFFFFFFFFFFF for v in ws[:24].view(torch.int64).cpu()]
+
+
+@pytest.mark.parametrize("algo", ["auto", "fallback_test"])
+def test_forward_step_in_a_graph(mhc, algo):
+    """The forward step (mhc_pre in the single pass, mhc_post, mhc_amax)
+    captured once and replayed 4 times; with the testing aid every replay runs
+    the single pass's fallback, which must give the same bits too."""
+    T, n, d, m = 12288, 4, 4096, 24            # AUTO takes the single pass here
     g = torch.Generator(device="cuda").manual_seed(31)
     X = torch.randn(T, n, d, device="cuda", generator=g).to(torch.bfloat16)
     Y = torch.randn(T, d, device="cuda", generator=g).to(torch.bfloat16)
@@ -37,13 +46,15 @@ def test_forward_step_in_a_graph(mhc):
     H = torch.empty((T, m), device="cuda")
     Xo = torch.empty_like(X)
     amax = torch.empty(T, device="cuda")
+    code = mhc.PRE_AUTO if algo == "auto" else mhc.PRE_ONE_PASS_FALLBACK_TEST
 
-    _, _, used_eager = mhc.pre_ex(X, phi, bias, mhc.PRE_AUTO, alpha=alpha, workspace=ws)
+    h_ref, H_ref, used_eager = mhc.pre_ex(X, phi, bias, mhc.PRE_AUTO, alpha=alpha, workspace=ws)
     assert used_eager == mhc.PRE_ONE_PASS
-    h_ref, H_ref, _ = mhc.pre_ex(X, phi, bias, mhc.PRE_TWO_PASS, alpha=alpha, workspace=ws)
     Xo_ref = mhc.post(X, Y, H_ref)
     a_ref = mhc.amax(H_ref.unsqueeze(0).contiguous(), n, want_all=False)["amax"]
     torch.cuda.synchronize()
+    hd = _header(ws)
+    assert hd[0] != hd[2] ^ ERR_FLIP
     refs = [t.clone() for t in (h_ref, H_ref, Xo_ref, a_ref)]
 
     s = torch.cuda.Stream()
@@ -51,14 +62,13 @@ def test_forward_step_in_a_graph(mhc):
     graph = torch.cuda.CUDAGraph()
     used = {}
     with torch.cuda.graph(graph, stream=s):
-        _, _, used["auto"] = mhc.pre_ex(X, phi, bias, mhc.PRE_AUTO, alpha=alpha, h=h, H=H, workspace=ws)
+        _, _, used["captured"] = mhc.pre_ex(X, phi, bias, code, alpha=alpha, h=h, H=H, workspace=ws)
         mhc.post(X, Y, H, out=Xo)
         mhc.amax(H.unsqueeze(0), n, out_amax=amax, want_all=False)
-        with pytest.raises(mhc.MhcError) as ei:
-            mhc.pre_ex(X, phi, bias, mhc.PRE_ONE_PASS, alpha=alpha, h=h, H=H, workspace=ws)
-        assert ei.value.status == 5                        # MHC_ERR_UNSUPPORTED, nothing captured
-    assert used["auto"] == mhc.PRE_TWO_PASS
+    assert used["captured"] == mhc.PRE_ONE_PASS
+    torch.cuda.synchronize()
 
+    seq = _header(ws)[1]
     for r in range(4):
         for t in (h, H, Xo, amax):
             t.zero_()
@@ -67,8 +77,11 @@ def test_forward_step_in_a_graph(mhc):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
+        hd = _header(ws)
+        assert hd[1] == seq + 2 * (r + 1), "every call, eager or replayed, advances the sequence number"
+        assert (hd[0] == hd[2] ^ ERR_FLIP) == (algo != "auto"), f"replay {r}: unexpected fallback state"
         for got, want, name in zip((h, H, Xo, amax), refs, ("h", "H", "X'", "amax")):
-            assert torch.equal(got, want), f"replay {r}: {name} differs from the eager two-pass result"
+            assert torch.equal(got, want), f"replay {r}: {name} differs from the eager single-pass result"
 
 
 def test_backward_and_post_pre_in_a_graph(mhc):

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import TOL, assert_close, dname, sample_tokens, to_device, to_host
+from gpu_helpers import TOL, assert_close, dname, for_token_chunks, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -80,33 +80,40 @@ def _hc_stack(mhc, w, T, L, maps):
     return X0, np.stack(phis), np.stack(biases), to_host(X), to_host(Hs), {k: to_host(v) for k, v in am.items()}
 
 
-@pytest.mark.parametrize("T,sampled", [(40, False), (4096, True)], ids=["T40", "T4096_sampled"])
-def test_hc_stack60(mhc, oracle_lib, T, sampled):
-    """The 60-layer stack with HC maps against the oracle: final state, every
-    layer's maps, per-token composite Amax; and the contrast: on the same
-    biases the mHC maps keep the composite at Amax ~1 while HC's grows by
-    orders of magnitude."""
+@pytest.mark.parametrize("T", [40, 4096])
+def test_hc_stack60(mhc, oracle_lib, T):
+    """The 60-layer stack with HC maps against the oracle on every token:
+    final state, every layer's maps, per-token composite Amax; and the
+    contrast: on the same biases the mHC maps keep the composite at Amax ~1
+    while HC's grows by orders of magnitude."""
     w = synth.WORKLOADS["hc_stack60_bf16_T4096_d2560"]
     L = w.layers
+    print(f"[hc] stack T={T}", flush=True)
     X0, phis, biases, Xg, Hg, am = _hc_stack(mhc, w, T, L, mhc.MAPS_HC)
-    tok = sample_tokens(T, 12) if sampled else np.arange(T, dtype=np.int64)
     alphas = np.tile(np.array(w.alpha, np.float32), (L, 1))
-    ref = oracle_lib.stack_hc(X0, phis, biases, alphas, eps=w.eps, tokens=tok)
     # The HC stack is ill-conditioned: one ulp on one input value moves the
     # oracle's own results this much (tests/test_stack_conditioning.py), so
     # the comparison sits above that: >= 95% of final values within the bf16
     # tolerance, every error within 0.5 of the token RMS, maps within 3e-3,
     # composite Amax within 5e-3.
-    g = synth.bf16_bits_to_f32(Xg[tok]).astype(np.float64)
-    r = synth.bf16_bits_to_f32(ref["X"]).astype(np.float64)
-    scale = np.sqrt(np.mean(r * r, axis=(1, 2), keepdims=True))
-    err = np.abs(g - r)
-    assert np.all(np.isfinite(g))
-    assert np.mean(err <= 2e-2 * np.abs(r) + 1e-2 * scale) >= 0.95
-    assert float(np.max(err / scale)) <= 0.5
-    assert_close(Hg[:, tok], ref["H"], 0.0, 3e-3, what="HC stack maps")
-    rel = np.abs(am["amax"][tok] - ref["amax"]) / ref["amax"]
-    assert np.all(rel <= 5e-3), rel.max()
+    counts = []
+
+    def cmp(tok):
+        ref = oracle_lib.stack_hc(X0, phis, biases, alphas, eps=w.eps, tokens=tok)
+        g = synth.bf16_bits_to_f32(Xg[tok]).astype(np.float64)
+        r = synth.bf16_bits_to_f32(ref["X"]).astype(np.float64)
+        scale = np.sqrt(np.mean(r * r, axis=(1, 2), keepdims=True))
+        err = np.abs(g - r)
+        assert np.all(np.isfinite(g))
+        inside = err <= 2e-2 * np.abs(r) + 1e-2 * scale
+        counts.append((int(inside.sum()), int(inside.size)))
+        assert float(np.max(err / scale)) <= 0.5, (int(tok[0]), float(np.max(err / scale)))
+        assert_close(Hg[:, tok], ref["H"], 0.0, 3e-3, what=f"HC stack maps, tokens {tok[0]}..")
+        rel = np.abs(am["amax"][tok] - ref["amax"]) / ref["amax"]
+        assert np.all(rel <= 5e-3), (int(tok[0]), float(rel.max()))
+
+    for_token_chunks(cmp, T, chunk=64)
+    assert sum(c[0] for c in counts) >= 0.95 * sum(c[1] for c in counts)
     assert np.median(am["amax"]) > 50.0
     _, _, _, _, _, am_m = _hc_stack(mhc, w, T, L, mhc.MAPS_MHC)
     assert np.max(am_m["amax"]) < 1.01

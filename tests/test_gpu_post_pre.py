@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import assert_close, check_stack_state, sample_tokens, to_device, to_host
+from gpu_helpers import assert_close, check_stack_every_token, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -80,18 +80,13 @@ def _stack_fused(mhc, w, T, L):
     return X0, np.stack(phis), np.stack(biases), to_host(X), to_host(Hs), {k: to_host(v) for k, v in am.items()}
 
 
-@pytest.mark.parametrize("T,sampled", [(40, False), (4096, True)], ids=["T40", "T4096_sampled"])
-def test_stack60_fused(mhc, oracle_lib, T, sampled):
+@pytest.mark.parametrize("T", [40, 4096])
+def test_stack60_fused(mhc, oracle_lib, T):
     """The 60-layer stack on mhc_post_pre: final state, every layer's maps and
-    the per-token composite Amax against the oracle (same criteria as the
-    unfused stack)."""
+    the per-token composite Amax against the oracle on every token (same
+    criteria as the unfused stack)."""
     w = synth.WORKLOADS["stack60_bf16_T4096_d2560"]
     L = w.layers
+    print(f"[post_pre] stack T={T}", flush=True)
     X0, phis, biases, Xg, Hg, am = _stack_fused(mhc, w, T, L)
-    tok = sample_tokens(T, 12) if sampled else np.arange(T, dtype=np.int64)
-    alphas = np.tile(np.array(w.alpha, np.float32), (L, 1))
-    ref = oracle_lib.stack(X0, phis, biases, alphas, eps=w.eps, t_max=w.t_max, tokens=tok)
-    check_stack_state(Xg[tok], ref["X"])
-    assert_close(Hg[:, tok], ref["H"], 1e-3, 1e-4, what="stack maps")
-    rel = np.abs(am["amax"][tok] - ref["amax"]) / ref["amax"]
-    assert np.all(rel <= 1e-3), rel.max()
+    check_stack_every_token(oracle_lib, w, X0, phis, biases, Xg, Hg, am, L)
