@@ -72,7 +72,8 @@ typedef enum mhc_status {
   MHC_ERR_UNSUPPORTED = 5,  /* valid for the method but not built for the device (n = 3, d % 8 != 0) */
   MHC_ERR_ALIAS = 6,        /* an output overlaps an input other than the permitted exact alias */
   MHC_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than the entry point's size query */
-  MHC_ERR_HIP = 8           /* a HIP runtime call or a kernel launch failed */
+  MHC_ERR_HIP = 8,          /* a HIP runtime call or a kernel launch failed */
+  MHC_ERR_SCRATCH = 9       /* the call needs more scratch than mhc_pre_noalloc's static buffer holds */
 } mhc_status;
 
 typedef enum mhc_dtype { MHC_FP32 = 0, MHC_BF16 = 1 } mhc_dtype;
@@ -184,6 +185,25 @@ size_t mhc_pre_workspace_size(const mhc_params* p);
 mhc_status mhc_pre_ex(const mhc_params* p, const void* X, const float* phi, const float* bias, void* h,
                       float* H, void* workspace, size_t workspace_bytes, int32_t algo, int32_t* algo_used,
                       void* stream);
+
+/* ---- mhc_pre_noalloc: mhc_pre without allocation or workspace ----------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * computation, arguments, form choice (MHC_PRE_AUTO) and results as mhc_pre,
+ * but no workspace argument: the scratch is a static device array of
+ * MHC_PRE_NOALLOC_SCRATCH_BYTES per GPU inside the library, allocated when
+ * the library's code is loaded on that GPU and held until the process ends.
+ * The call itself allocates and frees nothing.
+ *   Returns MHC_ERR_SCRATCH (before anything is enqueued) when
+ *   mhc_pre_workspace_size(p) exceeds MHC_PRE_NOALLOC_SCRATCH_BYTES: at
+ *   n = 4, d = 4096, bf16, up to about T = 19,700 tokens.
+ * Every call on a GPU uses that GPU's one array, which keeps the last call's
+ * contents (the single pass's sequence number carries over; nothing needs
+ * clearing).  Calls that overlap in time on one GPU race on it: issue them on
+ * one stream, or order them. */
+#define MHC_PRE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+mhc_status mhc_pre_noalloc(const mhc_params* p, const void* X, const float* phi, const float* bias, void* h,
+                           float* H, void* stream);
 
 /* ---- mhc_post: stream mixing + broadcast-add --------------------------------
  * X_out[t, i, :] = sum_j H_res[t, i, j] X[t, j, :] + H_post[t, i] Y[t, :]

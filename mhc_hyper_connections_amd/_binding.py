@@ -15,10 +15,12 @@ LIB_PATH = os.path.join(HERE, "libmhc.so")
 
 MHC_FP32, MHC_BF16 = 0, 1
 STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_DTYPE", 4: "MHC_ERR_ALIGN",
-          5: "MHC_ERR_UNSUPPORTED", 6: "MHC_ERR_ALIAS", 7: "MHC_ERR_WORKSPACE", 8: "MHC_ERR_HIP"}
+          5: "MHC_ERR_UNSUPPORTED", 6: "MHC_ERR_ALIAS", 7: "MHC_ERR_WORKSPACE", 8: "MHC_ERR_HIP", 9: "MHC_ERR_SCRATCH"}
 EXPORTS = ["mhc_pre", "mhc_pre_ex", "mhc_pre_workspace_size", "mhc_post", "mhc_amax", "mhc_gelu_half",
            "mhc_post_pre", "mhc_post_bwd", "mhc_post_bwd_ex", "mhc_post_bwd_workspace_size", "mhc_pre_bwd",
-           "mhc_pre_bwd_workspace_size", "mhc_workspace_size", "mhc_status_string", "mhc_abi_version"]
+           "mhc_pre_bwd_workspace_size", "mhc_workspace_size", "mhc_pre_noalloc", "mhc_status_string",
+           "mhc_abi_version"]
+PRE_NOALLOC_SCRATCH_BYTES = 32 << 20
 PRE_AUTO, PRE_TWO_PASS, PRE_ONE_PASS, PRE_ONE_PASS_FALLBACK_TEST = 0, 1, 2, 3
 OP_PRE, OP_POST, OP_POST_PRE, OP_AMAX, OP_POST_BWD, OP_PRE_BWD = 0, 1, 2, 3, 4, 5
 
@@ -77,6 +79,8 @@ def load_library(path: str = LIB_PATH):
     lib.mhc_pre_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mhc_pre_bwd.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.mhc_pre_bwd.restype = ctypes.c_int
+    lib.mhc_pre_noalloc.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P]
+    lib.mhc_pre_noalloc.restype = ctypes.c_int
     lib.mhc_workspace_size.argtypes = [ctypes.POINTER(Params), ctypes.c_int32]
     lib.mhc_workspace_size.restype = ctypes.c_size_t
     lib.mhc_status_string.argtypes = [ctypes.c_int]
@@ -198,6 +202,24 @@ def pre_ex(X, phi, bias, algo=PRE_AUTO, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_ma
                                         _ptr(workspace), ws_bytes, int(algo), ctypes.byref(used),
                                         _stream(stream, X.device)))
     return h, H, int(used.value)
+
+
+def pre_noalloc(X, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, h=None, H=None, stream=None,
+                maps=MAPS_MHC):
+    """mhc_pre_noalloc: mhc_pre on the library's static per-GPU scratch (no
+    workspace).  Returns (h, H); outputs not passed are allocated here."""
+    torch = _torch()
+    T, n, d = X.shape
+    m = n * n + 2 * n
+    p = make_params(T, n, d, _dtype_code(X), t_max, eps, alpha, maps)
+    if h is None:
+        h = torch.empty((T, d), dtype=X.dtype, device=X.device)
+    if H is None:
+        H = torch.empty((T, m), dtype=torch.float32, device=X.device)
+    _need_device(X, phi, bias, h, H)
+    _check("mhc_pre_noalloc", load_library().mhc_pre_noalloc(ctypes.byref(p), _ptr(X), _ptr(phi), _ptr(bias),
+                                                             _ptr(h), _ptr(H), _stream(stream, X.device)))
+    return h, H
 
 
 def post(X, Y, H, out=None, stream=None):

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmhc.so")
 BENCH_LIB = os.path.join(HERE, "libmhc_bench.so")
-SOURCES = ["capi.cpp", "pre.hip", "pre8.hip", "pre_fused.hip", "post.hip", "amax.hip", "bwd.hip"]
+SOURCES = ["capi.cpp", "pre.hip", "pre8.hip", "pre_fused.hip", "post.hip", "amax.hip", "bwd.hip", "noalloc.hip"]
 BENCH_SOURCES = ["bench_copy.hip"]
 ARCH = "gfx950"
 

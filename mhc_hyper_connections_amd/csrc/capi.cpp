@@ -71,6 +71,42 @@ mhc_status from_hip(hipError_t e) { return e == hipSuccess ? MHC_OK : MHC_ERR_HI
 
 }  // namespace
 
+namespace mhc {
+
+// mhc_pre's argument checks.  With check_workspace false the workspace is
+// the library's own (mhc_pre_noalloc) and is not checked here.
+mhc_status check_pre_call(const mhc_params* p, const void* X, const float* phi, const float* bias, const void* h,
+                          const float* H, const void* workspace, size_t workspace_bytes, bool check_workspace) {
+  mhc_status st = check_params(p);
+  if (st != MHC_OK) return st;
+  if (p->T == 0) return MHC_OK;
+  if (!X || !phi || !bias || !h || !H) return MHC_ERR_NULL;
+  const size_t need = pre_workspace_bytes(p->T, p->n, p->d);
+  if (check_workspace) {
+    if (need > 0 && !workspace) return MHC_ERR_WORKSPACE;
+    if (workspace_bytes < need) return MHC_ERR_WORKSPACE;
+  }
+  if (!aligned16(X) || !aligned16(h) || !aligned16(H) || !aligned16(phi) || !aligned16(bias)) return MHC_ERR_ALIGN;
+  if (check_workspace && need > 0 && !aligned16(workspace)) return MHC_ERR_ALIGN;
+  const int m = p->n * p->n + 2 * p->n;
+  const size_t sb = state_bytes(p->dtype);
+  const Range rX = range_of(X, static_cast<size_t>(p->T) * p->n * p->d * sb);
+  const Range rphi = range_of(phi, static_cast<size_t>(p->n) * p->d * m * 4);
+  const Range rb = range_of(bias, static_cast<size_t>(m) * 4);
+  const Range rh = range_of(h, static_cast<size_t>(p->T) * p->d * sb);
+  const Range rH = range_of(H, static_cast<size_t>(p->T) * m * 4);
+  if (overlap(rh, rX) || overlap(rh, rphi) || overlap(rh, rb) || overlap(rh, rH)) return MHC_ERR_ALIAS;
+  if (overlap(rH, rX) || overlap(rH, rphi) || overlap(rH, rb)) return MHC_ERR_ALIAS;
+  if (check_workspace && need > 0) {
+    const Range rw = range_of(workspace, need);
+    if (overlap(rw, rX) || overlap(rw, rphi) || overlap(rw, rb) || overlap(rw, rh) || overlap(rw, rH))
+      return MHC_ERR_ALIAS;
+  }
+  return MHC_OK;
+}
+
+}  // namespace mhc
+
 extern "C" {
 
 int mhc_abi_version(void) { return MHC_ABI_VERSION; }
@@ -86,6 +122,7 @@ const char* mhc_status_string(mhc_status s) {
     case MHC_ERR_ALIAS: return "an output overlaps an input";
     case MHC_ERR_WORKSPACE: return "workspace missing or too small";
     case MHC_ERR_HIP: return "a HIP call or kernel launch failed";
+    case MHC_ERR_SCRATCH: return "the call needs more scratch than mhc_pre_noalloc's static buffer holds";
   }
   return "unknown status";
 }
@@ -106,27 +143,8 @@ mhc_status mhc_pre_ex(const mhc_params* p, const void* X, const float* phi, cons
   if (algo != MHC_PRE_AUTO && algo != MHC_PRE_TWO_PASS && algo != MHC_PRE_ONE_PASS &&
       algo != MHC_PRE_ONE_PASS_FALLBACK_TEST)
     return MHC_ERR_SHAPE;
-  mhc_status st = check_params(p);
-  if (st != MHC_OK) return st;
-  if (p->T == 0) return MHC_OK;
-  if (!X || !phi || !bias || !h || !H) return MHC_ERR_NULL;
-  const size_t need = mhc::pre_workspace_bytes(p->T, p->n, p->d);
-  if (need > 0 && !workspace) return MHC_ERR_WORKSPACE;
-  if (workspace_bytes < need) return MHC_ERR_WORKSPACE;
-  if (!aligned16(X) || !aligned16(h) || !aligned16(H) || !aligned16(phi) || !aligned16(bias)) return MHC_ERR_ALIGN;
-  if (need > 0 && !aligned16(workspace)) return MHC_ERR_ALIGN;
-  const int m = p->n * p->n + 2 * p->n;
-  const size_t sb = state_bytes(p->dtype);
-  const Range rX = range_of(X, static_cast<size_t>(p->T) * p->n * p->d * sb);
-  const Range rphi = range_of(phi, static_cast<size_t>(p->n) * p->d * m * 4);
-  const Range rb = range_of(bias, static_cast<size_t>(m) * 4);
-  const Range rh = range_of(h, static_cast<size_t>(p->T) * p->d * sb);
-  const Range rH = range_of(H, static_cast<size_t>(p->T) * m * 4);
-  const Range rw = range_of(workspace, need);
-  if (overlap(rh, rX) || overlap(rh, rphi) || overlap(rh, rb) || overlap(rh, rH)) return MHC_ERR_ALIAS;
-  if (overlap(rH, rX) || overlap(rH, rphi) || overlap(rH, rb)) return MHC_ERR_ALIAS;
-  if (need > 0 && (overlap(rw, rX) || overlap(rw, rphi) || overlap(rw, rb) || overlap(rw, rh) || overlap(rw, rH)))
-    return MHC_ERR_ALIAS;
+  const mhc_status st = mhc::check_pre_call(p, X, phi, bias, h, H, workspace, workspace_bytes, true);
+  if (st != MHC_OK || p->T == 0) return st;
   const mhc::DeviceInfo dev = device_info();
   int used = MHC_PRE_TWO_PASS;
   const hipError_t e = mhc::launch_pre(*p, X, phi, bias, h, H, workspace, workspace_bytes, algo, &used, dev,

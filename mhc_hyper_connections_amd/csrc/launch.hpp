@@ -15,6 +15,11 @@ struct DeviceInfo {
   int num_cus = 256;       // compute units
 };
 
+// mhc_pre's argument checks (capi.cpp); check_workspace false skips the
+// workspace's (mhc_pre_noalloc supplies its own).
+mhc_status check_pre_call(const mhc_params* p, const void* X, const float* phi, const float* bias, const void* h,
+                          const float* H, const void* workspace, size_t workspace_bytes, bool check_workspace);
+
 // mhc_post: stream mixing + broadcast-add.
 hipError_t launch_post(const mhc_params& p, const void* X, const void* Y, const float* H, void* Xo,
                        hipStream_t stream);

@@ -38,8 +38,8 @@ def test_exports_every_declared_symbol(lib):
 def test_abi_version_and_status_strings(lib):
     ver = int(re.search(r"#define MHC_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
     assert lib.mhc_abi_version() == ver
-    for s in range(9):
-        assert lib.mhc_status_string(s)
+    for s in range(10):
+        assert lib.mhc_status_string(s) and lib.mhc_status_string(s) != b"unknown status"
     assert lib.mhc_status_string(12345) == b"unknown status"
 
 
@@ -266,3 +266,21 @@ def test_maps_field(lib):
     assert lib.mhc_pre_bwd(ctypes.byref(p), *A[:8], A[7] + 4096, A[7] + 8192,
                            lib.mhc_pre_bwd_workspace_size(ctypes.byref(p)), None) == 5   # no HC backward
     assert ctypes.sizeof(m.Params) == 48
+
+
+def test_pre_noalloc_host_checks(lib):
+    """mhc_pre_noalloc refuses, before anything reaches a device, what mhc_pre
+    refuses, and a call whose scratch would exceed its static buffer."""
+    import mhc_hyper_connections_amd as m
+    call = lambda p, ptrs=A[:5]: lib.mhc_pre_noalloc(None if p is None else ctypes.byref(p), *ptrs, None)
+    assert call(None) == 1                                                  # NULL params
+    assert call(_params(n=3)) == 5                                          # unsupported n
+    assert call(_params(T=-1)) == 2
+    assert call(_params(), (A[0], None, A[2], A[3], A[4])) == 1             # NULL phi
+    assert call(_params(T=0), (None,) * 5) == 0                             # T = 0 is a no-op
+    big = _params(T=40000, n=4, d=4096)
+    far = [0x1000000000 * (k + 1) for k in range(5)]                       # 64 GiB apart: no overlap
+    assert lib.mhc_pre_workspace_size(ctypes.byref(big)) > m.PRE_NOALLOC_SCRATCH_BYTES
+    assert call(big, far) == 9                                              # MHC_ERR_SCRATCH
+    fits = _params(T=16384, n=4, d=4096)
+    assert lib.mhc_pre_workspace_size(ctypes.byref(fits)) <= m.PRE_NOALLOC_SCRATCH_BYTES
