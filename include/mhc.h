@@ -338,8 +338,10 @@ mhc_status mhc_gelu_half(int64_t count, int32_t dtype, const void* h, void* Y, v
 #define MHC_OP_PRE_BWD 5
 size_t mhc_workspace_size(const mhc_params* p, int32_t op);
 
-/* Static description of a status code (never NULL). */
-const char* mhc_status_string(mhc_status status);
+/* Static description of a status code (never NULL; "unknown status" for a
+ * value that is no mhc_status).  Takes an int so that any value a caller
+ * passes is well defined. */
+const char* mhc_status_string(int status);
 
 /* MHC_ABI_VERSION of the loaded library. */
 int mhc_abi_version(void);

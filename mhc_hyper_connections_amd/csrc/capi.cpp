@@ -111,7 +111,7 @@ extern "C" {
 
 int mhc_abi_version(void) { return MHC_ABI_VERSION; }
 
-const char* mhc_status_string(mhc_status s) {
+const char* mhc_status_string(int s) {
   switch (s) {
     case MHC_OK: return "ok";
     case MHC_ERR_NULL: return "a required pointer is NULL";

@@ -24,5 +24,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def oracle_lib():
+    # tests/test_sanitizers.py runs the oracle's pins again on a copy built
+    # with AddressSanitizer and UndefinedBehaviorSanitizer, named here.
     import oracle
-    return oracle.load()
+    return oracle.load(os.environ.get("MHC_TEST_ORACLE_LIB") or None)

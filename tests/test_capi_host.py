@@ -14,6 +14,12 @@ HEADER = os.path.join(ROOT, "include", "mhc.h")
 @pytest.fixture(scope="module")
 def lib():
     import mhc_hyper_connections_amd as m
+    # tests/test_sanitizers.py runs these checks again on a copy of the
+    # library whose host code is built with AddressSanitizer and
+    # UndefinedBehaviorSanitizer, named here.
+    san = os.environ.get("MHC_TEST_LIBMHC")
+    if san:
+        return m.load_library(san)
     if not os.path.exists(m.LIB_PATH):
         from mhc_hyper_connections_amd import build
         build.build(force=False)
