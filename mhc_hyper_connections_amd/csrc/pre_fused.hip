@@ -24,10 +24,11 @@
 //    step k it forms tile k's m partial dot products with phi on MFMA (phi
 //    as bf16 hi + lo halves, kept in LDS) and the partial sums of squares
 //    (the diagonal of the tile's 16 x 16 Gram matrix, also on MFMA) into an
-//    LDS ring; sums its eighth of tile k-1's record over the
-//    8 waves (wave order) and posts it with one 16-byte store; and, once
-//    tile k-OD's H_pre has come back, forms h = H_pre . X for its positions
-//    from the registers that still hold that tile, and stores it.  These
+//    LDS ring; once tile k-OD's H_pre has come back, forms h = H_pre . X for
+//    its positions from the registers that still hold that tile, and stores
+//    it; prefetches tile k+OP; and last sums its eighth of tile k's record
+//    over the 8 waves (wave order) and posts it with one 16-byte store (by
+//    then the other waves have written tile k's partials).  These
 //    waves issue no memory operation but their X loads, the record store and
 //    the h store, a fixed number per step (masked lanes use out-of-range
 //    buffer offsets, which move no data), so the in-order completion count
@@ -100,8 +101,9 @@ constexpr unsigned kStartSpin = 1u << 12; // the team's meeting: members start w
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: loads read 0, stores drop
 
 // Progress and slot reuse.  In step k a streaming wave writes tile k's
-// partials, posts its share of tile k-1's record, then emits tile k-OD,
-// which waits for that tile's H_pre.  An exchange wave handles tile j once
+// partials, emits tile k-OD (which waits for that tile's H_pre), prefetches
+// tile k+OP and then posts its share of tile k's record (which waits until
+// every streaming wave has written tile k's partials).  An exchange wave handles tile j once
 // every streaming wave of its member has posted tile j's record: B (read the
 // members' records of the owned tokens, post H_pre) and C (read all owners'
 // H_pre).  Nothing waits for a later step, so every wait ends.
@@ -113,7 +115,12 @@ constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: loads
 // tile, k-OMR, has been emitted when OMR >= OD.
 static_assert(OSLOTS >= OD, "exchange words of a tile are rewritten only after every member has read them");
 static_assert(OMR >= OD, "an H_pre slot in LDS is rewritten only after its tile has been emitted");
-static_assert(OD >= 2, "a tile's H_pre needs the next step's record post");
+static_assert(OD >= 2, "a tile's H_pre comes back from the exchange at least a step after its record");
+// The partials ring needs no wait of its own: a wave writes tile k into slot
+// k % ORR in step k after its post of tile k-1, which waited until every
+// wave had written tile k-1's partials, so every wave had finished step k-2,
+// including its post (the last read) of tile k-2 and of tile k-ORR <= k-2.
+static_assert(ORR >= 2, "a partials slot is rewritten only after every wave has posted its tile");
 
 struct OneArgs {
   int64_t T;
@@ -387,23 +394,29 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
       f32x4 acc[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const bf16x8 xv = __builtin_bit_cast(bf16x8, x[i]);
-        gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, xv, gram, 0, 0, 0);
+      // phi operands come from LDS per stream, next to its MFMAs (reading the
+      // next stream's ahead measured no faster and costs 16 registers that
+      // the hold of X tiles needs).  A block narrower than 16 columns (the
+      // last one) repeats valid entries in its unused columns: output column
+      // c depends only on B column c, and columns >= m are never written out.
+      PhiOp<BF16> bop[2][NB];
+      auto read_phi = [&](int i, PhiOp<BF16> (&b)[NB]) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int cn = (M - 16 * nb < 16) ? M - 16 * nb : 16;
-          // A block narrower than 16 columns (the last one) repeats valid
-          // entries in its unused columns: output column c depends only on
-          // B column c, and columns >= m are never written out.
           const int ent = 64 * nb + g * cn + r16 % cn;
-          PhiOp<BF16> b;
-          b.hi = __builtin_bit_cast(bf16x8, phi_l[w][i][0][ent]);
-          b.lo = __builtin_bit_cast(bf16x8, phi_l[w][i][1][ent]);
-          acc[nb] = mfma_block(Raw8<BF16>{x[i]}, b, acc[nb]);
+          b[nb].hi = __builtin_bit_cast(bf16x8, phi_l[w][i][0][ent]);
+          b[nb].lo = __builtin_bit_cast(bf16x8, phi_l[w][i][1][ent]);
         }
-        __builtin_amdgcn_sched_barrier(0);   // read phi per stream, next to its MFMAs (registers)
+      };
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        read_phi(i, bop[i & 1]);
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, x[i]);
+        gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, xv, gram, 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_block(Raw8<BF16>{x[i]}, bop[i & 1][nb], acc[nb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       const int dv = r16 & 3;
       const float sqf = dv == 0 ? gram[0] : dv == 1 ? gram[1] : dv == 2 ? gram[2] : gram[3];
@@ -431,8 +444,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
         }
         if (ovf) sq = s64;
       }
-      const int slot = jt % ORR;
-      wait_all_ge(posted, jt - ORR + 1, vbroken, lane);   // every wave has posted the slot's last tile
+      const int slot = jt % ORR;   // free: see the static_assert on ORR
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = 16 * nb + r16;
@@ -530,10 +542,10 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
       for (int u = 0; u < ONB; ++u) {
         const int k = k0 + u;
         if (k < J) partials(k, xb[u]);
-        post_share(k - 1);
         emit(k - OD, xb[(u + OP) % ONB]);
         load_tile(k + OP, xb[(u + OP) % ONB]);
         __builtin_amdgcn_sched_barrier(0);
+        post_share(k);
       }
     }
   } else if (wave < OW + OX) {
