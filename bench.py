@@ -260,6 +260,47 @@ def time_stack(mhc, torch, reps=5, warmup=2):
     return out
 
 
+def time_post_pre(mhc, torch, w, X, Y, H, phi, bias, reps, stream):
+    """Layer l's mhc_post fused with layer l+1's mhc_pre at the workload's
+    shape, both forms, per call (HIP events at the ends of `reps` calls).
+    GB/s on the least bytes such a fused layer moves: X_l and Y read, X_{l+1}
+    and h written, the maps read and written (80 KiB per token at n = 4,
+    d = 4096, bf16)."""
+    T, n, d = X.shape
+    m = n * n + 2 * n
+    sb = X.element_size()
+    least = T * (2 * n * d * sb + 2 * d * sb + 2 * m * 4)
+    Xo, h2, H2 = torch.empty_like(X), torch.empty_like(Y), torch.empty_like(H)
+    ws = torch.zeros(mhc.pre_workspace_size(T, n, d, mhc.MHC_BF16 if sb == 2 else mhc.MHC_FP32), dtype=torch.uint8,
+                     device=X.device)
+    out = {"least_bytes_per_token": least // T, "forms": {}}
+    for name, algo in (("one-pass", mhc.PRE_ONE_PASS), ("two-pass", mhc.PRE_TWO_PASS)):
+        def call():
+            return mhc.post_pre_ex(X, Y, H, phi, bias, algo, alpha=w.alpha, eps=w.eps, t_max=w.t_max, out=Xo, h=h2,
+                                   H_next=H2, workspace=ws, stream=stream)[3]
+        try:
+            for _ in range(3):
+                call()
+        except mhc.MhcError:
+            out["forms"][name] = None
+            continue
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(reps):
+            call()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) / reps * 1e3
+        out["forms"][name] = {"avg_us": us, "GBps_on_least_bytes": least / (us * 1e-6) / 1e9,
+                              "frac_of_peak": least / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+    out["auto_form"] = {1: "two-pass", 2: "one-pass"}.get(
+        mhc.post_pre_ex(X, Y, H, phi, bias, mhc.PRE_AUTO, alpha=w.alpha, eps=w.eps, t_max=w.t_max, out=Xo, h=h2,
+                        H_next=H2, workspace=ws, stream=stream)[3])
+    torch.cuda.synchronize()
+    return out
+
+
 def traffic_bytes(path, workload, entry):
     """HBM bytes per launch of an entry point measured with rocprofv3
     counters, or None when absent or when the kernel source changed since."""
@@ -511,9 +552,12 @@ def cpu_baseline(w, seconds_target=15.0):
 # ---- rocprofv3 results -> profiles/ ------------------------------------------
 # Which kernels make up each entry point (substrings of the demangled names).
 ENTRY_KERNELS = {
-    "mhc_pre": ["pre_one_pass_kernel<4, false>", "pre_one_pass_fallback_kernel<4, false>"],   # MHC_PRE_AUTO's form
+    "mhc_pre": ["pre_one_pass_kernel<4, false, false>", "pre_one_pass_fallback_kernel<4, false, false>"],   # AUTO's form
     "mhc_pre_two_pass": ["pre_partial_kernel<mhc::BF16, 4, 2, 0, 8, false>", "pre_finish_kernel<mhc::BF16, 4, false, 4>"],
     "mhc_post": ["post_tile_kernel<mhc::BF16, 4>"],
+    "mhc_post_pre_one_pass": ["pre_one_pass_kernel<4, false, true>", "pre_one_pass_fallback_kernel<4, false, true>"],
+    "mhc_post_pre_two_pass": ["pre_partial_kernel<mhc::BF16, 4, 1, 2, 8, false>",
+                              "pre_finish_kernel<mhc::BF16, 4, false, 4>"],
     "mhc_amax": ["amax_kernel<4>"],
     "mhc_post_bwd": ["post_bwd_tile_kernel<mhc::BF16, 4>", "post_bwd_reduce_kernel<4>"],
     "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 2, 1, 8, false>", "pre_bwd_token_kernel<4, true>",
@@ -523,6 +567,8 @@ ENTRY_SOURCES = {
     "mhc_pre": ["pre_fused.hip", "pre_common.hpp", "device.hpp"],
     "mhc_pre_two_pass": ["pre.hip", "pre_common.hpp", "device.hpp"],
     "mhc_post": ["post.hip", "device.hpp"],
+    "mhc_post_pre_one_pass": ["pre_fused.hip", "pre_common.hpp", "device.hpp"],
+    "mhc_post_pre_two_pass": ["pre.hip", "pre_common.hpp", "device.hpp"],
     "mhc_amax": ["amax.hip", "device.hpp"],
     "mhc_post_bwd": ["bwd.hip", "device.hpp"],
     "mhc_pre_bwd": ["bwd.hip", "pre.hip", "pre_common.hpp", "device.hpp"],
@@ -656,6 +702,9 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the 60-layer stack timing")
     ap.add_argument("--stack-only", action="store_true",
                     help="time only the 60-layer stack (for a kernel trace of it); prints its JSON and exits")
+    ap.add_argument("--post-pre-only", action="store_true",
+                    help="time only mhc_post_pre's two forms at the workload's shape, after the plain copy (for "
+                         "counter runs); prints their JSON and exits")
     ap.add_argument("--pre-algo", type=int, default=0, choices=[0, 1, 2],
                     help="mhc_pre form: 0 auto, 1 two-pass, 2 one-pass")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
@@ -739,43 +788,75 @@ def main():
     # and the reference that scales the rocprofv3 byte counters.
     copy_GBps = time_copy(torch, X, Xo, stream)
     log(f"plain copy of the state (stream_copy_kernel): {copy_GBps:.0f} GB/s")
+    if args.post_pre_only:
+        step()
+        pp = time_post_pre(mhc, torch, w, X, Y, H, phi, bias, args.steps, stream)
+        print(json.dumps({"copy_GBps": copy_GBps, "post_pre": pp}), flush=True)
+        return 0
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    # The timed region: K steps back to back with HIP events (on the stream
+    # every call is launched on) only at its two ends, bracketed by device
+    # synchronisations.  `value` and `ms_per_step` come from it.
     log(f"timing {K} steps")
+    bev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    for k in range(K):
-        step(evs[k])
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    total_ms = evs[0][0].elapsed_time(evs[K - 1][3])
-    per = {"mhc_pre": [], "mhc_post": [], "mhc_amax": []}
-    for e in evs:
-        per["mhc_pre"].append(e[0].elapsed_time(e[1]))
-        per["mhc_post"].append(e[1].elapsed_time(e[2]))
-        per["mhc_amax"].append(e[2].elapsed_time(e[3]))
-    ms_step = total_ms / K
-    tokens_per_s = T / (ms_step * 1e-3)
-    # The same K steps with events only around them, to show what the
-    # per-entry-point events inside the timed steps cost.
-    torch.cuda.synchronize()
-    bev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     bev[0].record(stream)
     for k in range(K):
         step()
     bev[1].record(stream)
     torch.cuda.synchronize()
-    ms_step_bare = bev[0].elapsed_time(bev[1]) / K
+    t_wall = time.perf_counter() - t_wall
+    ms_step = bev[0].elapsed_time(bev[1]) / K
+    tokens_per_s = T / (ms_step * 1e-3)
+    # The per-entry-point breakdown: the same K steps again, right after,
+    # with an event between every two calls.  Each event splits the stream
+    # (about 25 us per step on MI355X), so these steps are longer than the
+    # timed ones; the durations of the calls themselves are what is used.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for k in range(K):
+        step(evs[k])
+    torch.cuda.synchronize()
+    ms_step_events = evs[0][0].elapsed_time(evs[K - 1][3]) / K
+    per = {"mhc_pre": [], "mhc_post": [], "mhc_amax": []}
+    for e in evs:
+        per["mhc_pre"].append(e[0].elapsed_time(e[1]))
+        per["mhc_post"].append(e[1].elapsed_time(e[2]))
+        per["mhc_amax"].append(e[2].elapsed_time(e[3]))
+    # Each entry point alone: K calls back to back on the same inputs, HIP
+    # events only at the ends.  This is the average duration of one call
+    # (its kernels and the gaps between them) with nothing between calls.
+    alone_calls = {
+        "mhc_pre": lambda: mhc.pre_ex(X, phi, bias, args.pre_algo, alpha=w.alpha, eps=w.eps, t_max=w.t_max, h=h,
+                                      H=H, workspace=ws, stream=stream),
+        "mhc_post": lambda: mhc.post(X, Y, H, out=Xo, stream=stream),
+        "mhc_amax": lambda: mhc.amax(H1, n, out_amax=amax, want_all=False, stream=stream),
+    }
+    alone = {}
+    for name, call in alone_calls.items():
+        for _ in range(3):
+            call()
+        aev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        aev[0].record(stream)
+        for _ in range(K):
+            call()
+        aev[1].record(stream)
+        torch.cuda.synchronize()
+        alone[name] = aev[0].elapsed_time(aev[1]) / K
     algo = algorithmic_bytes(T, n, d, sbytes)
     step_bytes = sum(algo.values())
     kernels = {}
     for name, ts in per.items():
-        avg_ms = float(np.mean(ts))
-        kernels[name] = {"avg_us": avg_ms * 1e3, "median_us": float(np.median(ts)) * 1e3,
+        avg_ms = alone[name]
+        kernels[name] = {"avg_us": avg_ms * 1e3,
+                         "in_step_with_events_avg_us": float(np.mean(ts)) * 1e3,
+                         "in_step_with_events_median_us": float(np.median(ts)) * 1e3,
                          "algorithmic_bytes": algo[name],
                          "GBps": algo[name] / (avg_ms * 1e-3) / 1e9,
                          "frac_of_peak": algo[name] / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -792,7 +873,7 @@ def main():
                 "frac": kd["GBps"] / HBM_PEAK_GBPS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": kd["algorithmic_bytes"], "avg_launch_us": kd["avg_us"],
                 "choice": "the entry point furthest below peak among those taking >= 25% of the step"}
-    log(f"{ms_step * 1e3:.1f} us/step ({ms_step_bare * 1e3:.1f} us without the per-call events), "
+    log(f"{ms_step * 1e3:.1f} us/step ({ms_step_events * 1e3:.1f} us with an event between calls), "
         f"{tokens_per_s / 1e6:.2f} M tokens/s; "
         + ", ".join(f"{k} {v['avg_us']:.1f} us ({v['GBps']:.0f} GB/s)" for k, v in kernels.items()))
 
@@ -816,6 +897,10 @@ def main():
             forms[name] = None
     log("mhc_pre forms: " + ", ".join(f"{k} {v['avg_us']:.1f} us" for k, v in forms.items() if v))
 
+    post_pre = time_post_pre(mhc, torch, w, X, Y, H, phi, bias, max(5, K // 2), stream)
+    log("mhc_post_pre (layer l's post + layer l+1's pre) at this shape: " + ", ".join(
+        f"{k} {v['avg_us']:.1f} us ({v['GBps_on_least_bytes']:.0f} GB/s on {post_pre['least_bytes_per_token']} B/token)"
+        for k, v in post_pre["forms"].items() if v) + f"; AUTO takes {post_pre['auto_form']}")
     n8 = time_n8(mhc, torch)
     small_cfg = time_small_configs(mhc, torch)
     log("smaller layers (forward step): " + ", ".join(
@@ -880,8 +965,11 @@ def main():
         "algorithmic_bytes_per_step": step_bytes,
         "copy_GBps": copy_GBps,
         "copy_kernel": "stream_copy_kernel (libmhc_bench.so): 16-byte non-temporal loads and stores, "
-                       "16 KiB per workgroup, of the 512 MiB state into a second buffer",
-        "ms_per_step_without_inner_events": ms_step_bare,
+                       "4 KiB per workgroup, of the 512 MiB state into a second buffer",
+        "timing": "value and ms_per_step: K steps with HIP events only at the two ends; kernels[*].avg_us: K "
+                  "calls of that entry point alone, events only at the ends; in_step_with_events_*: the K steps "
+                  "again with an event between calls (ms_per_step_with_events)",
+        "ms_per_step_with_events": ms_step_events,
         "step_roofline": {"bound": "hbm", "achieved": step_bytes / (ms_step * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                           "target_frac": 0.70},
@@ -890,6 +978,7 @@ def main():
         "kernels": kernels,
         "mhc_pre_forms": forms,
         "small_t": small_t,
+        "post_pre": post_pre,
         "n8": n8,
         "smaller_layers": small_cfg,
         "backward": backward,

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 6
+#define MHC_ABI_VERSION 7
 
 typedef enum mhc_status {
   MHC_OK = 0,
@@ -220,26 +220,52 @@ mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const flo
 
 /* ---- mhc_post_pre: mhc_post of layer l, then mhc_pre of layer l+1 -------------
  * In a stack the state a layer writes is the state the next layer reads.
- * This entry point does both in one pass over the new state: it forms
+ * This entry point does both with one pass over the new state: it forms
  *   X_out = H_res X + H_post^T Y            (layer l's maps H, as mhc_post)
  * and, from the stored X_out, layer l+1's maps H_next and its sublayer input
- * h (as mhc_pre with phi, bias and p's alphas / eps / t_max).  The results
- * are bitwise those of mhc_post followed by mhc_pre in its two-pass form
- * (MHC_PRE_TWO_PASS; the single pass agrees to rounding); the second read of X_out
- * that the separate calls make for the projection is saved (the pages fuse
- * the layer's kernels for the same reason: [t6] tbl-dsv4-mhc-kernels).
+ * h (as mhc_pre with phi, bias and p's alphas / eps / t_max).  The pages fuse
+ * the layer's kernels for the same reason: the post kernel reads (n+1) C
+ * values per token instead of (3n+1) C ("mHC" notes on DeepSeek-V4, table
+ * tbl-dsv4-mhc-kernels).  The results are bitwise those of mhc_post followed
+ * by mhc_pre_ex in the form that ran (*algo_used of mhc_post_pre_ex).
  *   X       in   [T, n, d] layer l's input state
  *   Y       in   [T, d] layer l's sublayer output
  *   H       in   [T, m] layer l's maps
- *   X_out   out  [T, n, d] X_{l+1}; may be exactly X, other overlap refused
+ *   X_out   out  [T, n, d] X_{l+1}; may be exactly X (then the two-pass
+ *                form runs), other overlap refused
  *   phi, bias    layer l+1's parameters
  *   h       out  [T, d] layer l+1's sublayer input
  *   H_next  out  [T, m] layer l+1's maps
- *   workspace    at least mhc_pre_workspace_size(p) bytes
- * n = 1 and n = 8 run the two entry points one after the other. */
+ *   workspace    at least mhc_pre_workspace_size(p) bytes, as mhc_pre's
+ *                (header included)
+ * Forms (mhc_post_pre is mhc_post_pre_ex(..., MHC_PRE_AUTO, NULL, stream)):
+ *   MHC_PRE_TWO_PASS  the post inside the split-K projection pass, which
+ *                     stores X_out; the maps + aggregation pass reads X_out
+ *                     again (per token: X, Y read, X_out written, X_out read
+ *                     again, h written).
+ *   MHC_PRE_ONE_PASS  mhc_pre's single pass with the post in front: each
+ *                     team member mixes its slice of X and Y into X_out in
+ *                     registers, stores it, and uses the stored values for
+ *                     the projection and, once H_pre is known, for h, so
+ *                     X_out never comes back from HBM (per token: X, Y read,
+ *                     X_out, h written).  Same conditions as mhc_pre_ex's
+ *                     single pass, and X_out must not overlap X (the
+ *                     fallback kernel recomputes from X): MHC_ERR_ALIAS
+ *                     when X_out == X, MHC_ERR_UNSUPPORTED when the shape
+ *                     does not apply.
+ *   MHC_PRE_AUTO      the two-pass form, which measured faster on MI355X
+ *                     (T = 16384, n = 4, d = 4096: 325-336 us against
+ *                     343-396 us): with the post in front, the single
+ *                     pass's streaming waves have registers for only one
+ *                     tile in flight.
+ *   MHC_PRE_ONE_PASS_FALLBACK_TEST   as for mhc_pre_ex.
+ * n = 1 and n = 8 run mhc_post, then mhc_pre's two-pass form. */
 mhc_status mhc_post_pre(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out,
                         const float* phi, const float* bias, void* h, float* H_next, void* workspace,
                         size_t workspace_bytes, void* stream);
+mhc_status mhc_post_pre_ex(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out,
+                           const float* phi, const float* bias, void* h, float* H_next, void* workspace,
+                           size_t workspace_bytes, int32_t algo, int32_t* algo_used, void* stream);
 
 /* ---- backward ----------------------------------------------------------------
  * The pages give no backward formulas; they state that the layer is trained

@@ -19,10 +19,10 @@ bfloat16; phi [n*d, n*n+2n], bias [n*n+2n] and H [T, n*n+2n] in float32.
 from ._binding import (EXPORTS, LIB_PATH, MAPS_HC, MAPS_MHC, MHC_BF16, MHC_FP32, OP_AMAX, OP_POST, OP_POST_BWD,
                        OP_POST_PRE, OP_PRE, OP_PRE_BWD, PRE_AUTO, PRE_ONE_PASS, PRE_ONE_PASS_FALLBACK_TEST,
                        PRE_TWO_PASS, MhcError, Params, amax, gelu_half, load_library, make_params, post, post_bwd,
-                       post_bwd_workspace_size, post_pre, pre, pre_bwd, pre_bwd_workspace_size, pre_ex,
+                       post_bwd_workspace_size, post_pre, post_pre_ex, pre, pre_bwd, pre_bwd_workspace_size, pre_ex,
                        pre_noalloc, pre_workspace_size, workspace_size, PRE_NOALLOC_SCRATCH_BYTES)
 
-__all__ = ["pre", "pre_ex", "pre_noalloc", "PRE_NOALLOC_SCRATCH_BYTES", "post", "post_pre", "amax", "gelu_half", "pre_workspace_size", "post_bwd",
+__all__ = ["pre", "pre_ex", "pre_noalloc", "PRE_NOALLOC_SCRATCH_BYTES", "post", "post_pre", "post_pre_ex", "amax", "gelu_half", "pre_workspace_size", "post_bwd",
            "post_bwd_workspace_size", "pre_bwd", "pre_bwd_workspace_size", "workspace_size", "load_library",
            "make_params", "Params", "MhcError", "MHC_FP32", "MHC_BF16", "MAPS_MHC", "MAPS_HC", "PRE_AUTO",
            "PRE_TWO_PASS", "PRE_ONE_PASS", "PRE_ONE_PASS_FALLBACK_TEST", "OP_PRE", "OP_POST", "OP_POST_PRE",

@@ -17,7 +17,7 @@ MHC_FP32, MHC_BF16 = 0, 1
 STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_DTYPE", 4: "MHC_ERR_ALIGN",
           5: "MHC_ERR_UNSUPPORTED", 6: "MHC_ERR_ALIAS", 7: "MHC_ERR_WORKSPACE", 8: "MHC_ERR_HIP", 9: "MHC_ERR_SCRATCH"}
 EXPORTS = ["mhc_pre", "mhc_pre_ex", "mhc_pre_workspace_size", "mhc_post", "mhc_amax", "mhc_gelu_half",
-           "mhc_post_pre", "mhc_post_bwd", "mhc_post_bwd_ex", "mhc_post_bwd_workspace_size", "mhc_pre_bwd",
+           "mhc_post_pre", "mhc_post_pre_ex", "mhc_post_bwd", "mhc_post_bwd_ex", "mhc_post_bwd_workspace_size", "mhc_pre_bwd",
            "mhc_pre_bwd_workspace_size", "mhc_workspace_size", "mhc_pre_noalloc", "mhc_status_string",
            "mhc_abi_version"]
 PRE_NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -69,6 +69,9 @@ def load_library(path: str = LIB_PATH):
     lib.mhc_gelu_half.restype = ctypes.c_int
     lib.mhc_post_pre.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.mhc_post_pre.restype = ctypes.c_int
+    lib.mhc_post_pre_ex.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                    ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), _P]
+    lib.mhc_post_pre_ex.restype = ctypes.c_int
     lib.mhc_post_bwd.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P]
     lib.mhc_post_bwd.restype = ctypes.c_int
     lib.mhc_post_bwd_ex.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -336,6 +339,14 @@ def post_pre(X, Y, H, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, o
     """mhc_post_pre: layer l's mixing, then layer l+1's maps and sublayer
     input.  Returns (X_next [T, n, d], h [T, d], H_next [T, m]); ``out`` may
     be X itself."""
+    X_next, h, H_next, _ = post_pre_ex(X, Y, H, phi, bias, PRE_AUTO, alpha=alpha, eps=eps, t_max=t_max, out=out, h=h,
+                                       H_next=H_next, workspace=workspace, stream=stream, maps=maps)
+    return X_next, h, H_next
+
+
+def post_pre_ex(X, Y, H, phi, bias, algo=PRE_AUTO, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, out=None, h=None,
+                H_next=None, workspace=None, stream=None, maps=MAPS_MHC):
+    """mhc_post_pre_ex: returns (X_next, h, H_next, algorithm that ran)."""
     torch = _torch()
     T, n, d = X.shape
     m = n * n + 2 * n
@@ -349,7 +360,8 @@ def post_pre(X, Y, H, phi, bias, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, o
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=X.device)
     _need_device(X, Y, H, phi, bias, out, h, H_next, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("mhc_post_pre", lib.mhc_post_pre(ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(H), _ptr(out), _ptr(phi),
-                                            _ptr(bias), _ptr(h), _ptr(H_next), _ptr(workspace), ws_bytes,
-                                            _stream(stream, X.device)))
-    return out, h, H_next
+    used = ctypes.c_int32(-1)
+    _check("mhc_post_pre_ex", lib.mhc_post_pre_ex(ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(H), _ptr(out), _ptr(phi),
+                                                  _ptr(bias), _ptr(h), _ptr(H_next), _ptr(workspace), ws_bytes,
+                                                  int(algo), ctypes.byref(used), _stream(stream, X.device)))
+    return out, h, H_next, int(used.value)

@@ -173,6 +173,17 @@ mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const flo
 mhc_status mhc_post_pre(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out,
                         const float* phi, const float* bias, void* h, float* H_next, void* workspace,
                         size_t workspace_bytes, void* stream) {
+  return mhc_post_pre_ex(p, X, Y, H, X_out, phi, bias, h, H_next, workspace, workspace_bytes, MHC_PRE_AUTO, nullptr,
+                         stream);
+}
+
+mhc_status mhc_post_pre_ex(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out,
+                           const float* phi, const float* bias, void* h, float* H_next, void* workspace,
+                           size_t workspace_bytes, int32_t algo, int32_t* algo_used, void* stream) {
+  if (algo_used) *algo_used = MHC_PRE_TWO_PASS;
+  if (algo != MHC_PRE_AUTO && algo != MHC_PRE_TWO_PASS && algo != MHC_PRE_ONE_PASS &&
+      algo != MHC_PRE_ONE_PASS_FALLBACK_TEST)
+    return MHC_ERR_SHAPE;
   mhc_status st = check_params(p);
   if (st != MHC_OK) return st;
   if (p->T == 0) return MHC_OK;
@@ -199,9 +210,15 @@ mhc_status mhc_post_pre(const mhc_params* p, const void* X, const void* Y, const
     for (int b = a + 1; b < 4; ++b)
       if (overlap(outs[a], outs[b])) return MHC_ERR_ALIAS;
   }
+  const bool one_pass = algo == MHC_PRE_ONE_PASS || algo == MHC_PRE_ONE_PASS_FALLBACK_TEST;
+  if (one_pass && X_out == X) return MHC_ERR_ALIAS;     // the single pass needs X_{l+1} apart from X_l
   const mhc::DeviceInfo dev = device_info();
-  return from_hip(mhc::launch_post_pre(*p, X, Y, H, X_out, phi, bias, h, H_next, workspace, dev,
-                                       static_cast<hipStream_t>(stream)));
+  int used = MHC_PRE_TWO_PASS;
+  const hipError_t e = mhc::launch_post_pre(*p, X, Y, H, X_out, phi, bias, h, H_next, workspace, workspace_bytes,
+                                            algo, &used, dev, static_cast<hipStream_t>(stream));
+  if (algo_used) *algo_used = used;
+  if (e == hipErrorNotSupported && one_pass) return MHC_ERR_UNSUPPORTED;
+  return from_hip(e);
 }
 
 size_t mhc_post_bwd_workspace_size(const mhc_params* p) {

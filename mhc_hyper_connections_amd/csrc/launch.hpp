@@ -31,10 +31,12 @@ hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, cons
                       float* H, void* workspace, size_t ws_bytes, int algo, int* used, const DeviceInfo& dev,
                       hipStream_t stream);
 
-// mhc_post of layer l fused with mhc_pre of layer l+1 (pre.hip); workspace as mhc_pre's.
+// mhc_post of layer l fused with mhc_pre of layer l+1 (pre.hip); workspace
+// as mhc_pre's.  algo as launch_pre's: the single pass takes the post in
+// front of it when Xout does not overlap X; *used receives the form that ran.
 hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, const float* Hprev, void* Xout,
-                           const float* phi, const float* bias, void* h, float* H, void* workspace, const DeviceInfo& dev,
-                           hipStream_t stream);
+                           const float* phi, const float* bias, void* h, float* H, void* workspace, size_t ws_bytes,
+                           int algo, int* used, const DeviceInfo& dev, hipStream_t stream);
 
 // mhc_pre for n = 8 (pre8.hip): split-K over 64-position slices, then one
 // token per wave.
@@ -57,6 +59,11 @@ bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev);   // what 
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
                             float* H, void* workspace, size_t ws_bytes, bool force_fallback, const DeviceInfo& dev,
                             hipStream_t stream);
+// The single pass with layer l's mhc_post in front: X is X_l, Xo (not
+// overlapping X) receives X_{l+1}, and h, H are layer l+1's.
+hipError_t launch_post_pre_fused(const mhc_params& p, const void* X, const void* Y, const float* Hp, void* Xo,
+                                 const float* phi, const float* bias, void* h, float* H, void* workspace,
+                                 size_t ws_bytes, bool force_fallback, const DeviceInfo& dev, hipStream_t stream);
 
 // Split-K partials of mhc_pre's projection plus, per stream i, <D, X_i> over
 // the slice (pre.hip).  part: [S][T][pre_part_width(n, true)] floats with

@@ -709,9 +709,28 @@ size_t pre_partial_bytes(int64_t T, int n, int d, bool with_d) {
 }
 
 hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, const float* Hprev, void* Xout,
-                           const float* phi, const float* bias, void* h, float* H, void* workspace, const DeviceInfo& dev,
-                           hipStream_t stream) {
+                           const float* phi, const float* bias, void* h, float* H, void* workspace, size_t ws_bytes,
+                           int algo, int* used, const DeviceInfo& dev, hipStream_t stream) {
+  if (used) *used = MHC_PRE_TWO_PASS;
   if (p.T == 0) return hipSuccess;
+  // The single pass recomputes from X_l when its waits run out, so it needs
+  // X_{l+1} in a buffer of its own.  MHC_PRE_AUTO takes the two-pass form:
+  // on MI355X at T = 16384, n = 4, d = 4096 it ran in 325-336 us against
+  // 343-396 us for the single pass, whose streaming waves can then keep only
+  // one tile in flight (the hold of the tiles awaiting H_pre, the chunk of Y
+  // and the mix fill the registers of three waves per SIMD).
+  const bool separate = Xout != X;
+  if (algo == MHC_PRE_ONE_PASS || algo == MHC_PRE_ONE_PASS_FALLBACK_TEST) {
+    if (!separate) return hipErrorNotSupported;
+    const hipError_t e = launch_post_pre_fused(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, ws_bytes,
+                                               algo == MHC_PRE_ONE_PASS_FALLBACK_TEST, dev, stream);
+    if (e == hipSuccess) {
+      if (used) *used = MHC_PRE_ONE_PASS;
+      return hipSuccess;
+    }
+    (void)hipGetLastError();                 // clear a refused launch
+    return e;
+  }
   const bool bf = p.dtype == MHC_BF16;
   void* body = static_cast<char*>(workspace) + kPreHeaderBytes;
   switch (p.n) {
@@ -722,9 +741,8 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
     default: {   // n = 1 (m = 3 maps per token) and n = 8: the two entry points one after the other
       hipError_t e = launch_post(p, X, Y, Hprev, Xout, stream);
       if (e != hipSuccess) return e;
-      int used = 0;
-      return launch_pre(p, Xout, phi, bias, h, H, workspace, pre_workspace_bytes(p.T, p.n, p.d), MHC_PRE_TWO_PASS,
-                        &used, dev, stream);
+      int u = 0;
+      return launch_pre(p, Xout, phi, bias, h, H, workspace, ws_bytes, MHC_PRE_TWO_PASS, &u, dev, stream);
     }
   }
 }

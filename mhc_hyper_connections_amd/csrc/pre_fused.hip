@@ -79,6 +79,8 @@ typedef unsigned long long u64;
 constexpr int OW = 8;                   // streaming waves
 constexpr int OX = 2;                   // exchange waves (tiles alternate between them)
 constexpr int OT = (OW + OX + 1) * 64;  // + the exchange waves + the Sinkhorn wave
+constexpr int OTP = OT + 64;            // with the previous layer's mhc_post fused in: + the maps loader wave
+constexpr int OHR = 4;                  // LDS ring of the previous layer's mixing maps (tiles)
 constexpr int OSLICE = OW * 32;         // positions of d per member
 constexpr int OR = 16;                  // tokens per tile
 constexpr int OS_MIN = 8;               // team size range (ceil(d / OSLICE))
@@ -90,7 +92,12 @@ constexpr int OMR = 5;                  // LDS ring of H_pre (tiles; a slot is r
 constexpr int OKR = 4;                  // LDS ring of Sinkhorn inputs (tiles; taken two at a time)
 constexpr int OD = 5;                   // tiles between a tile's partials and its h; see below
 constexpr int OP = 2;                   // X tiles in flight ahead of the one being multiplied
-constexpr int ONB = OD + OP;            // X tile buffers per lane
+// With the previous layer's post fused in, a step also holds a chunk of Y
+// and the mix's maps and temporaries: one tile fewer in flight and one fewer
+// held keep the streaming waves within 168 registers (3 waves per SIMD)
+// without spilling.
+constexpr int OD_POST = 4;
+constexpr int OP_POST = 1;
 constexpr size_t OHDR = kPreHeaderBytes;       // workspace header (error word, sequence number, current tag)
 constexpr u64 kTagBit = 1ull << 63;     // set in every call's tag: a cleared or zeroed word never matches one
 constexpr u64 kErrFlip = 0x5555555555555555ull;   // error word = tag ^ kErrFlip: never the raw sequence word
@@ -116,6 +123,7 @@ constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: loads
 static_assert(OSLOTS >= OD, "exchange words of a tile are rewritten only after every member has read them");
 static_assert(OMR >= OD, "an H_pre slot in LDS is rewritten only after its tile has been emitted");
 static_assert(OD >= 2, "a tile's H_pre comes back from the exchange at least a step after its record");
+static_assert(OD_POST >= 2 && OD_POST <= OD && OP_POST >= 1, "the fused form's ring use is the plain form's");
 // The partials ring needs no wait of its own: a wave writes tile k into slot
 // k % ORR in step k after its post of tile k-1, which waited until every
 // wave had written tile k-1's partials, so every wave had finished step k-2,
@@ -140,6 +148,10 @@ struct OneArgs {
   int nstart;      // start words in the workspace (max_teams(S) * OS_MAX)
   int xbytes, hbytes;
   int force_break; // testing aid: every workgroup starts broken, so the call falls back
+  // With the previous layer's mhc_post fused in front (X is then X_l):
+  const uint16_t* Y;   // [T, d] layer l's sublayer output
+  const float* Hp;     // [T, m] layer l's maps
+  uint16_t* Xo;        // [T, n, d] X_{l+1}, which the rest of the pass reads in place of X
 };
 
 __device__ __forceinline__ u64 xword(uint32_t v, uint32_t tag) {
@@ -217,8 +229,55 @@ __device__ __forceinline__ double row16_sum(double v) {
   return v;
 }
 
-template <int N, bool HC>
-__global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
+// mhc_post of one chunk (8 positions of all n streams of a token), in place:
+// X_{l+1}[i] = sum_j H_res[i][j] X_l[j] + H_post[i] Y, each output value
+// accumulated in fp32 in the order j = 0 .. n-1 and then the Y term, and
+// rounded to bf16 (nearest, ties to even): mhc_post's arithmetic, so the bits
+// are those mhc_post stores.
+template <int N, bool RELOAD, typename Maps>
+__device__ __forceinline__ void post_mix(u32x4 (&x)[N], const u32x4& y, const Maps& maps) {
+  // Word c of every stream holds the same two positions: all n outputs of
+  // them are formed from the n inputs, then written over those inputs.
+  // maps(i, j) is H_res[i][j] and maps(i, n) H_post[i]; with RELOAD they are
+  // fetched again for every word (from LDS), so that only one row is held.
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (RELOAD) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);   // one word at a time: the scheduler would unpack all 16 ahead
+    }
+    float xv[N][2];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      xv[j][0] = bf16_lo(x[j][c]);
+      xv[j][1] = bf16_hi(x[j][c]);
+    }
+    const float y0 = bf16_lo(y[c]), y1 = bf16_hi(y[c]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float r0 = maps(i, 0);
+      float o0 = r0 * xv[0][0];
+      float o1 = r0 * xv[0][1];
+#pragma unroll
+      for (int j = 1; j < N; ++j) {
+        const float rj = maps(i, j);
+        o0 = fmaf(rj, xv[j][0], o0);
+        o1 = fmaf(rj, xv[j][1], o1);
+      }
+      const float pi = maps(i, N);
+      o0 = fmaf(pi, y0, o0);
+      o1 = fmaf(pi, y1, o1);
+      x[i][c] = pack_bf16(o0, o1);
+    }
+  }
+}
+
+template <int N, bool HC, bool POST>
+__global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a) {
+  constexpr int NTHR = POST ? OTP : OT;
+  constexpr int OD = POST ? OD_POST : ::mhc::OD;   // see OD_POST
+  constexpr int OP = POST ? OP_POST : ::mhc::OP;
+  constexpr int ONB = OD + OP;                      // X tile buffers per lane
   constexpr int M = num_maps(N);
   constexpr int NB = (M + 15) / 16;
   constexpr int NN = N * N;
@@ -243,6 +302,9 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
   __shared__ int maps_tag[OMR];            // H_pre of tile t is in slot t % OMR once maps_tag[slot] > t
   __shared__ int sk_tag[OKR];              // likewise for the Sinkhorn inputs
   __shared__ int sk_free, broken;
+  constexpr int HF = N * N + N;            // a token's H_res and H_post (maps row words n .. m-1)
+  __shared__ float hmix[POST ? OHR : 1][OR][HF];   // the previous layer's maps of a tile's tokens
+  __shared__ int hmix_tag[OHR];             // slot t % OHR holds tile t's once hmix_tag[slot] > t
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -256,6 +318,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
   if (tid == 0) {
     xcc_l = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7);   // HW_REG_XCC_ID
     for (int q = 0; q < OMR; ++q) maps_tag[q] = 0;
+    for (int q = 0; q < OHR; ++q) hmix_tag[q] = 0;
     for (int q = 0; q < OKR; ++q) {
       sk_tag[q] = 0;
       for (int o = 0; o < OTPR; ++o) sktok[q][o] = -1;
@@ -299,12 +362,24 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
   };
   // The first X tiles go out before the set-up below, which they overlap.
   u32x4 xb[ONB][N];
+  // With the previous layer's post fused in: the chunk of Y_l of the tile to
+  // be mixed next (loaded one step ahead of its use).
+  const __amdgpu_buffer_rsrc_t yrx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(POST ? a.Y : a.X), 0, a.hbytes, 0x00020000);
+  auto load_y = [&](int jt) -> u32x4 {
+    const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + r16;
+    const bool ok = jt < J && t < T && jv;
+    const uint32_t o0 = ok ? static_cast<uint32_t>((t * d + j0) * 2) : kOob;
+    return __builtin_amdgcn_raw_buffer_load_b128(yrx, static_cast<int>(o0), 0, 2);
+  };
+  u32x4 yb = {0u, 0u, 0u, 0u};
   if (wave < OW) {
 #pragma unroll
     for (int p = 0; p < OP; ++p) {
       load_tile(p, xb[p]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (POST) yb = load_y(0);
   }
 
   // This member's slice of phi into LDS as bf16 hi / lo operand halves: the
@@ -314,11 +389,11 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
   {
     constexpr int G = (M % 4 == 0) ? 4 : 1;            // floats per load
     constexpr int PER = OSLICE * M / G;                  // loads per stream
-    constexpr int KPHI = (N * PER + OT - 1) / OT;
+    constexpr int KPHI = (N * PER + NTHR - 1) / NTHR;
     float pv[KPHI][G];
 #pragma unroll
     for (int k = 0; k < KPHI; ++k) {
-      const int q = tid + k * OT;
+      const int q = tid + k * NTHR;
       const int i = q / PER;
       const int f = (q - i * PER) * G;
       const int row = f / M;
@@ -335,7 +410,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < KPHI; ++k) {
-      const int q = tid + k * OT;
+      const int q = tid + k * NTHR;
       if (q < N * PER) {
         const int i = q / PER;
         const int f = (q - i * PER) * G;
@@ -362,9 +437,9 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
   // writer has cleared it.
   u64* const tring = a.ring + static_cast<int64_t>(team) * OSLOTS * a.slotw;
   const int64_t recw = static_cast<int64_t>(S) * OR * W;   // record words per slot
-  for (int q = tid; q < OSLOTS * OR * W; q += OT)
+  for (int q = tid; q < OSLOTS * OR * W; q += NTHR)
     tring[(q / (OR * W)) * a.slotw + static_cast<int64_t>(s) * OR * W + q % (OR * W)] = 0ull;
-  for (int q = tid; q < OSLOTS * OTPR * N; q += OT) {
+  for (int q = tid; q < OSLOTS * OTPR * N; q += NTHR) {
     const int sl = q / (OTPR * N);
     const int r = q - sl * (OTPR * N);
     const int tok = s + (r / N) * S;
@@ -533,16 +608,45 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
       __builtin_amdgcn_raw_buffer_store_b128(pack8(o, BF16{}).v, hr, static_cast<int>(ho), 0, 2);
     };
 
+    // The previous layer's mhc_post of tile jt, in place: X_l in x becomes
+    // X_{l+1} = H_res X_l + H_post Y_l with mhc_post's arithmetic and
+    // rounding, which is stored and from here on is the tile.  Its N stores
+    // are issued whether or not the tile exists (then out of range).
+    const __amdgpu_buffer_rsrc_t xor_ = __builtin_amdgcn_make_buffer_rsrc(POST ? a.Xo : a.h, 0,
+                                                                          POST ? a.xbytes : a.hbytes, 0x00020000);
+    auto mix = [&](int jt, u32x4 (&x)[N], const u32x4& y) {
+      const bool have = jt < J;
+      const int sl = jt % OHR;
+      if (have) wait_ge(&hmix_tag[sl], jt + 1, vbroken);
+      // (a tile past the end mixes whatever the slot holds; its stores are
+      // out of range and it is never used)
+      const float* hm = &hmix[sl][r16][0];
+      post_mix<N, true>(x, y, [&](int i, int j) { return j < N ? hm[i * N + j] : hm[N * N + i]; });
+      const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + r16;
+      const bool ok = have && t < T && jv;
+      const uint32_t o0 = ok ? static_cast<uint32_t>((t * N * d + j0) * 2) : kOob;
+      const uint32_t st = ok ? static_cast<uint32_t>(d * 2) : 0u;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(x[i], xor_, static_cast<int>(o0 + i * st), 0, 2);
+    };
+
     // Tile k lives in buffer k % ONB; the buffer of tile k - OD, emitted in
     // step k, then receives tile k + OP.  Every step issues N loads and two
-    // stores, with no branch around any of them.
+    // stores (with the post fused in: N + 1 loads and N + 2 stores), with no
+    // branch around any of them.
     const int kend = ((J + OD + ONB - 1) / ONB) * ONB;
     for (int k0 = 0; k0 < kend; k0 += ONB) {
 #pragma unroll
       for (int u = 0; u < ONB; ++u) {
         const int k = k0 + u;
+        if constexpr (POST) {
+          mix(k, xb[u], yb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if (k < J) partials(k, xb[u]);
         emit(k - OD, xb[(u + OP) % ONB]);
+        if constexpr (POST) yb = load_y(k + 1);
         load_tile(k + OP, xb[(u + OP) % ONB]);
         __builtin_amdgcn_sched_barrier(0);
         post_share(k);
@@ -703,7 +807,7 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
     }
     if (flag_get(vbroken) && lane == 0)
       __hip_atomic_store(a.hdr, tag ^ kErrFlip, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
+  } else if (wave == OW + OX) {
     // ----------------------------------------------------------------- Sinkhorn
     // Two tiles per pass: lanes 32 q .. 32 q + 31 take tile jt + q, 16 lanes
     // per owned token.
@@ -731,6 +835,31 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
         if (e < 2 * N) Ht[colg] = in.y;
       }
     }
+  } else if constexpr (POST) {
+    // ------------------------------------------------- previous layer's maps
+    // Tile j's H_res and H_post rows into LDS slot j % OHR, once every
+    // streaming wave has mixed tile j - OHR (its partials of that tile are
+    // written after the mix).  Tokens past T read as 0.
+    constexpr int HW = OR * HF;
+    for (int j = 0; j < J; ++j) {
+      const int sl = j % OHR;
+      if (j >= OHR && !wait_all_ge(part_ready, j - OHR + 1, vbroken, lane)) break;
+      float v[(HW + 63) / 64];
+#pragma unroll
+      for (int k = 0; k < (HW + 63) / 64; ++k) {
+        const int q = lane + 64 * k;
+        const int tok = q / HF;
+        const int64_t t = (team + static_cast<int64_t>(j) * teams) * OR + tok;
+        v[k] = (q < HW && t < T) ? a.Hp[t * M + N + (q - tok * HF)] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < (HW + 63) / 64; ++k) {
+        const int q = lane + 64 * k;
+        if (q < HW) hmix[sl][q / HF][q % HF] = v[k];
+      }
+      lds_done();
+      if (lane == 0) flag_set(&hmix_tag[sl], j + 1);
+    }
   }
 }
 
@@ -748,9 +877,11 @@ __global__ __launch_bounds__(OT) void pre_one_pass_kernel(OneArgs a) {
 //    the sum of squares in fp64);
 //  - the team's sums: the same fixed tree over 16 lanes (member = lane % 16,
 //    members past S add 0) in fp64;
-//  - logits, gates, Sinkhorn and h = H_pre . X by the same functions.
+//  - logits, gates, Sinkhorn and h = H_pre . X by the same functions;
+//  - with the previous layer's post fused in, X_{l+1} by the same mix,
+//    stored, and read back for h.
 // No exchange, so nothing here waits for another workgroup.
-template <int N, bool HC>
+template <int N, bool HC, bool POST>
 __global__ __launch_bounds__(OW * 64) void pre_one_pass_fallback_kernel(OneArgs a) {
   constexpr int M = num_maps(N);
   constexpr int NB = (M + 15) / 16;
@@ -793,6 +924,22 @@ __global__ __launch_bounds__(OW * 64) void pre_one_pass_fallback_kernel(OneArgs 
 #pragma unroll
       for (int i = 0; i < N; ++i)
         x[i] = (tv && jv) ? *reinterpret_cast<const u32x4*>(a.X + (t * N + i) * d + j0) : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (POST) {
+        float res[N][N], post[N];
+        const float* Hr = a.Hp + (tv ? t : 0) * M;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+#pragma unroll
+          for (int j = 0; j < N; ++j) res[i][j] = tv ? Hr[N + i * N + j] : 0.0f;
+          post[i] = tv ? Hr[N + NN + i] : 0.0f;
+        }
+        const u32x4 y = (tv && jv) ? *reinterpret_cast<const u32x4*>(a.Y + t * d + j0) : u32x4{0u, 0u, 0u, 0u};
+        post_mix<N, false>(x, y, [&](int i, int j) { return j < N ? res[i][j] : post[i]; });
+        if (tv && jv) {
+#pragma unroll
+          for (int i = 0; i < N; ++i) *reinterpret_cast<u32x4*>(a.Xo + (t * N + i) * d + j0) = x[i];
+        }
+      }
       f32x4 gram = {0.0f, 0.0f, 0.0f, 0.0f};
       f32x4 acc[NB];
 #pragma unroll
@@ -916,9 +1063,10 @@ __global__ __launch_bounds__(OW * 64) void pre_one_pass_fallback_kernel(OneArgs 
     for (int s = 0; s < S; ++s) {
       const int j0 = s * OSLICE + 32 * w + 8 * g;
       if (!tv || j0 >= d) continue;
+      const uint16_t* Xs = POST ? a.Xo : a.X;   // the pass's state: X_{l+1} as stored above
       u32x4 x[N];
 #pragma unroll
-      for (int i = 0; i < N; ++i) x[i] = *reinterpret_cast<const u32x4*>(a.X + (t * N + i) * d + j0);
+      for (int i = 0; i < N; ++i) x[i] = *reinterpret_cast<const u32x4*>(Xs + (t * N + i) * d + j0);
       float o[8];
       {
         float v[8];
@@ -947,10 +1095,10 @@ int64_t slot_words(int S, int n) { return static_cast<int64_t>(S) * OR * record_
 
 int max_teams(int S) { return OXCD * (48 / S); }   // devices with up to 48 CUs per XCD
 
-template <int N, bool HC>
+template <int N, bool HC, bool POST>
 void one_pass_kernels(const void** fn, const void** fb) {
-  *fn = reinterpret_cast<const void*>(&pre_one_pass_kernel<N, HC>);
-  *fb = reinterpret_cast<const void*>(&pre_one_pass_fallback_kernel<N, HC>);
+  *fn = reinterpret_cast<const void*>(&pre_one_pass_kernel<N, HC, POST>);
+  *fb = reinterpret_cast<const void*>(&pre_one_pass_fallback_kernel<N, HC, POST>);
 }
 
 }  // namespace
@@ -978,13 +1126,17 @@ bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev) {
   return (p.T + OR - 1) / OR >= 40 * teams;
 }
 
-// Launch the single-pass form and its fallback kernel when it applies;
-// returns hipErrorNotSupported (without launching anything) when it does
-// not, so the caller can take the two-pass form.
-hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
-                            float* H, void* workspace, size_t ws_bytes, bool force_fallback, const DeviceInfo& dev,
-                            hipStream_t stream) {
+namespace {
+
+// Launch the single-pass form (with the previous layer's post in front when
+// Y is not null) and its fallback kernel when it applies; returns
+// hipErrorNotSupported (without launching anything) when it does not, so
+// the caller can take the two-pass form.
+hipError_t launch_one_pass(const mhc_params& p, const void* X, const void* Y, const float* Hp, void* Xo,
+                           const float* phi, const float* bias, void* h, float* H, void* workspace, size_t ws_bytes,
+                           bool force_fallback, const DeviceInfo& dev, hipStream_t stream) {
   if (p.dtype != MHC_BF16 || (p.n != 4 && p.n != 2 && p.n != 1)) return hipErrorNotSupported;
+  const bool post = Y != nullptr;
   const int S = one_pass_slices(p.d);
   if (S < OS_MIN || S > OS_MAX || dev.num_cus % OXCD != 0) return hipErrorNotSupported;
   const int per_xcd = dev.num_cus / OXCD;
@@ -1002,13 +1154,22 @@ hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi
   const bool hc = p.maps == MHC_MAPS_HC;
   const void* fn = nullptr;
   const void* fb = nullptr;
-  switch (p.n) {
-    case 1: hc ? one_pass_kernels<1, true>(&fn, &fb) : one_pass_kernels<1, false>(&fn, &fb); break;
-    case 2: hc ? one_pass_kernels<2, true>(&fn, &fb) : one_pass_kernels<2, false>(&fn, &fb); break;
-    default: hc ? one_pass_kernels<4, true>(&fn, &fb) : one_pass_kernels<4, false>(&fn, &fb); break;
+  if (post) {
+    switch (p.n) {
+      case 1: hc ? one_pass_kernels<1, true, true>(&fn, &fb) : one_pass_kernels<1, false, true>(&fn, &fb); break;
+      case 2: hc ? one_pass_kernels<2, true, true>(&fn, &fb) : one_pass_kernels<2, false, true>(&fn, &fb); break;
+      default: hc ? one_pass_kernels<4, true, true>(&fn, &fb) : one_pass_kernels<4, false, true>(&fn, &fb); break;
+    }
+  } else {
+    switch (p.n) {
+      case 1: hc ? one_pass_kernels<1, true, false>(&fn, &fb) : one_pass_kernels<1, false, false>(&fn, &fb); break;
+      case 2: hc ? one_pass_kernels<2, true, false>(&fn, &fb) : one_pass_kernels<2, false, false>(&fn, &fb); break;
+      default: hc ? one_pass_kernels<4, true, false>(&fn, &fb) : one_pass_kernels<4, false, false>(&fn, &fb); break;
+    }
   }
+  const int threads = post ? OTP : OT;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, OT, 0) != hipSuccess || occ < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, threads, 0) != hipSuccess || occ < 1)
     return hipErrorNotSupported;
 
   char* base = static_cast<char*>(workspace);
@@ -1038,12 +1199,34 @@ hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi
   a.xbytes = static_cast<int>(xbytes);
   a.hbytes = static_cast<int>(hbytes);
   a.force_break = force_fallback ? 1 : 0;
+  a.Y = static_cast<const uint16_t*>(Y);
+  a.Hp = Hp;
+  a.Xo = static_cast<uint16_t*>(Xo);
   void* args[] = {&a};
-  hipError_t e = hipLaunchKernel(fn, dim3(dev.num_cus), dim3(OT), args, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3(dev.num_cus), dim3(threads), args, 0, stream);
   if (e != hipSuccess) return e;
   // Always launched: it advances the sequence number, and recomputes the
   // call only if a wait of the single pass ran out.
   return hipLaunchKernel(fb, dim3(dev.num_cus), dim3(OW * 64), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
+                            float* H, void* workspace, size_t ws_bytes, bool force_fallback, const DeviceInfo& dev,
+                            hipStream_t stream) {
+  return launch_one_pass(p, X, nullptr, nullptr, nullptr, phi, bias, h, H, workspace, ws_bytes, force_fallback, dev,
+                         stream);
+}
+
+// The previous layer's mhc_post fused in front of the single pass: X is X_l,
+// Xo receives X_{l+1} (Xo must not overlap X: the fallback recomputes from
+// X_l).
+hipError_t launch_post_pre_fused(const mhc_params& p, const void* X, const void* Y, const float* Hp, void* Xo,
+                                 const float* phi, const float* bias, void* h, float* H, void* workspace,
+                                 size_t ws_bytes, bool force_fallback, const DeviceInfo& dev, hipStream_t stream) {
+  if (!Y || !Hp || !Xo) return hipErrorInvalidValue;
+  return launch_one_pass(p, X, Y, Hp, Xo, phi, bias, h, H, workspace, ws_bytes, force_fallback, dev, stream);
 }
 
 }  // namespace mhc

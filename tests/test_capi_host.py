@@ -264,6 +264,15 @@ def test_post_pre_argument_checks(lib):
     assert f(p, X=A[0] + 4) == 4
     assert f(_params(T=0), X=None) == 0
 
+    def fx(algo, O=A[3]):
+        used = ctypes.c_int32(-7)
+        st = lib.mhc_post_pre_ex(ctypes.byref(p), A[0], A[1], A[2], O, A[4], A[5], A[6], A[7], A[7] + (1 << 24),
+                                 need, algo, ctypes.byref(used), None)
+        return st, used.value
+    assert fx(7) == (2, 1)                             # unknown algorithm; *algo_used reset to the two-pass code
+    assert fx(2, O=A[0]) == (6, 1)                     # the single pass needs X_{l+1} apart from X
+    assert fx(3, O=A[0]) == (6, 1)
+
 
 def test_maps_field(lib):
     import mhc_hyper_connections_amd as m

@@ -130,3 +130,42 @@ def test_backward_and_post_pre_in_a_graph(mhc):
         torch.cuda.synchronize()
         for k, (got, want) in enumerate(zip(outs, refs)):
             assert torch.equal(got, want), f"replay {r}: output {k} differs from the eager run"
+
+
+def test_post_pre_single_pass_in_a_graph(mhc):
+    """mhc_post_pre in its single pass (layer l's post in front of layer
+    l+1's pre) captured and replayed 4 times with eager single-pass calls on
+    the same workspace in between: every replay gives the eager bits."""
+    T, n, d, m = 12288, 4, 4096, 24
+    g = torch.Generator(device="cuda").manual_seed(41)
+    X = torch.randn(T, n, d, device="cuda", generator=g).to(torch.bfloat16)
+    Y = torch.randn(T, d, device="cuda", generator=g).to(torch.bfloat16)
+    phi = torch.randn(n * d, m, device="cuda", generator=g) * 0.02
+    bias = torch.randn(m, device="cuda", generator=g) * 0.1
+    alpha = (1.0, 1.0, 1.0)
+    _, H = mhc.pre(X, phi, bias, alpha=alpha)
+    ws = torch.zeros(mhc.pre_workspace_size(T, n, d, mhc.MHC_BF16), dtype=torch.uint8, device="cuda")
+    Xn, hn, Hn = torch.empty_like(X), torch.empty_like(Y), torch.empty((T, m), device="cuda")
+    Xr, hr, Hr, used = mhc.post_pre_ex(X, Y, H, phi, bias, mhc.PRE_ONE_PASS, alpha=alpha, workspace=ws)
+    assert used == mhc.PRE_ONE_PASS
+    torch.cuda.synchronize()
+    hd = _header(ws)
+    assert hd[0] != hd[2] ^ ERR_FLIP
+    refs = [t.clone() for t in (Xr, hr, Hr)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        mhc.post_pre_ex(X, Y, H, phi, bias, mhc.PRE_ONE_PASS, alpha=alpha, out=Xn, h=hn, H_next=Hn, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(4):
+        for t in (Xn, hn, Hn):
+            t.zero_()
+        mhc.post_pre_ex(X, Y, H, phi, bias, mhc.PRE_ONE_PASS, alpha=(0.5, 0.5, 0.5), workspace=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        hd = _header(ws)
+        assert hd[0] != hd[2] ^ ERR_FLIP, f"replay {r}: a wait ran out"
+        for got, want, name in zip((Xn, hn, Hn), refs, ("X_(l+1)", "h", "H")):
+            assert torch.equal(got, want), f"replay {r}: {name} differs from the eager result"

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import assert_close, check_stack_every_token, to_device, to_host
+from gpu_helpers import TOL, assert_close, check_stack_every_token, for_token_chunks, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -90,3 +90,129 @@ def test_stack60_fused(mhc, oracle_lib, T):
     print(f"[post_pre] stack T={T}", flush=True)
     X0, phis, biases, Xg, Hg, am = _stack_fused(mhc, w, T, L)
     check_stack_every_token(oracle_lib, w, X0, phis, biases, Xg, Hg, am, L)
+
+
+# ---------------------------------------------------------------------------
+# The single pass with layer l's post in front (MHC_PRE_ONE_PASS): X_{l+1} is
+# formed in registers, stored, and used for layer l+1's projection and h
+# without being read back.
+
+ERR_FLIP = 0x5555555555555555
+
+
+def _recomputed(ws) -> bool:
+    hd = [int(v) & 0xFFFFFFFFFFFFFFFF for v in ws[:24].view(torch.int64).cpu()]
+    return hd[0] == hd[2] ^ ERR_FLIP
+
+
+def _inputs(w, alpha=None):
+    X = synth.make_state(w)
+    Y = synth.make_sublayer_out(w)
+    phi0, b0 = synth.make_params(w, layer=0)
+    phi1, b1 = synth.make_params(synth.scaled(w, layers=2), layer=1)
+    return X, Y, phi0, b0, phi1, b1
+
+
+def _one_pass_pair(mhc, w, algo, alpha=None):
+    """Layer 0's maps, then (a) mhc_post + single-pass mhc_pre and (b)
+    mhc_post_pre_ex(algo) on the same inputs."""
+    alpha = w.alpha if alpha is None else alpha
+    X, Y, phi0, b0, phi1, b1 = (to_device(a) for a in _inputs(w))
+    _, H0 = mhc.pre(X, phi0, b0, alpha=alpha, eps=w.eps, t_max=w.t_max)
+    Xs = mhc.post(X, Y, H0)
+    ws1 = torch.zeros(mhc.pre_workspace_size(w.T, w.n, w.d, w.dtype), dtype=torch.uint8, device="cuda")
+    hs, Hs, used_s = mhc.pre_ex(Xs, phi1, b1, mhc.PRE_ONE_PASS, alpha=alpha, eps=w.eps, t_max=w.t_max, workspace=ws1)
+    ws2 = torch.zeros_like(ws1)
+    Xf, hf, Hf, used_f = mhc.post_pre_ex(X, Y, H0, phi1, b1, algo, alpha=alpha, eps=w.eps, t_max=w.t_max,
+                                         workspace=ws2)
+    torch.cuda.synchronize()
+    assert used_s == mhc.PRE_ONE_PASS and used_f == mhc.PRE_ONE_PASS
+    assert not _recomputed(ws1)
+    out = dict(X=to_host(X), Y=to_host(Y), H0=to_host(H0), Xs=to_host(Xs), hs=to_host(hs), Hs=to_host(Hs),
+               Xf=to_host(Xf), hf=to_host(hf), Hf=to_host(Hf), fell_back=_recomputed(ws2))
+    return out
+
+
+ONE_PASS_CASES = [
+    ("layer_bf16_T16384_d4096", {"T": 1024}),      # four tiles per team
+    ("layer_bf16_T16384_d4096", {"T": 2048}),      # eight tiles per team: the exchange ring wraps
+    ("layer_bf16_T16384_d4096", {"T": 4100}),      # ragged last tile, the ring wraps three times
+    ("layer_bf16_T4096_d2048", {"T": 4096}),       # team of 8
+    ("stack60_bf16_T4096_d2560", {"T": 1600, "layers": 1, "sublayer": "given"}),   # team of 10, ragged slice
+]
+
+
+@pytest.mark.parametrize("name,changes", ONE_PASS_CASES, ids=[f"{c[0]}_T{c[1]['T']}" for c in ONE_PASS_CASES])
+def test_post_pre_one_pass_equals_separate_calls(mhc, name, changes):
+    """Bit for bit the results of mhc_post followed by the single-pass mhc_pre."""
+    w = synth.scaled(synth.WORKLOADS[name], **changes)
+    print(f"[post_pre one pass] {w.name} T={w.T} d={w.d}", flush=True)
+    r = _one_pass_pair(mhc, w, mhc.PRE_ONE_PASS, alpha=(1.0, 1.0, 1.0))
+    assert not r["fell_back"], "an exchange wait ran out"
+    assert np.array_equal(r["Xs"], r["Xf"]), "X_{l+1}"
+    assert np.array_equal(r["hs"], r["hf"]), "h_{l+1}"
+    assert np.array_equal(r["Hs"], r["Hf"]), "H_{l+1}"
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_post_pre_one_pass_fewer_streams(mhc, n):
+    w = synth.Workload(f"post_pre_one_pass_n{n}", T=1024, n=n, d=4096, dtype=synth.BF16, seed=990 + n,
+                       alpha=(1.0, 0.5, -0.5))
+    r = _one_pass_pair(mhc, w, mhc.PRE_ONE_PASS)
+    assert not r["fell_back"]
+    assert np.array_equal(r["Xs"], r["Xf"]) and np.array_equal(r["hs"], r["hf"]) and np.array_equal(r["Hs"], r["Hf"])
+
+
+def test_post_pre_one_pass_fallback_is_bitwise(mhc):
+    """The recomputing kernel (every workgroup starting broken) gives the
+    single pass's bits."""
+    w = synth.scaled(synth.WORKLOADS["layer_bf16_T16384_d4096"], T=2100)
+    a = _one_pass_pair(mhc, w, mhc.PRE_ONE_PASS)
+    b = _one_pass_pair(mhc, w, mhc.PRE_ONE_PASS_FALLBACK_TEST)
+    assert not a["fell_back"] and b["fell_back"]
+    for k in ("Xf", "hf", "Hf"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def _oracle_every_token(o, w, r, alpha):
+    """X_{l+1} against the oracle's post of (X, Y, H0), and layer l+1's h and
+    H against the oracle's pre of the stored X_{l+1}, on every token."""
+    phi1, b1 = synth.make_params(synth.scaled(w, layers=2), layer=1)
+
+    def cmp(tok):
+        xo = o.post(r["X"], r["Y"], r["H0"][tok], tokens=tok)
+        assert_close(r["Xf"][tok], xo, *TOL[("bf16", "state")], what=f"X_(l+1), tokens {tok[0]}..")
+        ref = o.pre(r["Xf"], phi1, b1, alpha, eps=w.eps, t_max=w.t_max, tokens=tok)
+        assert_close(r["Hf"][tok], ref["H"], *TOL[("bf16", "maps")], what=f"H_(l+1), tokens {tok[0]}..")
+        assert_close(r["hf"][tok], ref["h"], *TOL[("bf16", "state")], what=f"h_(l+1), tokens {tok[0]}..")
+
+    for_token_chunks(cmp, w.T)
+
+
+@pytest.mark.parametrize("T", [4096, 16384])
+def test_post_pre_one_pass_every_token(mhc, oracle_lib, T):
+    """The single pass with the post in front against the oracle on every
+    token, at the headline shape (T = 16384: 64 tiles per team) and at a
+    quarter of it."""
+    w = synth.scaled(synth.WORKLOADS["layer_bf16_T16384_d4096"], T=T)
+    print(f"[post_pre one pass] oracle every token T={T}", flush=True)
+    r = _one_pass_pair(mhc, w, mhc.PRE_ONE_PASS)
+    assert not r["fell_back"]
+    _oracle_every_token(oracle_lib, w, r, w.alpha)
+
+
+def test_post_pre_auto_and_alias(mhc):
+    """AUTO takes the two-pass form (measured faster), in place or not; the
+    single pass refuses X_out == X."""
+    w = synth.WORKLOADS["layer_bf16_T16384_d4096"]
+    X, Y, phi0, b0, phi1, b1 = (to_device(a) for a in _inputs(w))
+    _, H0 = mhc.pre(X, phi0, b0, alpha=w.alpha, eps=w.eps, t_max=w.t_max)
+    _, _, _, used = mhc.post_pre_ex(X, Y, H0, phi1, b1, mhc.PRE_AUTO, alpha=w.alpha)
+    assert used == mhc.PRE_TWO_PASS
+    Xc = X.clone()
+    _, _, _, used = mhc.post_pre_ex(Xc, Y, H0, phi1, b1, mhc.PRE_AUTO, alpha=w.alpha, out=Xc)
+    assert used == mhc.PRE_TWO_PASS
+    with pytest.raises(mhc.MhcError) as ei:
+        mhc.post_pre_ex(X, Y, H0, phi1, b1, mhc.PRE_ONE_PASS, alpha=w.alpha, out=X)
+    assert ei.value.status == 6
+    torch.cuda.synchronize()
