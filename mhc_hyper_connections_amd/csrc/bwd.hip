@@ -328,14 +328,36 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
   const bool is_res = e < NN;
   const bool is_gate = e < 2 * N;
 
+  // The slices' partials, summed in slice order; loaded SB slices at a time
+  // (all loads of a batch out before any sum), not one latency per slice.
+  constexpr int SB = 8;
   double ss = 0.0, zr = 0.0, zg = 0.0, dp = 0.0;
   if (tv) {
-    for (int s = 0; s < S; ++s) {
-      const float* P = part + (static_cast<int64_t>(s) * T + t) * PW;
-      ss += *reinterpret_cast<const double*>(P + SSO);
-      if (is_res) zr += P[colr];
-      if (is_gate) zg += P[colg];
-      if (e < N) dp += P[M + e];
+    for (int s0 = 0; s0 < S; s0 += SB) {
+      double vss[SB];
+      float vr[SB], vg[SB], vd[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int s = s0 + u;
+        vss[u] = 0.0;
+        vr[u] = vg[u] = vd[u] = 0.0f;
+        if (s < S) {
+          const float* P = part + (static_cast<int64_t>(s) * T + t) * PW;
+          vss[u] = *reinterpret_cast<const double*>(P + SSO);
+          if (is_res) vr[u] = P[colr];
+          if (is_gate) vg[u] = P[colg];
+          if (e < N) vd[u] = P[M + e];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        if (s0 + u < S) {
+          ss += vss[u];
+          if (is_res) zr += vr[u];
+          if (is_gate) zg += vg[u];
+          if (e < N) dp += vd[u];
+        }
+      }
     }
   }
   const double inv_r = inv_rms(ss, N * d, eps);
@@ -678,17 +700,16 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
     for (int jb = 0; jb < NJB; ++jb) b.gt[jb] = *reinterpret_cast<const f32x4*>(gblk + (16 * jb + r16) * 32);
   };
 
-  // dX of the tile in flight: one buffer, loaded one tile ahead (two
-  // buffers of everything would not fit the registers).
-  Raw8<BF16> dxo[N];
-  auto load_dx = [&](int64_t q) {
+  // dX of a tile (read, added to, written back): two buffers, each loaded
+  // with its tile, two tiles ahead of its use.
+  auto load_dx = [&](int64_t q, Raw8<BF16> (&dxo)[N]) {
     const int64_t t = t_begin + q * 16 + r16;
     const int64_t tt = t < t_end ? t : 0;
 #pragma unroll
     for (int i = 0; i < N; ++i) dxo[i] = load_raw8<BF16>(dX + (tt * N + i) * d + jl);
   };
 
-  auto step = [&](int64_t q, ApplyTile<N>& b) {
+  auto step = [&](int64_t q, ApplyTile<N>& b, const Raw8<BF16> (&dxo)[N]) {
     const int64_t t = t_begin + q * 16 + r16;
     const bool ok = t < t_end && jv;
     {
@@ -735,7 +756,6 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
       }
       if (ok) store8<BF16>(dX + (t * N + i) * d + j0, r);     // the one branch around memory: a store
     }
-    load_dx(q + 1);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -767,18 +787,22 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
   // token 0 and store nothing): no load behind a branch, so the compiler's
   // waits drain only the buffer about to be used.
   ApplyTile<N> ta, tb;
+  Raw8<BF16> da[N], db[N];
   load(0, ta);
-  load_dx(0);
+  load_dx(0, da);
   load(1, tb);
+  load_dx(1, db);
   __builtin_amdgcn_sched_barrier(0);
   for (int64_t q = 0; q < ntile; q += 2) {
-    step(q, ta);
+    step(q, ta, da);
     dphi_tile(ta);
     load(q + 2, ta);
+    load_dx(q + 2, da);
     __builtin_amdgcn_sched_barrier(0);
-    step(q + 1, tb);
+    step(q + 1, tb, db);
     dphi_tile(tb);
     load(q + 3, tb);
+    load_dx(q + 3, db);
     __builtin_amdgcn_sched_barrier(0);
   }
 
