@@ -253,11 +253,11 @@ mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const flo
  *                     fallback kernel recomputes from X): MHC_ERR_ALIAS
  *                     when X_out == X, MHC_ERR_UNSUPPORTED when the shape
  *                     does not apply.
- *   MHC_PRE_AUTO      the two-pass form, which measured faster on MI355X
- *                     (T = 16384, n = 4, d = 4096: 325-336 us against
- *                     343-396 us): with the post in front, the single
- *                     pass's streaming waves have registers for only one
- *                     tile in flight.
+ *   MHC_PRE_AUTO      the two-pass form, which measured as fast or faster
+ *                     on MI355X (T = 16384, n = 4, d = 4096: 325-328 us
+ *                     against 317-335 us): with the post in front, the
+ *                     single pass's streaming waves have registers for only
+ *                     one tile in flight.
  *   MHC_PRE_ONE_PASS_FALLBACK_TEST   as for mhc_pre_ex.
  * n = 1 and n = 8 run mhc_post, then mhc_pre's two-pass form. */
 mhc_status mhc_post_pre(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out,

@@ -715,10 +715,11 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
   if (p.T == 0) return hipSuccess;
   // The single pass recomputes from X_l when its waits run out, so it needs
   // X_{l+1} in a buffer of its own.  MHC_PRE_AUTO takes the two-pass form:
-  // on MI355X at T = 16384, n = 4, d = 4096 it ran in 325-336 us against
-  // 343-396 us for the single pass, whose streaming waves can then keep only
-  // one tile in flight (the hold of the tiles awaiting H_pre, the chunk of Y
-  // and the mix fill the registers of three waves per SIMD).
+  // on MI355X at T = 16384, n = 4, d = 4096 it ran in 325-328 us against
+  // 317-335 us for the single pass (slower on two boxes of three), whose
+  // streaming waves can then keep only one tile in flight (the hold of the
+  // tiles awaiting H_pre, the chunk of Y and the mix fill the registers of
+  // three waves per SIMD).
   const bool separate = Xout != X;
   if (algo == MHC_PRE_ONE_PASS || algo == MHC_PRE_ONE_PASS_FALLBACK_TEST) {
     if (!separate) return hipErrorNotSupported;
