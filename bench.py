@@ -91,35 +91,45 @@ def time_backward(mhc, torch, w, X, Y, phi, bias, H, steps, warmup, stream):
     ws = torch.empty(mhc.pre_bwd_workspace_size(T, n, d, w.dtype), dtype=torch.uint8, device="cuda")
     ws_post = torch.empty(max(16, mhc.post_bwd_workspace_size(T, n, d, w.dtype)), dtype=torch.uint8, device="cuda")
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def post_split():
         mhc.post_bwd(X, Y, H, G, dX=dX, dY=dY, dH=dH, workspace=ws_post, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def pre_split():
         mhc.pre_bwd(X, phi, bias, D, dH, dX, alpha=w.alpha, eps=w.eps, t_max=w.t_max, dphi=dphi, dbias=dbias,
                     dalpha=dalpha, workspace=ws, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for k in range(steps):
-        step(evs[k])
-    torch.cuda.synchronize()
+    # The whole-dX pair: mhc_post_bwd skips dX, mhc_pre_bwd_ex writes all of it from G.
+    def post_whole():
+        mhc.post_bwd(X, Y, H, G, dY=dY, dH=dH, workspace=ws_post, stream=stream, skip_dX=True)
+
+    def pre_whole():
+        mhc.pre_bwd(X, phi, bias, D, dH, dX, alpha=w.alpha, eps=w.eps, t_max=w.t_max, dphi=dphi, dbias=dbias,
+                    dalpha=dalpha, workspace=ws, stream=stream, G=G)
+
+    def timed(calls, reps):
+        """Average time of one round of `calls`, `reps` rounds back to back, events at the ends."""
+        for _ in range(warmup):
+            for c in calls:
+                c()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(reps):
+            for c in calls:
+                c()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps * 1e3
+
     sb = 2 if w.dtype == synth.BF16 else 4
     algo = backward_bytes(T, n, d, sb)
-    out = {"workload": wb.name, "steps": steps}
-    for name, (a, b) in (("mhc_post_bwd", (0, 1)), ("mhc_pre_bwd", (1, 2))):
-        per = [e[a].elapsed_time(e[b]) for e in evs]
-        avg_ms = float(np.mean(per))
-        out[name] = {"avg_us": avg_ms * 1e3, "median_us": float(np.median(per)) * 1e3,
-                     "min_us": float(np.min(per)) * 1e3, "max_us": float(np.max(per)) * 1e3,
-                     "design_bytes": algo[name], "GBps_design_bytes": algo[name] / (avg_ms * 1e-3) / 1e9}
-    tot_us = out["mhc_post_bwd"]["avg_us"] + out["mhc_pre_bwd"]["avg_us"]
     least = backward_min_bytes(T, n, d, sb)
+    out = {"workload": wb.name, "steps": steps,
+           "timing": "each figure: `steps` rounds back to back, HIP events at the ends; total_us: the pair together"}
+    for name, fn in (("mhc_post_bwd", post_split), ("mhc_pre_bwd", pre_split)):
+        us = timed([fn], steps)
+        out[name] = {"avg_us": us, "design_bytes": algo[name], "GBps_design_bytes": algo[name] / (us * 1e-6) / 1e9}
+    tot_us = timed([post_split, pre_split], steps)
     out["total_us"] = tot_us
     out["min_bytes"] = least
     out["GBps"] = least / (tot_us * 1e-6) / 1e9
@@ -127,6 +137,14 @@ def time_backward(mhc, torch, w, X, Y, phi, bias, H, steps, warmup, stream):
     out["bytes_note"] = ("GBps and frac_of_peak use the least bytes the backward must move, (4n + 3) d values "
                          "per token (X, G, Y, D read once, dX and dY written once, one more pass over X); "
                          "GBps_design_bytes per entry point counts what each call moves by design")
+    whole = {"mhc_post_bwd_without_dX_us": timed([post_whole], steps),
+             "mhc_pre_bwd_ex_us": timed([pre_whole], steps)}
+    whole["total_us"] = timed([post_whole, pre_whole], steps)
+    whole["GBps"] = least / (whole["total_us"] * 1e-6) / 1e9
+    whole["frac_of_peak"] = whole["GBps"] / HBM_PEAK_GBPS
+    whole["note"] = ("mhc_post_bwd with dX NULL, then mhc_pre_bwd_ex with G: dX written once (X, G, Y read and dY "
+                     "written by the first; X, D read twice, G read, dX written by the second)")
+    out["whole_dX"] = whole
     # The scratch-free form of mhc_post_bwd (no workspace), for reference.
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     mhc.post_bwd(X, Y, H, G, dX=dX, dY=dY, dH=dH, tiled=False, stream=stream)
@@ -917,13 +935,14 @@ def main():
         log("timing the backward (mhc_post_bwd + mhc_pre_bwd)")
         backward = time_backward(mhc, torch, w, X, Y, phi, bias, H, max(5, K // 2), 3, stream)
         if backward is not None:
-            bwd_us = backward["mhc_post_bwd"]["avg_us"] + backward["mhc_pre_bwd"]["avg_us"]
+            bwd_us = min(backward["total_us"], backward["whole_dX"]["total_us"])
             backward["fwd_bwd_tokens_per_s"] = T / ((ms_step * 1e3 + bwd_us) * 1e-6)
             log(f"backward: post_bwd {backward['mhc_post_bwd']['avg_us']:.1f} us, pre_bwd "
-                f"{backward['mhc_pre_bwd']['avg_us']:.1f} us; {backward['GBps']:.0f} GB/s on the least bytes "
-                f"({100 * backward['frac_of_peak']:.0f}% of peak); per-step min/median/max post_bwd "
-                + "/".join(f"{backward['mhc_post_bwd'][k]:.0f}" for k in ("min_us", "median_us", "max_us"))
-                + ", pre_bwd " + "/".join(f"{backward['mhc_pre_bwd'][k]:.0f}" for k in ("min_us", "median_us", "max_us"))
+                f"{backward['mhc_pre_bwd']['avg_us']:.1f} us, together {backward['total_us']:.1f} us: "
+                f"{backward['GBps']:.0f} GB/s on the least bytes ({100 * backward['frac_of_peak']:.0f}% of peak); "
+                f"whole-dX pair {backward['whole_dX']['total_us']:.1f} us (post_bwd without dX "
+                f"{backward['whole_dX']['mhc_post_bwd_without_dX_us']:.1f} us, pre_bwd_ex "
+                f"{backward['whole_dX']['mhc_pre_bwd_ex_us']:.1f} us, {100 * backward['whole_dX']['frac_of_peak']:.0f}% of peak)"
                 + f"; post_bwd without workspace {backward['mhc_post_bwd_scratch_free_us']:.1f} us")
 
     stack = None

@@ -17,7 +17,7 @@ MHC_FP32, MHC_BF16 = 0, 1
 STATUS = {0: "MHC_OK", 1: "MHC_ERR_NULL", 2: "MHC_ERR_SHAPE", 3: "MHC_ERR_DTYPE", 4: "MHC_ERR_ALIGN",
           5: "MHC_ERR_UNSUPPORTED", 6: "MHC_ERR_ALIAS", 7: "MHC_ERR_WORKSPACE", 8: "MHC_ERR_HIP", 9: "MHC_ERR_SCRATCH"}
 EXPORTS = ["mhc_pre", "mhc_pre_ex", "mhc_pre_workspace_size", "mhc_post", "mhc_amax", "mhc_gelu_half",
-           "mhc_post_pre", "mhc_post_pre_ex", "mhc_post_bwd", "mhc_post_bwd_ex", "mhc_post_bwd_workspace_size", "mhc_pre_bwd",
+           "mhc_post_pre", "mhc_post_pre_ex", "mhc_post_bwd", "mhc_post_bwd_ex", "mhc_post_bwd_workspace_size", "mhc_pre_bwd", "mhc_pre_bwd_ex",
            "mhc_pre_bwd_workspace_size", "mhc_workspace_size", "mhc_pre_noalloc", "mhc_status_string",
            "mhc_abi_version"]
 PRE_NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -82,6 +82,9 @@ def load_library(path: str = LIB_PATH):
     lib.mhc_pre_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mhc_pre_bwd.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.mhc_pre_bwd.restype = ctypes.c_int
+    lib.mhc_pre_bwd_ex.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                   _P]
+    lib.mhc_pre_bwd_ex.restype = ctypes.c_int
     lib.mhc_pre_noalloc.argtypes = [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P]
     lib.mhc_pre_noalloc.restype = ctypes.c_int
     lib.mhc_workspace_size.argtypes = [ctypes.POINTER(Params), ctypes.c_int32]
@@ -274,19 +277,26 @@ def post_bwd_workspace_size(T, n, d, dtype=MHC_BF16) -> int:
     return int(load_library().mhc_post_bwd_workspace_size(ctypes.byref(make_params(T, n, d, dtype))))
 
 
-def post_bwd(X, Y, H, G, dX=None, dY=None, dH=None, workspace=None, tiled=True, stream=None):
+def post_bwd(X, Y, H, G, dX=None, dY=None, dH=None, workspace=None, tiled=True, stream=None, skip_dX=False):
     """mhc_post_bwd_ex: returns (dX [T, n, d], dY [T, d], dH [T, m]); dH's first
     n columns (the read map's) are left as they were.  With ``tiled`` (and d a
     multiple of 512) the call runs the tiled form, on ``workspace`` or on a
-    buffer allocated here; ``tiled=False`` runs mhc_post_bwd, which needs none."""
+    buffer allocated here; ``tiled=False`` runs mhc_post_bwd, which needs none.
+    ``skip_dX``: dX is not written (passed as NULL; returned as None), for
+    pre_bwd(..., G=G), which then forms the whole dX."""
     torch = _torch()
     T, n, d = X.shape
     m = n * n + 2 * n
     p = make_params(T, n, d, _dtype_code(X))
-    dX = torch.empty_like(X) if dX is None else dX
+    if skip_dX:
+        dX = None
+    elif dX is None:
+        dX = torch.empty_like(X)
     dY = torch.empty_like(Y) if dY is None else dY
     dH = torch.zeros((T, m), dtype=torch.float32, device=X.device) if dH is None else dH
-    _need_device(X, Y, H, G, dX, dY, dH)
+    _need_device(X, Y, H, G, dY, dH)
+    if dX is not None:
+        _need_device(dX)
     lib = load_library()
     if not tiled:
         _check("mhc_post_bwd", lib.mhc_post_bwd(ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(H), _ptr(G), _ptr(dX),
@@ -311,9 +321,11 @@ def pre_bwd_workspace_size(T, n, d, dtype=MHC_BF16) -> int:
 
 
 def pre_bwd(X, phi, bias, D, dH, dX, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=20, dphi=None, dbias=None,
-            dalpha=None, workspace=None, stream=None):
+            dalpha=None, workspace=None, stream=None, G=None):
     """mhc_pre_bwd: adds the read map's and the maps' share to dX (in place)
-    and returns (dphi [n*d, m], dbias [m], dalpha [3]), all fp32."""
+    and returns (dphi [n*d, m], dbias [m], dalpha [3]), all fp32.  With G
+    (dL/dX_out) it calls mhc_pre_bwd_ex, which writes the whole dX (after
+    post_bwd(..., skip_dX=True))."""
     torch = _torch()
     T, n, d = X.shape
     m = n * n + 2 * n
@@ -328,9 +340,15 @@ def pre_bwd(X, phi, bias, D, dH, dX, alpha=(0.01, 0.01, 0.01), eps=1e-6, t_max=2
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _need_device(X, phi, bias, D, dH, dX, dphi, dbias, dalpha, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("mhc_pre_bwd", lib.mhc_pre_bwd(ctypes.byref(p), _ptr(X), _ptr(phi), _ptr(bias), _ptr(D), _ptr(dH),
-                                          _ptr(dX), _ptr(dphi), _ptr(dbias), _ptr(dalpha), _ptr(workspace), ws_bytes,
-                                          _stream(stream, dev)))
+    if G is None:
+        _check("mhc_pre_bwd", lib.mhc_pre_bwd(ctypes.byref(p), _ptr(X), _ptr(phi), _ptr(bias), _ptr(D), _ptr(dH),
+                                              _ptr(dX), _ptr(dphi), _ptr(dbias), _ptr(dalpha), _ptr(workspace),
+                                              ws_bytes, _stream(stream, dev)))
+    else:
+        _need_device(G)
+        _check("mhc_pre_bwd_ex", lib.mhc_pre_bwd_ex(ctypes.byref(p), _ptr(X), _ptr(phi), _ptr(bias), _ptr(D),
+                                                    _ptr(dH), _ptr(G), _ptr(dX), _ptr(dphi), _ptr(dbias),
+                                                    _ptr(dalpha), _ptr(workspace), ws_bytes, _stream(stream, dev)))
     return dphi, dbias, dalpha
 
 

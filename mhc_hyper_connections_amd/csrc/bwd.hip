@@ -25,7 +25,9 @@
 //      maps' backward; writes g = dz / r, H_pre and (z . dz) / (K r^2) for C,
 //      and the token's dlogits and alpha terms for D;
 //   C. streams X, D and dX once more: dX += H_pre D + phi g - coef x, and
-//      accumulates this chunk of tokens' share of dphi = sum_t x_t g_t^T;
+//      accumulates this chunk of tokens' share of dphi = sum_t x_t g_t^T; in
+//      the whole-dX form (G given, mhc_post_bwd having skipped dX) it reads G
+//      instead of dX and writes dX = sum_j H_res[j][i] G_j + the same terms;
 //   D. fixed-order reductions of the dphi chunks and of dbias, dalpha over T.
 #include <type_traits>
 
@@ -35,9 +37,11 @@
 namespace mhc {
 namespace {
 
-// Per-token record written by B for C: g (m) | H_pre (n) | coef | zeros, 32
-// floats (one MFMA K-block of g for n <= 4).
-__host__ __device__ constexpr int tok_width(int) { return 32; }
+// Per-token record written by B for C, 48 floats: g (m) | H_pre (n) | coef |
+// zeros up to 32 (one MFMA K-block of g for n <= 4), then H_res by columns,
+// H_res[row][col] at 32 + 4 col + row (zeros past n), for C's whole-dX form.
+__host__ __device__ constexpr int tok_width(int) { return 48; }
+constexpr int kResCol = 32;               // record offset of H_res's columns
 // Per-token values written by B for D, column-major [pg_width][Tpad]:
 // dlogits (m columns), then the alpha terms pre, res, post.
 __host__ __device__ constexpr int pg_width(int n) { return num_maps(n) + 3; }
@@ -50,7 +54,7 @@ constexpr int APPLY_CH = 64;              // token records staged per batch in k
 // One wave per token: lanes walk the token's chunks of 8 values, write dX and
 // dY, and accumulate the n*n + n dot products, reduced across the wave at the
 // end.  H is read with wave-uniform (scalar) loads.
-template <typename ST, int N>
+template <typename ST, int N, bool WRITE_DX>
 __global__ __launch_bounds__(256) void post_bwd_kernel(int64_t T, int d, const typename ST::elem* __restrict__ X,
                                                        const typename ST::elem* __restrict__ Y,
                                                        const float* __restrict__ H,
@@ -107,17 +111,19 @@ __global__ __launch_bounds__(256) void post_bwd_kernel(int64_t T, int d, const t
       for (int e = 0; e < 8; ++e) a = fmaf(g[i][e], y[e], a);
       acc[NN + i] = a;
     }
+    if constexpr (WRITE_DX) {
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      float o[8];
+      for (int j = 0; j < N; ++j) {
+        float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float s = res[0][j] * g[0][e];
+        for (int e = 0; e < 8; ++e) {
+          float s = res[0][j] * g[0][e];
 #pragma unroll
-        for (int i = 1; i < N; ++i) s = fmaf(res[i][j], g[i][e], s);
-        o[e] = s;
+          for (int i = 1; i < N; ++i) s = fmaf(res[i][j], g[i][e], s);
+          o[e] = s;
+        }
+        store8<ST, true>(dX + xrow + static_cast<int64_t>(j) * d + off, o);
       }
-      store8<ST, true>(dX + xrow + static_cast<int64_t>(j) * d + off, o);
     }
     float o[8];
 #pragma unroll
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(256) void post_bwd_kernel(int64_t T, int d, const t
 // A token's n*n + n dot products are then split over its d / 512 slices: each
 // wave reduces its slice's across its lanes and writes them to the workspace,
 // part[t][slice][a], and a second kernel adds the slices in order into dH.
-template <typename ST, int N>
+template <typename ST, int N, bool WRITE_DX>
 __global__ __launch_bounds__(256) void post_bwd_tile_kernel(int64_t T, int d8, int nslice,
                                                             const typename ST::elem* __restrict__ X,
                                                             const typename ST::elem* __restrict__ Y,
@@ -209,17 +215,19 @@ __global__ __launch_bounds__(256) void post_bwd_tile_kernel(int64_t T, int d8, i
     for (int e = 1; e < 8; ++e) a = fmaf(g[i][e], y[e], a);
     acc[NN + i] = a;
   }
+  if constexpr (WRITE_DX) {
 #pragma unroll
-  for (int j = 0; j < N; ++j) {
-    float o[8];
+    for (int j = 0; j < N; ++j) {
+      float o[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float sum = res[0][j] * g[0][e];
+      for (int e = 0; e < 8; ++e) {
+        float sum = res[0][j] * g[0][e];
 #pragma unroll
-      for (int i = 1; i < N; ++i) sum = fmaf(res[i][j], g[i][e], sum);
-      o[e] = sum;
+        for (int i = 1; i < N; ++i) sum = fmaf(res[i][j], g[i][e], sum);
+        o[e] = sum;
+      }
+      store8<ST, true>(dX + xrow + static_cast<int64_t>(j) * d + off, o);
     }
-    store8<ST, true>(dX + xrow + static_cast<int64_t>(j) * d + off, o);
   }
   {
     float o[8];
@@ -283,18 +291,28 @@ hipError_t launch_post_bwd_t(const mhc_params& p, const void* X, const void* Y, 
     const int64_t rblocks = (p.T * NA + 255) / 256;
     if (blocks > 0x7FFFFFFF || rblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     float* part = static_cast<float*>(workspace);
-    hipLaunchKernelGGL((post_bwd_tile_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T,
-                       p.d / 8, nslice, static_cast<const E*>(X), static_cast<const E*>(Y), H,
-                       static_cast<const E*>(G), static_cast<E*>(dX), static_cast<E*>(dY), part);
+    if (dX != nullptr)
+      hipLaunchKernelGGL((post_bwd_tile_kernel<ST, N, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                         p.T, p.d / 8, nslice, static_cast<const E*>(X), static_cast<const E*>(Y), H,
+                         static_cast<const E*>(G), static_cast<E*>(dX), static_cast<E*>(dY), part);
+    else
+      hipLaunchKernelGGL((post_bwd_tile_kernel<ST, N, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                         p.T, p.d / 8, nslice, static_cast<const E*>(X), static_cast<const E*>(Y), H,
+                         static_cast<const E*>(G), static_cast<E*>(dX), static_cast<E*>(dY), part);
     hipLaunchKernelGGL((post_bwd_reduce_kernel<N>), dim3(static_cast<unsigned>(rblocks)), dim3(256), 0, stream, p.T,
                        nslice, part, dH);
     return hipGetLastError();
   }
   const int64_t blocks = (p.T + 3) / 4;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((post_bwd_kernel<ST, N>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T, p.d,
-                     static_cast<const E*>(X), static_cast<const E*>(Y), H, static_cast<const E*>(G),
-                     static_cast<E*>(dX), static_cast<E*>(dY), dH);
+  if (dX != nullptr)
+    hipLaunchKernelGGL((post_bwd_kernel<ST, N, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T,
+                       p.d, static_cast<const E*>(X), static_cast<const E*>(Y), H, static_cast<const E*>(G),
+                       static_cast<E*>(dX), static_cast<E*>(dY), dH);
+  else
+    hipLaunchKernelGGL((post_bwd_kernel<ST, N, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p.T,
+                       p.d, static_cast<const E*>(X), static_cast<const E*>(Y), H, static_cast<const E*>(G),
+                       static_cast<E*>(dX), static_cast<E*>(dY), dH);
   return hipGetLastError();
 }
 
@@ -492,19 +510,30 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
     pcol[(M + 1) * Tpad] = tres;
     pcol[(M + 2) * Tpad] = tpost;
   }
-  if (M + N + 1 + e < TW) rec[M + N + 1 + e] = 0.0f;
-  if (M + N + 17 + e < TW) rec[M + N + 17 + e] = 0.0f;
+  if (M + N + 1 + e < kResCol) rec[M + N + 1 + e] = 0.0f;
+  if (M + N + 17 + e < kResCol) rec[M + N + 17 + e] = 0.0f;
+  // H_res as recomputed above, by columns: lane e writes word e, entry
+  // (row e % 4, column e / 4), which lane row * n + column of the token holds.
+  {
+    const int col = e >> 2, row = e & 3;
+    const bool in = row < N && col < N;
+    const float hv = __shfl(mv, (lane & ~15) + (in ? row * N + col : 0));
+    rec[kResCol + e] = in ? hv : 0.0f;
+  }
 }
 
 // ---- launch C: dX update and chunked dphi, one position per thread ------------
 // Block (x, y): positions k = x * 256 + thread of vec(X) (k = i d + c), tokens
-// of chunk y.  Each thread keeps its row of phi and its 24 dphi sums.
+// of chunk y.  Each thread keeps its row of phi and its 24 dphi sums.  With G
+// (the whole-dX form) the thread forms mhc_post_bwd's residual part
+// sum_j H_res[j][i] G_j itself instead of reading it from dX.
 template <typename ST, int N>
 __global__ __launch_bounds__(APPLY_THREADS) void pre_bwd_apply_kernel(int64_t T, int d, int64_t tchunk,
                                                                       const typename ST::elem* __restrict__ X,
                                                                       const typename ST::elem* __restrict__ D,
                                                                       const float* __restrict__ phi,
                                                                       const float* __restrict__ tok,
+                                                                      const typename ST::elem* __restrict__ G,
                                                                       typename ST::elem* __restrict__ dX,
                                                                       float* __restrict__ dphi_part) {
   constexpr int M = num_maps(N);
@@ -534,7 +563,15 @@ __global__ __launch_bounds__(APPLY_THREADS) void pre_bwd_apply_kernel(int64_t T,
       const int64_t t = t0 + tt;
       const float x = static_cast<float>(load_elem<ST>(X, t * K + k));
       const float dd = static_cast<float>(load_elem<ST>(D, t * d + c));
-      float v = static_cast<float>(load_elem<ST>(dX, t * K + k));
+      float v;
+      if (G != nullptr) {
+        v = rec[tt][kResCol + 4 * i] * static_cast<float>(load_elem<ST>(G, t * K + c));
+#pragma unroll
+        for (int q = 1; q < N; ++q)
+          v = fmaf(rec[tt][kResCol + 4 * i + q], static_cast<float>(load_elem<ST>(G, t * K + q * d + c)), v);
+      } else {
+        v = static_cast<float>(load_elem<ST>(dX, t * K + k));
+      }
       float s = 0.0f;
 #pragma unroll
       for (int j = 0; j < M; ++j) {
@@ -614,13 +651,17 @@ struct ApplyTile {
   f32x4 gt[(num_maps(N) + 15) / 16];   // gT operand of the tile's dphi block
 };
 
-template <int N>
+// WHOLE: dX is written, not added to: mhc_post_bwd's residual part
+// sum_j H_res[j][i] G_j is formed here from G (read where dX would be) and the
+// token records' H_res columns.
+template <int N, bool WHOLE>
 __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t T, int d, int64_t tchunk,
                                                                         const uint16_t* __restrict__ X,
                                                                         const uint16_t* __restrict__ D,
                                                                         const float* __restrict__ phi,
                                                                         const float* __restrict__ tok,
                                                                         const float* __restrict__ gT,
+                                                                        const uint16_t* __restrict__ G,
                                                                         uint16_t* __restrict__ dX,
                                                                         float* __restrict__ dphi_part) {
   constexpr int M = num_maps(N);
@@ -700,13 +741,17 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
     for (int jb = 0; jb < NJB; ++jb) b.gt[jb] = *reinterpret_cast<const f32x4*>(gblk + (16 * jb + r16) * 32);
   };
 
-  // dX of a tile (read, added to, written back): two buffers, each loaded
-  // with its tile, two tiles ahead of its use.
+  // dX of a tile (read, added to, written back), or G in the whole-dX form:
+  // two buffers, each loaded with its tile, two tiles ahead of its use.
+  // The whole-dX form loads, with G, column lane/16 of the token's H_res.
+  const uint16_t* const rsrc = WHOLE ? G : dX;
+  f32x4 hc = {0.0f, 0.0f, 0.0f, 0.0f};
   auto load_dx = [&](int64_t q, Raw8<BF16> (&dxo)[N]) {
     const int64_t t = t_begin + q * 16 + r16;
     const int64_t tt = t < t_end ? t : 0;
 #pragma unroll
-    for (int i = 0; i < N; ++i) dxo[i] = load_raw8<BF16>(dX + (tt * N + i) * d + jl);
+    for (int i = 0; i < N; ++i) dxo[i] = load_raw8<BF16>(rsrc + (tt * N + i) * d + jl);
+    if constexpr (WHOLE) hc = *reinterpret_cast<const f32x4*>(tok + tt * TW + kResCol + 4 * g);
   };
 
   auto step = [&](int64_t q, ApplyTile<N>& b, const Raw8<BF16> (&dxo)[N]) {
@@ -748,7 +793,26 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
       }
       float x[8], xo[8], r[8];
       unpack8(b.x[i], x);
-      unpack8(dxo[i], xo);
+      if constexpr (WHOLE) {
+        // Column i of H_res from lane 16 i + r16 (same token), then
+        // sum_q H_res[q][i] G_q in q order.
+        float hcol[N];
+#pragma unroll
+        for (int q = 0; q < N; ++q)
+          hcol[q] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (16 * i + r16), __float_as_int(hc[q])));
+        float gq[8];
+        unpack8(dxo[0], gq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xo[e] = hcol[0] * gq[e];
+#pragma unroll
+        for (int q = 1; q < N; ++q) {
+          unpack8(dxo[q], gq);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xo[e] = fmaf(hcol[q], gq[e], xo[e]);
+        }
+      } else {
+        unpack8(dxo[i], xo);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         r[e] = xo[e] + fmaf(b.hp[i], dv[e], o[0][e] - b.coef * x[e]);
@@ -759,8 +823,10 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // No barrier before the contraction: the staged tile was written before
+  // the step's barrier and only read since.  The barrier after it lets the
+  // next step overwrite the stage.
   auto dphi_tile = [&](const ApplyTile<N>& b) {
-    __syncthreads();
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
       s16x4 bhi, blo;
@@ -787,23 +853,47 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
   // token 0 and store nothing): no load behind a branch, so the compiler's
   // waits drain only the buffer about to be used.
   ApplyTile<N> ta, tb;
-  Raw8<BF16> da[N], db[N];
-  load(0, ta);
-  load_dx(0, da);
-  load(1, tb);
-  load_dx(1, db);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int64_t q = 0; q < ntile; q += 2) {
-    step(q, ta, da);
-    dphi_tile(ta);
-    load(q + 2, ta);
-    load_dx(q + 2, da);
+  if constexpr (WHOLE) {
+    // One G buffer, loaded a tile ahead at the end of each step: two would
+    // not fit beside the residual's sums.
+    Raw8<BF16> da[N];
+    load(0, ta);
+    load_dx(0, da);
+    load(1, tb);
     __builtin_amdgcn_sched_barrier(0);
-    step(q + 1, tb, db);
-    dphi_tile(tb);
-    load(q + 3, tb);
-    load_dx(q + 3, db);
+    for (int64_t q = 0; q < ntile; q += 2) {
+      step(q, ta, da);
+      load_dx(q + 1, da);
+      __builtin_amdgcn_sched_barrier(0);
+      dphi_tile(ta);
+      load(q + 2, ta);
+      __builtin_amdgcn_sched_barrier(0);
+      step(q + 1, tb, da);
+      load_dx(q + 2, da);
+      __builtin_amdgcn_sched_barrier(0);
+      dphi_tile(tb);
+      load(q + 3, tb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    Raw8<BF16> da[N], db[N];
+    load(0, ta);
+    load_dx(0, da);
+    load(1, tb);
+    load_dx(1, db);
     __builtin_amdgcn_sched_barrier(0);
+    for (int64_t q = 0; q < ntile; q += 2) {
+      step(q, ta, da);
+      dphi_tile(ta);
+      load(q + 2, ta);
+      load_dx(q + 2, da);
+      __builtin_amdgcn_sched_barrier(0);
+      step(q + 1, tb, db);
+      dphi_tile(tb);
+      load(q + 3, tb);
+      load_dx(q + 3, db);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   float* out = dphi_part + static_cast<int64_t>(blockIdx.y) * N * static_cast<int64_t>(d) * M;
@@ -922,8 +1012,8 @@ BwdLayout bwd_layout(int64_t T, int n, int d, int dtype) {
 
 template <typename ST, int N>
 hipError_t launch_pre_bwd_t(const mhc_params& p, const void* X, const float* phi, const float* bias, const void* D,
-                            const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* workspace,
-                            const DeviceInfo& dev, hipStream_t stream) {
+                            const float* dH, const void* G, void* dX, float* dphi, float* dbias, float* dalpha,
+                            void* workspace, const DeviceInfo& dev, hipStream_t stream) {
   typedef typename ST::elem E;
   constexpr int M = num_maps(N);
   const BwdLayout L = bwd_layout(p.T, N, p.d, p.dtype);
@@ -963,15 +1053,24 @@ hipError_t launch_pre_bwd_t(const mhc_params& p, const void* X, const float* phi
   }
 
   if (std::is_same<ST, BF16>::value) {
-    hipLaunchKernelGGL((pre_bwd_apply_mfma_kernel<N>), dim3(static_cast<unsigned>(L.S), static_cast<unsigned>(L.nch)),
-                       dim3(AM_THREADS), 0, stream, p.T, p.d, L.tchunk, static_cast<const uint16_t*>(X),
-                       static_cast<const uint16_t*>(D), phi, static_cast<const float*>(tok),
-                       static_cast<const float*>(gT), static_cast<uint16_t*>(dX), dphi_part);
+    if (G != nullptr)
+      hipLaunchKernelGGL((pre_bwd_apply_mfma_kernel<N, true>), dim3(static_cast<unsigned>(L.S), static_cast<unsigned>(L.nch)),
+                         dim3(AM_THREADS), 0, stream, p.T, p.d, L.tchunk, static_cast<const uint16_t*>(X),
+                         static_cast<const uint16_t*>(D), phi, static_cast<const float*>(tok),
+                         static_cast<const float*>(gT), static_cast<const uint16_t*>(G), static_cast<uint16_t*>(dX),
+                         dphi_part);
+    else
+      hipLaunchKernelGGL((pre_bwd_apply_mfma_kernel<N, false>), dim3(static_cast<unsigned>(L.S), static_cast<unsigned>(L.nch)),
+                         dim3(AM_THREADS), 0, stream, p.T, p.d, L.tchunk, static_cast<const uint16_t*>(X),
+                         static_cast<const uint16_t*>(D), phi, static_cast<const float*>(tok),
+                         static_cast<const float*>(gT), static_cast<const uint16_t*>(nullptr),
+                         static_cast<uint16_t*>(dX), dphi_part);
   } else {
     const int64_t kblocks = kblocks_of(K);
     hipLaunchKernelGGL((pre_bwd_apply_kernel<ST, N>), dim3(static_cast<unsigned>(kblocks), static_cast<unsigned>(L.nch)),
                        dim3(APPLY_THREADS), 0, stream, p.T, p.d, L.tchunk, static_cast<const E*>(X),
-                       static_cast<const E*>(D), phi, static_cast<const float*>(tok), static_cast<E*>(dX), dphi_part);
+                       static_cast<const E*>(D), phi, static_cast<const float*>(tok), static_cast<const E*>(G),
+                       static_cast<E*>(dX), dphi_part);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -988,12 +1087,12 @@ hipError_t launch_pre_bwd_t(const mhc_params& p, const void* X, const float* phi
 
 template <typename ST>
 hipError_t launch_pre_bwd_n(const mhc_params& p, const void* X, const float* phi, const float* bias, const void* D,
-                            const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* ws,
-                            const DeviceInfo& dev, hipStream_t stream) {
+                            const float* dH, const void* G, void* dX, float* dphi, float* dbias, float* dalpha,
+                            void* ws, const DeviceInfo& dev, hipStream_t stream) {
   switch (p.n) {
-    case 1: return launch_pre_bwd_t<ST, 1>(p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, ws, dev, stream);
-    case 2: return launch_pre_bwd_t<ST, 2>(p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, ws, dev, stream);
-    case 4: return launch_pre_bwd_t<ST, 4>(p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, ws, dev, stream);
+    case 1: return launch_pre_bwd_t<ST, 1>(p, X, phi, bias, D, dH, G, dX, dphi, dbias, dalpha, ws, dev, stream);
+    case 2: return launch_pre_bwd_t<ST, 2>(p, X, phi, bias, D, dH, G, dX, dphi, dbias, dalpha, ws, dev, stream);
+    case 4: return launch_pre_bwd_t<ST, 4>(p, X, phi, bias, D, dH, G, dX, dphi, dbias, dalpha, ws, dev, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1020,11 +1119,11 @@ int pre_bwd_max_tmax() { return kBwdMaxTmax; }
 size_t pre_bwd_workspace_bytes(int64_t T, int n, int d, int dtype) { return bwd_layout(T, n, d, dtype).total; }
 
 hipError_t launch_pre_bwd(const mhc_params& p, const void* X, const float* phi, const float* bias, const void* D,
-                          const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* workspace,
-                          const DeviceInfo& dev, hipStream_t stream) {
+                          const float* dH, const void* G, void* dX, float* dphi, float* dbias, float* dalpha,
+                          void* workspace, const DeviceInfo& dev, hipStream_t stream) {
   if (p.dtype == MHC_BF16)
-    return launch_pre_bwd_n<BF16>(p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, workspace, dev, stream);
-  return launch_pre_bwd_n<F32>(p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, workspace, dev, stream);
+    return launch_pre_bwd_n<BF16>(p, X, phi, bias, D, dH, G, dX, dphi, dbias, dalpha, workspace, dev, stream);
+  return launch_pre_bwd_n<F32>(p, X, phi, bias, D, dH, G, dX, dphi, dbias, dalpha, workspace, dev, stream);
 }
 
 }  // namespace mhc

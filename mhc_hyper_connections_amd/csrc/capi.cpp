@@ -232,7 +232,7 @@ mhc_status mhc_post_bwd_ex(const mhc_params* p, const void* X, const void* Y, co
   if (st != MHC_OK) return st;
   if (p->T == 0) return MHC_OK;
   if (p->n > 4) return MHC_ERR_UNSUPPORTED;
-  if (!X || !Y || !H || !G || !dX || !dY || !dH) return MHC_ERR_NULL;
+  if (!X || !Y || !H || !G || !dY || !dH) return MHC_ERR_NULL;      // dX may be NULL: see the header
   const size_t need = mhc::post_bwd_workspace_bytes(p->T, p->n, p->d);
   if (workspace && workspace_bytes < need) return MHC_ERR_WORKSPACE;
   if (need == 0) workspace = nullptr;
@@ -245,7 +245,7 @@ mhc_status mhc_post_bwd_ex(const mhc_params* p, const void* X, const void* Y, co
   const size_t yb = static_cast<size_t>(p->T) * p->d * sb;
   const Range ins[4] = {range_of(X, xb), range_of(Y, yb), range_of(H, static_cast<size_t>(p->T) * m * 4),
                         range_of(G, xb)};
-  const Range outs[4] = {range_of(dX, xb), range_of(dY, yb), range_of(dH, static_cast<size_t>(p->T) * m * 4),
+  const Range outs[4] = {range_of(dX, dX ? xb : 0), range_of(dY, yb), range_of(dH, static_cast<size_t>(p->T) * m * 4),
                          range_of(workspace, workspace ? need : 0)};
   for (int a = 0; a < 4; ++a) {
     for (int b = 0; b < 4; ++b)
@@ -269,6 +269,12 @@ size_t mhc_pre_bwd_workspace_size(const mhc_params* p) {
 mhc_status mhc_pre_bwd(const mhc_params* p, const void* X, const float* phi, const float* bias, const void* D,
                        const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* workspace,
                        size_t workspace_bytes, void* stream) {
+  return mhc_pre_bwd_ex(p, X, phi, bias, D, dH, nullptr, dX, dphi, dbias, dalpha, workspace, workspace_bytes, stream);
+}
+
+mhc_status mhc_pre_bwd_ex(const mhc_params* p, const void* X, const float* phi, const float* bias, const void* D,
+                          const float* dH, const void* G, void* dX, float* dphi, float* dbias, float* dalpha,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   mhc_status st = check_params(p);
   if (st != MHC_OK) return st;
   if (p->n > 4 || p->t_max > mhc::pre_bwd_max_tmax() || p->maps != MHC_MAPS_MHC) return MHC_ERR_UNSUPPORTED;
@@ -277,27 +283,27 @@ mhc_status mhc_pre_bwd(const mhc_params* p, const void* X, const float* phi, con
   const size_t need = mhc::pre_bwd_workspace_bytes(p->T, p->n, p->d, p->dtype);
   if (!workspace || workspace_bytes < need) return MHC_ERR_WORKSPACE;
   if (!aligned16(X) || !aligned16(phi) || !aligned16(bias) || !aligned16(D) || !aligned16(dH) || !aligned16(dX) ||
-      !aligned16(dphi) || !aligned16(dbias) || !aligned16(dalpha) || !aligned16(workspace))
+      !aligned16(dphi) || !aligned16(dbias) || !aligned16(dalpha) || !aligned16(workspace) || !aligned16(G))
     return MHC_ERR_ALIGN;
   const bool empty = p->T == 0;
   const int m = p->n * p->n + 2 * p->n;
   const size_t sb = state_bytes(p->dtype);
   const size_t xb = static_cast<size_t>(p->T) * p->n * p->d * sb;
-  const Range ins[5] = {range_of(X, xb), range_of(phi, empty ? 0 : static_cast<size_t>(p->n) * p->d * m * 4),
+  const Range ins[6] = {range_of(X, xb), range_of(phi, empty ? 0 : static_cast<size_t>(p->n) * p->d * m * 4),
                         range_of(bias, empty ? 0 : static_cast<size_t>(m) * 4),
                         range_of(D, static_cast<size_t>(p->T) * p->d * sb),
-                        range_of(dH, static_cast<size_t>(p->T) * m * 4)};
+                        range_of(dH, static_cast<size_t>(p->T) * m * 4), range_of(G, G ? xb : 0)};
   const Range outs[5] = {range_of(dX, xb), range_of(dphi, static_cast<size_t>(p->n) * p->d * m * 4),
                          range_of(dbias, static_cast<size_t>(m) * 4), range_of(dalpha, 3 * 4),
                          range_of(workspace, need)};
   for (int a = 0; a < 5; ++a) {
-    for (int b = 0; b < 5; ++b)
+    for (int b = 0; b < 6; ++b)
       if (overlap(outs[a], ins[b])) return MHC_ERR_ALIAS;
     for (int b = a + 1; b < 5; ++b)
       if (overlap(outs[a], outs[b])) return MHC_ERR_ALIAS;
   }
   const mhc::DeviceInfo dev = device_info();
-  return from_hip(mhc::launch_pre_bwd(*p, X, phi, bias, D, dH, dX, dphi, dbias, dalpha, workspace, dev,
+  return from_hip(mhc::launch_pre_bwd(*p, X, phi, bias, D, dH, G, dX, dphi, dbias, dalpha, workspace, dev,
                                       static_cast<hipStream_t>(stream)));
 }
 

@@ -85,9 +85,11 @@ hipError_t launch_post_bwd(const mhc_params& p, const void* X, const void* Y, co
                            void* dY, float* dH, void* workspace, hipStream_t stream);
 size_t pre_bwd_workspace_bytes(int64_t T, int n, int d, int dtype);
 int pre_bwd_max_tmax();
+// G NULL: dX += (pre's terms); G given: dX = sum_j H_res[j][i] G_j + (pre's terms),
+// the residual part mhc_post_bwd then skipped (its dX NULL).
 hipError_t launch_pre_bwd(const mhc_params& p, const void* X, const float* phi, const float* bias, const void* D,
-                          const float* dH, void* dX, float* dphi, float* dbias, float* dalpha, void* workspace,
-                          const DeviceInfo& dev, hipStream_t stream);
+                          const float* dH, const void* G, void* dX, float* dphi, float* dbias, float* dalpha,
+                          void* workspace, const DeviceInfo& dev, hipStream_t stream);
 
 // mhc_amax: composite-map Amax.
 hipError_t launch_amax(int64_t T, int n, int L, const float* Hs, float* amax, float* gfwd, float* gbwd,

@@ -246,6 +246,25 @@ def test_pre_bwd_argument_checks(lib):
     assert lib.mhc_pre_bwd_workspace_size(ctypes.byref(_params(n=3))) == 0
 
 
+def test_pre_bwd_ex_argument_checks(lib):
+    """mhc_pre_bwd_ex: G must not overlap an output and must be aligned;
+    mhc_post_bwd accepts a NULL dX (the whole-dX pair)."""
+    p = _params()
+    need = lib.mhc_pre_bwd_workspace_size(ctypes.byref(p))
+    far = [0x1000000000 * (k + 1) for k in range(12)]
+
+    def f(G, dX=far[7]):
+        return lib.mhc_pre_bwd_ex(ctypes.byref(p), far[0], far[1], far[2], far[3], far[4], G, dX, far[8], far[9],
+                                  far[10], far[11], need, None)
+    assert f(far[5] + 8) == 4                          # G misaligned
+    assert f(far[7]) == 6                              # G onto dX
+    assert f(far[8]) == 6                              # G onto dphi
+    assert lib.mhc_post_bwd_ex(ctypes.byref(p), far[0], far[1], far[2], far[3], None, None, far[6], None, 0,
+                               None) == 1              # dY NULL is still refused
+    assert lib.mhc_post_bwd_ex(ctypes.byref(p), far[0], far[1], far[2], far[3], None, far[3], far[6], None, 0,
+                               None) == 6              # dY onto G, with dX NULL
+
+
 def test_post_pre_argument_checks(lib):
     p = _params()
     need = lib.mhc_pre_workspace_size(ctypes.byref(p))

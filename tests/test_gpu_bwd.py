@@ -4,7 +4,8 @@ The checked quantity is the gradient of sum_t <G_t, X'_t> + <D_t, h_t> with
 G = dX' and D = dh drawn as inputs (the sublayer stays outside the layer).
 The chain is the one a training step runs: mhc_post_bwd writes dX (residual
 part), dY and dH's res / post columns; mhc_pre_bwd adds the read map's and the
-maps' share to dX and writes dphi, dbias, dalpha.
+maps' share to dX and writes dphi, dbias, dalpha.  In the whole-dX form
+mhc_post_bwd skips dX and mhc_pre_bwd_ex writes all of it from G.
 
 Tolerances: dX and dY as the forward's state outputs (fp32: 1e-5 / 1e-6;
 bf16: 2e-2 / 1e-2).  dH and the parameter gradients are fp32 sums over d or
@@ -52,19 +53,27 @@ def _inputs(w, T=None):
     return X, Y, G, D, phi, bias
 
 
-def _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha, t_max=None):
-    """Forward maps, then the backward chain.  Returns host arrays."""
+def _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha, t_max=None, whole=False):
+    """Forward maps, then the backward chain.  Returns host arrays.  whole:
+    mhc_post_bwd skips dX, mhc_pre_bwd_ex writes all of it (into a buffer
+    filled with NaN first, so a value it failed to write shows)."""
     t_max = w.t_max if t_max is None else t_max
     dX_, dY_, dG, dD = to_device(X), to_device(Y), to_device(G), to_device(D)
     dphi_, dbias_ = to_device(phi), to_device(bias)
     _, H = mhc.pre(dX_, dphi_, dbias_, alpha=alpha, eps=w.eps, t_max=t_max)
     m = w.m
     dH = torch.full((X.shape[0], m), 7.0, dtype=torch.float32, device="cuda")
-    gX, gY, dH = mhc.post_bwd(dX_, dY_, H, dG, dH=dH)
+    gX, gY, dH = mhc.post_bwd(dX_, dY_, H, dG, dH=dH, skip_dX=whole)
     torch.cuda.synchronize()
-    dX_post = to_host(gX).copy()
+    if whole:
+        assert gX is None
+        gX = torch.full_like(dX_, float("nan"))
+        dX_post = None
+    else:
+        dX_post = to_host(gX).copy()
     dH_host = to_host(dH).copy()
-    gphi, gbias, galpha = mhc.pre_bwd(dX_, dphi_, dbias_, dD, dH, gX, alpha=alpha, eps=w.eps, t_max=t_max)
+    gphi, gbias, galpha = mhc.pre_bwd(dX_, dphi_, dbias_, dD, dH, gX, alpha=alpha, eps=w.eps, t_max=t_max,
+                                      G=dG if whole else None)
     torch.cuda.synchronize()
     return {"dX": to_host(gX), "dY": to_host(gY), "dH": dH_host, "dX_post": dX_post,
             "dphi": to_host(gphi), "dbias": to_host(gbias), "dalpha": to_host(galpha)}
@@ -100,13 +109,29 @@ CASES = [
 
 @pytest.mark.parametrize("name,changes,alpha", CASES,
                          ids=[f"{c[0]}_T{c[1].get('T', 'all')}_{'acfg' if c[2] is None else 'a1'}" for c in CASES])
-def test_backward_every_token(mhc, oracle_lib, name, changes, alpha):
+@pytest.mark.parametrize("whole", [False, True], ids=["split_dX", "whole_dX"])
+def test_backward_every_token(mhc, oracle_lib, name, changes, alpha, whole):
     w = synth.scaled(synth.WORKLOADS[name], **changes)
     alpha = w.alpha if alpha is None else alpha
     X, Y, G, D, phi, bias = _inputs(w)
-    print(f"[bwd] {w.name} T={w.T} n={w.n} d={w.d} alpha={alpha}", flush=True)
-    got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha)
+    print(f"[bwd] {w.name} T={w.T} n={w.n} d={w.d} alpha={alpha} whole={whole}", flush=True)
+    got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha, whole=whole)
     _check(oracle_lib, w, got, X, Y, G, D, phi, bias, alpha)
+
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+def test_whole_dx_matches_split_form(mhc, n):
+    """The whole-dX form changes only dX (rounded once instead of twice): the
+    other outputs are bit for bit those of the split form, and dX agrees to
+    bf16 rounding."""
+    w = synth.Workload(f"whole_dx_n{n}", T=700, n=n, d=1024, dtype=synth.BF16, seed=960 + n, alpha=(0.8, 1.1, -0.5))
+    X, Y, G, D, phi, bias = _inputs(w)
+    a = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, w.alpha)
+    b = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, w.alpha, whole=True)
+    for k in ("dY", "dH", "dphi", "dbias", "dalpha"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.all(np.isfinite(values(b["dX"])))
+    assert_close(b["dX"], values(a["dX"]), 2e-2, 1e-2, "whole dX against split dX")
 
 
 @pytest.mark.parametrize("n", [1, 2])
@@ -115,8 +140,9 @@ def test_backward_fewer_streams(mhc, oracle_lib, n):
         w = synth.Workload(f"bwd_n{n}_{dname(dtype)}", T=97, n=n, d=264, dtype=dtype, seed=900 + n)
         alpha = (0.9, 1.2, -0.7)
         X, Y, G, D, phi, bias = _inputs(w)
-        got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha)
-        _check(oracle_lib, w, got, X, Y, G, D, phi, bias, alpha)
+        for whole in (False, True):
+            got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha, whole=whole)
+            _check(oracle_lib, w, got, X, Y, G, D, phi, bias, alpha)
 
 
 @pytest.mark.parametrize("t_max", [0, 1, 3])
@@ -203,7 +229,8 @@ def test_backward_empty_and_deterministic(mhc):
 
 
 @pytest.mark.slow
-def test_backward_full_size(mhc, oracle_lib):
+@pytest.mark.parametrize("whole", [False, True], ids=["split_dX", "whole_dX"])
+def test_backward_full_size(mhc, oracle_lib, whole):
     """T = 16384, n = 4, d = 4096 bf16 in the launch configuration the
     benchmark times, checked on EVERY token: the oracle runs over 256-token
     chunks on host threads (each chunk's per-token gradients are compared as
@@ -211,8 +238,8 @@ def test_backward_full_size(mhc, oracle_lib):
     chunk order."""
     w = synth.WORKLOADS["layer_fwdbwd_bf16_T16384_d4096"]
     X, Y, G, D, phi, bias = _inputs(w)
-    print(f"[bwd] full size {w.name}", flush=True)
-    got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, w.alpha)
+    print(f"[bwd] full size {w.name} whole={whole}", flush=True)
+    got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, w.alpha, whole=whole)
     n, T, chunk = w.n, w.T, 256
     assert np.all(got["dH"][:, :n] == 7.0), "mhc_post_bwd wrote the read map's columns of dH"
     dn = dname(w.dtype)
