@@ -280,7 +280,8 @@ def time_stack(mhc, torch, reps=5, warmup=2):
 
 def time_post_pre(mhc, torch, w, X, Y, H, phi, bias, reps, stream):
     """Layer l's mhc_post fused with layer l+1's mhc_pre at the workload's
-    shape, both forms, per call (HIP events at the ends of `reps` calls).
+    shape, both forms, per call (HIP events at the ends of `reps` calls, the
+    median of three rounds).
     GB/s on the least bytes such a fused layer moves: X_l and Y read, X_{l+1}
     and h written, the maps read and written (80 KiB per token at n = 4,
     d = 4096, bf16)."""
@@ -292,25 +293,34 @@ def time_post_pre(mhc, torch, w, X, Y, H, phi, bias, reps, stream):
     ws = torch.zeros(mhc.pre_workspace_size(T, n, d, mhc.MHC_BF16 if sb == 2 else mhc.MHC_FP32), dtype=torch.uint8,
                      device=X.device)
     out = {"least_bytes_per_token": least // T, "forms": {}}
-    for name, algo in (("one-pass", mhc.PRE_ONE_PASS), ("two-pass", mhc.PRE_TWO_PASS)):
-        def call():
+    forms = [("one-pass", mhc.PRE_ONE_PASS), ("two-pass", mhc.PRE_TWO_PASS)]
+    calls = {}
+    for name, algo in forms:
+        def call(algo=algo):
             return mhc.post_pre_ex(X, Y, H, phi, bias, algo, alpha=w.alpha, eps=w.eps, t_max=w.t_max, out=Xo, h=h2,
                                    H_next=H2, workspace=ws, stream=stream)[3]
         try:
             for _ in range(3):
                 call()
+            calls[name] = call
         except mhc.MhcError:
             out["forms"][name] = None
-            continue
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        for _ in range(reps):
-            call()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        us = ev[0].elapsed_time(ev[1]) / reps * 1e3
-        out["forms"][name] = {"avg_us": us, "GBps_on_least_bytes": least / (us * 1e-6) / 1e9,
+    # Three rounds, the order of the forms alternating, and each form's median
+    # round: the first calls after start-up run slower, whichever form they are.
+    runs = {name: [] for name in calls}
+    for rnd in range(3):
+        for name in (list(calls) if rnd % 2 == 0 else list(calls)[::-1]):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            for _ in range(reps):
+                calls[name]()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            runs[name].append(ev[0].elapsed_time(ev[1]) / reps * 1e3)
+    for name, v in runs.items():
+        us = sorted(v)[len(v) // 2]
+        out["forms"][name] = {"avg_us": us, "rounds_us": v, "GBps_on_least_bytes": least / (us * 1e-6) / 1e9,
                               "frac_of_peak": least / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
     out["auto_form"] = {1: "two-pass", 2: "one-pass"}.get(
         mhc.post_pre_ex(X, Y, H, phi, bias, mhc.PRE_AUTO, alpha=w.alpha, eps=w.eps, t_max=w.t_max, out=Xo, h=h2,

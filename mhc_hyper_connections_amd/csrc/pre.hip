@@ -714,13 +714,19 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
   if (used) *used = MHC_PRE_TWO_PASS;
   if (p.T == 0) return hipSuccess;
   // The single pass recomputes from X_l when its waits run out, so it needs
-  // X_{l+1} in a buffer of its own.  MHC_PRE_AUTO takes the two-pass form:
-  // on MI355X at T = 16384, n = 4, d = 4096 it ran in 325-328 us against
-  // 317-335 us for the single pass (slower on two boxes of three), whose
-  // streaming waves can then keep only one tile in flight (the hold of the
-  // tiles awaiting H_pre, the chunk of Y and the mix fill the registers of
-  // three waves per SIMD).
+  // X_{l+1} in a buffer of its own.  MHC_PRE_AUTO takes it where plain
+  // mhc_pre's AUTO does and X_{l+1} is separate (on MI355X at T = 16384,
+  // n = 4, d = 4096: 293-294 us against 326 us for the two-pass form),
+  // else the two-pass form.
   const bool separate = Xout != X;
+  if (algo == MHC_PRE_AUTO && separate && pre_fused_preferred(p, dev)) {
+    if (launch_post_pre_fused(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, ws_bytes, false, dev, stream) ==
+        hipSuccess) {
+      if (used) *used = MHC_PRE_ONE_PASS;
+      return hipSuccess;
+    }
+    (void)hipGetLastError();                 // refused: the two-pass form below
+  }
   if (algo == MHC_PRE_ONE_PASS || algo == MHC_PRE_ONE_PASS_FALLBACK_TEST) {
     if (!separate) return hipErrorNotSupported;
     const hipError_t e = launch_post_pre_fused(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, ws_bytes,

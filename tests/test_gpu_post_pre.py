@@ -202,16 +202,22 @@ def test_post_pre_one_pass_every_token(mhc, oracle_lib, T):
 
 
 def test_post_pre_auto_and_alias(mhc):
-    """AUTO takes the two-pass form (measured faster), in place or not; the
-    single pass refuses X_out == X."""
+    """AUTO takes the single pass (measured faster) when X_out is a buffer of
+    its own and the two-pass form in place, each bit for bit the form it
+    reports; the single pass refuses X_out == X."""
     w = synth.WORKLOADS["layer_bf16_T16384_d4096"]
     X, Y, phi0, b0, phi1, b1 = (to_device(a) for a in _inputs(w))
     _, H0 = mhc.pre(X, phi0, b0, alpha=w.alpha, eps=w.eps, t_max=w.t_max)
-    _, _, _, used = mhc.post_pre_ex(X, Y, H0, phi1, b1, mhc.PRE_AUTO, alpha=w.alpha)
-    assert used == mhc.PRE_TWO_PASS
+    auto = mhc.post_pre_ex(X, Y, H0, phi1, b1, mhc.PRE_AUTO, alpha=w.alpha)
+    assert auto[3] == mhc.PRE_ONE_PASS
+    one = mhc.post_pre_ex(X, Y, H0, phi1, b1, mhc.PRE_ONE_PASS, alpha=w.alpha)
+    assert all(torch.equal(a, b) for a, b in zip(auto[:3], one[:3]))
     Xc = X.clone()
-    _, _, _, used = mhc.post_pre_ex(Xc, Y, H0, phi1, b1, mhc.PRE_AUTO, alpha=w.alpha, out=Xc)
-    assert used == mhc.PRE_TWO_PASS
+    inpl = mhc.post_pre_ex(Xc, Y, H0, phi1, b1, mhc.PRE_AUTO, alpha=w.alpha, out=Xc)
+    assert inpl[3] == mhc.PRE_TWO_PASS
+    two = mhc.post_pre_ex(X, Y, H0, phi1, b1, mhc.PRE_TWO_PASS, alpha=w.alpha)
+    assert all(torch.equal(a, b) for a, b in zip(inpl[:3], two[:3]))
+    assert torch.equal(auto[0], two[0])          # X_{l+1}: the same mix in both forms
     with pytest.raises(mhc.MhcError) as ei:
         mhc.post_pre_ex(X, Y, H0, phi1, b1, mhc.PRE_ONE_PASS, alpha=w.alpha, out=X)
     assert ei.value.status == 6
