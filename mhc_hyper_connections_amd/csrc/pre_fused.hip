@@ -77,7 +77,7 @@ namespace {
 typedef unsigned long long u64;
 
 constexpr int OW = 8;                   // streaming waves
-constexpr int OX = 2;                   // exchange waves (tiles alternate between them)
+constexpr int OX = 2;                   // exchange waves (tiles alternate between them; three measured the same)
 constexpr int OT = (OW + OX + 1) * 64;  // + the exchange waves + the Sinkhorn wave
 constexpr int OTP = OT + 64;            // with the previous layer's mhc_post fused in: + the maps loader wave
 constexpr int OHR = 4;                  // LDS ring of the previous layer's mixing maps (tiles)
@@ -90,12 +90,13 @@ constexpr int OSLOTS = 5;               // exchange ring depth (tiles); see belo
 constexpr int ORR = 3;                  // LDS ring of partials (tiles)
 constexpr int OMR = 5;                  // LDS ring of H_pre (tiles; a slot is rewritten once its tile's h is out)
 constexpr int OKR = 4;                  // LDS ring of Sinkhorn inputs (tiles; taken two at a time)
-constexpr int OD = 5;                   // tiles between a tile's partials and its h; see below
+constexpr int OD = 4;                   // tiles between a tile's partials and its h; see below
 constexpr int OP = 2;                   // X tiles in flight ahead of the one being multiplied
-// With the previous layer's post fused in, a step also holds a chunk of Y
-// and the mix's maps and temporaries: one tile fewer in flight and one fewer
-// held keep the streaming waves within 168 registers (3 waves per SIMD)
-// without spilling.
+// Both forms fit the streaming waves in 168 registers (3 waves per SIMD)
+// without spilling.  The plain form's also hold three phi operands in flight
+// (see partials); with the previous layer's post fused in, a step holds a
+// chunk of Y and the mix's maps and temporaries instead, and one tile fewer
+// is in flight.
 constexpr int OD_POST = 4;
 constexpr int OP_POST = 1;
 constexpr size_t OHDR = kPreHeaderBytes;       // workspace header (error word, sequence number, current tag)
@@ -279,18 +280,18 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
   constexpr int OP = POST ? OP_POST : ::mhc::OP;
   constexpr int ONB = OD + OP;                      // X tile buffers per lane
   constexpr int M = num_maps(N);
-  constexpr int NB = (M + 15) / 16;
+  constexpr int NB = (2 * M + 15) / 16;   // column blocks: the m columns of a line's first half, then its second's
   constexpr int NN = N * N;
   constexpr int SSO = (M + 1) & ~1;     // word of the sum of squares in a token record (even)
   constexpr int W = SSO + 2;            // words per token record (even: records are 16-byte pairs)
   constexpr int NP = W / 2;             // word pairs per token record
   constexpr int NRB = (NP + 3) / 4;     // reduce-scatter loads per owned token (a pair per 16-lane row)
-  constexpr int PHE = 4 * M;            // phi operand entries per (wave, stream, half)
+  constexpr int PHE = 64 * NB;          // phi operand entries per (line, stream, bf16 part)
   constexpr int MP = (M + 3) / 4;       // 4-column groups per token in the partials ring
   constexpr int SHARE = (OR * NP + OW - 1) / OW;   // record pairs each streaming wave posts per tile
   static_assert(SHARE <= 64, "one pair per lane");
 
-  __shared__ u32x4 phi_l[OW][N][2][PHE];   // MFMA B operands, entry nb*64 + g*cn + r (cn = columns of block nb)
+  __shared__ u32x4 phi_l[4][N][2][PHE];    // MFMA B operands per line: entry 64 nb + 16 g + c
   __shared__ f32x4 red[ORR][OW][OR][MP];   // per wave and token: m partials (padded to 4s)
   __shared__ double red_ss[ORR][OW][OR];
   __shared__ double xs[OX][OTPR][W];       // an owned token's column sums over the team, per exchange wave
@@ -343,16 +344,27 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
   const int teams = a.teams;
   const int J = (a.ntiles > team) ? static_cast<int>((a.ntiles - team + teams - 1) / teams) : 0;
 
-  // Streaming lanes: lane = (token row r16, position group g) of wave w.
+  // Streaming lanes.  Wave w takes line L = w % 4 of the member's slice (64
+  // positions: 128 bytes of every stream row) for tokens 8 (w / 4) .. + 7 of
+  // a tile.  Lane 16 g + k holds token k % 8 at chunk g + 4 (k / 8) of the
+  // line (8 positions), so every load and store covers 8 whole 128-byte
+  // lines (16 rows of 64 bytes, half lines, ran 13% slower on reads alone).
+  // Read as an MFMA A operand (row = lane % 16, K group = lane / 16), rows
+  // 0..7 hold the line's first 32 positions of the 8 tokens and rows 8..15
+  // its last 32: row 8 h + k carries exactly what row 8 (w / 4) + k of the
+  // 32-position block 2 L + h did when a wave took a 16 x 32 block.
+  static_assert(OW == 8 && OSLICE == 256 && OR == 16, "4 lines x 2 token halves per member");
   const int w = wave;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int j0 = s * OSLICE + 32 * w + 8 * g;
+  const int L = w & 3;
+  const int tk = 8 * (w >> 2) + (lane & 7);   // token within the tile
+  const int j0 = s * OSLICE + 64 * L + 8 * (g + 4 * (r16 >> 3));
   const bool jv = wave < OW && j0 < d;
   const __amdgpu_buffer_rsrc_t xrx =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X), 0, a.xbytes, 0x00020000);
   auto load_tile = [&](int jt, u32x4 (&x)[N]) {
-    const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + r16;
+    const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + tk;
     const bool ok = jt < J && t < T && jv;
     const uint32_t o0 = ok ? static_cast<uint32_t>((t * N * d + j0) * 2) : kOob;
     const uint32_t st = ok ? static_cast<uint32_t>(d * 2) : 0u;
@@ -367,7 +379,7 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
   const __amdgpu_buffer_rsrc_t yrx =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(POST ? a.Y : a.X), 0, a.hbytes, 0x00020000);
   auto load_y = [&](int jt) -> u32x4 {
-    const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + r16;
+    const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + tk;
     const bool ok = jt < J && t < T && jv;
     const uint32_t o0 = ok ? static_cast<uint32_t>((t * d + j0) * 2) : kOob;
     return __builtin_amdgcn_raw_buffer_load_b128(yrx, static_cast<int>(o0), 0, 0);
@@ -382,10 +394,12 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
     if constexpr (POST) yb = load_y(0);
   }
 
-  // This member's slice of phi into LDS as bf16 hi / lo operand halves: the
+  // This member's slice of phi into LDS as bf16 hi / lo operand parts: the
   // slice's rows of each stream are contiguous in phi, read in 16-byte
-  // pieces (all issued before any is used), and each value goes to element
-  // e of operand entry (wave, stream, column) for its position 32 w + 8 g + e.
+  // pieces (all issued before any is used).  Line L's operand column
+  // q = 16 nb + c is map column q of the line's first 32 positions for
+  // q < m and map column q - m of its last 32 for q >= m (zero past 2 m);
+  // position 64 L + 32 h + 8 g + e is element e of entry 64 nb + 16 g + c.
   {
     constexpr int G = (M % 4 == 0) ? 4 : 1;            // floats per load
     constexpr int PER = OSLICE * M / G;                  // loads per stream
@@ -408,6 +422,12 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
         pv[k][0] = ok ? *src : 0.0f;
       }
     }
+    if constexpr (2 * M < 16 * NB) {
+      for (int q = tid; q < 4 * N * 2 * PHE; q += NTHR) {
+        const int ent = q % PHE;
+        if (16 * (ent >> 6) + (ent & 15) >= 2 * M) (&phi_l[0][0][0][0])[q] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
 #pragma unroll
     for (int k = 0; k < KPHI; ++k) {
       const int q = tid + k * NTHR;
@@ -415,17 +435,15 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
         const int i = q / PER;
         const int f = (q - i * PER) * G;
         const int row = f / M;
-        const int ww = row >> 5, gg = (row >> 3) & 3, e = row & 7;
+        const int ln = row >> 6, hh = (row >> 5) & 1, gg = (row >> 3) & 3, e = row & 7;
 #pragma unroll
         for (int c = 0; c < G; ++c) {
-          const int col = f - row * M + c;
-          const int nb = col >> 4;
-          const int cn = (M - 16 * nb < 16) ? M - 16 * nb : 16;
-          const int ent = 64 * nb + gg * cn + (col & 15);
+          const int col = hh * M + f - row * M + c;
+          const int ent = 64 * (col >> 4) + 16 * gg + (col & 15);
           const __bf16 hi = static_cast<__bf16>(pv[k][c]);
           const __bf16 lo = static_cast<__bf16>(pv[k][c] - static_cast<float>(hi));
-          reinterpret_cast<__bf16*>(&phi_l[ww][i][0][ent])[e] = hi;
-          reinterpret_cast<__bf16*>(&phi_l[ww][i][1][ent])[e] = lo;
+          reinterpret_cast<__bf16*>(&phi_l[ln][i][0][ent])[e] = hi;
+          reinterpret_cast<__bf16*>(&phi_l[ln][i][1][ent])[e] = lo;
         }
       }
     }
@@ -458,50 +476,73 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
     // ---------------------------------------------------------------- streaming
     const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(a.h, 0, a.hbytes, 0x00020000);
 
-    // Tile jt's partials over this wave's 32 positions into the LDS ring.
-    // Sum of squares: with A = B = the tile (16 tokens x 32 positions), the
-    // MFMA's diagonal entry (t, t) is token t's sum of squares over the
-    // wave's positions; bf16 products are exact in fp32, the accumulation
-    // over the 4 streams' 128 values is fp32, the sums across waves and
-    // members fp64.  Entry (t, t) sits in lane 16 (t / 4) + t, element t % 4.
+    // Tile jt's partials over this wave's 64 positions into the LDS ring, one
+    // row per (token, half line): row 8 h + k is token 8 (w / 4) + k over
+    // positions 32 h .. 32 h + 31 of the line.  Output column q of a block
+    // is valid in the rows of the half that operand column q belongs to
+    // (rows 0..7 for q < m, 8..15 for q >= m); the other half's entries
+    // there are discarded.
+    // Sum of squares: with A = B = the tile, the MFMA's diagonal entry
+    // (rho, rho) is row rho's sum of squares; bf16 products are exact in
+    // fp32, the accumulation over the 4 streams' 128 values is fp32, the sums
+    // across rows, waves and members fp64.  Entry (rho, rho) sits in lane
+    // 16 (rho / 4) + rho, element rho % 4.
     auto partials = [&](int jt, const u32x4 (&x)[N]) {
       f32x4 gram = {0.0f, 0.0f, 0.0f, 0.0f};
       f32x4 acc[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      // phi operands come from LDS per stream, next to its MFMAs (reading the
-      // next stream's ahead measured no faster and costs 16 registers that
-      // the hold of X tiles needs).  A block narrower than 16 columns (the
-      // last one) repeats valid entries in its unused columns: output column
-      // c depends only on B column c, and columns >= m are never written out.
-      PhiOp<BF16> bop[2][NB];
-      auto read_phi = [&](int i, PhiOp<BF16> (&b)[NB]) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int cn = (M - 16 * nb < 16) ? M - 16 * nb : 16;
-          const int ent = 64 * nb + g * cn + r16 % cn;
-          b[nb].hi = __builtin_bit_cast(bf16x8, phi_l[w][i][0][ent]);
-          b[nb].lo = __builtin_bit_cast(bf16x8, phi_l[w][i][1][ent]);
-        }
+      // phi operands come from LDS.  The plain form keeps three (stream,
+      // block) operands in flight ahead of the MFMAs, so the LDS latency is
+      // met once per tile rather than once per stream (7 us less at
+      // T = 16384, n = 4, d = 4096); the fused form has no registers for
+      // that and reads each stream's operands next to its MFMAs.
+      auto read_phi = [&](int q, PhiOp<BF16>& o) {
+        const int i = q / NB, nb = q % NB;
+        o.hi = __builtin_bit_cast(bf16x8, phi_l[L][i][0][64 * nb + lane]);
+        o.lo = __builtin_bit_cast(bf16x8, phi_l[L][i][1][64 * nb + lane]);
       };
+      if constexpr (!POST) {
+        constexpr int QN = N * NB;
+        constexpr int DP = QN < 3 ? QN : 3;
+        PhiOp<BF16> bq[DP];
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        read_phi(i, bop[i & 1]);
-        const bf16x8 xv = __builtin_bit_cast(bf16x8, x[i]);
-        gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, xv, gram, 0, 0, 0);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_block(Raw8<BF16>{x[i]}, bop[i & 1][nb], acc[nb]);
+        for (int q = 0; q < DP; ++q) read_phi(q, bq[q]);
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
+          const int i = q / NB, nb = q % NB;
+          if (nb == 0) {
+            const bf16x8 xv = __builtin_bit_cast(bf16x8, x[i]);
+            gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, xv, gram, 0, 0, 0);
+          }
+          acc[nb] = mfma_block(Raw8<BF16>{x[i]}, bq[q % DP], acc[nb]);
+          if (q + DP < QN) read_phi(q + DP, bq[q % DP]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const bf16x8 xv = __builtin_bit_cast(bf16x8, x[i]);
+          gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, xv, gram, 0, 0, 0);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            PhiOp<BF16> b;
+            read_phi(i * NB + nb, b);
+            acc[nb] = mfma_block(Raw8<BF16>{x[i]}, b, acc[nb]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       const int dv = r16 & 3;
       const float sqf = dv == 0 ? gram[0] : dv == 1 ? gram[1] : dv == 2 ? gram[2] : gram[3];
       double sq = static_cast<double>(sqf);
       const bool ovf = g == (r16 >> 2) && !__builtin_isfinite(sqf);
       if (__any(ovf)) {
-        // fp32 overflow (|x| beyond ~1e18): the token's sum again in fp64
-        // from the 4 lanes that hold its positions (lane 16 q + t holds
-        // positions 8 q .. 8 q + 7).  Wave-uniform branch: every lane
-        // takes part in the permutes.
+        // fp32 overflow (|x| beyond ~1e18): the row's sum again in fp64
+        // from the 4 lanes that hold its positions (lane 16 q + rho holds
+        // row rho's 8 positions of K group q).  Wave-uniform branch: every
+        // lane takes part in the permutes.
         double s64 = 0.0;
         for (int q = 0; q < 4; ++q) {
           const int src = 16 * q + r16;
@@ -522,8 +563,9 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
       const int slot = jt % ORR;   // free: see the static_assert on ORR
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int col = 16 * nb + r16;
-        if (col < M) {
+        const int q = 16 * nb + r16;              // rows 4 g .. 4 g + 3 lie in half g / 2
+        const int col = q - (g >> 1) * M;
+        if (col >= 0 && col < M) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) red[slot][w][4 * g + v][col >> 2][col & 3] = acc[nb][v];
         }
@@ -547,24 +589,40 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
       const int p = qq - tok * NP;
       const int rs = (have ? jp : 0) % ORR;
       uint32_t v0 = 0u, v1 = 0u;
+      // Token tok's rows: row 8 h + tok % 8 of waves 4 (tok / 8) .. + 3, added
+      // in position order (block 2 L + h for line L, half h).
+      const int t8 = tok & 7, wb = 4 * (tok >> 3);
       if (qv) {
         if (2 * p == SSO) {
-          double sd = red_ss[rs][0][tok];
+          double sd = red_ss[rs][wb][t8];
+          sd += red_ss[rs][wb][8 + t8];
 #pragma unroll
-          for (int ww = 1; ww < OW; ++ww) sd += red_ss[rs][ww][tok];
+          for (int l4 = 1; l4 < 4; ++l4) {
+            sd += red_ss[rs][wb + l4][t8];
+            sd += red_ss[rs][wb + l4][8 + t8];
+          }
           const u64 b = __builtin_bit_cast(u64, sd);
           v0 = static_cast<uint32_t>(b);
           v1 = static_cast<uint32_t>(b >> 32);
         } else {
-          // columns 2p and 2p + 1: one 8-byte read per wave
-          const float2* r2 = reinterpret_cast<const float2*>(&red[rs][0][tok][0]) + p;
+          // columns 2p and 2p + 1: one 8-byte read per row
+          const float2* r2 = reinterpret_cast<const float2*>(&red[rs][wb][t8][0]) + p;
           constexpr int WS = OR * MP * 2;                 // float2 stride between waves
+          constexpr int HS = 8 * MP * 2;                  // and between the two halves of a line
           float2 x = r2[0];
-#pragma unroll
-          for (int ww = 1; ww < OW; ++ww) {
-            const float2 y = r2[ww * WS];
+          {
+            const float2 y = r2[HS];
             x.x += y.x;
             x.y += y.y;
+          }
+#pragma unroll
+          for (int l4 = 1; l4 < 4; ++l4) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const float2 y = r2[l4 * WS + hf * HS];
+              x.x += y.x;
+              x.y += y.y;
+            }
           }
           v0 = __float_as_uint(x.x);
           v1 = __float_as_uint(x.y);
@@ -585,7 +643,7 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
       if (have) {
         wait_ge(&maps_tag[jt % OMR], jt + 1, vbroken);
 #pragma unroll
-        for (int i = 0; i < N; ++i) hp[i] = maps[jt % OMR][r16][i];
+        for (int i = 0; i < N; ++i) hp[i] = maps[jt % OMR][tk][i];
       }
       const u32x4 (&y)[N] = x;
       float o[8];
@@ -602,14 +660,11 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = fmaf(hp[i], v[e], o[e]);
       }
-      const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + r16;
+      const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + tk;
       const bool ok = have && t < T && jv;
       const uint32_t ho = ok ? static_cast<uint32_t>((t * d + j0) * 2) : kOob;
-      // A plain store, not a non-temporal one: a wave writes 64 bytes of each
-      // of 16 rows, the other half of each 128-byte line comes from the next
-      // wave, and the L2 merges the halves before writing the line back.
-      // Non-temporal stores went out as half lines: 35% more HBM write
-      // traffic for h (182 against 148 MB at T = 16384, d = 4096).
+      // A plain store (whole lines; with half lines from two waves the L2 had
+      // to merge them, which non-temporal stores defeated).
       __builtin_amdgcn_raw_buffer_store_b128(pack8(o, BF16{}).v, hr, static_cast<int>(ho), 0, 0);
     };
 
@@ -625,9 +680,9 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
       if (have) wait_ge(&hmix_tag[sl], jt + 1, vbroken);
       // (a tile past the end mixes whatever the slot holds; its stores are
       // out of range and it is never used)
-      const float* hm = &hmix[sl][r16][0];
+      const float* hm = &hmix[sl][tk][0];
       post_mix<N, true>(x, y, [&](int i, int j) { return j < N ? hm[i * N + j] : hm[N * N + i]; });
-      const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + r16;
+      const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + tk;
       const bool ok = have && t < T && jv;
       const uint32_t o0 = ok ? static_cast<uint32_t>((t * N * d + j0) * 2) : kOob;
       const uint32_t st = ok ? static_cast<uint32_t>(d * 2) : 0u;
