@@ -370,8 +370,12 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
     const uint32_t st = ok ? static_cast<uint32_t>(d * 2) : 0u;
 #pragma unroll
     for (int i = 0; i < N; ++i)
-      x[i] = __builtin_amdgcn_raw_buffer_load_b128(xrx, static_cast<int>(o0 + i * st), 0, 0);
+      x[i] = __builtin_amdgcn_raw_buffer_load_b128(xrx, static_cast<int>(o0 + i * st), 0, 2);
   };
+  // X (and Y) are read with non-temporal loads: each instruction covers
+  // whole 128-byte lines, so nothing is fetched twice, and X is not left in
+  // the caches for the next kernel (in a model the sublayer runs between
+  // this call and mhc_post).
   // The first X tiles go out before the set-up below, which they overlap.
   u32x4 xb[ONB][N];
   // With the previous layer's post fused in: the chunk of Y_l of the tile to
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(POST ? OTP : OT) void pre_one_pass_kernel(OneArgs a
     const int64_t t = (team + static_cast<int64_t>(jt) * teams) * OR + tk;
     const bool ok = jt < J && t < T && jv;
     const uint32_t o0 = ok ? static_cast<uint32_t>((t * d + j0) * 2) : kOob;
-    return __builtin_amdgcn_raw_buffer_load_b128(yrx, static_cast<int>(o0), 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(yrx, static_cast<int>(o0), 0, 2);
   };
   u32x4 yb = {0u, 0u, 0u, 0u};
   if (wave < OW) {
