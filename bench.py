@@ -614,9 +614,13 @@ ENTRY_KERNELS = {
     "mhc_post_pre_two_pass": ["pre_partial_kernel<mhc::BF16, 4, 1, 2, 8, false>",
                               "pre_finish_kernel<mhc::BF16, 4, false, 4>"],
     "mhc_amax": ["amax_kernel<4>"],
-    "mhc_post_bwd": ["post_bwd_tile_kernel<mhc::BF16, 4>", "post_bwd_reduce_kernel<4>"],
+    "mhc_post_bwd": ["post_bwd_tile_kernel<mhc::BF16, 4, true>", "post_bwd_reduce_kernel<4>"],
     "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 2, 1, 8, false>", "pre_bwd_token_kernel<4, true>",
-                    "pre_bwd_apply_mfma_kernel<4>", "reduce_chunks_kernel", "reduce_columns_kernel"],
+                    "pre_bwd_apply_mfma_kernel<4, false>", "reduce_chunks_kernel", "reduce_columns_kernel"],
+    # the whole-dX pair: mhc_post_bwd with dX NULL, then mhc_pre_bwd_ex with G
+    "mhc_post_bwd_without_dX": ["post_bwd_tile_kernel<mhc::BF16, 4, false>", "post_bwd_reduce_kernel<4>"],
+    "mhc_pre_bwd_ex_with_G": ["pre_partial_kernel<mhc::BF16, 4, 2, 1, 8, false>", "pre_bwd_token_kernel<4, true>",
+                              "pre_bwd_apply_mfma_kernel<4, true>", "reduce_chunks_kernel", "reduce_columns_kernel"],
 }
 ENTRY_SOURCES = {
     "mhc_pre": ["pre_fused.hip", "pre_common.hpp", "device.hpp"],
@@ -627,6 +631,8 @@ ENTRY_SOURCES = {
     "mhc_amax": ["amax.hip", "device.hpp"],
     "mhc_post_bwd": ["bwd.hip", "device.hpp"],
     "mhc_pre_bwd": ["bwd.hip", "pre.hip", "pre_common.hpp", "device.hpp"],
+    "mhc_post_bwd_without_dX": ["bwd.hip", "device.hpp"],
+    "mhc_pre_bwd_ex_with_G": ["bwd.hip", "pre.hip", "pre_common.hpp", "device.hpp"],
 }
 COPY_KERNEL = "stream_copy_kernel"  # libmhc_bench's streaming copy of the 512 MiB state: one read, one write
 
@@ -753,6 +759,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-s", type=float, default=0.2,
+                    help="seconds of untimed steps before the warm-up steps (0: none, as in the profiler runs)")
     ap.add_argument("--workload", default="layer_bf16_T16384_d4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
@@ -853,10 +861,10 @@ def main():
 
     # The first few milliseconds of steps after start-up run several percent
     # slower on MI355X, whatever the kernels: before the W warm-up steps the
-    # step runs, untimed, for at least 0.2 s.
+    # step runs, untimed, for at least --settle-s seconds (0.2 by default).
     t_settle = time.perf_counter()
     n_settle = 0
-    while time.perf_counter() - t_settle < 0.2:
+    while time.perf_counter() - t_settle < args.settle_s:
         for _ in range(20):
             step()
         torch.cuda.synchronize()
@@ -946,23 +954,35 @@ def main():
         + ", ".join(f"{k} {v['avg_us']:.1f} us ({v['GBps']:.0f} GB/s)" for k, v in kernels.items()))
 
     # The other form of mhc_pre on the same inputs, for reference.
+    # The two forms in three rounds, their order alternating, each form's
+    # median round (the first calls after an idle moment run slower).
     forms = {}
+    pre_calls = {}
     for form_algo, name in ((2, "one-pass"), (1, "two-pass")):
+        def pcall(form_algo=form_algo):
+            mhc.pre_ex(X, phi, bias, form_algo, alpha=w.alpha, eps=w.eps, t_max=w.t_max, h=h, H=H, workspace=ws,
+                       stream=stream)
         try:
             for _ in range(3):
-                mhc.pre_ex(X, phi, bias, form_algo, alpha=w.alpha, eps=w.eps, t_max=w.t_max, h=h, H=H, workspace=ws,
-                           stream=stream)
-            fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            fev[0].record(stream)
-            for _ in range(max(5, K // 2)):
-                mhc.pre_ex(X, phi, bias, form_algo, alpha=w.alpha, eps=w.eps, t_max=w.t_max, h=h, H=H, workspace=ws,
-                           stream=stream)
-            fev[1].record(stream)
-            torch.cuda.synchronize()
-            us = fev[0].elapsed_time(fev[1]) / max(5, K // 2) * 1e3
-            forms[name] = {"avg_us": us, "GBps": algorithmic_bytes(T, n, d, sbytes)["mhc_pre"] / (us * 1e-6) / 1e9}
+                pcall()
+            pre_calls[name] = pcall
         except mhc.MhcError:
             forms[name] = None
+    pre_runs = {name: [] for name in pre_calls}
+    for rnd in range(3):
+        for name in (list(pre_calls) if rnd % 2 == 0 else list(pre_calls)[::-1]):
+            fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            fev[0].record(stream)
+            for _ in range(max(5, K // 2)):
+                pre_calls[name]()
+            fev[1].record(stream)
+            torch.cuda.synchronize()
+            pre_runs[name].append(fev[0].elapsed_time(fev[1]) / max(5, K // 2) * 1e3)
+    for name, v in pre_runs.items():
+        us = sorted(v)[len(v) // 2]
+        forms[name] = {"avg_us": us, "rounds_us": v,
+                       "GBps": algorithmic_bytes(T, n, d, sbytes)["mhc_pre"] / (us * 1e-6) / 1e9}
     log("mhc_pre forms: " + ", ".join(f"{k} {v['avg_us']:.1f} us" for k, v in forms.items() if v))
 
     post_pre = time_post_pre(mhc, torch, w, X, Y, H, phi, bias, max(5, K // 2), stream)
