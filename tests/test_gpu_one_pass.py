@@ -81,12 +81,17 @@ CASES = [
     ("layer_bf16_T16384_d4096", {"T": 4100}),            # 16-17 tiles per team, ragged: wraps three times
     ("layer_bf16_T4096_d2048", {"T": 2048}),             # team of 8
     ("layer_bf16_T4096_d2048", {"T": 4096}),             # team of 8, 8 tiles per team: wraps
-    ("stack60_bf16_T4096_d2560", {"T": 1600, "layers": 1, "sublayer": "given"}),   # team of 10, ragged slice
+    ("stack60_bf16_T4096_d2560", {"T": 1600, "layers": 1, "sublayer": "given"}),   # team of 10, ragged last tile
     ("stack60_bf16_T4096_d2560", {"T": 4096, "layers": 1, "sublayer": "given"}),   # team of 10, ~11 tiles each
+    # d not a multiple of 256: the last member's slice ends inside a line
+    # (lanes of a 128-byte line partly past d), teams of 12 and 9
+    ("layer_bf16_T16384_d4096", {"T": 2048, "d": 3000}),
+    ("layer_bf16_T16384_d4096", {"T": 1500, "d": 2056}),
 ]
 
 
-@pytest.mark.parametrize("name,changes", CASES, ids=[f"{c[0]}_T{c[1]['T']}" for c in CASES])
+@pytest.mark.parametrize("name,changes", CASES,
+                         ids=[f"{c[0]}_T{c[1]['T']}" + (f"_d{c[1]['d']}" if "d" in c[1] else "") for c in CASES])
 @pytest.mark.parametrize("alpha", [None, (1.0, 1.0, 1.0)], ids=["alpha_cfg", "alpha_1"])
 def test_one_pass_every_token(mhc, oracle_lib, name, changes, alpha):
     w = synth.scaled(synth.WORKLOADS[name], **changes)

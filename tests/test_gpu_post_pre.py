@@ -138,11 +138,13 @@ ONE_PASS_CASES = [
     ("layer_bf16_T16384_d4096", {"T": 2048}),      # eight tiles per team: the exchange ring wraps
     ("layer_bf16_T16384_d4096", {"T": 4100}),      # ragged last tile, the ring wraps three times
     ("layer_bf16_T4096_d2048", {"T": 4096}),       # team of 8
-    ("stack60_bf16_T4096_d2560", {"T": 1600, "layers": 1, "sublayer": "given"}),   # team of 10, ragged slice
+    ("stack60_bf16_T4096_d2560", {"T": 1600, "layers": 1, "sublayer": "given"}),   # team of 10, ragged last tile
+    ("layer_bf16_T16384_d4096", {"T": 2048, "d": 3000}),   # team of 12, the last slice ends inside a line
 ]
 
 
-@pytest.mark.parametrize("name,changes", ONE_PASS_CASES, ids=[f"{c[0]}_T{c[1]['T']}" for c in ONE_PASS_CASES])
+@pytest.mark.parametrize("name,changes", ONE_PASS_CASES,
+                         ids=[f"{c[0]}_T{c[1]['T']}" + (f"_d{c[1]['d']}" if "d" in c[1] else "") for c in ONE_PASS_CASES])
 def test_post_pre_one_pass_equals_separate_calls(mhc, name, changes):
     """Bit for bit the results of mhc_post followed by the single-pass mhc_pre."""
     w = synth.scaled(synth.WORKLOADS[name], **changes)
