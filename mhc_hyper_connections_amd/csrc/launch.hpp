@@ -55,7 +55,12 @@ constexpr size_t kPreHeaderBytes = 256;
 // force_fallback (a testing aid) makes every workgroup start as if a wait had
 // run out, so the fallback kernel recomputes the call.
 size_t pre_fused_body_bytes(int n, int d);
-bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev);   // what MHC_PRE_AUTO picks
+// What MHC_PRE_AUTO picks: the single pass when each team gets at least
+// min_tiles 16-token tiles (kAutoTilesPre for mhc_pre, kAutoTilesPostPre for
+// mhc_post_pre).
+constexpr int kAutoTilesPre = 6;
+constexpr int kAutoTilesPostPre = 16;
+bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev, int min_tiles);
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
                             float* H, void* workspace, size_t ws_bytes, bool force_fallback, const DeviceInfo& dev,
                             hipStream_t stream);

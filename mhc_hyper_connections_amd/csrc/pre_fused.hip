@@ -1177,17 +1177,21 @@ size_t pre_fused_body_bytes(int n, int d) {
          static_cast<size_t>(teams) * OSLOTS * static_cast<size_t>(slot_words(S, n)) * sizeof(u64);
 }
 
-// Whether MHC_PRE_AUTO takes the single pass: measured faster on MI355X for
-// n = 4 when the teams fill whole XCDs and each gets at least 40 tiles (at
-// T = 16384, d = 4096: 194 us against 227 us); for n <= 2 a tile carries too
-// little data to hide the exchange.
-bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev) {
+// Whether MHC_PRE_AUTO takes the single pass: for n = 4 when the teams fill
+// whole XCDs and each gets at least min_tiles tiles.  Measured on MI355X
+// (single pass against two-pass form): mhc_pre 27.1 against 32.3 us at 6
+// tiles per team (T = 1536, d = 4096) and 27.6 against 32.5 us (T = 3072,
+// d = 2048), even at 4; mhc_post_pre 74.6 against 84.1 us at 16 tiles
+// (T = 4096, d = 4096) and 76.7 against 90.5 us (T = 8192, d = 2048), even
+// or slower at 8-12.  For n <= 2 a tile carries too little data to hide the
+// exchange.
+bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev, int min_tiles) {
   if (p.dtype != MHC_BF16 || p.n != 4 || dev.num_cus % OXCD != 0) return false;
   const int S = one_pass_slices(p.d);
   const int per_xcd = dev.num_cus / OXCD;
   if (S < OS_MIN || S > OS_MAX || per_xcd % S != 0) return false;
   const int64_t teams = static_cast<int64_t>(OXCD) * (per_xcd / S);
-  return (p.T + OR - 1) / OR >= 40 * teams;
+  return (p.T + OR - 1) / OR >= static_cast<int64_t>(min_tiles) * teams;
 }
 
 namespace {
