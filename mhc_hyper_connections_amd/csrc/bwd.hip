@@ -325,6 +325,17 @@ hipError_t launch_post_bwd_t(const mhc_params& p, const void* X, const void* Y, 
 // they go to LDS.
 constexpr int kRegTmax = 20;
 
+// Sum over the 16 lanes of a token, the same bits on every lane: quads
+// (partners e^1, e^2), then the quad pairs (rotation by 8 within the row),
+// then the other pair (rotation by 4: either direction reaches it).  DPP, not
+// lane permutes through the LDS unit, which sat on the serial chain.
+__device__ __forceinline__ float sum16(float v) {
+  v = v + lane_xor1(v);
+  v = v + lane_xor2(v);
+  v = v + lane_rot8(v);
+  return v + lane_rot4(v);
+}
+
 template <int N, bool REG>
 __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tpad, int d, int S, int PW, int SSO,
                                                            const float* __restrict__ part,
@@ -386,9 +397,17 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
   if (is_gate) sg = sigmoidf_(logit_of(zg, inv_r, a_gate, bias[colg]));
   float lr = -INFINITY;
   if (is_res) lr = logit_of(zr, inv_r, a_res, bias[colr]);
+  // The forward's Sinkhorn (the same max, sums and order: H_res comes out
+  // bitwise as the forward wrote it), with the iterates kept.
   float mx = lr;
-#pragma unroll
-  for (int off = 1; off < NN; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if constexpr (NN >= 4) {
+    mx = fmaxf(mx, lane_xor1(mx));
+    mx = fmaxf(mx, lane_xor2(mx));
+  }
+  if constexpr (NN >= 16) {
+    mx = fmaxf(mx, lane_rot8(mx));
+    mx = fmaxf(mx, lane_rot4(mx));
+  }
   if (t_max == 0) mx = 0.0f;
   const float m0 = is_res ? expf(lr - mx) : 0.0f;
   float mv = m0;
@@ -403,15 +422,9 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
   };
   auto sk_pass = [&](int it) {
     put(2 * it, mv);
-    float cs = mv;
-#pragma unroll
-    for (int off = N; off < NN; off <<= 1) cs += __shfl_xor(cs, off);
-    mv = mv / cs;
+    mv = mv / col_sum<N>(mv);
     put(2 * it + 1, mv);
-    float rs = mv;
-#pragma unroll
-    for (int off = 1; off < N; off <<= 1) rs += __shfl_xor(rs, off);
-    mv = mv / rs;
+    mv = mv / row_sum<N>(mv);
   };
   if constexpr (REG) {
 #pragma unroll
@@ -430,24 +443,10 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
   // Sinkhorn in reverse.  Step 2 it normalised columns, step 2 it + 1 rows.
   auto sk_back = [&](int st) {
     const float A = get(st);
-    const bool col = (st & 1) == 0;
-    float sum = A, dot;
-    if (col) {
-#pragma unroll
-      for (int off = N; off < NN; off <<= 1) sum += __shfl_xor(sum, off);
-    } else {
-#pragma unroll
-      for (int off = 1; off < N; off <<= 1) sum += __shfl_xor(sum, off);
-    }
+    const bool col = (st & 1) == 0;     // wave-uniform
+    const float sum = col ? col_sum<N>(A) : row_sum<N>(A);
     const float B = A / sum;
-    dot = dm * B;
-    if (col) {
-#pragma unroll
-      for (int off = N; off < NN; off <<= 1) dot += __shfl_xor(dot, off);
-    } else {
-#pragma unroll
-      for (int off = 1; off < N; off <<= 1) dot += __shfl_xor(dot, off);
-    }
+    const float dot = col ? col_sum<N>(dm * B) : row_sum<N>(dm * B);
     dm = (dm - dot) / sum;
   };
   if constexpr (REG) {
@@ -470,13 +469,10 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
   float tpre = (e < N) ? dl_gate * z_gate : 0.0f;
   float tres = is_res ? dl_res * z_res : 0.0f;
   float tpost = (is_gate && e >= N) ? dl_gate * z_gate : 0.0f;
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
-    zdz += __shfl_xor(zdz, off);
-    tpre += __shfl_xor(tpre, off);
-    tres += __shfl_xor(tres, off);
-    tpost += __shfl_xor(tpost, off);
-  }
+  zdz = sum16(zdz);
+  tpre = sum16(tpre);
+  tres = sum16(tres);
+  tpost = sum16(tpost);
   if (t >= Tpad) return;
   float* gblk = gT + (t >> 5) * 32 * 32 + (t & 31);
   if (!tv) {                                   // padding token: zero operand column and sums
