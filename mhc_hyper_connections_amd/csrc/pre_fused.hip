@@ -18,17 +18,19 @@
 // rotation, a team's members would sit on different XCDs, their exchange
 // words would not meet in one L2, and the bounded waits would report it.
 // A workgroup runs eleven waves with fixed roles:
-//  * waves 0-7 stream.  Wave w holds positions 32 w .. 32 w + 31 of the
-//    member's slice for a tile's 16 tokens in registers (lane = token row
-//    and 8 positions, the MFMA A layout; one 16-byte load per stream).  In
-//    step k it forms tile k's m partial dot products with phi on MFMA (phi
-//    as bf16 hi + lo halves, kept in LDS) and the partial sums of squares
-//    (the diagonal of the tile's 16 x 16 Gram matrix, also on MFMA) into an
-//    LDS ring; once tile k-OD's H_pre has come back, forms h = H_pre . X for
-//    its positions from the registers that still hold that tile, and stores
-//    it; prefetches tile k+OP; and last sums its eighth of tile k's record
-//    over the 8 waves (wave order) and posts it with one 16-byte store (by
-//    then the other waves have written tile k's partials).  These
+//  * waves 0-7 stream.  Wave w holds line w % 4 of the member's slice (64
+//    positions, 128 bytes of every stream row) for tokens 8 (w / 4) .. + 7
+//    of a tile in registers (lane = token and 8 positions of all n streams;
+//    each load and store covers whole 128-byte lines).  In step k it forms
+//    tile k's m partial dot products with phi on MFMA (phi as bf16 hi + lo
+//    halves, kept in LDS; the A operand's rows 0..7 hold the line's first
+//    32 positions, rows 8..15 its last 32) and the partial sums of squares
+//    (the diagonal of a 16 x 16 Gram matrix, also on MFMA) into an LDS ring;
+//    once tile k-OD's H_pre has come back, forms h = H_pre . X for its
+//    positions from the registers that still hold that tile, and stores it;
+//    prefetches tile k+OP; and last sums its eighth of tile k's record over
+//    the token's rows (position order) and posts it with one 16-byte store
+//    (by then the other waves have written tile k's partials).  These
 //    waves issue no memory operation but their X loads, the record store and
 //    the h store, a fixed number per step (masked lanes use out-of-range
 //    buffer offsets, which move no data), so the in-order completion count
