@@ -98,6 +98,14 @@ def test_one_pass_every_token(mhc, oracle_lib, name, changes, alpha):
     _check(mhc, oracle_lib, w, alpha=alpha)
 
 
+def test_one_pass_twice_the_headline_size(mhc, oracle_lib):
+    """T = 32768 (1 GiB of state, 128 tiles per team: the exchange ring
+    wraps 25 times), every token against the oracle."""
+    w = synth.scaled(synth.WORKLOADS["layer_bf16_T16384_d4096"], T=32768)
+    print(f"[one pass] every token at T={w.T}", flush=True)
+    _check(mhc, oracle_lib, w)
+
+
 @pytest.mark.parametrize("n", [1, 2])
 def test_one_pass_fewer_streams(mhc, oracle_lib, n):
     w = synth.Workload(f"one_pass_n{n}", T=1024, n=n, d=4096, dtype=synth.BF16, seed=777 + n)
