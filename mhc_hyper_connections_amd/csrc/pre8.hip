@@ -5,14 +5,16 @@
 // "Kernmechanismen" for the unconstrained HC maps), in two passes:
 //  1. pre_partial8_kernel -- persistent split-K projection.  At n = 8 a
 //     lane cannot hold its rows of phi for all 80 columns and all streams
-//     (8 streams x 5 column blocks x hi/lo = 320 registers), so a
-//     workgroup's eight waves split the contraction by stream: wave w takes
-//     streams 2 (w % 4) and 2 (w % 4) + 1 of position group w / 4 (32
-//     positions) of the workgroup's 64-position slice and keeps those rows
-//     of phi for all 80 columns in registers (80).  Every wave reads its own
-//     part of the X tile (16 tokens x 2 streams x 32 positions).  The eight
-//     waves' partials are added in LDS in wave order and written as the same
-//     per-token records as n <= 4 (m partials, fp64 sum of squares).
+//     (8 streams x 5 column blocks x hi/lo = 320 registers), so a slice is
+//     512 positions of one stream (512 rows of the contraction, 164 KiB of
+//     phi operands) and a workgroup's eight waves split it: wave w takes
+//     positions 64 w .. 64 w + 63 of the slice and keeps those rows of phi
+//     for all 80 columns in registers (80).  A slice of one stream rather
+//     than 64 positions of every stream makes each load instruction one
+//     token's contiguous 1 KiB of X (the 128-byte pieces of the other form
+//     read X at about half the rate).  The eight waves' partials are added
+//     in LDS in wave order and written as per-token records (m partials,
+//     fp64 sum of squares); slices are numbered stream by stream.
 //  2. pre_finish8_kernel -- one token per wave, one Sinkhorn entry per lane:
 //     sums the slices in order (fp64), forms r, the logits, the gates and
 //     Sinkhorn (column sums over lanes e ^ 8, 16, 32; row sums over e ^ 1,
@@ -26,11 +28,9 @@ namespace {
 constexpr int P8_N = 8;
 constexpr int P8_M = num_maps(P8_N);          // 80
 constexpr int P8_CB = P8_M / 16;              // 16-column blocks
-constexpr int P8_SP = P8_N / 2;               // stream pairs
-constexpr int P8_PG = 2;                      // position groups of 32
-constexpr int P8_WAVES = P8_SP * P8_PG;       // 8
+constexpr int P8_WAVES = 8;
 constexpr int P8_THREADS = P8_WAVES * 64;
-constexpr int P8_SLICE = 32 * P8_PG;          // positions of d per slice
+constexpr int P8_SLICE = 64 * P8_WAVES;       // positions of one stream per slice
 // Token record of one slice: 80 partials, 2 words of padding, the fp64 sum
 // of squares at word 82; 84 words keep every record 16-byte aligned.
 constexpr int P8_SSO = P8_M + 2;
@@ -51,39 +51,45 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
   __shared__ f32x4 red[P8_WAVES][R][M / 4];
   __shared__ double red_ss[P8_WAVES][R];
   // bf16: the tile arrives with each load instruction covering one token's
-  // 8 stream rows x 128 bytes (the slice), goes through LDS and is read
-  // back in the MFMA A layout; 16 bytes of padding per token keep the 16
-  // tokens of a read on distinct banks.
+  // 1 KiB of the slice, goes through LDS and is read back in the MFMA A
+  // layout; 16 bytes of padding per token keep the 16 tokens of a read on
+  // distinct banks.
   constexpr bool STAGE = GRAM;
   static_assert(!STAGE || MB == 2, "the staged layout gives each wave 4 of the tile's 32 tokens");
-  constexpr int STS = N * 128 + 16;
+  constexpr int STS = P8_SLICE * 2 + 16;
   __shared__ __attribute__((aligned(16))) unsigned char stage_l[STAGE ? R * STS : 16];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int sp = w % P8_SP;
-  const int pg = w / P8_SP;
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int s = blockIdx.x % S;
   const int64_t ntg = gridDim.x / S;
   float* const trash = part + static_cast<int64_t>(S) * T * P8_PW;
-  const int j0 = s * P8_SLICE + 32 * pg + 8 * g;
-  const bool jv = j0 < d;
-  const int jl = jv ? j0 : 0;
+  const int bps = S / N;                      // slices per stream
+  const int si = s / bps;                     // the slice's stream
+  const int p0 = (s - si * bps) * P8_SLICE;   // its first position
+  // K block q of this lane: positions p0 + 64 w + 32 q + 8 g .. +7.
+  int jq[2];
+  bool jvq[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int j = p0 + 64 * w + 32 * q + 8 * g;
+    jvq[q] = j < d;
+    jq[q] = jvq[q] ? j : 0;
+  }
 
-  // This lane's rows of phi: rows i*d + j0 .. +7 (streams i = 2 sp, 2 sp + 1)
-  // of column 16 b + r16, every column block b.
+  // This lane's rows of phi: rows si*d + jq[q] .. +7 of column 16 b + r16,
+  // every column block b.
   PhiOp<ST> bop[2][P8_CB];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int i = 2 * sp + q;
 #pragma unroll
     for (int b = 0; b < P8_CB; ++b) {
       float f[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        f[e] = jv ? phi[static_cast<int64_t>(i * d + j0 + e) * M + 16 * b + r16] : 0.0f;
+        f[e] = jvq[q] ? phi[(static_cast<int64_t>(si) * d + jq[q] + e) * M + 16 * b + r16] : 0.0f;
       bop[q][b] = make_phi_op(f, ST{});
     }
   }
@@ -92,11 +98,9 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
   // Unconditional loads from valid addresses: tokens past T read token 0,
   // lanes past d read position 0 (zero phi rows; their squares are masked).
   // Staged load layout: load k of wave w covers token 4 w + k of the tile
-  // (8 per mb block), stream lane / 8, 8 positions at jls.
-  const int sst = lane >> 3;
-  const int jls0 = s * P8_SLICE + 8 * (lane & 7);
-  const bool jvs = jls0 < d;
-  const int jls = jvs ? jls0 : 0;
+  // (2 mb + q), 8 positions at jls.
+  const int jls0 = p0 + 8 * lane;
+  const int jls = jls0 < d ? jls0 : 0;
   auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][2]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -105,11 +109,11 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
         if constexpr (STAGE) {
           const int64_t t = tile * R + 4 * w + 2 * mb + q;
           const int64_t tt = t < T ? t : 0;
-          x[mb][q] = load_raw8<ST>(X + (tt * N + sst) * d + jls);
+          x[mb][q] = load_raw8<ST>(X + (tt * N + si) * d + jls);
         } else {
           const int64_t t = tile * R + mb * 16 + r16;
           const int64_t tt = t < T ? t : 0;
-          x[mb][q] = load_raw8<ST>(X + (tt * N + 2 * sp + q) * d + jl);
+          x[mb][q] = load_raw8<ST>(X + (tt * N + si) * d + jq[q]);
         }
       }
     }
@@ -121,16 +125,15 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
-          *reinterpret_cast<u32x4*>(stage_l + (4 * w + 2 * mb + q) * STS + sst * 128 + (lane & 7) * 16) =
-              cur[mb][q].v;
+          *reinterpret_cast<u32x4*>(stage_l + (4 * w + 2 * mb + q) * STS + lane * 16) = cur[mb][q].v;
       }
       __syncthreads();
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
-          cur[mb][q].v = *reinterpret_cast<const u32x4*>(stage_l + (mb * 16 + r16) * STS + (2 * sp + q) * 128 +
-                                                         (32 * pg + 8 * g) * 2);
+          cur[mb][q].v = *reinterpret_cast<const u32x4*>(stage_l + (mb * 16 + r16) * STS +
+                                                         (64 * w + 32 * q + 8 * g) * 2);
       }
     }
     f32x4 acc[MB][P8_CB];
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
       Raw8<ST> xm[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        xm[q] = jv ? cur[mb][q] : zero_raw8<ST>();
+        xm[q] = jvq[q] ? cur[mb][q] : zero_raw8<ST>();
 #pragma unroll
         for (int b = 0; b < P8_CB; ++b) acc[mb][b] = mfma_block(cur[mb][q], bop[q][b], acc[mb][b]);
       }
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(256) void pre_finish8_kernel(int64_t T, int d, int 
   }
 }
 
-int slices8(int d) { return (d + P8_SLICE - 1) / P8_SLICE; }
+int slices8(int d) { return P8_N * ((d + P8_SLICE - 1) / P8_SLICE); }
 
 template <typename ST>
 hipError_t launch_pre8_t(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h, float* H,

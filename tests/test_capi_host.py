@@ -119,9 +119,9 @@ def test_workspace_size_formula(lib):
         assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == 256 + max(body, one_pass)
     for (T, d) in ((64, 256), (1, 8), (4096, 4104)):
         # n = 8: records of 80 partials, 2 words of padding and an fp64 (84 words, 16-byte
-        # aligned) over slices of 64 positions, plus trash slots
+        # aligned) over slices of 512 positions of one stream, plus trash slots
         p = _params(T=T, n=8, d=d)
-        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == 256 + -(-d // 64) * T * 84 * 4 + 512 * 16
+        assert lib.mhc_pre_workspace_size(ctypes.byref(p)) == 256 + 8 * -(-d // 512) * T * 84 * 4 + 512 * 16
     assert lib.mhc_pre_workspace_size(None) == 0
     assert lib.mhc_pre_workspace_size(ctypes.byref(_params(n=3))) == 0
 

@@ -2,7 +2,7 @@
 64-entry Sinkhorn-Knopp on one wave per token), mhc_post, mhc_post_pre and
 mhc_amax against the oracle.
 
-Shapes cover d below one 64-position slice, ragged last slices, T = 1 and T
+Shapes cover d below one 512-position slice, ragged last slices, T = 1 and T
 not a multiple of the 16-token tile, both storage types, both map forms; one
 case runs at d = 4096 with enough tokens for several persistent passes.
 """
@@ -30,10 +30,10 @@ CASES = [
     # (d, T, dtype)
     (8, 1, synth.FP32),
     (64, 17, synth.BF16),
-    (264, 65, synth.BF16),      # 4 full slices and an 8-position one
-    (520, 33, synth.FP32),
+    (264, 65, synth.BF16),      # one 264-position slice per stream
+    (520, 33, synth.FP32),      # a full slice and an 8-position one per stream
     (1024, 130, synth.BF16),
-    (4096, 700, synth.BF16),    # 64 slices; 44 tiles over more workgroup passes than one
+    (4096, 700, synth.BF16),    # 64 slices; 22 tiles over more workgroup passes than one
 ]
 
 
