@@ -161,10 +161,12 @@ size_t mhc_pre_workspace_size(const mhc_params* p);
  *                     comes from the workspace, not the host, so the form
  *                     may be captured into a HIP graph and replayed.
  *                     Returns MHC_ERR_UNSUPPORTED when it does not apply.
- *   MHC_PRE_AUTO      the one-pass form where it measures faster on MI355X
- *                     (n = 4, teams that fill whole XCDs, at least 6 tiles
- *                     of 16 tokens per team: T >= 1536 at d = 4096, 3072 at
- *                     d = 2048), else the two-pass form.
+ *   MHC_PRE_AUTO      the one-pass form where it measures faster on MI355X:
+ *                     n = 4 and enough 16-token tiles per team, from 6 for
+ *                     teams of 8 or 16 (T >= 1536 at d = 4096, 3072 at
+ *                     d = 2048) to 24 for teams of 11, which leave 10 of an
+ *                     XCD's 32 compute units idle (T >= 3840 at d = 2560,
+ *                     teams of 10); else the two-pass form.
  *   MHC_PRE_ONE_PASS_FALLBACK_TEST
  *                     testing aid: the one-pass form with every workgroup
  *                     starting as if a wait had run out, so the recomputing
@@ -254,10 +256,11 @@ mhc_status mhc_post(const mhc_params* p, const void* X, const void* Y, const flo
  *                     when X_out == X, MHC_ERR_UNSUPPORTED when the shape
  *                     does not apply.
  *   MHC_PRE_AUTO      the single pass when X_out is separate from X, n = 4
- *                     and each team gets at least 16 tiles (T >= 4096 at
- *                     d = 4096, 8192 at d = 2048; on MI355X at T = 16384,
- *                     d = 4096: 265-272 us against 326-329 us for the
- *                     two-pass form), else the two-pass form.
+ *                     and each team gets enough tiles: 10 to 48 by team
+ *                     size (T >= 4096 at d = 4096, 5120 at d = 2048, 3840
+ *                     at d = 2560; on MI355X at T = 16384, d = 4096:
+ *                     265-272 us against 326-329 us for the two-pass
+ *                     form), else the two-pass form.
  *   MHC_PRE_ONE_PASS_FALLBACK_TEST   as for mhc_pre_ex.
  * n = 1 and n = 8 run mhc_post, then mhc_pre's two-pass form. */
 mhc_status mhc_post_pre(const mhc_params* p, const void* X, const void* Y, const float* H, void* X_out,

@@ -55,12 +55,15 @@ constexpr size_t kPreHeaderBytes = 256;
 // force_fallback (a testing aid) makes every workgroup start as if a wait had
 // run out, so the fallback kernel recomputes the call.
 size_t pre_fused_body_bytes(int n, int d);
-// What MHC_PRE_AUTO picks: the single pass when each team gets at least
-// min_tiles 16-token tiles (kAutoTilesPre for mhc_pre, kAutoTilesPostPre for
-// mhc_post_pre).
-constexpr int kAutoTilesPre = 6;
-constexpr int kAutoTilesPostPre = 16;
-bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev, int min_tiles);
+// What MHC_PRE_AUTO picks: the single pass when each team gets at least as
+// many 16-token tiles as the table gives for its team size S = 8 .. 16
+// (mhc_pre, then mhc_post_pre with the post in front).  The entries are the
+// crossovers measured on MI355X at n = 4, T = 1024 .. 16384, ties going to
+// the two-pass form.  Teams that leave CUs of an XCD idle (S = 11 and 12
+// leave 10 and 8 of 32) need more tiles before the single pass wins.
+constexpr int kAutoTilesPre[9] = {6, 10, 10, 24, 18, 14, 12, 12, 6};
+constexpr int kAutoTilesPostPre[9] = {10, 16, 10, 48, 28, 16, 12, 12, 16};
+bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev, bool post);
 hipError_t launch_pre_fused(const mhc_params& p, const void* X, const float* phi, const float* bias, void* h,
                             float* H, void* workspace, size_t ws_bytes, bool force_fallback, const DeviceInfo& dev,
                             hipStream_t stream);

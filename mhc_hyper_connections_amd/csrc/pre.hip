@@ -715,11 +715,11 @@ hipError_t launch_post_pre(const mhc_params& p, const void* X, const void* Y, co
   if (p.T == 0) return hipSuccess;
   // The single pass recomputes from X_l when its waits run out, so it needs
   // X_{l+1} in a buffer of its own.  MHC_PRE_AUTO takes it when X_{l+1} is
-  // separate and each team gets at least kAutoTilesPostPre tiles (on MI355X
-  // at T = 16384, n = 4, d = 4096: 265-272 us against 326-329 us for the
-  // two-pass form), else the two-pass form.
+  // separate and each team gets at least kAutoTilesPostPre[S] tiles (on
+  // MI355X at T = 16384, n = 4, d = 4096: 265-272 us against 326-329 us for
+  // the two-pass form), else the two-pass form.
   const bool separate = Xout != X;
-  if (algo == MHC_PRE_AUTO && separate && pre_fused_preferred(p, dev, kAutoTilesPostPre)) {
+  if (algo == MHC_PRE_AUTO && separate && pre_fused_preferred(p, dev, true)) {
     if (launch_post_pre_fused(p, X, Y, Hprev, Xout, phi, bias, h, H, workspace, ws_bytes, false, dev, stream) ==
         hipSuccess) {
       if (used) *used = MHC_PRE_ONE_PASS;
@@ -779,7 +779,7 @@ hipError_t launch_pre(const mhc_params& p, const void* X, const float* phi, cons
                       hipStream_t stream) {
   if (used) *used = MHC_PRE_TWO_PASS;
   if (p.T == 0) return hipSuccess;
-  if (algo == MHC_PRE_AUTO && pre_fused_preferred(p, dev, kAutoTilesPre)) {
+  if (algo == MHC_PRE_AUTO && pre_fused_preferred(p, dev, false)) {
     if (launch_pre_fused(p, X, phi, bias, h, H, workspace, ws_bytes, false, dev, stream) == hipSuccess) {
       if (used) *used = MHC_PRE_ONE_PASS;
       return hipSuccess;

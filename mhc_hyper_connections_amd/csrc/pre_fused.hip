@@ -1187,11 +1187,13 @@ size_t pre_fused_body_bytes(int n, int d) {
 // (T = 4096, d = 4096) and 76.7 against 90.5 us (T = 8192, d = 2048), even
 // or slower at 8-12.  For n <= 2 a tile carries too little data to hide the
 // exchange.
-bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev, int min_tiles) {
+bool pre_fused_preferred(const mhc_params& p, const DeviceInfo& dev, bool post) {
   if (p.dtype != MHC_BF16 || p.n != 4 || dev.num_cus % OXCD != 0) return false;
   const int S = one_pass_slices(p.d);
   const int per_xcd = dev.num_cus / OXCD;
-  if (S < OS_MIN || S > OS_MAX || per_xcd % S != 0) return false;
+  if (S < OS_MIN || S > OS_MAX || per_xcd < S) return false;
+  static_assert(OS_MAX - OS_MIN + 1 == 9, "one threshold per team size");
+  const int min_tiles = post ? kAutoTilesPostPre[S - OS_MIN] : kAutoTilesPre[S - OS_MIN];
   const int64_t teams = static_cast<int64_t>(OXCD) * (per_xcd / S);
   return (p.T + OR - 1) / OR >= static_cast<int64_t>(min_tiles) * teams;
 }

@@ -63,32 +63,38 @@ def test_post_pre_fewer_streams(mhc, n):
         assert np.array_equal(Xs, Xf) and np.array_equal(hs, hf) and np.array_equal(Hs, Hf)
 
 
-def _stack_fused(mhc, w, T, L):
-    """The L-layer stack as pre_0, then (0.5 GELU, post_pre) per layer, then a last post."""
+def _stack_fused(mhc, w, T, L, pingpong=False):
+    """The L-layer stack as pre_0, then (0.5 GELU, post_pre) per layer, then a
+    last post; in place, or with X_{l+1} in the other of two buffers (where
+    MHC_PRE_AUTO may take the single pass)."""
     X0 = synth.make_state(w, T)
     phis, biases = zip(*(synth.make_params(w, layer=l) for l in range(L)))
     X = to_device(X0)
+    other = torch.empty_like(X) if pingpong else X
     Hs = torch.empty((L, T, w.m), dtype=torch.float32, device="cuda")
     h, _ = mhc.pre(X, to_device(phis[0]), to_device(biases[0]), alpha=w.alpha, eps=w.eps, t_max=w.t_max, H=Hs[0])
     for l in range(L - 1):
         Y = mhc.gelu_half(h)
-        X, h, _ = mhc.post_pre(X, Y, Hs[l], to_device(phis[l + 1]), to_device(biases[l + 1]), alpha=w.alpha,
-                               eps=w.eps, t_max=w.t_max, out=X, H_next=Hs[l + 1])
+        Xn, h, _ = mhc.post_pre(X, Y, Hs[l], to_device(phis[l + 1]), to_device(biases[l + 1]), alpha=w.alpha,
+                                eps=w.eps, t_max=w.t_max, out=other, H_next=Hs[l + 1])
+        X, other = Xn, X
     X = mhc.post(X, mhc.gelu_half(h), Hs[L - 1], out=X)
     am = mhc.amax(Hs, w.n)
     torch.cuda.synchronize()
     return X0, np.stack(phis), np.stack(biases), to_host(X), to_host(Hs), {k: to_host(v) for k, v in am.items()}
 
 
-@pytest.mark.parametrize("T", [40, 4096])
-def test_stack60_fused(mhc, oracle_lib, T):
+@pytest.mark.parametrize("T,pingpong", [(40, False), (4096, False), (4096, True)])
+def test_stack60_fused(mhc, oracle_lib, T, pingpong):
     """The 60-layer stack on mhc_post_pre: final state, every layer's maps and
     the per-token composite Amax against the oracle on every token (same
-    criteria as the unfused stack)."""
+    criteria as the unfused stack).  In place the two-pass form runs; with two
+    state buffers at T = 4096 MHC_PRE_AUTO takes the single pass (teams of 10
+    at d = 2560, 10.7 tiles each)."""
     w = synth.WORKLOADS["stack60_bf16_T4096_d2560"]
     L = w.layers
-    print(f"[post_pre] stack T={T}", flush=True)
-    X0, phis, biases, Xg, Hg, am = _stack_fused(mhc, w, T, L)
+    print(f"[post_pre] stack T={T} pingpong={pingpong}", flush=True)
+    X0, phis, biases, Xg, Hg, am = _stack_fused(mhc, w, T, L, pingpong)
     check_stack_every_token(oracle_lib, w, X0, phis, biases, Xg, Hg, am, L)
 
 
@@ -201,6 +207,26 @@ def test_post_pre_one_pass_every_token(mhc, oracle_lib, T):
     r = _one_pass_pair(mhc, w, mhc.PRE_ONE_PASS)
     assert not r["fell_back"]
     _oracle_every_token(oracle_lib, w, r, w.alpha)
+
+
+def test_auto_takes_single_pass_for_teams_of_ten(mhc):
+    """At d = 2560 a team has 10 members, so 2 of each XCD's 32 compute units
+    stay idle; from 10 tiles per team (T = 4096) MHC_PRE_AUTO still takes the
+    single pass for both entry points, bit for bit the forced form, and the
+    two-pass form below that (T = 3072, 8 tiles per team)."""
+    for T, want in ((4096, mhc.PRE_ONE_PASS), (3072, mhc.PRE_TWO_PASS)):
+        w = synth.scaled(synth.WORKLOADS["stack60_bf16_T4096_d2560"], T=T, layers=1, sublayer="given")
+        X, Y, phi0, b0, phi1, b1 = (to_device(a) for a in _inputs(w))
+        kw = dict(alpha=w.alpha, eps=w.eps, t_max=w.t_max)
+        ha, Ha, used = mhc.pre_ex(X, phi0, b0, mhc.PRE_AUTO, **kw)
+        assert used == want, (T, used)
+        hf, Hf, _ = mhc.pre_ex(X, phi0, b0, want, **kw)
+        assert torch.equal(ha, hf) and torch.equal(Ha, Hf)
+        auto = mhc.post_pre_ex(X, Y, Ha, phi1, b1, mhc.PRE_AUTO, **kw)
+        assert auto[3] == want, (T, auto[3])
+        forced = mhc.post_pre_ex(X, Y, Ha, phi1, b1, want, **kw)
+        assert all(torch.equal(a, b) for a, b in zip(auto[:3], forced[:3]))
+    torch.cuda.synchronize()
 
 
 def test_post_pre_auto_and_alias(mhc):
