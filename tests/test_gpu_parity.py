@@ -205,9 +205,12 @@ def test_amax_matches_oracle(mhc, oracle_lib, n, L):
     assert np.all(err <= 1e-4 * scale + 1e-6), float((err / scale).max())
 
 
-def test_gelu_half(mhc, oracle_lib):
+@pytest.mark.parametrize("count", [7, 1003, 24581])
+def test_gelu_half(mhc, oracle_lib, count):
+    """Fewer values than one 8-value chunk, a ragged tail, and several
+    workgroups of 512 chunks with a ragged tail."""
     for dt in (synth.FP32, synth.BF16):
-        h = synth.normal(5, 1, (1003,), 0.0, 2.0, dt)
+        h = synth.normal(5, 1, (count,), 0.0, 2.0, dt)
         y = to_host(mhc.gelu_half(to_device(h)))
         tol = (1e-5, 1e-6) if dt == synth.FP32 else (8e-3, 1e-6)
         assert_close(y, oracle_lib.gelu_half(h), *tol, what="gelu_half")
