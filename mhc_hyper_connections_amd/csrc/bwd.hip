@@ -911,23 +911,26 @@ __global__ __launch_bounds__(AM_THREADS) void pre_bwd_apply_mfma_kernel(int64_t 
 }
 
 // ---- launch D: fixed-order reductions ------------------------------------------
-// dphi[k][j] = sum over chunks in order.
-__global__ __launch_bounds__(256) void reduce_chunks_kernel(int64_t count, int nch, const float* __restrict__ part,
-                                                            float* __restrict__ out) {
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (q >= count) return;
-  float s = 0.0f;
-  for (int ch = 0; ch < nch; ++ch) s += part[static_cast<int64_t>(ch) * count + q];
-  out[q] = s;
-}
-
-// Column sums of pg [W][Tpad] over tokens: one block per column, thread k
-// adds tokens k, k + 256, ... (coalesced), then a fixed tree.  Columns
-// 0 .. m-1 go to dbias, m .. m+2 to dalpha.
-__global__ __launch_bounds__(256) void reduce_columns_kernel(int64_t Tpad, int m, const float* __restrict__ pg,
-                                                             float* __restrict__ dbias, float* __restrict__ dalpha) {
+// One launch for both: blocks 0 .. nbc-1 sum dphi's chunk partials, the
+// next m + 3 blocks the columns of pg.
+//  * dphi[k][j] = sum over chunks in order.
+//  * Column sums of pg [W][Tpad] over tokens: one block per column, thread k
+//    adds tokens k, k + 256, ... (coalesced), then a fixed tree.  Columns
+//    0 .. m-1 go to dbias, m .. m+2 to dalpha.
+__global__ __launch_bounds__(256) void reduce_grads_kernel(int64_t count, int nch, int64_t nbc,
+                                                           const float* __restrict__ part, float* __restrict__ out,
+                                                           int64_t Tpad, int m, const float* __restrict__ pg,
+                                                           float* __restrict__ dbias, float* __restrict__ dalpha) {
   __shared__ float red[256];
-  const int col = blockIdx.x;
+  if (static_cast<int64_t>(blockIdx.x) < nbc) {                       // block-uniform
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (q >= count) return;
+    float s = 0.0f;
+    for (int ch = 0; ch < nch; ++ch) s += part[static_cast<int64_t>(ch) * count + q];
+    out[q] = s;
+    return;
+  }
+  const int col = static_cast<int>(blockIdx.x - nbc);
   const float* c = pg + static_cast<int64_t>(col) * Tpad;
   float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
   int64_t t = threadIdx.x;
@@ -1072,12 +1075,11 @@ hipError_t launch_pre_bwd_t(const mhc_params& p, const void* X, const float* phi
   if (err != hipSuccess) return err;
 
   const int64_t count = K * M;
-  hipLaunchKernelGGL(reduce_chunks_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, stream,
-                     count, L.nch, static_cast<const float*>(dphi_part), dphi);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(reduce_columns_kernel, dim3(pg_width(N)), dim3(256), 0, stream, L.Tpad, M,
-                     static_cast<const float*>(pg), dbias, dalpha);
+  const int64_t nbc = (count + 255) / 256;
+  if (nbc + pg_width(N) > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(reduce_grads_kernel, dim3(static_cast<unsigned>(nbc + pg_width(N))), dim3(256), 0, stream, count,
+                     L.nch, nbc, static_cast<const float*>(dphi_part), dphi, L.Tpad, M, static_cast<const float*>(pg),
+                     dbias, dalpha);
   return hipGetLastError();
 }
 
