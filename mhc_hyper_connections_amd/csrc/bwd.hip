@@ -266,8 +266,19 @@ __global__ __launch_bounds__(256) void post_bwd_reduce_kernel(int64_t T, int nsl
   const int64_t t = q / NA;
   const int a = static_cast<int>(q - t * NA);
   const float* src = part + t * nslice * NA + a;
+  // Slices in order; eight loads out before their sums (a loop with one load
+  // per trip waits for each in turn).  Indices past the last slice are
+  // clamped to a valid one and their values dropped.
   float v = src[0];
-  for (int sl = 1; sl < nslice; ++sl) v += src[static_cast<int64_t>(sl) * NA];
+  for (int sl = 1; sl < nslice; sl += 8) {
+    const int nb = (nslice - sl < 8) ? nslice - sl : 8;
+    float w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = src[static_cast<int64_t>(sl + (u < nb ? u : 0)) * NA];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < nb) v += w[u];
+  }
   dH[t * M + N + a] = v;
 }
 
@@ -925,8 +936,18 @@ __global__ __launch_bounds__(256) void reduce_grads_kernel(int64_t count, int nc
   if (static_cast<int64_t>(blockIdx.x) < nbc) {                       // block-uniform
     const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (q >= count) return;
+    // Chunks in order, eight loads out before their sums (indices past the
+    // last chunk clamped, their values dropped).
     float s = 0.0f;
-    for (int ch = 0; ch < nch; ++ch) s += part[static_cast<int64_t>(ch) * count + q];
+    for (int ch = 0; ch < nch; ch += 8) {
+      const int nb = (nch - ch < 8) ? nch - ch : 8;
+      float w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = part[static_cast<int64_t>(ch + (u < nb ? u : 0)) * count + q];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u < nb) s += w[u];
+    }
     out[q] = s;
     return;
   }
@@ -934,6 +955,20 @@ __global__ __launch_bounds__(256) void reduce_grads_kernel(int64_t count, int nc
   const float* c = pg + static_cast<int64_t>(col) * Tpad;
   float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
   int64_t t = threadIdx.x;
+  // Four rounds' sixteen loads out before their sums, added in the order the
+  // round-by-round loop below adds them.
+  for (; t + 3 * 1024 + 768 < Tpad; t += 4096) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = c[t + 256 * u];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      s0 += v[4 * k];
+      s1 += v[4 * k + 1];
+      s2 += v[4 * k + 2];
+      s3 += v[4 * k + 3];
+    }
+  }
   for (; t + 768 < Tpad; t += 1024) {
     s0 += c[t];
     s1 += c[t + 256];

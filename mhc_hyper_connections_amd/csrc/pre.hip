@@ -124,7 +124,10 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
   // select on the data (either would make the compiler wait for the load on
   // the spot): tokens past T read token 0 (their rows are never written) and
   // lanes past d read position 0 (their phi rows are zero and their squares
-  // are dropped below).
+  // are dropped below).  The backward's pass (WITH_D) reads X and D
+  // non-temporally: the apply pass reads them again only after the token
+  // pass, and at T = 16384, n = 4, d = 4096 that took 12 us off mhc_pre_bwd
+  // (cached loads measured no faster in the forward's modes).
   const int jl = STAGE ? (jvl ? jl0 : 0) : (jv ? j0 : 0);
   auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][NX], f32x4 (&hv)[MB][HV]) {
 #pragma unroll
@@ -132,8 +135,8 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
       const int64_t t = tile * R + mb * 16 + (STAGE ? trow : r16);
       const int64_t tt = t < T ? t : 0;
 #pragma unroll
-      for (int i = 0; i < N; ++i) x[mb][i] = load_raw8<ST>(X + (tt * N + i) * d + jl);
-      if constexpr (WITH_D || FUSE_POST) x[mb][N] = load_raw8<ST>(Dg + tt * d + jl);
+      for (int i = 0; i < N; ++i) x[mb][i] = load_raw8<ST, WITH_D>(X + (tt * N + i) * d + jl);
+      if constexpr (WITH_D || FUSE_POST) x[mb][N] = load_raw8<ST, WITH_D>(Dg + tt * d + jl);
       if constexpr (FUSE_POST) {
 #pragma unroll
         for (int v = 0; v < HV; ++v) hv[mb][v] = *reinterpret_cast<const f32x4*>(Hin + tt * M + 4 * v);
@@ -668,7 +671,10 @@ template <typename ST, int N>
 hipError_t launch_partial_d_t(const mhc_params& p, const void* X, const void* D, const float* phi, float* part,
                               const DeviceInfo& dev, hipStream_t stream) {
   typedef typename ST::elem E;
-  constexpr int MB = (sizeof(typename ST::elem) == 2) ? 2 : 1;     // fits the registers without spilling
+  // 16-token tiles: twice the tiles of the forward's 32, each with fewer
+  // registers live (174 against 226); at T = 16384, n = 4, d = 4096 that
+  // took another 11 us off mhc_pre_bwd, with the same bits.
+  constexpr int MB = 1;
   constexpr int R = 16 * MB;
   const int S = num_slices(p.d);
   const int64_t ntiles = (p.T + R - 1) / R;
