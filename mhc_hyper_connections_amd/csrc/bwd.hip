@@ -347,8 +347,13 @@ __device__ __forceinline__ float sum16(float v) {
   return v + lane_rot4(v);
 }
 
+// Four tokens per wave; with REG four waves per workgroup (a quarter of the
+// workgroups to dispatch: 2.5 us less at T = 16384), otherwise one, whose
+// iterates then fill the LDS.
+constexpr int token_waves(bool reg) { return reg ? 4 : 1; }
+
 template <int N, bool REG>
-__global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tpad, int d, int S, int PW, int SSO,
+__global__ __launch_bounds__(64 * token_waves(REG)) void pre_bwd_token_kernel(int64_t T, int64_t Tpad, int d, int S, int PW, int SSO,
                                                            const float* __restrict__ part,
                                                            const float* __restrict__ bias, float a_pre,
                                                            float a_res, float a_post, float eps, int t_max,
@@ -358,10 +363,10 @@ __global__ __launch_bounds__(64) void pre_bwd_token_kernel(int64_t T, int64_t Tp
   constexpr int M = num_maps(N);
   constexpr int NN = N * N;
   constexpr int TW = tok_width(N);
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int q = lane >> 4;
   const int e = lane & 15;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + q;
+  const int64_t t = (static_cast<int64_t>(blockIdx.x) * token_waves(REG) + (threadIdx.x >> 6)) * 4 + q;
   const bool tv = t < T;
   const int colr = N + e;
   const int colg = (e < N) ? e : (N + NN + (e - N));
@@ -1074,8 +1079,10 @@ hipError_t launch_pre_bwd_t(const mhc_params& p, const void* X, const float* phi
   if (tblocks > 0x7FFFFFFF || kblocks_of(K) > 0x7FFFFFFF) return hipErrorInvalidValue;
   const size_t lds = static_cast<size_t>(2 * (p.t_max > 0 ? p.t_max : 1)) * 64 * sizeof(float);
   if (tblocks > 0) {
+    constexpr int TW4 = token_waves(true);
     if (p.t_max <= kRegTmax)
-      hipLaunchKernelGGL((pre_bwd_token_kernel<N, true>), dim3(static_cast<unsigned>(tblocks)), dim3(64), 0, stream,
+      hipLaunchKernelGGL((pre_bwd_token_kernel<N, true>), dim3(static_cast<unsigned>((tblocks + TW4 - 1) / TW4)),
+                         dim3(64 * TW4), 0, stream,
                          p.T, L.Tpad, p.d, L.S, L.PW, L.SSO, static_cast<const float*>(part), bias, p.alpha_pre,
                          p.alpha_res, p.alpha_post, p.eps, p.t_max, dH, tok, gT, pg);
     else

@@ -158,6 +158,18 @@ def test_backward_few_sinkhorn_passes(mhc, oracle_lib, t_max):
     _check(oracle_lib, w, got, X, Y, G, D, phi, bias, alpha, t_max=t_max)
 
 
+@pytest.mark.parametrize("t_max,dtype", [(21, synth.FP32), (40, synth.BF16)], ids=["tmax21_fp32", "tmax40_bf16"])
+def test_backward_many_sinkhorn_passes(mhc, oracle_lib, t_max, dtype):
+    """More Sinkhorn passes than the token kernel keeps in registers (20):
+    its iterates then go to LDS, one wave per workgroup."""
+    w = synth.Workload(f"bwd_tmax{t_max}", T=83, n=4, d=512, dtype=dtype, seed=960 + t_max)
+    alpha = (0.5, 1.5, 0.5)
+    X, Y, G, D, phi, bias = _inputs(w)
+    for whole in (False, True):
+        got = _gpu_bwd(mhc, w, X, Y, G, D, phi, bias, alpha, t_max=t_max, whole=whole)
+        _check(oracle_lib, w, got, X, Y, G, D, phi, bias, alpha, t_max=t_max)
+
+
 POST_FORMS = [
     # (T, n, d, dtype): d a multiple of 512 takes the tiled form when given a workspace
     (1, 4, 512, synth.BF16),
