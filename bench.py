@@ -616,11 +616,11 @@ ENTRY_KERNELS = {
                               "pre_finish_kernel<mhc::BF16, 4, false, 4>"],
     "mhc_amax": ["amax_kernel<4>"],
     "mhc_post_bwd": ["post_bwd_tile_kernel<mhc::BF16, 4, true>", "post_bwd_reduce_kernel<4>"],
-    "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 2, 1, 8, false>", "pre_bwd_token_kernel<4, true>",
+    "mhc_pre_bwd": ["pre_partial_kernel<mhc::BF16, 4, 1, 1, 8, false>", "pre_bwd_token_kernel<4, true>",
                     "pre_bwd_apply_mfma_kernel<4, false>", "reduce_grads_kernel"],
     # the whole-dX pair: mhc_post_bwd with dX NULL, then mhc_pre_bwd_ex with G
     "mhc_post_bwd_without_dX": ["post_bwd_tile_kernel<mhc::BF16, 4, false>", "post_bwd_reduce_kernel<4>"],
-    "mhc_pre_bwd_ex_with_G": ["pre_partial_kernel<mhc::BF16, 4, 2, 1, 8, false>", "pre_bwd_token_kernel<4, true>",
+    "mhc_pre_bwd_ex_with_G": ["pre_partial_kernel<mhc::BF16, 4, 1, 1, 8, false>", "pre_bwd_token_kernel<4, true>",
                               "pre_bwd_apply_mfma_kernel<4, true>", "reduce_grads_kernel"],
 }
 ENTRY_SOURCES = {

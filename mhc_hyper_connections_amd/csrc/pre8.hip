@@ -109,7 +109,7 @@ __global__ __launch_bounds__(P8_THREADS) void pre_partial8_kernel(int64_t T, int
         if constexpr (STAGE) {
           const int64_t t = tile * R + 4 * w + 2 * mb + q;
           const int64_t tt = t < T ? t : 0;
-          x[mb][q] = load_raw8<ST>(X + (tt * N + si) * d + jls);
+          x[mb][q] = load_raw8<ST, true>(X + (tt * N + si) * d + jls);   // non-temporal: 6 us less at T = 16384
         } else {
           const int64_t t = tile * R + mb * 16 + r16;
           const int64_t tt = t < T ? t : 0;
