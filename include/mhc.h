@@ -357,9 +357,10 @@ mhc_status mhc_amax(int64_t T, int32_t n, int32_t L, const float* H_stack, float
                     float* gain_fwd, float* gain_bwd, float* composite, void* stream);
 
 /* ---- mhc_gelu_half: the synthetic sublayer of the layer-stack workload ------
- * Y = 0.5 * GELU(h) = 0.5 * h * Phi(h) elementwise (exact erf form), in the
- * state dtype.  Stands in for attention / MLP so that a many-layer stack can
- * run without a GEMM; it is not part of the mHC method.
+ * Y = 0.5 * GELU(h) = 0.5 * h * Phi(h) elementwise (the erf form, with Phi
+ * evaluated as erfc(-h / sqrt 2) / 2: within 2e-5 relative of the exact value
+ * in fp32), in the state dtype.  Stands in for attention / MLP so that a
+ * many-layer stack can run without a GEMM; it is not part of the mHC method.
  *   h in [count], Y out [count]; Y may be exactly h, other overlap is an error. */
 mhc_status mhc_gelu_half(int64_t count, int32_t dtype, const void* h, void* Y, void* stream);
 

@@ -71,7 +71,36 @@ __global__ __launch_bounds__(256) void amax_kernel(int64_t T, int L, const float
   }
 }
 
-__device__ __forceinline__ float gelu_half_f(float v) { return 0.25f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+// 0.5 GELU(v) = 0.25 v (1 + erf(v / sqrt 2)) = 0.25 v erfc(u), u = -v / sqrt 2.
+// erfc by the Chebyshev-fitted formula of Press, Teukolsky, Vetterling and
+// Flannery, Numerical Recipes in C (2nd ed.), section 6.2: for z >= 0,
+// erfc(z) = t exp(-z^2 + P(t)) with t = 1 / (1 + z / 2) and P a degree-9
+// polynomial, fractional error below 1.2e-7 for every z; erfc(-z) = 2 -
+// erfc(z).  Against 1 + erff(x): no cancellation for negative v (near v = -5
+// that sum was off by up to about 4% of its value, in bf16 results too), and
+// no branch (erff takes one of two ranges per value, and a wave whose values
+// fall in both ran both: about 60 instructions a value against about 20;
+// T = 4096, d = 2560 bf16 took 12.2 us, now 10.1 us).  Evaluated in fp32 the
+// result stays within 2e-5 relative, and 3e-7 absolute, of the exact value
+// for |v| <= 12.
+__device__ __forceinline__ float gelu_half_f(float v) {
+  const float u = -v * 0.70710678118654752f;
+  const float z = fabsf(u);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  p = fmaf(p, t, -1.26551223f);
+  const float e = t * __expf(fmaf(-z, z, p));
+  const float c = (u >= 0.0f) ? e : 2.0f - e;
+  return 0.25f * v * c;
+}
 
 template <typename ST>
 __global__ __launch_bounds__(256) void gelu_half_kernel(int64_t count, const typename ST::elem* h,
