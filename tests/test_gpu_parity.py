@@ -216,6 +216,35 @@ def test_gelu_half(mhc, oracle_lib, count):
         assert_close(y, oracle_lib.gelu_half(h), *tol, what="gelu_half")
 
 
+def test_gelu_half_extremes(mhc, oracle_lib):
+    """Values far in both tails (the 60-layer stack's state reaches ~1e18),
+    where 1 + erf(h / sqrt 2) cancels for negative h, plus +-inf and NaN, which
+    propagate as in the oracle.  The oracle forms 1 + erf in double, whose
+    absolute error near erf = -1 is up to 2^-53 (from h ~ -8.3 on it returns
+    0 where the value is ~1e-19): the bound adds 0.25 |h| 2^-52 for that."""
+    big = [-1e30, -1e18, -1e4, -20.0, -12.0, -9.0, -5.5, -5.0, -4.0, -3.0, -1.0, -1e-3, -0.0, 0.0, 1e-3, 1.0, 3.0, 5.0,
+           9.0, 20.0, 1e4, 1e18, 1e30]
+    for dt in (synth.FP32, synth.BF16):
+        f = np.array(big, np.float64)
+        h = f.astype(np.float32) if dt == synth.FP32 else oracle_lib.round_bf16(f)
+        hv = h.astype(np.float64) if dt == synth.FP32 else synth.bf16_bits_to_f32(h).astype(np.float64)
+        y = to_host(mhc.gelu_half(to_device(h)))
+        yv = y.astype(np.float64) if dt == synth.FP32 else synth.bf16_bits_to_f32(y).astype(np.float64)
+        ref = oracle_lib.gelu_half(h)
+        rtol = 2e-5 if dt == synth.FP32 else 8e-3
+        bound = rtol * np.abs(ref) + 0.25 * np.abs(hv) * 2.0 ** -52 + 1e-30
+        assert np.all(np.abs(yv - ref) <= bound), (dt, hv[np.abs(yv - ref) > bound], yv[np.abs(yv - ref) > bound],
+                                                   ref[np.abs(yv - ref) > bound])
+        s = np.array([np.inf, -np.inf, np.nan], np.float64)
+        hs = s.astype(np.float32) if dt == synth.FP32 else oracle_lib.round_bf16(s)
+        ys = to_host(mhc.gelu_half(to_device(hs)))
+        ys = synth.bf16_bits_to_f32(ys) if dt == synth.BF16 else ys
+        ref = oracle_lib.gelu_half(hs)
+        assert ys[0] == np.inf and ref[0] == np.inf
+        assert np.isnan(ys[1]) and np.isnan(ref[1])      # -inf * 0 in both
+        assert np.isnan(ys[2]) and np.isnan(ref[2])
+
+
 def _stack(mhc, w, T, L):
     """L layers of pre -> 0.5 GELU -> post on the GPU; returns X_L and the maps."""
     X0 = synth.make_state(w, T)
