@@ -4,13 +4,14 @@ mhc_amax against the oracle.
 
 Shapes cover d below one 512-position slice, ragged last slices, T = 1 and T
 not a multiple of the 16-token tile, both storage types, both map forms; one
-case runs at d = 4096 with enough tokens for several persistent passes.
+case runs at d = 4096 with enough tokens for several persistent passes, and
+one at the benchmark's n = 8 shape (T = 16384, d = 4096), every token.
 """
 import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import TOL, assert_close, dname, to_device, to_host
+from gpu_helpers import TOL, assert_close, dname, for_token_chunks, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +64,31 @@ def test_n8_layer_every_token(mhc, oracle_lib, d, T, dtype, maps):
     assert_close(to_host(h), ref["h"], *TOL[(dn, "state")], what=f"{w.name} {maps} h")
     Xo_ref = oracle_lib.post(X, Y, to_host(H))
     assert_close(to_host(Xo), Xo_ref, *TOL[(dn, "state")], what=f"{w.name} {maps} X'")
+
+
+def test_n8_full_size_every_token(mhc, oracle_lib):
+    """The benchmark's n = 8 shape (T = 16384, d = 4096, bf16: 1 GiB of state,
+    64 slices of 512 positions, many persistent passes), the workloads'
+    distributions: h, H and X' of every token against the oracle."""
+    w = synth.Workload("n8_T16384_d4096", T=16384, n=8, d=4096, dtype=synth.BF16, seed=5901)
+    print(f"[parity] full size {w.name}", flush=True)
+    X, Y = synth.make_state(w), synth.make_sublayer_out(w)
+    phi, bias = synth.make_params(w)
+    dX, dY = to_device(X), to_device(Y)
+    h, H = mhc.pre(dX, to_device(phi), to_device(bias), alpha=w.alpha, eps=w.eps, t_max=w.t_max)
+    Xo = mhc.post(dX, dY, H)
+    torch.cuda.synchronize()
+    Hh, hh, Xoh = to_host(H), to_host(h), to_host(Xo)
+    del dX, dY, h, H, Xo
+
+    def cmp(tok):
+        ref = oracle_lib.pre(X, phi, bias, w.alpha, eps=w.eps, t_max=w.t_max, tokens=tok)
+        assert_close(Hh[tok], ref["H"], *TOL[("bf16", "maps")], what=f"{w.name} H, tokens {tok[0]}..")
+        assert_close(hh[tok], ref["h"], *TOL[("bf16", "state")], what=f"{w.name} h, tokens {tok[0]}..")
+        Xo_ref = oracle_lib.post(X, Y, ref["H"].astype(np.float32), tokens=tok)
+        assert_close(Xoh[tok], Xo_ref, *TOL[("bf16", "state")], what=f"{w.name} X', tokens {tok[0]}..")
+
+    for_token_chunks(cmp, w.T)
 
 
 def test_n8_sinkhorn_is_doubly_stochastic(mhc, oracle_lib):
