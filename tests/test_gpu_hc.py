@@ -48,6 +48,28 @@ def test_hc_maps_every_token(mhc, oracle_lib, name, changes, alpha):
     assert_close(to_host(h), ref["h"], *TOL[(dn, "state")], what=f"{w.name} HC h")
 
 
+def test_hc_full_size_every_token(mhc, oracle_lib):
+    """The HC maps at the headline shape (T = 16384, d = 4096: MHC_PRE_AUTO's
+    single pass, 64 tiles per team), h and H of every token against the
+    oracle, threaded over token chunks."""
+    w = synth.WORKLOADS["layer_bf16_T16384_d4096"]
+    print(f"[parity] full size HC {w.name}", flush=True)
+    X = synth.make_state(w)
+    phi, bias = synth.make_params(w)
+    h, H = mhc.pre(to_device(X), to_device(phi), to_device(bias), alpha=w.alpha, eps=w.eps, maps=mhc.MAPS_HC)
+    torch.cuda.synchronize()
+    Hh, hh = to_host(H), to_host(h)
+    rtol, atol = TOL[("bf16", "maps")]
+    atol = atol * max(1.0, 4.0 * max(abs(a) for a in w.alpha))
+
+    def cmp(tok):
+        ref = oracle_lib.pre_hc(X, phi, bias, w.alpha, eps=w.eps, tokens=tok)
+        assert_close(Hh[tok], ref["H"], rtol, atol, what=f"{w.name} HC maps, tokens {tok[0]}..")
+        assert_close(hh[tok], ref["h"], *TOL[("bf16", "state")], what=f"{w.name} HC h, tokens {tok[0]}..")
+
+    for_token_chunks(cmp, w.T)
+
+
 def test_hc_forms_agree(mhc):
     """HC maps through both forms of mhc_pre agree to rounding, and differ
     from mHC's on the same inputs."""
