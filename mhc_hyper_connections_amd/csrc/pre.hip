@@ -127,7 +127,8 @@ __global__ __launch_bounds__(PWV * 64) void pre_partial_kernel(int64_t T, int d,
   // are dropped below).  The backward's pass (WITH_D) reads X and D
   // non-temporally: the apply pass reads them again only after the token
   // pass, and at T = 16384, n = 4, d = 4096 that took 12 us off mhc_pre_bwd
-  // (cached loads measured no faster in the forward's modes).
+  // (in the forward's modes non-temporal loads measured no faster, so they
+  // stay cached).
   const int jl = STAGE ? (jvl ? jl0 : 0) : (jv ? j0 : 0);
   auto load_tile = [&](int64_t tile, Raw8<ST> (&x)[MB][NX], f32x4 (&hv)[MB][HV]) {
 #pragma unroll
