@@ -150,6 +150,51 @@ __global__ __launch_bounds__(256) void post_bwd_kernel(int64_t T, int d, const t
   }
 }
 
+// The NA sums of v[0..NA) over a wave's 64 lanes by a transposed butterfly:
+// in each exchange (lane distance 32, 16, ..., 1) a lane keeps half of the
+// values it still carries (the upper half if its lane bit is set), adds its
+// partner's copy of that half, and hands over the other half; 22 exchanges
+// for NA = 20 instead of 6 NA.  Every value still takes the plain butterfly's
+// additions in its order, so the sums are bitwise those of reducing each
+// value on its own.  Returns the lane's sum and sets a to its index, or -1
+// for lanes left with padding.
+template <int NA>
+__device__ __forceinline__ float wave_sums_transposed(const float (&v)[NA], int lane, int& a) {
+  constexpr int C0 = NA, C1 = (C0 + 1) / 2, C2 = (C1 + 1) / 2, C3 = (C2 + 1) / 2, C4 = (C3 + 1) / 2,
+                C5 = (C4 + 1) / 2, C6 = (C5 + 1) / 2;
+  static_assert(C6 == 1, "at most 64 values");
+  float w0[C0];
+#pragma unroll
+  for (int k = 0; k < C0; ++k) w0[k] = v[k];
+  float w1[C1], w2[C2], w3[C3], w4[C4], w5[C5], w6[C6];
+  auto stage = [&](auto& src, auto& dst, int c, int h, int mask) {
+    const bool up = (lane & mask) != 0;
+#pragma unroll
+    for (int k = 0; k < h; ++k) {
+      const float lo = src[k];
+      const float hi = (h + k < c) ? src[h + k] : 0.0f;
+      dst[k] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, mask);
+    }
+  };
+  stage(w0, w1, C0, C1, 32);
+  stage(w1, w2, C1, C2, 16);
+  stage(w2, w3, C2, C3, 8);
+  stage(w3, w4, C3, C4, 4);
+  stage(w4, w5, C4, C5, 2);
+  stage(w5, w6, C5, C6, 1);
+  // The lane's slot back through the stages: an upper half adds its offset.
+  int i = 0;
+  bool ok = true;
+  const int cs[7] = {C0, C1, C2, C3, C4, C5, C6};
+#pragma unroll
+  for (int j = 5; j >= 0; --j) {                 // stage j exchanged over lane bit 5 - j
+    if (lane & (1 << (5 - j))) i += cs[j + 1];
+    ok = ok && i < cs[j];
+  }
+  a = ok ? i : -1;
+  return w6[0];
+}
+
 // The tiled form (d a multiple of 512, with a workspace): a workgroup covers
 // 4 tokens x 512 values of d, one token per wave, and consecutive workgroups
 // walk along d, the order in which MI355X streams fastest (as for mhc_post).
@@ -240,19 +285,9 @@ __global__ __launch_bounds__(256) void post_bwd_tile_kernel(int64_t T, int d8, i
     }
     store8<ST, true>(dY + t * d + off, o);
   }
-#pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    float v = acc[a];
-#pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) v += __shfl_xor(v, sh);
-    acc[a] = v;
-  }
-  if (lane < NA) {
-    float v = acc[0];
-#pragma unroll
-    for (int a = 1; a < NA; ++a) v = (lane == a) ? acc[a] : v;
-    part[(t * nslice + slice) * NA + lane] = v;
-  }
+  int a;
+  const float v = wave_sums_transposed<NA>(acc, lane, a);
+  if (a >= 0) part[(t * nslice + slice) * NA + a] = v;
 }
 
 // dH[t][n + a] = sum over slices, in slice order, of part[t][slice][a].
